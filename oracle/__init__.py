@@ -1,0 +1,190 @@
+"""ctypes wrapper of the plain CPU oracle (``moe_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg use this module.  The GPU package never imports it, and it
+imports nothing from the GPU package.  Inputs come from ``moe_synth``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+CFLAGS = ["-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
+
+
+def build() -> str:
+    """Compile the oracle with gcc (no fast-math, no FMA contraction)."""
+    tmp = _LIB + ".tmp"
+    subprocess.check_call(["gcc", *CFLAGS, "-o", tmp, _SRC, "-lm"])
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        _lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I = ctypes.c_int
+        _lib.orc_layout.argtypes = [I, I, I, P]
+        _lib.orc_dequant.argtypes = [P, P, I, I, I, P]
+        _lib.orc_router_logits.argtypes = [P, P, I, I, I, P]
+        _lib.orc_topk.argtypes = [P, I, I, I, P, P]
+        _lib.orc_build_csr.argtypes = [P, P, I, I, I, P, P, P, P]
+        _lib.orc_residency.argtypes = [P, I, I, P]
+        _lib.orc_expert_rows.argtypes = [P, I, I, I, P, P, I, P]
+        _lib.orc_shared.argtypes = [P, I, I, I, P, I, P, P]
+        _lib.orc_block.argtypes = [P, P, I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P]
+        _lib.orc_tokens_bruteforce.argtypes = [P, P, I, I, I, I, I, I, I, P, P, P, P, I, I, P]
+        for f in ("orc_layout", "orc_router_logits", "orc_topk", "orc_build_csr", "orc_expert_rows",
+                  "orc_shared", "orc_block", "orc_tokens_bruteforce", "orc_max_threads"):
+            getattr(_lib, f).restype = ctypes.c_int
+    return _lib
+
+
+def _p(a: Optional[np.ndarray]):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle inputs must be C-contiguous"
+    return a.ctypes.data
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise ValueError(f"oracle {what}: invalid input")
+
+
+def max_threads() -> int:
+    return lib().orc_max_threads()
+
+
+def layout(hidden: int, inter: int, group: int) -> dict:
+    out = np.zeros(7, dtype=np.uint64)
+    _check(lib().orc_layout(hidden, inter, group, _p(out)), "layout")
+    keys = ["gate_w", "gate_sb", "up_w", "up_sb", "down_w", "down_sb", "stride"]
+    return {k: int(v) for k, v in zip(keys, out)}
+
+
+def dequant(record: np.ndarray, matrix: str, hidden: int, inter: int, group: int) -> np.ndarray:
+    """Decode matrix 'gate' | 'up' | 'down' of one record to float64 [N, K]."""
+    L = layout(hidden, inter, group)
+    N, K = (inter, hidden) if matrix in ("gate", "up") else (hidden, inter)
+    rec = np.ascontiguousarray(record, dtype=np.uint8)
+    W = np.empty((N, K), dtype=np.float64)
+    base = rec.ctypes.data
+    lib().orc_dequant(base + L[matrix + "_w"], base + L[matrix + "_sb"], N, K, group, _p(W))
+    return W
+
+
+def router_logits(x: np.ndarray, w_router: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    w = np.ascontiguousarray(w_router, dtype=np.float32)
+    t, h = x.shape
+    E = w.shape[0]
+    out = np.empty((t, E), dtype=np.float32)
+    _check(lib().orc_router_logits(_p(x), _p(w), t, h, E, _p(out)), "router_logits")
+    return out
+
+
+def topk(logits: np.ndarray, k: int):
+    lg = np.ascontiguousarray(logits, dtype=np.float32)
+    t, E = lg.shape
+    idx = np.empty((t, k), dtype=np.uint32)
+    w = np.empty((t, k), dtype=np.float32)
+    _check(lib().orc_topk(_p(lg), t, E, k, _p(idx), _p(w)), "topk")
+    return idx, w
+
+
+def build_csr(idx: np.ndarray, wts: np.ndarray, E: int):
+    idx = np.ascontiguousarray(idx, dtype=np.uint32)
+    wts = np.ascontiguousarray(wts, dtype=np.float32)
+    t, k = idx.shape
+    offsets = np.empty(E + 1, dtype=np.uint32)
+    rows = np.empty(t * k, dtype=np.uint32)
+    cw = np.empty(t * k, dtype=np.float32)
+    pos = np.empty(t * k, dtype=np.uint32)
+    _check(lib().orc_build_csr(_p(idx), _p(wts), t, k, E, _p(offsets), _p(rows), _p(cw), _p(pos)), "build_csr")
+    return offsets, rows, cw, pos
+
+
+def residency(offsets: np.ndarray, n_keep: int) -> np.ndarray:
+    offsets = np.ascontiguousarray(offsets, dtype=np.uint32)
+    E = offsets.size - 1
+    keep = np.empty(E, dtype=np.uint8)
+    lib().orc_residency(_p(offsets), E, n_keep, _p(keep))
+    return keep.astype(bool)
+
+
+def expert_rows(record: np.ndarray, hidden: int, inter: int, group: int, x: np.ndarray,
+                rows: Sequence[int]) -> np.ndarray:
+    rec = np.ascontiguousarray(record, dtype=np.uint8)
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    r = np.ascontiguousarray(rows, dtype=np.uint32)
+    y = np.empty((r.size, hidden), dtype=np.float64)
+    _check(lib().orc_expert_rows(_p(rec), hidden, inter, group, _p(x), _p(r), r.size, _p(y)), "expert_rows")
+    return y
+
+
+def shared(record: np.ndarray, hidden: int, inter: int, group: int, x: np.ndarray,
+           gate_w: Optional[np.ndarray] = None) -> np.ndarray:
+    rec = np.ascontiguousarray(record, dtype=np.uint8)
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    g = None if gate_w is None else np.ascontiguousarray(gate_w, dtype=np.uint16)
+    ys = np.empty((x.shape[0], hidden), dtype=np.float64)
+    _check(lib().orc_shared(_p(rec), hidden, inter, group, _p(x), x.shape[0], _p(g), _p(ys)), "shared")
+    return ys
+
+
+def _record_ptrs(records: np.ndarray):
+    recs = np.ascontiguousarray(records, dtype=np.uint8)
+    ptrs = (ctypes.c_void_p * recs.shape[0])(*[recs.ctypes.data + e * recs.shape[1] for e in range(recs.shape[0])])
+    return recs, ptrs
+
+
+def block(wl, shared_expert: bool = True):
+    """Whole block through the grouped path. Returns dict of outputs."""
+    c = wl.cfg
+    x = np.ascontiguousarray(wl.x, dtype=np.uint16)
+    t = x.shape[0]
+    recs, ptrs = _record_ptrs(wl.records)
+    out = np.empty((t, c.hidden), dtype=np.float32)
+    idx = np.empty((t, c.k), dtype=np.uint32)
+    w = np.empty((t, c.k), dtype=np.float32)
+    offsets = np.empty(c.experts + 1, dtype=np.uint32)
+    rows = np.empty(t * c.k, dtype=np.uint32)
+    cw = np.empty(t * c.k, dtype=np.float32)
+    pos = np.empty(t * c.k, dtype=np.uint32)
+    srec = np.ascontiguousarray(wl.shared_record) if shared_expert else None
+    gate = None if wl.gate_w is None else np.ascontiguousarray(wl.gate_w, dtype=np.uint16)
+    wr = np.ascontiguousarray(wl.w_router, dtype=np.float32)
+    _check(lib().orc_block(_p(x), _p(wr), t, c.hidden, c.inter, c.inter_shared, c.experts, c.k, c.group,
+                           ptrs, _p(srec), _p(gate), _p(out), _p(idx), _p(w), _p(offsets), _p(rows),
+                           _p(cw), _p(pos)), "block")
+    return dict(out=out, topk_idx=idx, topk_w=w, offsets=offsets, csr_rows=rows, csr_w=cw, csr_pos=pos)
+
+
+def tokens_bruteforce(wl, sample: Sequence[int], order: int = 0, shared_expert: bool = True) -> np.ndarray:
+    """Per-token outputs (float64) of the sample rows, computed without grouping."""
+    c = wl.cfg
+    x = np.ascontiguousarray(wl.x, dtype=np.uint16)
+    recs, ptrs = _record_ptrs(wl.records)
+    s = np.ascontiguousarray(sample, dtype=np.int32)
+    out = np.empty((s.size, c.hidden), dtype=np.float64)
+    srec = np.ascontiguousarray(wl.shared_record) if shared_expert else None
+    gate = None if wl.gate_w is None else np.ascontiguousarray(wl.gate_w, dtype=np.uint16)
+    wr = np.ascontiguousarray(wl.w_router, dtype=np.float32)
+    _check(lib().orc_tokens_bruteforce(_p(x), _p(wr), x.shape[0], c.hidden, c.inter, c.inter_shared,
+                                       c.experts, c.k, c.group, ptrs, _p(srec), _p(gate), _p(s), s.size,
+                                       order, _p(out)), "tokens_bruteforce")
+    return out

@@ -1,0 +1,373 @@
+"""Pins of the CPU oracle against facts fixed outside it.
+
+Each test ties one oracle function to a closed form, a library routine
+(numpy / torch float64), an invariant the pages state, or a hand-derived
+fixture, so that a plausible slip (a dropped term, a wrong sign or index, a
+transposed operand, a wrong order) fails at least one of them.
+"""
+import json
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import moe_synth as ms
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+U = 2.0 ** -24
+
+
+def bf16(a):
+    return ms.f32_to_bf16_bits(np.asarray(a, dtype=np.float32))
+
+
+def xf(xbits):
+    return ms.bf16_bits_to_f32(xbits).astype(np.float64)
+
+
+# ------------------------------------------------------------------ record format
+
+def test_layout_matches_generator_and_sizes(orc):
+    for h, I, G in [(256, 128, 32), (2048, 768, 64), (4096, 1536, 64), (512, 192, 32)]:
+        a = orc.layout(h, I, G)
+        b = ms.layout(h, I, G)
+        for k, v in a.items():
+            assert v == getattr(b, k), (h, I, G, k)
+    # record bytes R = 3*h*I*(1/2 + 4/G), already 4096-aligned at these shapes
+    assert orc.layout(2048, 768, 64)["stride"] == 2_654_208
+    assert orc.layout(4096, 1536, 64)["stride"] == 10_616_832
+    assert orc.layout(256, 128, 32)["stride"] == 61_440
+
+
+def test_dequant_codes_only(orc):
+    """scale = 1, bias = 0 -> W = q exactly (pins code positions)."""
+    h, I, G = 256, 128, 32
+    L = ms.layout(h, I, G)
+    g = np.random.default_rng(1)
+    mats = {}
+    for m in ("gate", "up", "down"):
+        N, K = ms.matrix_shape(L, m)
+        mats[m] = (g.integers(0, 16, (N, K)), np.ones((N, K // G)), np.zeros((N, K // G)))
+    rec = ms.pack_record(L, mats)
+    for m in ("gate", "up", "down"):
+        W = orc.dequant(rec, m, h, I, G)
+        assert np.array_equal(W, mats[m][0].astype(np.float64)), m
+
+
+def test_dequant_hand_placed_byte(orc):
+    """One byte written by hand from the stated format decodes to the stated positions.
+
+    Tile (ob=1, kb=2) of gate (K = h = 256 -> 4 tiles per row block), lane 33,
+    word 2, byte 2 = 0x5A: word 2 holds codes c = 16..23; byte 2 holds bits
+    16..23 = code c%8=1 (bits 16-19) and c%8=3 (bits 20-23).  So row
+    32*1 + 33%32 = 33, columns 64*2 + 32 + 17 = 177 (q = 0xA) and 179 (q = 5).
+    """
+    h, I, G = 256, 128, 64
+    L = ms.layout(h, I, G)
+    rec = np.zeros(L.stride, dtype=np.uint8)
+    tile = 1 * (h // 64) + 2
+    rec[L.gate_w + tile * 1024 + 16 * 33 + 4 * 2 + 2] = 0x5A
+    # scale 1.0 (0x3C00), bias 0 for every entry of the gate sb section
+    nent = I * h // G
+    sb = np.zeros(nent, dtype=np.uint32) | 0x3C00
+    rec[L.gate_sb: L.gate_sb + 4 * nent] = sb.astype("<u4").view(np.uint8)
+    W = orc.dequant(rec, "gate", h, I, G)
+    nz = np.argwhere(W != 0)
+    assert nz.tolist() == [[33, 177], [33, 179]]
+    assert W[33, 177] == 10.0 and W[33, 179] == 5.0
+
+
+@pytest.mark.parametrize("G", [32, 64])
+def test_dequant_scale_bias_per_group(orc, G):
+    """q = 0 -> W = bias of the group; dyadic scale 2^-4 with codes -> exact s*q + b."""
+    h, I = 256, 64
+    L = ms.layout(h, I, G)
+    g = np.random.default_rng(2)
+    mats = {}
+    for m in ("gate", "up", "down"):
+        N, K = ms.matrix_shape(L, m)
+        s = np.full((N, K // G), 2.0 ** -4)
+        b = g.integers(-64, 64, (N, K // G)) * 2.0 ** -8
+        q = np.zeros((N, K), dtype=np.int64) if m == "gate" else g.integers(0, 16, (N, K))
+        mats[m] = (q, s, b)
+    rec = ms.pack_record(L, mats)
+    for m in ("gate", "up", "down"):
+        q, s, b = mats[m]
+        W = orc.dequant(rec, m, h, I, G)
+        expect = np.repeat(b, G, axis=1) + np.repeat(s, G, axis=1) * q
+        assert np.array_equal(W, expect), m
+    # q = 0: every column of a group equals that group's bias
+    Wg = orc.dequant(rec, "gate", h, I, G)
+    assert np.array_equal(Wg[:, ::G], mats["gate"][2])
+
+
+def test_f16_decode_special_values(orc):
+    """fp16 subnormal, negative, and max decode exactly (scale = value, q = 1, bias = 0)."""
+    h, I, G = 64, 64, 64
+    L = ms.layout(h, I, G)
+    vals = np.array([2.0 ** -24, -2.0 ** -14, 65504.0, -0.5, 1.0 + 2.0 ** -10], dtype=np.float16)
+    mats = {}
+    for m in ("gate", "up", "down"):
+        N, K = ms.matrix_shape(L, m)
+        s = np.resize(vals, (N, K // G)).astype(np.float16)
+        mats[m] = (np.ones((N, K), dtype=np.int64), s, np.zeros((N, K // G), dtype=np.float16))
+    rec = ms.pack_record(L, mats)
+    W = orc.dequant(rec, "up", h, I, G)
+    assert np.array_equal(W[:, 0], mats["up"][1][:, 0].astype(np.float64))
+
+
+# ------------------------------------------------------------------ router
+
+def test_router_golden_order(orc):
+    with open(os.path.join(GOLDEN, "router_order.json")) as f:
+        cases = json.load(f)["cases"]
+    h = 256
+    x = bf16(np.ones((1, h)))
+    for c in cases:
+        w = np.zeros((1, h), dtype=np.float32)
+        for i, v in c["w"].items():
+            w[0, int(i)] = v
+        got = orc.router_logits(x, w)[0, 0]
+        assert got == c["canonical"] and not np.signbit(got), c["name"]
+        # the fixture's 'sequential' value really is the left-to-right float32 sum
+        acc = np.float32(0)
+        for i in range(h):
+            acc = np.float32(acc + w[0, i])
+        assert acc == c["sequential"], c["name"]
+
+
+def test_router_zero_and_one_hot(orc):
+    h, E = 512, 7
+    g = np.random.default_rng(3)
+    w = g.normal(0, 0.02, (E, h)).astype(np.float32)
+    lz = orc.router_logits(bf16(g.normal(0, 1, (3, h))), np.zeros((E, h), np.float32))
+    assert np.all(lz == 0) and not np.any(np.signbit(lz))
+    for i in (0, 3, 255, 256, 511):
+        x = np.zeros((1, h), np.float32)
+        x[0, i] = 1.0
+        assert np.array_equal(orc.router_logits(bf16(x), w)[0], w[:, i])
+
+
+def test_router_exact_on_dyadic_inputs(orc):
+    """Small integers times multiples of 2^-4 sum exactly in any order: equals the float64 matmul."""
+    h, E, t = 1024, 9, 5
+    g = np.random.default_rng(4)
+    x = g.integers(-8, 9, (t, h)).astype(np.float32)
+    w = (g.integers(-16, 17, (E, h)) / 16.0).astype(np.float32)
+    got = orc.router_logits(bf16(x), w)
+    assert np.array_equal(got.astype(np.float64), x.astype(np.float64) @ w.T.astype(np.float64))
+
+
+@pytest.mark.parametrize("h", [256, 2048, 4096])
+def test_router_error_bound(orc, h):
+    """|fp32 canonical - exact| <= (h/64 + 6) * 2^-24 * sum|x_i w_i| (fmaf chains of h/64, 6 tree levels)."""
+    g = np.random.default_rng(h)
+    xb = bf16(g.normal(0, 1, (8, h)))
+    w = g.normal(0, 0.02, (16, h)).astype(np.float32)
+    got = orc.router_logits(xb, w).astype(np.float64)
+    x = xf(xb)
+    exact = x @ w.T.astype(np.float64)
+    bound = (h / 64 + 6) * U * (np.abs(x) @ np.abs(w.T.astype(np.float64))) * 1.0001
+    assert np.all(np.abs(got - exact) <= bound)
+
+
+# ------------------------------------------------------------------ top-k
+
+def ref_topk(lg, k):
+    """Library stable sort: descending logit, ties to lower id."""
+    order = np.argsort(-lg.astype(np.float64), axis=1, kind="stable")
+    return order[:, :k]
+
+
+def test_topk_matches_stable_sort(orc):
+    g = np.random.default_rng(5)
+    lg = g.normal(0, 1, (200, 64)).astype(np.float32)
+    lg[::7, 3] = lg[::7, 10]          # exact ties
+    lg[::11, 5] = -0.0
+    lg[::11, 6] = 0.0                 # -0 vs +0 tie
+    for k in (1, 2, 8, 64):
+        idx, w = orc.topk(lg, k)
+        assert np.array_equal(idx, ref_topk(lg, k))
+        assert np.all(np.abs(w.astype(np.float64).sum(1) - 1) <= k * U * 2)
+
+
+def test_topk_ties_and_special_k(orc):
+    E = 12
+    idx, w = orc.topk(np.zeros((3, E), np.float32), 4)
+    assert np.array_equal(idx, np.tile(np.arange(4), (3, 1)))
+    assert np.all(w == np.float32(0.25))
+    g = np.random.default_rng(6)
+    lg = g.normal(0, 2, (50, E)).astype(np.float32)
+    idx, w = orc.topk(lg, E)
+    assert all(sorted(r) == list(range(E)) for r in idx.tolist())
+    idx1, w1 = orc.topk(lg, 1)
+    assert np.all(w1 == 1.0)
+    # k = 2 closed form: w1 = 1 / (1 + exp(l2 - l1))
+    idx2, w2 = orc.topk(lg, 2)
+    l1 = lg[np.arange(50), idx2[:, 0]].astype(np.float64)
+    l2 = lg[np.arange(50), idx2[:, 1]].astype(np.float64)
+    assert np.allclose(w2[:, 0], 1 / (1 + np.exp(l2 - l1)), rtol=0, atol=1e-7)
+
+
+def test_topk_is_softmax_then_renormalise(orc):
+    """Equals torch softmax over all E (float64), top-k, divided by the selected mass."""
+    g = np.random.default_rng(7)
+    lg = g.normal(0, 1.5, (40, 32)).astype(np.float32)
+    idx, w = orc.topk(lg, 6)
+    p = torch.softmax(torch.from_numpy(lg.astype(np.float64)), dim=1).numpy()
+    sel = np.take_along_axis(p, idx.astype(np.int64), 1)
+    assert np.allclose(w, sel / sel.sum(1, keepdims=True), rtol=0, atol=2e-7)
+
+
+# ------------------------------------------------------------------ grouping
+
+def check_csr_invariants(idx, w, E, offsets, rows, cw, pos):
+    t, k = idx.shape
+    counts = np.diff(offsets.astype(np.int64))
+    assert offsets[0] == 0 and offsets[-1] == t * k and np.all(counts >= 0)
+    assert np.array_equal(np.bincount(rows, minlength=t), np.full(t, k))     # each row exactly k times
+    for e in range(E):
+        seg = rows[offsets[e]:offsets[e + 1]]
+        assert np.all(np.diff(seg.astype(np.int64)) > 0)                      # stable, distinct
+        assert np.array_equal(np.sort(seg), np.nonzero((idx == e).any(1))[0])
+    flat = idx.reshape(-1)
+    assert np.array_equal(rows[pos], np.repeat(np.arange(t), k))             # inverse map
+    assert np.array_equal(np.searchsorted(offsets, pos, side="right") - 1, flat)
+    assert np.array_equal(cw[pos], w.reshape(-1))
+
+
+def test_csr_matches_stable_sort_and_invariants(orc):
+    g = np.random.default_rng(8)
+    for t, E, k in [(1, 4, 2), (33, 16, 3), (300, 64, 8), (64, 8, 8)]:
+        lg = g.normal(0, 1, (t, E)).astype(np.float32)
+        idx, w = orc.topk(lg, k)
+        offsets, rows, cw, pos = orc.build_csr(idx, w, E)
+        check_csr_invariants(idx, w, E, offsets, rows, cw, pos)
+        flat = idx.reshape(-1).astype(np.int64)
+        order = np.argsort(flat, kind="stable")       # library stable sort of (e, r)
+        assert np.array_equal(rows, order // k)
+        assert np.array_equal(cw, w.reshape(-1)[order])
+
+
+def test_residency_stable_by_count(orc):
+    offsets = np.cumsum([0, 5, 0, 7, 5, 1, 7, 0, 2]).astype(np.uint32)
+    keep = orc.residency(offsets, 3)
+    counts = np.diff(offsets)
+    ranked = sorted([e for e in range(8) if counts[e]], key=lambda e: -counts[e])
+    assert set(np.nonzero(keep)[0]) == set(ranked[:3]) == {2, 5, 0}
+
+
+# ------------------------------------------------------------------ expert FFN and block
+
+def torch_swiglu(orc, rec, h, I, G, x64):
+    Wg = torch.from_numpy(orc.dequant(rec, "gate", h, I, G))
+    Wu = torch.from_numpy(orc.dequant(rec, "up", h, I, G))
+    Wd = torch.from_numpy(orc.dequant(rec, "down", h, I, G))
+    X = torch.from_numpy(x64)
+    a = torch.nn.functional.silu(X @ Wg.T) * (X @ Wu.T)
+    return (a @ Wd.T).numpy()
+
+
+def test_expert_ffn_is_textbook_swiglu(orc):
+    wl = ms.small_case(0, 24, 256, 192, 1, 1, 32, centred=True)
+    y = orc.expert_rows(wl.records[0], 256, 192, 32, wl.x, list(range(24)))
+    ref = torch_swiglu(orc, wl.records[0], 256, 192, 32, xf(wl.x))
+    assert np.max(np.abs(y - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def test_zero_gate_gives_zero_output(orc):
+    h, I, G = 128, 64, 64
+    L = ms.layout(h, I, G)
+    g = np.random.default_rng(9)
+    mats = {}
+    for m in ("gate", "up", "down"):
+        N, K = ms.matrix_shape(L, m)
+        z = (m == "gate")
+        mats[m] = (g.integers(0, 16, (N, K)), np.zeros((N, K // G)) if z else g.uniform(0.005, 0.02, (N, K // G)),
+                   np.zeros((N, K // G)) if z else g.normal(0, 0.01, (N, K // G)))
+    rec = ms.pack_record(L, mats)
+    x = bf16(g.normal(0, 1, (4, h)))
+    assert np.all(orc.expert_rows(rec, h, I, G, x, [0, 1, 2, 3]) == 0)
+
+
+def test_shared_expert_and_gate(orc):
+    wl = ms.small_case(1, 12, 256, 128, 2, 1, 64, centred=True)
+    ref = torch_swiglu(orc, wl.shared_record, 256, 128, 64, xf(wl.x))
+    ys = orc.shared(wl.shared_record, 256, 128, 64, wl.x)
+    assert np.max(np.abs(ys - ref)) <= 1e-12 * np.max(np.abs(ref))
+    half = orc.shared(wl.shared_record, 256, 128, 64, wl.x, gate_w=np.zeros(256, np.uint16))
+    assert np.array_equal(half, 0.5 * ys)                       # sigmoid(0) = 1/2 exactly
+    gw = bf16(np.random.default_rng(10).normal(0, 0.05, 256))
+    gated = orc.shared(wl.shared_record, 256, 128, 64, wl.x, gate_w=gw)
+    z = xf(wl.x) @ xf(gw)
+    assert np.allclose(gated, ys * torch.sigmoid(torch.from_numpy(z)).numpy()[:, None], rtol=1e-12, atol=0)
+
+
+@pytest.mark.parametrize("centred", [False, True])
+def test_block_grouped_equals_bruteforce(orc, centred):
+    """Grouped path == per-token sum in ascending expert id (bitwise after rounding); slot order within 1e-12."""
+    wl = ms.small_case(2, 40, 256, 128, 8, 3, 32, centred=centred)
+    r = orc.block(wl)
+    check_csr_invariants(r["topk_idx"], r["topk_w"], 8, r["offsets"], r["csr_rows"], r["csr_w"], r["csr_pos"])
+    bf = orc.tokens_bruteforce(wl, list(range(40)), order=0)
+    assert np.array_equal(bf.astype(np.float32), r["out"])
+    bf1 = orc.tokens_bruteforce(wl, list(range(40)), order=1)
+    assert np.max(np.abs(bf1 - bf)) <= 1e-12 * np.max(np.abs(bf))
+    # routing outputs of the block equal the separate calls
+    lg = orc.router_logits(wl.x, wl.w_router)
+    idx, w = orc.topk(lg, 3)
+    assert np.array_equal(idx, r["topk_idx"]) and np.array_equal(w, r["topk_w"])
+
+
+def test_dense_limit_is_softmax_mixture(orc):
+    """k = E: out = shared + sum_e softmax(logits)_e * FFN_e(x), with torch float64 library ops."""
+    E, h, I, G, t = 4, 256, 64, 64, 6
+    wl = ms.small_case(3, t, h, I, E, E, G, centred=True)
+    r = orc.block(wl)
+    lg = torch.from_numpy(orc.router_logits(wl.x, wl.w_router).astype(np.float64))
+    p = torch.softmax(lg, dim=1).numpy()
+    ref = torch_swiglu(orc, wl.shared_record, h, I, G, xf(wl.x))
+    for e in range(E):
+        ref = ref + p[:, e:e + 1] * torch_swiglu(orc, wl.records[e], h, I, G, xf(wl.x))
+    err = np.max(np.abs(r["out"] - ref))
+    assert err <= 1e-6 * np.max(np.abs(ref))
+
+
+def test_block_without_shared_and_k1(orc):
+    """k = 1, no shared expert: each row's output is exactly its single expert's FFN (weight 1)."""
+    wl = ms.small_case(4, 20, 256, 64, 5, 1, 64)
+    r = orc.block(wl, shared_expert=False)
+    assert np.all(r["topk_w"] == 1.0)
+    for e in range(5):
+        rows = np.nonzero(r["topk_idx"][:, 0] == e)[0]
+        if rows.size:
+            y = orc.expert_rows(wl.records[e], 256, 64, 64, wl.x, rows)
+            assert np.array_equal(r["out"][rows], y.astype(np.float32))
+
+
+def test_thread_count_does_not_change_bits(tmp_path):
+    code = (
+        "import sys, numpy as np, moe_synth as ms, oracle\n"
+        "wl = ms.small_case(5, 64, 512, 128, 16, 4, 64)\n"
+        "r = oracle.block(wl)\n"
+        "np.save(sys.argv[1], np.concatenate([r['out'].view(np.uint32).ravel(), r['csr_rows'], r['topk_w'].view(np.uint32).ravel()]))\n"
+    )
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    outs = []
+    for n in (1, 3, 8):
+        p = tmp_path / f"o{n}.npy"
+        env = dict(os.environ, OMP_NUM_THREADS=str(n), PYTHONPATH=root)
+        subprocess.check_call([sys.executable, "-c", code, str(p)], env=env, cwd=root)
+        outs.append(np.load(p))
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])
+
+
+def test_generator_is_reproducible():
+    with open(os.path.join(GOLDEN, "input_hashes.json")) as f:
+        want = json.load(f)["hashes"]
+    for name in ("tiny", "mid"):
+        assert ms.make_workload(name).content_hash() == want[name], name

@@ -1,0 +1,208 @@
+"""Benchmark of the routed-expert MoE prefill block on one MI355X.
+
+One step = one whole block over one chunk: moe_shared -> moe_route ->
+moe_build_csr -> moe_prefill_experts, on inputs already resident in HBM.
+Default workload: the full prefill chunk (t = 4096 rows, hidden 2048, expert
+inter 768, 128 experts, top-8, shared expert inter 768, 4-bit group-64
+weights, Zipf(1.1) expert popularity).  Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config full|mid|decode|decode1|large|tiny]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "MoE-layer prefill tokens/sec at t=4096; % of bf16 MFMA / HBM roofline"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mixture_experts_prefill_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic(cfg, t, counts):
+    """FLOPs and bytes the method itself must do (no padding, no intermediates)."""
+    import numpy as np
+
+    h, I, Is, E, k = cfg.hidden, cfg.inter, cfg.inter_shared, cfg.experts, cfg.k
+    import moe_synth as ms
+
+    R = ms.layout(h, I, cfg.group).stride
+    Rs = ms.layout(h, Is, cfg.group).stride
+    touched = int((np.asarray(counts) > 0).sum())
+    return dict(
+        flop_gateup=4.0 * t * k * h * I,
+        flop_down=2.0 * t * k * h * I,
+        flop_shared=6.0 * t * h * Is,
+        flop_router=2.0 * t * h * E,
+        bytes_total=touched * R + Rs + 4.0 * E * h + 2.0 * t * h + 4.0 * t * h,
+        touched=touched,
+    )
+
+
+def traffic_for(kernel_key: str):
+    """HBM bytes per launch from the committed counter runs, if they match this build."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    ent = data.get(kernel_key)
+    if not ent or ent.get("source_hash") != source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg_name: str, rows: int):
+    """The oracle, as it stands, on the first `rows` rows of the same workload."""
+    import dataclasses
+
+    import moe_synth as ms
+    import oracle
+
+    wl = ms.make_workload(cfg_name)
+    wl = dataclasses.replace(wl, x=wl.x[:rows].copy(), cfg=dataclasses.replace(wl.cfg, t=rows))
+    t0 = time.perf_counter()
+    oracle.block(wl)
+    dt = time.perf_counter() - t0
+    return {"value": rows / dt, "unit": "tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": f"full block (router, top-k, CSR, routed experts, shared expert, combine) in double "
+                      f"on the first {rows} of {cfg_name}'s {ms.CONFIGS[cfg_name].t} rows; {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="full")
+    ap.add_argument("--copies", type=int, default=2, help="weight copies rotated per step (defeats the MALL)")
+    ap.add_argument("--cpu-rows", type=int, default=256, help="rows of the oracle CPU-baseline sample (0: skip)")
+    ap.add_argument("--phases", action="store_true", help="also time every phase in an extra pass")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the block is built and measured "
+              f"on a single MI355X, with no sharding or collectives.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mixture_experts_prefill_amd as mep
+    import moe_synth as ms
+
+    cfg = ms.CONFIGS[args.config]
+    log(f"[bench] generating workload {cfg.name} ...")
+    wl = ms.make_workload(cfg)
+    torch.cuda.set_device(0)
+    resident = None
+    blk = mep.MoeBlock.from_workload(wl)
+    log("[bench] uploaded; routing once for the residency split / counts")
+    blk.route()
+    blk.build_csr()
+    torch.cuda.synchronize()
+    counts = np.diff(blk.offsets.cpu().numpy().astype(np.int64))
+    if cfg.resident:
+        order = sorted([e for e in range(cfg.experts) if counts[e] > 0], key=lambda e: -counts[e])
+        resident = np.zeros(cfg.experts, dtype=bool)
+        resident[order[:cfg.resident]] = True
+        blk = mep.MoeBlock.from_workload(wl, resident=resident)
+    tables = [blk.table]
+    pools = [blk.pool]
+    for c in range(1, args.copies if resident is None else 1):
+        pool = blk.pool.clone()
+        pools.append(pool)
+        tab = blk.table.clone()
+        nz = tab != 0
+        tab[nz] = tab[nz] - blk.pool.data_ptr() + pool.data_ptr()
+        tables.append(tab)
+
+    def step(i):
+        blk.table = tables[i % len(tables)]
+        blk.forward()
+
+    log(f"[bench] warmup {args.warmup}")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    dominant = "gateup"
+    mep.moe_profile_begin([dominant])
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    prof = mep.moe_profile_end()
+    gpu_ms = e0.elapsed_time(e1)
+    ms_per_step = gpu_ms / args.steps
+    t = wl.x.shape[0]
+    value = t * args.steps / (gpu_ms / 1e3)
+    log(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f} ms/step)")
+
+    work = algorithmic(cfg, t, counts)
+    dom_ms, dom_n = prof[dominant]
+    dom_avg_s = dom_ms / dom_n / 1e3
+    achieved = work["flop_gateup"] / dom_avg_s / 1e12
+    roofline = {"kernel": "k_gemm gate/up (routed, grouped int4 -> bf16 MFMA, SiLU*up epilogue)",
+                "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic_for(f"gateup_{cfg.name}"),
+                "avg_launch_us": round(dom_avg_s * 1e6, 2)}
+
+    block_flop = work["flop_gateup"] + work["flop_down"] + work["flop_shared"]
+    step_s = ms_per_step / 1e3
+    extra = {"block_mfma_frac": round(block_flop / step_s / 1e12 / PEAK_BF16_TFLOPS, 4),
+             "block_hbm_frac": round(work["bytes_total"] / step_s / 1e9 / PEAK_HBM_GBS, 4),
+             "touched_experts": work["touched"], "max_rows_per_expert": int(counts.max()),
+             "weight_copies": len(tables)}
+
+    if args.phases:
+        mep.moe_profile_begin(mep.PHASES)
+        for i in range(args.steps):
+            step(i)
+        torch.cuda.synchronize()
+        ph = mep.moe_profile_end()
+        extra["phase_us"] = {p: round(v[0] / v[1] * 1e3, 2) for p, v in ph.items()}
+
+    cpu = None
+    if args.cpu_rows > 0:
+        log(f"[bench] oracle CPU baseline on {args.cpu_rows} rows ...")
+        cpu = cpu_baseline(cfg.name, min(args.cpu_rows, t))
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {cfg.description}", "t": t, "hidden": cfg.hidden, "inter": cfg.inter,
+                   "inter_shared": cfg.inter_shared, "experts": cfg.experts, "top_k": cfg.k, "group": cfg.group,
+                   "weights": "int4 + fp16 scale/bias per group", "zipf_s": cfg.zipf_s,
+                   "resident_experts": int(resident.sum()) if resident is not None else cfg.experts,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": roofline, "cpu_baseline": cpu, "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,222 @@
+/*
+ * moe.h -- C ABI of the routed-expert MoE prefill block for MI355X (gfx950).
+ *
+ * One block over a chunk of t <= 4096 token rows (the row cap of the
+ * cherenkov prefill engine: prefill.rs page, const MAX_PREFILL_ROWS):
+ *
+ *   1. moe_shared(accumulate = 0)    shared expert over all rows -> out
+ *   2. moe_route                     router logits, top-k, renormalised weights
+ *   3. moe_build_csr                 rows grouped by expert (CSR)
+ *   4. moe_prefill_experts(acc = 1)  per-expert gather, gate/up, SiLU*up, down,
+ *                                    weighted add into out
+ *
+ * This is the order the experts.rs page runs the block in (fn pf_experts:
+ * zero the output, shared expert over all rows, then the routed experts one
+ * at a time, each scatter-added with its routing weight), so each row sums
+ * its terms as shared first, then experts in ascending id.
+ *
+ * Conventions for every call:
+ *   - Pointers are device pointers unless marked [host].  Buffers are owned
+ *     by the caller; the library never allocates or frees device memory in
+ *     these calls.  Device buffers must stay alive until the stream has
+ *     passed the call.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls only enqueue work on it, except moe_prefill_experts with
+ *     streamed experts, which reads the expert offsets back (one small
+ *     device-to-host copy and a stream synchronisation).
+ *   - Arguments are validated before anything is enqueued; on any error
+ *     nothing runs, outputs are untouched, the status is returned and
+ *     moe_last_error() describes it.  Kernel faults are asynchronous and
+ *     surface at the caller's next synchronisation.
+ *   - bf16 values are passed as uint16_t bit patterns.  Every row of every
+ *     matrix argument is contiguous (row-major) and 16-byte aligned.
+ *   - Calls are reentrant.  A ring handle serves one call at a time.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_MAX_ROWS 4096   /* t <= 4096: prefill.rs page, const MAX_PREFILL_ROWS */
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_K 32
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID = 1,   /* bad argument (shape, null pointer, alignment) */
+    MOE_ERR_CAPACITY = 2,  /* t outside 1..MOE_MAX_ROWS ("empty chunk" / row cap) */
+    MOE_ERR_WORKSPACE = 3, /* workspace smaller than moe_workspace_bytes() */
+    MOE_ERR_HIP = 4        /* the HIP runtime returned an error */
+} moe_status;
+
+/* Message of the last failing call on this thread (empty if none). */
+const char *moe_last_error(void);
+
+/*
+ * Byte layout of one expert record: six sections (codes and scale/bias of
+ * the gate, up and down matrices) in one contiguous record of `stride`
+ * bytes, the structure the experts.rs page addresses with per-matrix w/s/b
+ * offsets inside a record of `stride` bytes (fn pf_experts, struct Q views
+ * at_offset(rec); fn ring_read: record e at e * stride).  gate and up are
+ * [inter x hidden], down is [hidden x inter] (rows = outputs).
+ *
+ * Codes: unsigned 4-bit q, weight = scale * q + bias, one fp16 (scale, bias)
+ * pair per `group` consecutive inputs of a row.  Code tiles are 32 rows x 64
+ * columns, tile (ob, kb) at byte (ob * (K/64) + kb) * 1024 of the code
+ * section; lane L in [0, 64) of a tile owns bytes [16L, 16L+16): row
+ * 32*ob + L%32, columns 64*kb + 32*(L/32) + c, c in [0, 32), code c in the
+ * little-endian 32-bit word c/8 at bit 4*((c%8)/2) + 16*(c%2).  The
+ * scale/bias section holds, per tile in the same order, (64/group)*32
+ * entries of 4 bytes (fp16 scale, fp16 bias): entry gi*32 + row%32 for the
+ * tile's group gi.  Sections are 256-byte aligned, the stride 4096-byte
+ * aligned.  bits is always 4.
+ */
+typedef struct {
+    int32_t hidden, inter, group, bits;
+    uint64_t gate_w, gate_sb, up_w, up_sb, down_w, down_sb; /* byte offsets */
+    uint64_t stride;                                        /* record bytes */
+} moe_layout;
+
+/*
+ * Fills *out [host] for hidden % 256 == 0, inter % 64 == 0, group in {32, 64}.
+ * Returns MOE_ERR_INVALID otherwise.  Host only; needs no GPU.
+ */
+moe_status moe_layout_make(int32_t hidden, int32_t inter, int32_t group, moe_layout *out);
+
+/*
+ * Bytes of the one workspace buffer that moe_build_csr, moe_shared and
+ * moe_prefill_experts share for t rows, top-k k, E experts, routed layout
+ * `routed` [host] and shared layout `shared` [host] (NULL: no shared
+ * expert).  The three calls use disjoint parts of it.  Returns 0 for invalid
+ * arguments.  Host only.
+ */
+size_t moe_workspace_bytes(int32_t t, int32_t k, int32_t E, const moe_layout *routed,
+                           const moe_layout *shared);
+
+/*
+ * Router, top-k and renormalised weights (prefill.rs page, fn pf_layer: the
+ * router_b call on the block input `mixed`, writing topk_idx and topk_w for
+ * k = num_experts_per_tok; experts.rs page, fn prepare_expert_jobs reads
+ * them back as u32 and f32).
+ *
+ *   x         bf16 [t][h]   block input rows
+ *   w_router  fp32 [E][h]   router weight, one row per expert
+ *   logits    fp32 [t][E]   output: logit[r][e] in the canonical fp32 order
+ *                           (h cut into 4-element chunks, chunk c feeds
+ *                           partial c % 64, each partial an fma chain from +0
+ *                           in ascending index, then p[l] += p[l+off] for
+ *                           off = 32, 16, 8, 4, 2, 1; the logit is p[0])
+ *   topk_idx  u32  [t][k]   output: the k largest logits per row, descending,
+ *                           ties to the lower expert id
+ *   topk_w    fp32 [t][k]   output: exp(l_j - l_max) / sum_selected exp(l - l_max)
+ *                           (softmax, top-k, renormalise)
+ * Requires 1 <= t <= 4096, h % 256 == 0, 1 <= k <= min(E, 32), E <= 1024.
+ */
+moe_status moe_route(const uint16_t *x, const float *w_router, int32_t t, int32_t h, int32_t E,
+                     int32_t k, float *logits, uint32_t *topk_idx, float *topk_w, void *stream);
+
+/*
+ * Rows grouped by expert (experts.rs page, fn prepare_expert_jobs: each
+ * expert's rows listed in row order, lists concatenated in expert order;
+ * this call builds the same lists on the GPU instead of on the host).
+ *
+ *   topk_idx, topk_w  [t][k] from moe_route
+ *   offsets   u32 [E+1]  output: expert e's segment is [offsets[e], offsets[e+1]);
+ *                        offsets[E] = t*k
+ *   csr_rows  u32 [t*k]  output: row index of each CSR entry, ascending within a segment
+ *   csr_w     fp32 [t*k] output: that entry's routing weight (a copy of topk_w)
+ *   csr_pos   u32 [t*k]  output: csr_pos[r*k+j] = CSR index of (r, topk_idx[r][j])
+ * Every topk_idx value must be < E, and the k experts of a row distinct
+ * (as moe_route produces); other input gives unspecified (in-bounds) output.
+ */
+moe_status moe_build_csr(const uint32_t *topk_idx, const float *topk_w, int32_t t, int32_t k,
+                         int32_t E, uint32_t *offsets, uint32_t *csr_rows, float *csr_w,
+                         uint32_t *csr_pos, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Shared expert over all t rows (experts.rs page, fn pf_experts: qmm with
+ * the shared gate/up/down matrices over `mixed`, silu_mul, then
+ * shared_add_rows into the block output, one row per threadgroup with the
+ * shared-gate tensor bound):
+ *
+ *   out[r] (+)= g_r * W_down (silu(W_gate x_r) * (W_up x_r))
+ *
+ *   x        bf16 [t][h]
+ *   Ls       [host] layout of the shared record (Ls->hidden == h)
+ *   record   the shared expert's record (Ls->stride bytes)
+ *   gate_w   bf16 [h] or NULL: g_r = sigmoid(x_r . gate_w), or 1 without it
+ *   out      fp32 [t][h]; accumulate = 0 overwrites, 1 adds
+ */
+moe_status moe_shared(const uint16_t *x, int32_t t, const moe_layout *Ls, const void *record,
+                      const uint16_t *gate_w, float *out, int32_t accumulate, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+/*
+ * Expert ring for records that are not resident in device memory
+ * (prefill.rs page, consts RING = 64 slots and GROUP = 8 experts per fetch
+ * batch; experts.rs page, fn pf_experts: batch bi's records are copied into
+ * ring slots only after the GPU has finished batch bi - RING/GROUP, and the
+ * experts of batch bi run only after their copy is done).
+ *
+ *   L        [host] routed layout (the slot size is L->stride)
+ *   slots    device buffer of n_slots * L->stride bytes, owned by the caller
+ *   n_slots  ring slots (64 in the pages), group = jobs per batch (8); requires
+ *            n_slots >= group >= 1 and n_slots % group == 0
+ *   out      [host] receives the handle
+ * The handle owns HIP events, a copy stream and pinned host bookkeeping;
+ * moe_ring_destroy releases them (after synchronising its copy stream).
+ */
+typedef struct moe_ring moe_ring;
+moe_status moe_ring_create(const moe_layout *L, void *slots, int32_t n_slots, int32_t group,
+                           moe_ring **out);
+void moe_ring_destroy(moe_ring *ring);
+
+/* Counters of the last moe_prefill_experts call that used the ring. */
+typedef struct {
+    int32_t jobs;           /* non-empty experts */
+    int32_t streamed;       /* of which streamed through the ring */
+    int32_t batches;        /* batches of `group` jobs */
+    uint64_t fetched_bytes; /* bytes copied host -> device (streamed * stride) */
+    double wait_ms;         /* host time spent waiting to reuse ring slots */
+} moe_ring_stats;
+moe_status moe_ring_get_stats(const moe_ring *ring, moe_ring_stats *out);
+
+/*
+ * Routed experts (experts.rs page, fn pf_experts: per non-empty expert in
+ * ascending id, gather its rows, gate and up projections, silu_mul, down
+ * projection, scatter_add_rows with the routing weights):
+ *
+ *   out[r] (+)= sum over the row's k entries, in ascending expert id, of
+ *               csr_w[p] * W_down,e (silu(W_gate,e x_r) * (W_up,e x_r))
+ *
+ *   x          bf16 [t][h]
+ *   L          [host] routed layout (L->hidden == h)
+ *   offsets, csr_rows, csr_w, csr_pos   from moe_build_csr
+ *   records    u64 [E] device array: device address of expert e's record,
+ *              or 0 if expert e is not resident and must be streamed
+ *   host_records [host] array of E pinned host pointers (hipHostMalloc or
+ *              torch pin_memory) to each streamed expert's record; may be
+ *              NULL when every used expert is resident
+ *   ring       required when a used expert has records[e] == 0
+ *   out        fp32 [t][h]; accumulate = 0 overwrites, 1 adds
+ * Experts with no rows cost nothing and are never read.  The sum over a
+ * row's entries is taken in a fixed order, so results are bitwise
+ * reproducible and independent of residency.
+ */
+moe_status moe_prefill_experts(const uint16_t *x, int32_t t, int32_t k, int32_t E,
+                               const moe_layout *L, const uint32_t *offsets,
+                               const uint32_t *csr_rows, const float *csr_w,
+                               const uint32_t *csr_pos, const uint64_t *records,
+                               const void *const *host_records, moe_ring *ring, float *out,
+                               int32_t accumulate, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

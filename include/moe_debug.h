@@ -1,0 +1,51 @@
+/*
+ * moe_debug.h -- host-only inspection hooks of libmoe, for tests.
+ *
+ * moe_ring_plan_debug: the expert ring's host schedule for one call, without
+ * touching a GPU.  offsets [E+1] as produced by moe_build_csr; resident [E]
+ * nonzero for experts whose record is in device memory; n_slots and group as
+ * given to moe_ring_create.  Fills slot[e] (ring slot of a streamed expert,
+ * -1 if resident or without rows), batch[e] (batch of expert e, -1 without
+ * rows) and wait[b] (the batch whose completion gates batch b's copies, -1 if
+ * none; wait must hold at least E entries).  Returns the number of batches.
+ * The schedule follows the experts.rs page (fns prepare_expert_jobs and
+ * pf_experts): jobs are the non-empty experts in ascending id, slot =
+ * ordinal among streamed jobs mod n_slots, batches of `group` jobs, and batch
+ * b's copies wait for batch b - n_slots/group.
+ */
+#ifndef MOE_DEBUG_H
+#define MOE_DEBUG_H
+#include <stdint.h>
+#ifdef __cplusplus
+extern "C" {
+#endif
+int moe_ring_plan_debug(const uint32_t *offsets, const uint64_t *resident, int32_t E, int32_t n_slots,
+                        int32_t group, int32_t *slot, int32_t *batch, int32_t *wait);
+
+/*
+ * Per-kernel timing.  moe_profile_begin(mask) makes later calls on this
+ * process record a pair of HIP events on their own stream around every
+ * kernel launch whose phase bit is set in `mask` (bit p = phase p below);
+ * moe_profile_end synchronises those events, writes the summed milliseconds
+ * and launch counts per phase into ms[MOE_PHASES] and launches[MOE_PHASES]
+ * (either may be NULL), and stops recording.  Returns the number of timed
+ * launches, or -1 on a HIP error.  Not thread safe; meant for benchmarks.
+ */
+enum {
+    MOE_PHASE_ROUTER = 0,      /* router logits */
+    MOE_PHASE_TOPK = 1,        /* top-k and weights */
+    MOE_PHASE_CSR = 2,         /* CSR count, scan and place */
+    MOE_PHASE_SHARED_GU = 3,   /* shared expert gate/up + SiLU*up */
+    MOE_PHASE_SHARED_DOWN = 4, /* shared expert down, writes out */
+    MOE_PHASE_SCHEDULE = 5,    /* M-tile schedule */
+    MOE_PHASE_GATEUP = 6,      /* routed grouped gate/up + SiLU*up */
+    MOE_PHASE_DOWN = 7,        /* routed grouped down */
+    MOE_PHASE_COMBINE = 8,     /* weighted combine into out */
+    MOE_PHASES = 9
+};
+void moe_profile_begin(uint32_t mask);
+int moe_profile_end(double *ms, int64_t *launches);
+#ifdef __cplusplus
+}
+#endif
+#endif

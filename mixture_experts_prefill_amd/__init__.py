@@ -1,0 +1,227 @@
+"""Routed-expert MoE prefill block on MI355X: Python binding of libmoe.
+
+Thin ctypes marshalling over the C ABI in ``include/moe.h``: every function
+here has the name of the C entry point it calls, takes torch tensors that
+already live on the GPU, passes their device pointers and the current HIP
+stream, and raises ``MoeError`` on a non-zero status.  All computation runs
+in the HIP kernels of ``libmoe.so``; nothing here computes on the host.
+The library must be built first (``python -m mixture_experts_prefill_amd.build``);
+importing the functions without it raises instead of falling back.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+MAX_ROWS = 4096
+MAX_EXPERTS = 1024
+MAX_K = 32
+
+STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID", 2: "MOE_ERR_CAPACITY", 3: "MOE_ERR_WORKSPACE", 4: "MOE_ERR_HIP"}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+class moe_layout(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32), ("group", ctypes.c_int32),
+                ("bits", ctypes.c_int32), ("gate_w", ctypes.c_uint64), ("gate_sb", ctypes.c_uint64),
+                ("up_w", ctypes.c_uint64), ("up_sb", ctypes.c_uint64), ("down_w", ctypes.c_uint64),
+                ("down_sb", ctypes.c_uint64), ("stride", ctypes.c_uint64)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+class moe_ring_stats(ctypes.Structure):
+    _fields_ = [("jobs", ctypes.c_int32), ("streamed", ctypes.c_int32), ("batches", ctypes.c_int32),
+                ("fetched_bytes", ctypes.c_uint64), ("wait_ms", ctypes.c_double)]
+
+
+_lib = None
+EXPORTS = ["moe_last_error", "moe_layout_make", "moe_workspace_bytes", "moe_route", "moe_build_csr",
+           "moe_shared", "moe_ring_create", "moe_ring_destroy", "moe_ring_get_stats", "moe_prefill_experts",
+           "moe_ring_plan_debug", "moe_profile_begin", "moe_profile_end"]
+PHASES = ["router", "topk", "csr", "shared_gateup", "shared_down", "schedule", "gateup", "down", "combine"]
+
+
+def lib():
+    """Load libmoe.so; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built: run python -m mixture_experts_prefill_amd.build")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, Z = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    LP = ctypes.POINTER(moe_layout)
+    L.moe_last_error.restype = ctypes.c_char_p
+    L.moe_layout_make.argtypes = [I, I, I, LP]
+    L.moe_workspace_bytes.argtypes = [I, I, I, LP, LP]
+    L.moe_workspace_bytes.restype = Z
+    L.moe_route.argtypes = [P, P, I, I, I, I, P, P, P, P]
+    L.moe_build_csr.argtypes = [P, P, I, I, I, P, P, P, P, P, Z, P]
+    L.moe_shared.argtypes = [P, I, LP, P, P, P, I, P, Z, P]
+    L.moe_ring_create.argtypes = [LP, P, I, I, ctypes.POINTER(P)]
+    L.moe_ring_destroy.argtypes = [P]
+    L.moe_ring_destroy.restype = None
+    L.moe_ring_get_stats.argtypes = [P, ctypes.POINTER(moe_ring_stats)]
+    L.moe_prefill_experts.argtypes = [P, I, I, I, LP, P, P, P, P, P, P, P, P, I, P, Z, P]
+    L.moe_ring_plan_debug.argtypes = [P, P, I, I, I, P, P, P]
+    L.moe_profile_begin.argtypes = [ctypes.c_uint32]
+    L.moe_profile_begin.restype = None
+    L.moe_profile_end.argtypes = [P, P]
+    L.moe_profile_end.restype = ctypes.c_int
+    for f in ("moe_layout_make", "moe_route", "moe_build_csr", "moe_shared", "moe_ring_create",
+              "moe_ring_get_stats", "moe_prefill_experts"):
+        getattr(L, f).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != 0:
+        raise MoeError(status, lib().moe_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libmoe must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+# ------------------------------------------------------------------ entry points
+
+def moe_layout_make(hidden: int, inter: int, group: int) -> moe_layout:
+    out = moe_layout()
+    _check(lib().moe_layout_make(hidden, inter, group, ctypes.byref(out)))
+    return out
+
+
+def moe_workspace_bytes(t: int, k: int, E: int, routed: moe_layout, shared: Optional[moe_layout] = None) -> int:
+    return lib().moe_workspace_bytes(t, k, E, ctypes.byref(routed), ctypes.byref(shared) if shared else None)
+
+
+def moe_route(x: torch.Tensor, w_router: torch.Tensor, k: int, logits: torch.Tensor, topk_idx: torch.Tensor,
+              topk_w: torch.Tensor, stream=None) -> None:
+    t, h = x.shape
+    E = w_router.shape[0]
+    _check(lib().moe_route(_ptr(x), _ptr(w_router), t, h, E, k, _ptr(logits), _ptr(topk_idx), _ptr(topk_w),
+                           _stream(stream)))
+
+
+def moe_build_csr(topk_idx: torch.Tensor, topk_w: torch.Tensor, E: int, offsets: torch.Tensor,
+                  csr_rows: torch.Tensor, csr_w: torch.Tensor, csr_pos: torch.Tensor, workspace: torch.Tensor,
+                  stream=None) -> None:
+    t, k = topk_idx.shape
+    _check(lib().moe_build_csr(_ptr(topk_idx), _ptr(topk_w), t, k, E, _ptr(offsets), _ptr(csr_rows), _ptr(csr_w),
+                               _ptr(csr_pos), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                               _stream(stream)))
+
+
+def moe_shared(x: torch.Tensor, layout: moe_layout, record: torch.Tensor, gate_w: Optional[torch.Tensor],
+               out: torch.Tensor, accumulate: int, workspace: torch.Tensor, stream=None) -> None:
+    t = x.shape[0]
+    _check(lib().moe_shared(_ptr(x), t, ctypes.byref(layout), _ptr(record), _ptr(gate_w), _ptr(out), accumulate,
+                            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+class MoeRing:
+    """Owner of a moe_ring handle (events, copy stream); slots are caller memory."""
+
+    def __init__(self, layout: moe_layout, slots: torch.Tensor, n_slots: int = 64, group: int = 8):
+        self._h = ctypes.c_void_p()
+        self.slots = slots
+        _check(lib().moe_ring_create(ctypes.byref(layout), _ptr(slots), n_slots, group, ctypes.byref(self._h)))
+
+    @property
+    def handle(self):
+        return self._h
+
+    def stats(self) -> dict:
+        s = moe_ring_stats()
+        _check(lib().moe_ring_get_stats(self._h, ctypes.byref(s)))
+        return {f: getattr(s, f) for f, _ in s._fields_}
+
+    def close(self):
+        if self._h:
+            lib().moe_ring_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def moe_prefill_experts(x: torch.Tensor, k: int, E: int, layout: moe_layout, offsets: torch.Tensor,
+                        csr_rows: torch.Tensor, csr_w: torch.Tensor, csr_pos: torch.Tensor, records: torch.Tensor,
+                        out: torch.Tensor, accumulate: int, workspace: torch.Tensor,
+                        host_records: Optional[Sequence[Optional[torch.Tensor]]] = None,
+                        ring: Optional[MoeRing] = None, stream=None) -> None:
+    t = x.shape[0]
+    hr = None
+    if host_records is not None:
+        hr = (ctypes.c_void_p * E)(*[(r.data_ptr() if r is not None else None) for r in host_records])
+    _check(lib().moe_prefill_experts(_ptr(x), t, k, E, ctypes.byref(layout), _ptr(offsets), _ptr(csr_rows),
+                                     _ptr(csr_w), _ptr(csr_pos), _ptr(records), hr,
+                                     ring.handle if ring is not None else None, _ptr(out), accumulate,
+                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                     _stream(stream)))
+
+
+def moe_ring_plan_debug(offsets, resident, n_slots: int = 64, group: int = 8):
+    """Host-only ring schedule (numpy in, numpy out): slot[E], batch[E], wait[batches]."""
+    import numpy as np
+
+    offsets = np.ascontiguousarray(offsets, dtype=np.uint32)
+    resident = np.ascontiguousarray(resident, dtype=np.uint64)
+    E = offsets.size - 1
+    slot = np.empty(E, np.int32)
+    batch = np.empty(E, np.int32)
+    wait = np.empty(max(E, 1), np.int32)
+    nb = lib().moe_ring_plan_debug(offsets.ctypes.data, resident.ctypes.data, E, n_slots, group,
+                                   slot.ctypes.data, batch.ctypes.data, wait.ctypes.data)
+    return slot, batch, wait[:nb]
+
+
+def moe_profile_begin(phases: Sequence[str]) -> None:
+    """Start timing every kernel of the named phases (see PHASES) with HIP events."""
+    mask = 0
+    for p in phases:
+        mask |= 1 << PHASES.index(p)
+    lib().moe_profile_begin(mask)
+
+
+def moe_profile_end() -> dict:
+    """Stop timing; returns {phase: (total_ms, launches)} for phases that ran."""
+    import numpy as np
+
+    ms = np.zeros(len(PHASES), np.float64)
+    n = np.zeros(len(PHASES), np.int64)
+    if lib().moe_profile_end(ms.ctypes.data, n.ctypes.data) < 0:
+        raise MoeError(4, "profile events failed")
+    return {p: (float(ms[i]), int(n[i])) for i, p in enumerate(PHASES) if n[i]}
+
+
+from .block import MoeBlock  # noqa: E402  (device-buffer owner built on the calls above)

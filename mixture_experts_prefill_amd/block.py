@@ -1,0 +1,125 @@
+"""Device buffers for one MoE block and the four calls in their order.
+
+Owns the GPU tensors of one layer shape (inputs, routing outputs, CSR,
+workspace, output) and runs
+
+    moe_shared(accumulate=0) -> moe_route -> moe_build_csr -> moe_prefill_experts(accumulate=1)
+
+the order of the cherenkov experts.rs page (fn pf_experts: shared expert into
+the zeroed output, then routed experts added in ascending id).  Only
+allocation and call sequencing live here; the arithmetic is in libmoe.
+"""
+from __future__ import annotations
+
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import (MoeRing, moe_build_csr, moe_layout_make, moe_prefill_experts, moe_route, moe_shared,
+               moe_workspace_bytes)
+
+
+def bf16_tensor(bits: np.ndarray, device) -> torch.Tensor:
+    """uint16 bf16 bit patterns -> torch.bfloat16 tensor on device (bit-exact)."""
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
+
+
+class MoeBlock:
+    def __init__(self, t: int, hidden: int, inter: int, inter_shared: Optional[int], experts: int, k: int,
+                 group: int, device="cuda"):
+        self.t, self.h, self.I, self.E, self.k, self.G = t, hidden, inter, experts, k, group
+        self.Is = inter_shared
+        self.device = torch.device(device)
+        self.L = moe_layout_make(hidden, inter, group)
+        self.Ls = moe_layout_make(hidden, inter_shared, group) if inter_shared else None
+        d = self.device
+        self.logits = torch.empty((t, experts), dtype=torch.float32, device=d)
+        self.topk_idx = torch.empty((t, k), dtype=torch.int32, device=d)
+        self.topk_w = torch.empty((t, k), dtype=torch.float32, device=d)
+        self.offsets = torch.empty(experts + 1, dtype=torch.int32, device=d)
+        self.csr_rows = torch.empty(t * k, dtype=torch.int32, device=d)
+        self.csr_w = torch.empty(t * k, dtype=torch.float32, device=d)
+        self.csr_pos = torch.empty(t * k, dtype=torch.int32, device=d)
+        self.out = torch.empty((t, hidden), dtype=torch.float32, device=d)
+        nbytes = moe_workspace_bytes(t, k, experts, self.L, self.Ls)
+        if nbytes == 0:
+            raise ValueError("invalid block shape")
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=d)
+        self.x = self.w_router = self.pool = self.table = self.shared_record = self.gate_w = None
+        self.host_records: Optional[Sequence[Optional[torch.Tensor]]] = None
+        self.ring: Optional[MoeRing] = None
+
+    @classmethod
+    def from_workload(cls, wl, device="cuda", resident: Optional[np.ndarray] = None, ring_slots: int = 64,
+                      group: int = 8, shared: bool = True):
+        """Upload a moe_synth workload.  resident[e] False -> expert e streams through a ring."""
+        c = wl.cfg
+        b = cls(wl.x.shape[0], c.hidden, c.inter, c.inter_shared if shared else None, c.experts, c.k, c.group, device)
+        b.set_inputs(wl.x, wl.w_router)
+        b.set_records(wl.records, resident, ring_slots, group)
+        if shared:
+            b.set_shared(wl.shared_record, wl.gate_w)
+        return b
+
+    def set_inputs(self, x_bits: np.ndarray, w_router: np.ndarray):
+        self.x = bf16_tensor(x_bits, self.device)
+        self.w_router = torch.from_numpy(np.ascontiguousarray(w_router, dtype=np.float32)).to(self.device)
+
+    def set_records(self, records: np.ndarray, resident: Optional[np.ndarray] = None, ring_slots: int = 64,
+                    group: int = 8):
+        E, stride = records.shape
+        assert stride == self.L.stride and E == self.E
+        if resident is None:
+            resident = np.ones(E, dtype=bool)
+        res_ids = np.nonzero(resident)[0]
+        self.pool = torch.from_numpy(np.ascontiguousarray(records[res_ids])).to(self.device)
+        table = np.zeros(E, dtype=np.int64)
+        base = self.pool.data_ptr()
+        table[res_ids] = base + np.arange(res_ids.size, dtype=np.int64) * stride
+        self.table = torch.from_numpy(table).to(self.device)
+        if resident.all():
+            self.host_records, self.ring = None, None
+            return
+        self.host_records = [None] * E
+        for e in np.nonzero(~resident)[0]:
+            self.host_records[e] = torch.from_numpy(records[e]).pin_memory()
+        self.ring_slots = torch.empty((ring_slots, stride), dtype=torch.uint8, device=self.device)
+        self.ring = MoeRing(self.L, self.ring_slots, ring_slots, group)
+
+    def use_ring(self, ring_slots: int = 64, group: int = 8):
+        """Run the all-resident records through a ring too (every batch gated by events)."""
+        self.ring_slots = torch.empty((ring_slots, self.L.stride), dtype=torch.uint8, device=self.device)
+        self.ring = MoeRing(self.L, self.ring_slots, ring_slots, group)
+        self.host_records = [None] * self.E
+
+    def set_shared(self, record: np.ndarray, gate_bits: Optional[np.ndarray] = None):
+        self.shared_record = torch.from_numpy(np.ascontiguousarray(record)).to(self.device)
+        self.gate_w = None if gate_bits is None else bf16_tensor(gate_bits, self.device)
+
+    # ---------------------------------------------------------------- calls
+    def route(self, stream=None):
+        moe_route(self.x, self.w_router, self.k, self.logits, self.topk_idx, self.topk_w, stream)
+
+    def build_csr(self, stream=None):
+        moe_build_csr(self.topk_idx, self.topk_w, self.E, self.offsets, self.csr_rows, self.csr_w, self.csr_pos,
+                      self.workspace, stream)
+
+    def shared(self, accumulate: int = 0, stream=None):
+        moe_shared(self.x, self.Ls, self.shared_record, self.gate_w, self.out, accumulate, self.workspace, stream)
+
+    def experts(self, accumulate: int = 1, stream=None):
+        moe_prefill_experts(self.x, self.k, self.E, self.L, self.offsets, self.csr_rows, self.csr_w, self.csr_pos,
+                            self.table, self.out, accumulate, self.workspace, self.host_records, self.ring, stream)
+
+    def forward(self, stream=None) -> torch.Tensor:
+        if self.Ls is not None:
+            self.shared(0, stream)
+            self.route(stream)
+            self.build_csr(stream)
+            self.experts(1, stream)
+        else:
+            self.route(stream)
+            self.build_csr(stream)
+            self.experts(0, stream)
+        return self.out

@@ -1,0 +1,275 @@
+// C ABI of libmoe: argument checks, workspace plan and launch sequencing.
+//
+// Every entry point validates all arguments before it enqueues anything, in
+// the manner of the cherenkov prefill.rs page (fn prefill_chunk: "empty
+// chunk" and capacity checks up front, errors returned with a message).
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "moe_internal.h"
+#include "ring.h"
+
+namespace moe {
+
+static thread_local std::string g_err;
+
+moe_status fail(moe_status st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+moe_status hip_fail(hipError_t e, const char *what) {
+    return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+static size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+static bool layout_ok(const moe_layout *L) {
+    if (!L) return false;
+    moe_layout ref;
+    if (moe_layout_make(L->hidden, L->inter, L->group, &ref) != MOE_OK) return false;
+    return std::memcmp(&ref, L, sizeof ref) == 0;
+}
+
+bool workspace_plan(int t, int k, int E, const moe_layout *routed, const moe_layout *shared,
+                    Workspace *w) {
+    if (t < 1 || t > MOE_MAX_ROWS || k < 1 || k > MOE_MAX_K || E < k || E > MOE_MAX_EXPERTS)
+        return false;
+    if (!layout_ok(routed) || (shared && !layout_ok(shared))) return false;
+    if (shared && shared->hidden != routed->hidden) return false;
+    const size_t P = (size_t)t * k;
+    const size_t tiles = (size_t)(t + kCsrTileRows - 1) / kCsrTileRows;
+    const size_t max_mt = P / kMinBM + (size_t)E + 1;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off = align256(off + bytes);
+        return at;
+    };
+    w->csr_hist = take(tiles * E * 4);
+    w->sched = take(max_mt * 16);
+    w->sched_n = take(16);
+    w->jobs = take((size_t)E * 8);
+    w->hg = take(P * routed->inter * 2);
+    w->ye = take(P * routed->hidden * 2);
+    w->hs = take(shared ? (size_t)t * shared->inter * 2 : 0);
+    w->gate = take((size_t)t * 4);
+    w->total = off;
+    return true;
+}
+
+int pick_bm(int t, int k, int E) {
+    // mean rows per non-empty expert, assuming every expert gets some rows
+    const long P = (long)t * k;
+    const long used = P < E ? P : E;
+    const long mean = P / (used > 0 ? used : 1);
+    return mean >= 96 ? 128 : mean >= 48 ? 64 : 32;
+}
+
+static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+static moe_status check_rows(int t) {
+    if (t < 1) return fail(MOE_ERR_CAPACITY, "empty chunk (t = %d)", t);
+    if (t > MOE_MAX_ROWS) return fail(MOE_ERR_CAPACITY, "t = %d exceeds the %d-row chunk cap", t, MOE_MAX_ROWS);
+    return MOE_OK;
+}
+
+static moe_status check_routing(int t, int k, int E) {
+    if (moe_status st = check_rows(t)) return st;
+    if (E < 1 || E > MOE_MAX_EXPERTS) return fail(MOE_ERR_INVALID, "E = %d outside 1..%d", E, MOE_MAX_EXPERTS);
+    if (k < 1 || k > E || k > MOE_MAX_K) return fail(MOE_ERR_INVALID, "k = %d outside 1..min(E = %d, %d)", k, E, MOE_MAX_K);
+    return MOE_OK;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+const char *moe_last_error(void) { return g_err.c_str(); }
+
+moe_status moe_layout_make(int32_t hidden, int32_t inter, int32_t group, moe_layout *out) {
+    if (!out) return fail(MOE_ERR_INVALID, "layout: null output");
+    if (hidden <= 0 || hidden % 256) return fail(MOE_ERR_INVALID, "hidden = %d must be a positive multiple of 256", hidden);
+    if (inter <= 0 || inter % 64) return fail(MOE_ERR_INVALID, "inter = %d must be a positive multiple of 64", inter);
+    if (group != 32 && group != 64) return fail(MOE_ERR_INVALID, "group = %d must be 32 or 64", group);
+    moe_layout L;
+    std::memset(&L, 0, sizeof L);
+    L.hidden = hidden;
+    L.inter = inter;
+    L.group = group;
+    L.bits = 4;
+    const uint64_t codes = (uint64_t)hidden * inter / 2;
+    const uint64_t sb = (uint64_t)hidden * inter / group * 4;
+    uint64_t off = 0;
+    uint64_t *secs[6] = {&L.gate_w, &L.gate_sb, &L.up_w, &L.up_sb, &L.down_w, &L.down_sb};
+    for (int m = 0; m < 3; ++m) {
+        *secs[2 * m] = off;
+        off = (off + codes + 255) / 256 * 256;
+        *secs[2 * m + 1] = off;
+        off = (off + sb + 255) / 256 * 256;
+    }
+    L.stride = (off + 4095) / 4096 * 4096;
+    *out = L;
+    return MOE_OK;
+}
+
+size_t moe_workspace_bytes(int32_t t, int32_t k, int32_t E, const moe_layout *routed,
+                           const moe_layout *shared) {
+    Workspace w;
+    return workspace_plan(t, k, E, routed, shared, &w) ? w.total : 0;
+}
+
+moe_status moe_route(const uint16_t *x, const float *w_router, int32_t t, int32_t h, int32_t E,
+                     int32_t k, float *logits, uint32_t *topk_idx, float *topk_w, void *stream) {
+    if (moe_status st = check_routing(t, k, E)) return st;
+    if (h <= 0 || h % 256) return fail(MOE_ERR_INVALID, "route: h = %d must be a positive multiple of 256", h);
+    if (!x || !w_router || !logits || !topk_idx || !topk_w) return fail(MOE_ERR_INVALID, "route: null pointer");
+    if (!aligned16(x) || !aligned16(w_router)) return fail(MOE_ERR_INVALID, "route: x and w_router must be 16-byte aligned");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_router_logits(x, w_router, t, h, E, logits, s);
+    if (e != hipSuccess) return hip_fail(e, "router logits");
+    e = launch_topk(logits, t, E, k, topk_idx, topk_w, s);
+    if (e != hipSuccess) return hip_fail(e, "top-k");
+    return MOE_OK;
+}
+
+moe_status moe_build_csr(const uint32_t *topk_idx, const float *topk_w, int32_t t, int32_t k,
+                         int32_t E, uint32_t *offsets, uint32_t *csr_rows, float *csr_w,
+                         uint32_t *csr_pos, void *workspace, size_t workspace_bytes, void *stream) {
+    if (moe_status st = check_routing(t, k, E)) return st;
+    if (!topk_idx || !topk_w || !offsets || !csr_rows || !csr_w || !csr_pos || !workspace)
+        return fail(MOE_ERR_INVALID, "build_csr: null pointer");
+    const size_t need = (size_t)((t + kCsrTileRows - 1) / kCsrTileRows) * E * 4;
+    if (workspace_bytes < need)
+        return fail(MOE_ERR_WORKSPACE, "build_csr: workspace %zu bytes < %zu needed", workspace_bytes, need);
+    // the CSR scratch sits at the start of the workspace in every plan
+    uint32_t *hist = static_cast<uint32_t *>(workspace);
+    hipError_t e = launch_csr(topk_idx, topk_w, t, k, E, offsets, csr_rows, csr_w, csr_pos, hist,
+                              static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "build_csr");
+    return MOE_OK;
+}
+
+moe_status moe_shared(const uint16_t *x, int32_t t, const moe_layout *Ls, const void *record,
+                      const uint16_t *gate_w, float *out, int32_t accumulate, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+    if (moe_status st = check_rows(t)) return st;
+    if (!layout_ok(Ls)) return fail(MOE_ERR_INVALID, "shared: layout not made by moe_layout_make");
+    if (!x || !record || !out || !workspace) return fail(MOE_ERR_INVALID, "shared: null pointer");
+    if (!aligned16(x) || !aligned16(record) || !aligned16(out))
+        return fail(MOE_ERR_INVALID, "shared: x, record and out must be 16-byte aligned");
+    // The shared expert's scratch is the end of the workspace: [.. | hs | gate].
+    const size_t g_bytes = align256((size_t)t * 4), hs_bytes = align256((size_t)t * Ls->inter * 2);
+    const size_t end = workspace_bytes & ~size_t(255);
+    if (end < g_bytes + hs_bytes)
+        return fail(MOE_ERR_WORKSPACE, "shared: workspace %zu bytes < %zu needed", workspace_bytes,
+                    g_bytes + hs_bytes);
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    uint16_t *hs = reinterpret_cast<uint16_t *>(ws + end - g_bytes - hs_bytes);
+    float *g = reinterpret_cast<float *>(ws + end - g_bytes);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (gate_w) {
+        e = launch_shared_gate(x, gate_w, t, Ls->hidden, g, s);
+        if (e != hipSuccess) return hip_fail(e, "shared gate");
+    }
+    GemmArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.x = x;
+    a.record = record;
+    a.t = t;
+    a.hidden = Ls->hidden;
+    a.inter = Ls->inter;
+    a.group = Ls->group;
+    a.w_off = Ls->gate_w;
+    a.sb_off = Ls->gate_sb;
+    a.w2_off = Ls->up_w;
+    a.sb2_off = Ls->up_sb;
+    a.hg = hs;
+    const int bm = t >= 512 ? 128 : t >= 64 ? 64 : 32;
+    e = launch_gateup(a, bm, s);
+    if (e != hipSuccess) return hip_fail(e, "shared gate/up");
+    a.act = hs;
+    a.w_off = Ls->down_w;
+    a.sb_off = Ls->down_sb;
+    a.out = out;
+    a.gate = gate_w ? g : nullptr;
+    a.accumulate = accumulate;
+    e = launch_down(a, bm, s);
+    if (e != hipSuccess) return hip_fail(e, "shared down");
+    return MOE_OK;
+}
+
+moe_status moe_prefill_experts(const uint16_t *x, int32_t t, int32_t k, int32_t E,
+                               const moe_layout *L, const uint32_t *offsets,
+                               const uint32_t *csr_rows, const float *csr_w,
+                               const uint32_t *csr_pos, const uint64_t *records,
+                               const void *const *host_records, moe_ring *ring, float *out,
+                               int32_t accumulate, void *workspace, size_t workspace_bytes,
+                               void *stream) {
+    if (moe_status st = check_routing(t, k, E)) return st;
+    if (!layout_ok(L)) return fail(MOE_ERR_INVALID, "experts: layout not made by moe_layout_make");
+    if (!x || !offsets || !csr_rows || !csr_w || !csr_pos || !records || !out || !workspace)
+        return fail(MOE_ERR_INVALID, "experts: null pointer");
+    if (!aligned16(x) || !aligned16(out)) return fail(MOE_ERR_INVALID, "experts: x and out must be 16-byte aligned");
+    Workspace w;
+    workspace_plan(t, k, E, L, nullptr, &w);
+    const size_t need = w.gate;  // everything before the shared scratch
+    if (workspace_bytes < need)
+        return fail(MOE_ERR_WORKSPACE, "experts: workspace %zu bytes < %zu needed", workspace_bytes, need);
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    GemmArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.x = x;
+    a.rows = csr_rows;
+    a.records = records;
+    a.sched = reinterpret_cast<int4 *>(ws + w.sched);
+    a.sched_n = reinterpret_cast<uint32_t *>(ws + w.sched_n);
+    a.t = t;
+    a.hidden = L->hidden;
+    a.inter = L->inter;
+    a.group = L->group;
+    a.hg = reinterpret_cast<uint16_t *>(ws + w.hg);
+    a.ye = reinterpret_cast<uint16_t *>(ws + w.ye);
+    const int bm = pick_bm(t, k, E);
+    a.max_tiles = (int)((size_t)t * k / bm + (size_t)E + 1);
+
+    if (ring || host_records) {
+        return ring_run(ring, host_records, a, bm, offsets, csr_pos, csr_w, t, k, E, L, out,
+                        accumulate, reinterpret_cast<uint64_t *>(ws + w.jobs), s);
+    }
+
+    hipError_t e = launch_schedule(offsets, 0, E, bm, const_cast<int4 *>(a.sched),
+                                   const_cast<uint32_t *>(a.sched_n), s);
+    if (e != hipSuccess) return hip_fail(e, "schedule");
+    a.w_off = L->gate_w;
+    a.sb_off = L->gate_sb;
+    a.w2_off = L->up_w;
+    a.sb2_off = L->up_sb;
+    e = launch_gateup(a, bm, s);
+    if (e != hipSuccess) return hip_fail(e, "experts gate/up");
+    a.act = a.hg;
+    a.w_off = L->down_w;
+    a.sb_off = L->down_sb;
+    e = launch_down(a, bm, s);
+    if (e != hipSuccess) return hip_fail(e, "experts down");
+    e = launch_combine(a.ye, csr_pos, csr_w, t, k, L->hidden, out, accumulate, s);
+    if (e != hipSuccess) return hip_fail(e, "combine");
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,80 @@
+// Internal declarations shared by the HIP kernels and the host API of libmoe.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+#include "../../include/moe_debug.h"
+#include "profile.h"
+
+namespace moe {
+
+// ------------------------------------------------------------------ workspace
+
+// Disjoint regions of the caller's workspace, 256-byte aligned.
+struct Workspace {
+    size_t csr_hist;   // u32 [row_tiles][E]: per-tile expert counts, then segment bases
+    size_t sched;      // int4 [max_tiles]: (expert, first CSR position, rows, 0) per M-tile
+    size_t sched_n;    // u32 [4]: number of M-tiles
+    size_t jobs;       // u64 [E]: record address per expert for the ring path
+    size_t hg;         // bf16 [t*k][I]: SiLU(gate)*up of every CSR entry
+    size_t ye;         // bf16 [t*k][h]: down projection of every CSR entry
+    size_t hs;         // bf16 [t][I_s]: shared expert's SiLU(gate)*up
+    size_t gate;       // f32 [t]: shared-expert gate factors
+    size_t total;
+};
+
+constexpr int kCsrTileRows = 64;  // rows per CSR tile (one 64-bit mask per expert)
+constexpr int kMinBM = 32;        // smallest GEMM M-tile
+
+bool workspace_plan(int t, int k, int E, const moe_layout *routed, const moe_layout *shared,
+                    Workspace *out);
+
+// ------------------------------------------------------------------ launchers
+// Every launcher only enqueues; arguments were validated by the caller.
+
+hipError_t launch_router_logits(const uint16_t *x, const float *w, int t, int h, int E,
+                                float *logits, hipStream_t s);
+hipError_t launch_topk(const float *logits, int t, int E, int k, uint32_t *idx, float *wts,
+                       hipStream_t s);
+hipError_t launch_csr(const uint32_t *idx, const float *wts, int t, int k, int E,
+                      uint32_t *offsets, uint32_t *rows, float *csr_w, uint32_t *pos,
+                      uint32_t *hist, hipStream_t s);
+
+// M-tile schedule of the grouped GEMMs: for experts [e0, e1) with rows, tiles of
+// bm rows; written to sched/sched_n.
+hipError_t launch_schedule(const uint32_t *offsets, int e0, int e1, int bm, int4 *sched,
+                           uint32_t *sched_n, hipStream_t s);
+
+struct GemmArgs {
+    // B-operand rows (tokens): x rows gathered through `rows` (routed gate/up),
+    // identity rows (shared gate/up), or consecutive rows of `act` (down).
+    const uint16_t *x;       // bf16 [t][h] block input
+    const uint32_t *rows;    // CSR row list (routed gate/up) or nullptr
+    const uint16_t *act;     // bf16 activations for the down projection
+    const uint64_t *records; // device table of record addresses, per expert
+    const void *record;      // the one record (shared expert) when records == nullptr
+    const int4 *sched;       // M-tiles (routed) or nullptr (dense rows 0..t)
+    const uint32_t *sched_n;
+    int max_tiles;           // grid bound on M-tiles
+    int t;                   // rows (dense mode)
+    int hidden, inter, group;
+    uint64_t w_off, sb_off, w2_off, sb2_off;  // sections: gate & up (gate/up), down (down)
+    // outputs
+    uint16_t *hg;            // gate/up: bf16 [rows][inter]
+    uint16_t *ye;            // down routed: bf16 [t*k][hidden]
+    float *out;              // down shared: fp32 [t][hidden]
+    const float *gate;       // shared gate factors or nullptr
+    int accumulate;
+};
+
+hipError_t launch_gateup(const GemmArgs &a, int bm, hipStream_t s);
+hipError_t launch_down(const GemmArgs &a, int bm, hipStream_t s);
+hipError_t launch_shared_gate(const uint16_t *x, const uint16_t *gate_w, int t, int h, float *g,
+                              hipStream_t s);
+hipError_t launch_combine(const uint16_t *ye, const uint32_t *pos, const float *csr_w, int t,
+                          int k, int h, float *out, int accumulate, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,168 @@
+"""Host-side tests of the C ABI: no GPU needed, no kernel is launched.
+
+Checks that libmoe loads and exports every symbol its headers declare, that
+its record layout and workspace plan agree with the independent copies in the
+generator and the oracle, that argument validation returns the right status
+before anything is enqueued, and that the expert ring's host schedule keeps
+the slot-reuse rule of the experts.rs page (fn pf_experts).
+"""
+import ctypes
+import glob
+import os
+import re
+
+import numpy as np
+import pytest
+
+import moe_synth as ms
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+mep = pytest.importorskip("mixture_experts_prefill_amd")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mep.LIB_PATH):
+        from mixture_experts_prefill_amd import build
+
+        build.build()
+    return mep.lib()
+
+
+def header_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"\b(moe_[a-z_0-9]+)\s*\(", text):
+            names.add(m.group(1))
+    return names
+
+
+def test_exports_every_declared_symbol(lib):
+    names = header_functions()
+    assert {"moe_route", "moe_build_csr", "moe_prefill_experts", "moe_shared"} <= names
+    for n in sorted(names):
+        assert hasattr(lib, n), n
+    assert set(mep.EXPORTS) >= names
+
+
+@pytest.mark.parametrize("h,I,G", [(256, 128, 32), (2048, 768, 64), (4096, 1536, 64), (512, 192, 32)])
+def test_layout_agrees_with_generator_and_oracle(lib, orc, h, I, G):
+    L = mep.moe_layout_make(h, I, G).as_dict()
+    g = ms.layout(h, I, G)
+    o = orc.layout(h, I, G)
+    for k in ("gate_w", "gate_sb", "up_w", "up_sb", "down_w", "down_sb", "stride"):
+        assert L[k] == getattr(g, k) == o[k], k
+    assert L["bits"] == 4 and L["hidden"] == h and L["inter"] == I and L["group"] == G
+
+
+@pytest.mark.parametrize("h,I,G", [(128, 64, 64), (256, 96, 64), (256, 128, 16), (0, 64, 64)])
+def test_layout_rejects_bad_shapes(lib, h, I, G):
+    with pytest.raises(mep.MoeError) as e:
+        mep.moe_layout_make(h, I, G)
+    assert e.value.status == 1
+
+
+def test_workspace_plan(lib):
+    L = mep.moe_layout_make(2048, 768, 64)
+    Ls = mep.moe_layout_make(2048, 768, 64)
+    t, k, E = 4096, 8, 128
+    n = mep.moe_workspace_bytes(t, k, E, L, Ls)
+    P = t * k
+    # hg and ye (bf16) dominate: P*I*2 + P*h*2, plus shared scratch t*Is*2
+    assert n >= P * 768 * 2 + P * 2048 * 2 + t * 768 * 2
+    assert n < P * 768 * 2 + P * 2048 * 2 + t * 768 * 2 + 8 * 2**20
+    assert n % 256 == 0
+    assert mep.moe_workspace_bytes(0, k, E, L, Ls) == 0
+    assert mep.moe_workspace_bytes(4097, k, E, L, Ls) == 0
+    assert mep.moe_workspace_bytes(t, 9, 8, L, Ls) == 0
+
+
+def P(v):
+    return ctypes.c_void_p(v)
+
+
+FAKE = 1 << 20  # never dereferenced: validation fails before any use
+
+
+@pytest.mark.parametrize("t,h,E,k,status", [
+    (0, 256, 8, 2, 2),       # empty chunk
+    (4097, 256, 8, 2, 2),    # over the row cap
+    (16, 255, 8, 2, 1),      # h not a multiple of 256
+    (16, 256, 8, 9, 1),      # k > E
+    (16, 256, 0, 1, 1),      # no experts
+    (16, 256, 2048, 2, 1),   # too many experts
+    (16, 256, 64, 33, 1),    # k above the cap
+])
+def test_route_validation(lib, t, h, E, k, status):
+    rc = lib.moe_route(P(FAKE), P(FAKE), t, h, E, k, P(FAKE), P(FAKE), P(FAKE), None)
+    assert rc == status
+    assert lib.moe_last_error().decode()
+
+
+def test_null_and_alignment_checks(lib):
+    assert lib.moe_route(None, P(FAKE), 16, 256, 8, 2, P(FAKE), P(FAKE), P(FAKE), None) == 1
+    assert lib.moe_route(P(FAKE + 2), P(FAKE), 16, 256, 8, 2, P(FAKE), P(FAKE), P(FAKE), None) == 1
+    L = mep.moe_layout_make(256, 128, 32)
+    assert lib.moe_shared(P(FAKE), 16, ctypes.byref(L), None, None, P(FAKE), 0, P(FAKE), 1 << 20, None) == 1
+    bad = mep.moe_layout_make(256, 128, 32)
+    bad.stride += 1
+    assert lib.moe_shared(P(FAKE), 16, ctypes.byref(bad), P(FAKE), None, P(FAKE), 0, P(FAKE), 1 << 20, None) == 1
+    assert lib.moe_shared(P(FAKE), 0, ctypes.byref(L), P(FAKE), None, P(FAKE), 0, P(FAKE), 1 << 20, None) == 2
+
+
+def test_workspace_too_small(lib):
+    L = mep.moe_layout_make(256, 128, 32)
+    need = mep.moe_workspace_bytes(16, 2, 8, L, L)
+    assert lib.moe_build_csr(P(FAKE), P(FAKE), 4096, 8, 1024, P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), 1024,
+                             None) == 3
+    assert lib.moe_shared(P(FAKE), 16, ctypes.byref(L), P(FAKE), None, P(FAKE), 0, P(FAKE), 256, None) == 3
+    assert lib.moe_prefill_experts(P(FAKE), 16, 2, 8, ctypes.byref(L), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE),
+                                   None, None, P(FAKE), 1, P(FAKE), need // 4, None) == 3
+
+
+def test_ring_create_validation(lib):
+    L = mep.moe_layout_make(256, 128, 32)
+    h = ctypes.c_void_p()
+    assert lib.moe_ring_create(ctypes.byref(L), P(FAKE), 4, 8, ctypes.byref(h)) == 1   # slots < group
+    assert lib.moe_ring_create(ctypes.byref(L), P(FAKE), 12, 8, ctypes.byref(h)) == 1  # not a multiple
+    assert lib.moe_ring_create(ctypes.byref(L), None, 64, 8, ctypes.byref(h)) == 1
+
+
+# ------------------------------------------------------------------ ring schedule simulator
+
+def random_offsets(rng, E, t, k, empty_frac):
+    counts = rng.integers(1, 50, E)
+    counts[rng.random(E) < empty_frac] = 0
+    return np.concatenate([[0], np.cumsum(counts)]).astype(np.uint32)
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("n_slots,group", [(64, 8), (8, 2), (16, 16), (6, 3)])
+def test_ring_schedule_reuse_rule(lib, seed, n_slots, group):
+    rng = np.random.default_rng(seed)
+    E = int(rng.integers(1, 400))
+    offsets = random_offsets(rng, E, 0, 0, rng.random() * 0.5)
+    resident = (rng.random(E) < rng.random()).astype(np.uint64)
+    slot, batch, wait = mep.moe_ring_plan_debug(offsets, resident, n_slots, group)
+    counts = np.diff(offsets.astype(np.int64))
+    jobs = [e for e in range(E) if counts[e] > 0]
+    # jobs in ascending id, consecutive batches of `group`
+    assert [batch[e] for e in jobs] == [i // group for i in range(len(jobs))]
+    assert all(batch[e] == -1 and slot[e] == -1 for e in range(E) if counts[e] == 0)
+    streamed = [e for e in jobs if not resident[e]]
+    assert [slot[e] for e in streamed] == [i % n_slots for i in range(len(streamed))]
+    assert all(slot[e] == -1 for e in jobs if resident[e])
+    lag = n_slots // group
+    assert list(wait) == [b - lag if b >= lag else -1 for b in range(len(wait))]
+    # reuse rule: when a slot is taken again, the new user's batch waits for a
+    # batch at or after the previous user's batch (so the previous user is done)
+    last_user = {}
+    for e in streamed:
+        s, b = slot[e], batch[e]
+        if s in last_user:
+            prev_b = last_user[s]
+            assert prev_b < b
+            assert wait[b] >= prev_b
+        last_user[s] = b

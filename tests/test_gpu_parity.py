@@ -1,0 +1,276 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars (the block's acceptance criteria):
+  - topk_idx, offsets, csr_rows, csr_pos: bitwise equal to the oracle;
+  - topk_w, csr_w: within 1e-6 absolute of the oracle, and csr_w bitwise
+    equal to the GPU's own topk_w at the same (row, expert);
+  - block output: relative Frobenius error <= 5e-3 and
+    max |gpu - ref| <= 1e-2 * max |ref| (bf16 activations and weights,
+    fp32 accumulation, against the oracle's double result).
+Full-size configs compare routing and CSR on every row and outputs on sampled
+rows that the oracle's brute-force path computes one by one.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import moe_synth as ms
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+REL_FRO = 5e-3
+MAX_ABS_REL = 1e-2
+W_ABS = 1e-6
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module")
+def mep():
+    import mixture_experts_prefill_amd as m
+
+    m.lib()
+    return m
+
+
+def run(mep, wl, resident=None, ring_slots=64, group=8, shared=True, force_ring=False):
+    blk = mep.MoeBlock.from_workload(wl, resident=resident, ring_slots=ring_slots, group=group, shared=shared)
+    if force_ring:
+        blk.use_ring(ring_slots, group)
+    blk.forward()
+    torch.cuda.synchronize()
+    g = dict(
+        topk_idx=blk.topk_idx.cpu().numpy().view(np.uint32),
+        topk_w=blk.topk_w.cpu().numpy(),
+        offsets=blk.offsets.cpu().numpy().view(np.uint32),
+        csr_rows=blk.csr_rows.cpu().numpy().view(np.uint32),
+        csr_w=blk.csr_w.cpu().numpy(),
+        csr_pos=blk.csr_pos.cpu().numpy().view(np.uint32),
+        out=blk.out.cpu().numpy(),
+    )
+    g["ring_stats"] = blk.ring.stats() if blk.ring is not None else None
+    del blk
+    return g
+
+
+def check_routing(g, r):
+    assert np.array_equal(g["topk_idx"], r["topk_idx"]), "top-k indices differ"
+    assert np.max(np.abs(g["topk_w"] - r["topk_w"])) <= W_ABS
+    assert np.array_equal(g["offsets"], r["offsets"]), "offsets differ"
+    assert np.array_equal(g["csr_rows"], r["csr_rows"]), "csr_rows differ"
+    assert np.array_equal(g["csr_pos"], r["csr_pos"]), "csr_pos differ"
+    assert np.max(np.abs(g["csr_w"] - r["csr_w"])) <= W_ABS
+    assert np.array_equal(g["csr_w"][g["csr_pos"]], g["topk_w"].reshape(-1)), "csr_w is not the GPU's topk_w"
+
+
+def check_out(got, ref):
+    ref = np.asarray(ref, dtype=np.float64)
+    d = got.astype(np.float64) - ref
+    fro = np.linalg.norm(d) / np.linalg.norm(ref)
+    mx = np.max(np.abs(d)) / np.max(np.abs(ref))
+    say(f"    rel_fro={fro:.2e} max_abs_rel={mx:.2e}")
+    assert fro <= REL_FRO and mx <= MAX_ABS_REL, (fro, mx)
+
+
+# ------------------------------------------------------------------ small shapes, full oracle
+
+@pytest.mark.parametrize("centred", [False, True])
+def test_tiny_config(mep, orc, centred):
+    wl = ms.make_workload("tiny", centred=centred)
+    g = run(mep, wl)
+    r = orc.block(wl)
+    check_routing(g, r)
+    check_out(g["out"], r["out"])
+
+
+SWEEP = [
+    # seed, t, h, I, E, k, G, centred, gate
+    (0, 1, 256, 64, 1, 1, 64, False, False),
+    (1, 7, 256, 128, 4, 2, 32, True, False),
+    (2, 33, 512, 192, 16, 3, 64, True, True),
+    (3, 64, 256, 64, 64, 10, 32, False, False),
+    (4, 65, 768, 128, 8, 8, 64, True, False),     # k = E: dense softmax mixture
+    (5, 40, 256, 256, 33, 5, 64, False, True),
+    (6, 129, 512, 128, 12, 4, 32, True, False),   # several M-tiles per expert, ragged tail
+    (7, 300, 256, 64, 3, 2, 64, True, False),     # > 100 rows per expert
+    (8, 16, 1024, 320, 30, 6, 32, True, True),    # inter not a multiple of 128
+]
+
+
+@pytest.mark.parametrize("case", SWEEP, ids=[f"s{c[0]}-t{c[1]}-h{c[2]}-I{c[3]}-E{c[4]}-k{c[5]}" for c in SWEEP])
+def test_small_sweep(mep, orc, case):
+    seed, t, h, I, E, k, G, centred, gate = case
+    wl = ms.small_case(seed, t, h, I, E, k, G, centred=centred, with_gate=gate)
+    g = run(mep, wl)
+    r = orc.block(wl)
+    check_routing(g, r)
+    check_out(g["out"], r["out"])
+
+
+def test_max_rows_small_dims(mep, orc):
+    """t = 4096 (the row cap) at small hidden size: CSR tiles of 64 rows, max tiles."""
+    wl = ms.small_case(9, 4096, 256, 64, 16, 4, 64, centred=True)
+    g = run(mep, wl)
+    r = orc.block(wl)
+    check_routing(g, r)
+    check_out(g["out"], r["out"])
+
+
+def test_no_shared_expert(mep, orc):
+    wl = ms.small_case(10, 50, 256, 128, 6, 2, 64, centred=True)
+    g = run(mep, wl, shared=False)
+    r = orc.block(wl, shared_expert=False)
+    check_routing(g, r)
+    check_out(g["out"], r["out"])
+
+
+# ------------------------------------------------------------------ the five workloads
+
+def test_mid_config(mep, orc):
+    wl = ms.make_workload("mid")
+    g = run(mep, wl)
+    say("  oracle mid ...")
+    r = orc.block(wl)
+    check_routing(g, r)
+    check_out(g["out"], r["out"])
+
+
+@pytest.mark.parametrize("name", ["decode", "decode1"])
+def test_decode_configs(mep, orc, name):
+    wl = ms.make_workload(name)
+    g = run(mep, wl)
+    say(f"  oracle {name} ...")
+    r = orc.block(wl)
+    check_routing(g, r)
+    check_out(g["out"], r["out"])
+
+
+def sample_rows(t, n, seed):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, t - 1], rng.choice(t, n, replace=False)])).astype(np.int32)
+
+
+def full_routing_ref(orc, wl):
+    lg = orc.router_logits(wl.x, wl.w_router)
+    idx, w = orc.topk(lg, wl.cfg.k)
+    offsets, rows, cw, pos = orc.build_csr(idx, w, wl.cfg.experts)
+    return dict(topk_idx=idx, topk_w=w, offsets=offsets, csr_rows=rows, csr_w=cw, csr_pos=pos)
+
+
+def test_full_config(mep, orc):
+    wl = ms.make_workload("full")
+    g = run(mep, wl)
+    say("  oracle routing full ...")
+    r = full_routing_ref(orc, wl)
+    check_routing(g, r)
+    s = sample_rows(wl.cfg.t, 40, 1)
+    say(f"  oracle brute force on {s.size} rows ...")
+    ref = orc.tokens_bruteforce(wl, s)
+    check_out(g["out"][s], ref)
+
+
+def test_large_config_streamed(mep, orc):
+    """Top-64 experts by row count resident, the rest streamed through a 64-slot ring in batches of 8."""
+    wl = ms.make_workload("large")
+    say("  oracle routing large ...")
+    r = full_routing_ref(orc, wl)
+    resident = orc.residency(r["offsets"], wl.cfg.resident)
+    g = run(mep, wl, resident=resident)
+    check_routing(g, r)
+    st = g["ring_stats"]
+    n_streamed = int(((np.diff(r["offsets"].astype(np.int64)) > 0) & ~resident).sum())
+    assert st["streamed"] == n_streamed and st["fetched_bytes"] == n_streamed * wl.layout.stride
+    g_res = run(mep, wl)
+    assert np.array_equal(g["out"], g_res["out"]), "ring output differs from all-resident output"
+    s = sample_rows(wl.cfg.t, 10, 2)
+    say(f"  oracle brute force on {s.size} rows ...")
+    ref = orc.tokens_bruteforce(wl, s)
+    check_out(g["out"][s], ref)
+
+
+# ------------------------------------------------------------------ invariants of the GPU path
+
+def test_ring_equals_resident_with_poison(mep, monkeypatch):
+    """A small ring (4 slots, batches of 2) with released slots poisoned must not change a bit."""
+    wl = ms.make_workload("mid")
+    base = run(mep, wl)
+    resident = np.zeros(wl.cfg.experts, dtype=bool)
+    resident[::5] = True
+    monkeypatch.setenv("MOE_RING_POISON", "1")
+    g = run(mep, wl, resident=resident, ring_slots=4, group=2)
+    assert np.array_equal(g["out"], base["out"])
+    monkeypatch.setenv("MOE_RING_POISON", "0")
+    monkeypatch.setenv("MOE_RING_DELAY_US", "200")
+    g2 = run(mep, wl, resident=resident, ring_slots=8, group=4)
+    assert np.array_equal(g2["out"], base["out"])
+
+
+def test_ring_with_everything_resident(mep):
+    wl = ms.make_workload("tiny")
+    a = run(mep, wl)
+    b = run(mep, wl, force_ring=True, ring_slots=2, group=1)
+    assert np.array_equal(a["out"], b["out"])
+
+
+def test_deterministic(mep):
+    wl = ms.small_case(11, 200, 512, 128, 16, 4, 64, centred=True)
+    a = run(mep, wl)
+    b = run(mep, wl)
+    for key in ("topk_idx", "topk_w", "offsets", "csr_rows", "csr_w", "csr_pos", "out"):
+        assert np.array_equal(a[key], b[key]), key
+
+
+def test_accumulate_semantics(mep, orc):
+    wl = ms.small_case(12, 24, 256, 128, 8, 2, 64, centred=True)
+    blk = mep.MoeBlock.from_workload(wl)
+    blk.out.fill_(float("nan"))
+    blk.shared(accumulate=0)
+    shared_only = blk.out.clone()
+    blk.route()
+    blk.build_csr()
+    blk.out.fill_(float("nan"))
+    blk.experts(accumulate=0)
+    experts_only = blk.out.clone()
+    blk.out.copy_(shared_only)
+    blk.experts(accumulate=1)
+    torch.cuda.synchronize()
+    assert torch.isfinite(shared_only).all() and torch.isfinite(experts_only).all()
+    ys = orc.shared(wl.shared_record, 256, 128, 64, wl.x)
+    check_out(shared_only.cpu().numpy(), ys)
+    r = orc.block(wl)
+    check_out(blk.out.cpu().numpy(), r["out"])
+    r0 = orc.block(wl, shared_expert=False)
+    check_out(experts_only.cpu().numpy(), r0["out"])
+
+
+def test_bad_arguments_leave_outputs_untouched(mep):
+    wl = ms.make_workload("tiny")
+    blk = mep.MoeBlock.from_workload(wl)
+    blk.out.fill_(7.0)
+    blk.topk_idx.fill_(-1)
+    with pytest.raises(mep.MoeError) as e:
+        mep.moe_route(blk.x, blk.w_router, 9, blk.logits, blk.topk_idx, blk.topk_w)   # k > E
+    assert e.value.status == 1
+    with pytest.raises(mep.MoeError) as e:
+        mep.moe_prefill_experts(blk.x, 2, 8, blk.L, blk.offsets, blk.csr_rows, blk.csr_w, blk.csr_pos, blk.table,
+                                blk.out, 1, blk.workspace[:1024])
+    assert e.value.status == 3
+    table = blk.table.clone()
+    table[3] = 0                                  # expert 3 not resident, no ring
+    blk.route()
+    blk.build_csr()
+    torch.cuda.synchronize()
+    if int(blk.offsets[4] - blk.offsets[3]) > 0:
+        ring_slots = torch.empty((4, blk.L.stride), dtype=torch.uint8, device="cuda")
+        ring = mep.MoeRing(blk.L, ring_slots, 4, 2)
+        with pytest.raises(mep.MoeError):
+            mep.moe_prefill_experts(blk.x, 2, 8, blk.L, blk.offsets, blk.csr_rows, blk.csr_w, blk.csr_pos, table,
+                                    blk.out, 1, blk.workspace, host_records=[None] * 8, ring=ring)
+        ring.close()
+    torch.cuda.synchronize()
+    assert bool((blk.out == 7.0).all())

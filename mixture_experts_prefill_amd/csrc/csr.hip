@@ -38,35 +38,57 @@ __global__ void __launch_bounds__(256) k_csr_count(const uint32_t *__restrict__ 
         hist[(size_t)tile * E + e] = (uint32_t)__popcll(mask[e]);
 }
 
-// One workgroup of 1024 threads: thread e walks the tiles of expert e
-// (exclusive running sum), then a block scan over experts gives offsets.
+// One workgroup of 1024 threads (16 waves).  Row tiles number at most
+// 4096 / 64 = 64, so a wave scans one expert's per-tile counts with lane =
+// tile (shuffle scan), 8 experts per pass with their loads issued together.
+// A block scan over the expert totals then gives the offsets, and every
+// (tile, expert) entry becomes its absolute segment start.
 __global__ void __launch_bounds__(1024) k_csr_scan(int tiles, int E, int total,
                                                    uint32_t *__restrict__ hist,
                                                    uint32_t *__restrict__ offsets) {
+    __shared__ uint32_t tot[1024];
     __shared__ uint32_t part[1024];
-    const int e = threadIdx.x;
-    uint32_t run = 0;
-    if (e < E)
-        for (int tl = 0; tl < tiles; ++tl) {
-            uint32_t c = hist[(size_t)tl * E + e];
-            hist[(size_t)tl * E + e] = run;
-            run += c;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    constexpr int kPass = 8;
+    for (int e0 = wave * kPass; e0 < E; e0 += 16 * kPass) {
+        uint32_t v[kPass];
+#pragma unroll
+        for (int j = 0; j < kPass; ++j)
+            v[j] = (lane < tiles && e0 + j < E) ? hist[(size_t)lane * E + e0 + j] : 0u;
+#pragma unroll
+        for (int j = 0; j < kPass; ++j) {
+            uint32_t incl = v[j];
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const uint32_t o = __shfl_up(incl, d, 64);
+                if (lane >= d) incl += o;
+            }
+            if (e0 + j < E) {
+                if (lane < tiles) hist[(size_t)lane * E + e0 + j] = incl - v[j];
+                if (lane == 63) tot[e0 + j] = incl;
+            }
         }
-    part[e] = (e < E) ? run : 0;
+    }
     __syncthreads();
-    // Hillis-Steele inclusive scan over 1024 entries.
-    for (int d = 1; d < 1024; d <<= 1) {
-        uint32_t v = (e >= d) ? part[e - d] : 0;
+    const uint32_t mine = tid < E ? tot[tid] : 0u;
+    part[tid] = mine;
+    __syncthreads();
+    for (int d = 1; d < 1024; d <<= 1) {  // Hillis-Steele inclusive scan
+        const uint32_t o = tid >= d ? part[tid - d] : 0u;
         __syncthreads();
-        part[e] += v;
+        part[tid] += o;
         __syncthreads();
     }
-    const uint32_t base = (e < E) ? part[e] - run : 0;  // exclusive
-    if (e < E) {
-        offsets[e] = base;
-        for (int tl = 0; tl < tiles; ++tl) hist[(size_t)tl * E + e] += base;
+    if (tid < E) {
+        tot[tid] = part[tid] - mine;  // exclusive: segment start of expert tid
+        offsets[tid] = part[tid] - mine;
     }
-    if (e == 0) offsets[E] = (uint32_t)total;
+    if (tid == 0) offsets[E] = (uint32_t)total;
+    __syncthreads();
+    for (int e0 = wave * kPass; e0 < E; e0 += 16 * kPass)
+#pragma unroll
+        for (int j = 0; j < kPass; ++j)
+            if (lane < tiles && e0 + j < E) hist[(size_t)lane * E + e0 + j] += tot[e0 + j];
 }
 
 __global__ void __launch_bounds__(256) k_csr_place(const uint32_t *__restrict__ idx,

@@ -17,8 +17,9 @@
 // feeds two MFMAs.  Per 64-wide K step:
 //   - the workgroup stages BM activation rows x 128 bytes into LDS (gathered
 //     through csr_rows for the routed gate/up projection), double-buffered,
-//     16-byte chunks XOR-swizzled by row so the B-fragment reads of 32 rows
-//     at one column hit distinct banks;
+//     each row padded to 144 bytes: 9 sixteen-byte bank groups per row is
+//     coprime with any power-of-two bank count, so the B-fragment reads of 32
+//     rows at one column hit distinct banks;
 //   - each wave loads its two 1 KB code tiles (one 16-byte load per lane,
 //     fully coalesced thanks to the record's tile order) and their fp16
 //     scale/bias pairs, and dequantises in registers: a nibble pair OR'ed
@@ -37,6 +38,16 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+// Pointers into device memory, so loads compile to global_* rather than flat_*.
+#define GLOBAL __attribute__((address_space(1)))
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_g16(const void *p) {
+    const u32x4 v = *reinterpret_cast<const GLOBAL u32x4 *>(reinterpret_cast<uintptr_t>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t ld_g4(const void *p) {
+    return *reinterpret_cast<const GLOBAL uint32_t *>(reinterpret_cast<uintptr_t>(p));
+}
 
 enum Mode { GU_GATHER = 0, GU_DENSE = 1, DOWN_YE = 2, DOWN_OUT = 3 };
 
@@ -45,42 +56,99 @@ __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
-// 8 codes of one 32-bit word -> 8 bf16 weights (element j = code j).
-__device__ __forceinline__ bf16x8 dequant8(uint32_t w, float s, float c) {
-    uint32_t o[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const uint32_t h = ((w >> (4 * p)) & 0x000F000Fu) | 0x64006400u;
-        const half2_t hv = __builtin_bit_cast(half2_t, h);
-        o[p] = pk_bf16(__builtin_fmaf((float)hv.x, s, c), __builtin_fmaf((float)hv.y, s, c));
-    }
-    uint4 u = make_uint4(o[0], o[1], o[2], o[3]);
+// Per-lane dequantisation constants of one (row, group): codes at nibble
+// positions 0-3 / 16-19 become fp16 1024 + q, codes at 4-7 / 20-23 become
+// 1024 + 16 q, so  w = v * s + (b - 1024 s)  or  w = v * (s/16) + (b - 64 s).
+struct Deq {
+    float s, c, s16, c16;
+};
+__device__ __forceinline__ Deq deq_consts(uint32_t sb) {
+    const half2_t h = __builtin_bit_cast(half2_t, sb);
+    const float s = (float)h.x, b = (float)h.y;
+    return Deq{s, __builtin_fmaf(-1024.0f, s, b), s * 0.0625f, __builtin_fmaf(-64.0f, s, b)};
+}
+
+// Loop-invariant bit masks kept in VGPRs: VOP3 on gfx950 takes no literal, so
+// hiding the constants lets the compiler form v_and_or_b32.
+struct Masks {
+    uint32_t lo, hi, magic;
+};
+__device__ __forceinline__ Masks make_masks() {
+    Masks m;
+    asm volatile("v_mov_b32 %0, 0xf000f" : "=v"(m.lo));
+    asm volatile("v_mov_b32 %0, 0xf000f0" : "=v"(m.hi));
+    asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(m.magic));
+    return m;
+}
+
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) { return (x & m) | c; }
+
+// 8 codes of one 32-bit word (code j at bit 4*(j/2) + 16*(j%2)) -> 8 bf16 weights.
+__device__ __forceinline__ bf16x8 dequant8(uint32_t w, const Deq &d, const Masks &m) {
+    const uint32_t w8 = w >> 8;
+    const half2_t p0 = __builtin_bit_cast(half2_t, and_or(w, m.lo, m.magic));   // q0, q1
+    const half2_t p1 = __builtin_bit_cast(half2_t, and_or(w, m.hi, m.magic));   // 16 q2, 16 q3
+    const half2_t p2 = __builtin_bit_cast(half2_t, and_or(w8, m.lo, m.magic));  // q4, q5
+    const half2_t p3 = __builtin_bit_cast(half2_t, and_or(w8, m.hi, m.magic));  // 16 q6, 16 q7
+    uint4 u;
+    u.x = pk_bf16(__builtin_fmaf((float)p0.x, d.s, d.c), __builtin_fmaf((float)p0.y, d.s, d.c));
+    u.y = pk_bf16(__builtin_fmaf((float)p1.x, d.s16, d.c16), __builtin_fmaf((float)p1.y, d.s16, d.c16));
+    u.z = pk_bf16(__builtin_fmaf((float)p2.x, d.s, d.c), __builtin_fmaf((float)p2.y, d.s, d.c));
+    u.w = pk_bf16(__builtin_fmaf((float)p3.x, d.s16, d.c16), __builtin_fmaf((float)p3.y, d.s16, d.c16));
     return __builtin_bit_cast(bf16x8, u);
 }
 
+// SiLU(g) * u with the hardware exp and reciprocal (about 1 ulp each).
 __device__ __forceinline__ float silu_mul(float g, float u) {
-    return g / (1.0f + __expf(-g)) * u;
+    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
-template <int MODE, int BM>
-__global__ void __launch_bounds__(256, 2) k_gemm(const GemmArgs a) {
+// Codes and scale/bias of a wave's two fragments for one 64-wide K step.
+struct Stage {
+    uint4 c[2];
+    uint32_t sb[2];
+};
+
+template <int MODE, int BM, int WAVES>
+__global__ void __launch_bounds__(64 * WAVES, (WAVES >= 8) ? 1 : 2) k_gemm(const GemmArgs a) {
     constexpr bool kGateUp = (MODE == GU_GATHER || MODE == GU_DENSE);
-    constexpr int TB = BM / 32;            // token blocks of 32
-    constexpr int CH = BM * 8 / 256;       // 16-byte row chunks staged per thread per K step
-    static_assert(BM % 32 == 0 && CH >= 1, "BM must be a multiple of 32");
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2][BM * 128];
+    constexpr bool kDense = (MODE == GU_DENSE || MODE == DOWN_OUT);
+    constexpr int NT = 64 * WAVES;
+    constexpr int TB = BM / 32;                         // token blocks of 32
+    constexpr int CHUNKS = BM * 8;                      // 16-byte chunks per staged K step
+    constexpr int CH = (CHUNKS + NT - 1) / NT;          // chunks per thread
+    constexpr int FEAT = kGateUp ? 32 * WAVES : 64 * WAVES;  // output features per workgroup
+    static_assert(BM % 32 == 0, "BM must be a multiple of 32");
+    constexpr int ROW = 144;                            // padded LDS row (bytes)
+    // Epilogue tile per wave: 32 token rows x C output columns, row padded by
+    // 16 bytes (an odd number of 16-byte bank groups).
+    constexpr int C = kGateUp ? 32 : 64;
+    constexpr int EB = (MODE == DOWN_OUT) ? 4 : 2;
+    constexpr int EROW = C * EB + 16;
+    constexpr int STAGE_BYTES = 2 * BM * ROW, EPI_BYTES = WAVES * 32 * EROW;
+    __shared__ __attribute__((aligned(16))) uint8_t lds_raw[STAGE_BYTES > EPI_BYTES ? STAGE_BYTES : EPI_BYTES];
+    uint8_t(*lds)[BM * ROW] = reinterpret_cast<uint8_t(*)[BM * ROW]>(lds_raw);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-    // ---- M-tile
+    // ---- which (M-tile, feature block): tiles of one XCD are contiguous in
+    // the logical order (expert-major, then M-tile, then feature block), so
+    // the CUs of an XCD share an expert's weights and rows in their L2.
+    const int n_out = kGateUp ? a.inter : a.hidden;
+    const int nblk = (n_out + FEAT - 1) / FEAT;
+    const int m_tiles = kDense ? (a.t + BM - 1) / BM : (int)*a.sched_n;
+    const int total = m_tiles * nblk;
+    const int chunk = (total + 7) >> 3;
+    const int logical = (blockIdx.x & 7) * chunk + (blockIdx.x >> 3);
+    if ((int)(blockIdx.x >> 3) >= chunk || logical >= total) return;
+    const int mt = logical / nblk, nb = logical % nblk;
+
     int expert = 0, p0, n;
-    if (MODE == GU_DENSE || MODE == DOWN_OUT) {
-        p0 = blockIdx.y * BM;
-        if (p0 >= a.t) return;
+    if (kDense) {
+        p0 = mt * BM;
         n = min(BM, a.t - p0);
     } else {
-        if (blockIdx.y >= *a.sched_n) return;
-        const int4 tl = a.sched[blockIdx.y];
+        const int4 tl = a.sched[mt];
         expert = tl.x;
         p0 = tl.y;
         n = tl.z;
@@ -88,63 +156,59 @@ __global__ void __launch_bounds__(256, 2) k_gemm(const GemmArgs a) {
     const uint8_t *rec = static_cast<const uint8_t *>(
         a.records ? reinterpret_cast<const void *>(a.records[expert]) : a.record);
 
-    // ---- features of this wave: two fragments of 32 rows of the weight matrix
-    const int n_out = kGateUp ? a.inter : a.hidden;   // rows of the weight matrix
-    const int K = kGateUp ? a.hidden : a.inter;       // reduction length
+    const int K = kGateUp ? a.hidden : a.inter;
     const int nk = K >> 6;
-    const int obs = n_out >> 5;                       // 32-row blocks
+    const int obs = n_out >> 5;
     int ob[2];
     if (kGateUp) {
-        ob[0] = ob[1] = blockIdx.x * 4 + wave;        // gate and up of the same features
+        ob[0] = ob[1] = nb * WAVES + wave;               // gate and up of the same 32 features
     } else {
-        ob[0] = blockIdx.x * 8 + wave * 2;
+        ob[0] = (nb * WAVES + wave) * 2;                 // two adjacent 32-feature blocks
         ob[1] = ob[0] + 1;
     }
     const bool live0 = ob[0] < obs, live1 = ob[1] < obs;
-    const uint64_t woff[2] = {a.w_off, kGateUp ? a.w2_off : a.w_off};
-    const uint64_t soff[2] = {a.sb_off, kGateUp ? a.sb2_off : a.sb_off};
+    const uint8_t *wbase[2], *sbase[2];
     const int sb_tile_bytes = (64 / a.group) * 32 * 4;
     const int sb_entry = (a.group == 64) ? (lane & 31) : lane;
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+        const bool live = f ? live1 : live0;
+        const size_t row0 = (size_t)(live ? ob[f] : 0) * nk;
+        const uint64_t wo = (kGateUp && f) ? a.w2_off : a.w_off;
+        const uint64_t so = (kGateUp && f) ? a.sb2_off : a.sb_off;
+        wbase[f] = rec + wo + row0 * 1024 + lane * 16;
+        sbase[f] = rec + so + row0 * sb_tile_bytes + sb_entry * 4;
+    }
 
-    // ---- B-operand source rows for the chunks this thread stages
+    // ---- activation rows this thread stages
     const uint16_t *src[CH];
     bool valid[CH];
     int lds_off[CH];
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-        const int ch = tid + 256 * c;
-        const int i = ch >> 3, q = ch & 7;   // tile row, 16-byte chunk
-        valid[c] = i < n;
+        const int ch = tid + NT * c;
+        const int i = ch >> 3, q = ch & 7;
+        valid[c] = ch < CHUNKS && i < n;
         const int ii = valid[c] ? i : 0;
         size_t row;
-        int ld;
-        if (MODE == GU_GATHER) {
+        if (MODE == GU_GATHER)
             row = a.rows[p0 + ii];
-            ld = a.hidden;
-        } else if (MODE == GU_DENSE) {
+        else
             row = (size_t)(p0 + ii);
-            ld = a.hidden;
-        } else {
-            row = (size_t)(p0 + ii);
-            ld = a.inter;
-        }
         const uint16_t *base = kGateUp ? a.x : a.act;
-        src[c] = base + row * ld + q * 8;
-        lds_off[c] = (i * 8 + (q ^ (i & 7))) * 16;
+        src[c] = base + row * (kGateUp ? a.hidden : a.inter) + q * 8;
+        lds_off[c] = (ch < CHUNKS) ? i * ROW + q * 16 : -1;
     }
 
-    auto load_b = [&](int kb, uint4 *v) {
+    auto load_x = [&](int kb, uint4 *v) {
 #pragma unroll
-        for (int c = 0; c < CH; ++c)
-            v[c] = valid[c] ? *reinterpret_cast<const uint4 *>(src[c] + kb * 64) : make_uint4(0, 0, 0, 0);
+        for (int c = 0; c < CH; ++c) v[c] = valid[c] ? ld_g16(src[c] + kb * 64) : make_uint4(0, 0, 0, 0);
     };
-    auto load_a = [&](int kb, uint4 *codes, uint32_t *sb) {
+    auto load_w = [&](int kb, Stage &st) {
 #pragma unroll
         for (int f = 0; f < 2; ++f) {
-            const bool live = f ? live1 : live0;
-            const size_t tile = (size_t)(live ? ob[f] : 0) * nk + kb;
-            codes[f] = *reinterpret_cast<const uint4 *>(rec + woff[f] + tile * 1024 + lane * 16);
-            sb[f] = *reinterpret_cast<const uint32_t *>(rec + soff[f] + tile * sb_tile_bytes + sb_entry * 4);
+            st.c[f] = ld_g16(wbase[f] + (size_t)kb * 1024);
+            st.sb[f] = ld_g4(sbase[f] + (size_t)kb * sb_tile_bytes);
         }
     };
 
@@ -156,96 +220,158 @@ __global__ void __launch_bounds__(256, 2) k_gemm(const GemmArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[f][b][r] = 0.0f;
 
-    uint4 bv[CH], codes[2];
-    uint32_t sb[2];
-    load_b(0, bv);
-    load_a(0, codes, sb);
-
-    // B-fragment read position: row (tb*32 + lane%32), chunk 4*(lane/32) + s.
+    const Masks msk = make_masks();
     const int brow = lane & 31, bhalf = lane >> 5;
 
-    for (int kb = 0; kb < nk; ++kb) {
+    uint4 xv[CH];
+    Stage s0, s1, s2;
+    load_x(0, xv);
+    load_w(0, s0);
+    if (nk > 1) load_w(1, s1);
+
+    // One K step: stage x[kb] into LDS, prefetch x[kb+1] and weights[kb+2]
+    // (into `nxt2`), then 4 MFMA steps per token block.  The weight fragments
+    // of MFMA step st+1 are dequantised while the MFMAs of step st run (the
+    // sched_group_barrier pattern interleaves them: one LDS read, two MFMAs,
+    // a slice of dequant VALU), and step 0 of the next K step is dequantised
+    // before the barrier, so the matrix core is fed as soon as LDS is ready.
+    auto frag = [&](const Stage &sg, int st, const Deq &d0, const Deq &d1, bf16x8 *out) {
+        const uint32_t w0 = st == 0 ? sg.c[0].x : st == 1 ? sg.c[0].y : st == 2 ? sg.c[0].z : sg.c[0].w;
+        const uint32_t w1 = st == 0 ? sg.c[1].x : st == 1 ? sg.c[1].y : st == 2 ? sg.c[1].z : sg.c[1].w;
+        out[0] = dequant8(w0, d0, msk);
+        out[1] = dequant8(w1, d1, msk);
+    };
+    bf16x8 af[2];
+    {
+        const Deq d0 = deq_consts(s0.sb[0]), d1 = deq_consts(s0.sb[1]);
+        frag(s0, 0, d0, d1, af);
+    }
+    auto step = [&](int kb, const Stage &cur, const Stage &nxt, Stage &nxt2) {
         uint8_t *buf = lds[kb & 1];
 #pragma unroll
-        for (int c = 0; c < CH; ++c) *reinterpret_cast<uint4 *>(buf + lds_off[c]) = bv[c];
-        const uint4 cur[2] = {codes[0], codes[1]};
-        const uint32_t csb[2] = {sb[0], sb[1]};
+        for (int c = 0; c < CH; ++c)
+            if (lds_off[c] >= 0) *reinterpret_cast<uint4 *>(buf + lds_off[c]) = xv[c];
         __syncthreads();
-        if (kb + 1 < nk) {
-            load_b(kb + 1, bv);
-            load_a(kb + 1, codes, sb);
-        }
-        float s[2], off[2];
+        if (kb + 1 < nk) load_x(kb + 1, xv);
+        if (kb + 2 < nk) load_w(kb + 2, nxt2);
+        const Deq d0 = deq_consts(cur.sb[0]), d1 = deq_consts(cur.sb[1]);
+        // B fragments are read one MFMA step ahead of their use.
+        bf16x8 bcur[TB];
 #pragma unroll
-        for (int f = 0; f < 2; ++f) {
-            const half2_t h = __builtin_bit_cast(half2_t, csb[f]);
-            s[f] = (float)h.x;
-            off[f] = __builtin_fmaf(-1024.0f, s[f], (float)h.y);
-        }
+        for (int b = 0; b < TB; ++b)
+            bcur[b] = *reinterpret_cast<const bf16x8 *>(buf + (b * 32 + brow) * ROW + (4 * bhalf) * 16);
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
-            bf16x8 af[2];
-            af[0] = dequant8(st == 0 ? cur[0].x : st == 1 ? cur[0].y : st == 2 ? cur[0].z : cur[0].w, s[0], off[0]);
-            af[1] = dequant8(st == 0 ? cur[1].x : st == 1 ? cur[1].y : st == 2 ? cur[1].z : cur[1].w, s[1], off[1]);
+            const bf16x8 a0 = af[0], a1 = af[1];
+            bf16x8 bnxt[TB];
+            if (st < 3) {
+#pragma unroll
+                for (int b = 0; b < TB; ++b)
+                    bnxt[b] = *reinterpret_cast<const bf16x8 *>(buf + (b * 32 + brow) * ROW + (4 * bhalf + st + 1) * 16);
+            }
+            if (st < 3) {
+                frag(cur, st + 1, d0, d1, af);
+            } else if (kb + 1 < nk) {
+                const Deq e0 = deq_consts(nxt.sb[0]), e1 = deq_consts(nxt.sb[1]);
+                frag(nxt, 0, e0, e1, af);
+            }
 #pragma unroll
             for (int b = 0; b < TB; ++b) {
-                const int row = b * 32 + brow;
-                const int q = (4 * bhalf + st) ^ (row & 7);
-                const bf16x8 bf = *reinterpret_cast<const bf16x8 *>(buf + (row * 8 + q) * 16);
-                acc[0][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0], bf, acc[0][b], 0, 0, 0);
-                acc[1][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1], bf, acc[1][b], 0, 0, 0);
+                acc[0][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bcur[b], acc[0][b], 0, 0, 0);
+                acc[1][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bcur[b], acc[1][b], 0, 0, 0);
+            }
+            if (st < 3) {
+#pragma unroll
+                for (int b = 0; b < TB; ++b) bcur[b] = bnxt[b];
+            }
+#pragma unroll
+            for (int b = 0; b < TB; ++b) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // 2 MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 36 / TB, 0);  // dequant VALU slice
             }
         }
+    };
+    // Unrolled by three so the weight stages rotate by renaming, not by copies.
+    for (int kb = 0; kb < nk; kb += 3) {
+        step(kb, s0, s1, s2);
+        if (kb + 1 < nk) step(kb + 1, s1, s2, s0);
+        if (kb + 2 < nk) step(kb + 2, s2, s0, s1);
     }
 
-    // ---- epilogue.  acc[f][b][r]: feature 8*(r/4) + 4*(lane/32) + r%4 of
-    // fragment f, token b*32 + lane%32 of the tile.
+    // ---- epilogue.  acc[f][b][r] holds feature 8*(r/4) + 4*(lane/32) + r%4 of
+    // fragment f for token b*32 + lane%32.  Each 32-token block goes through
+    // the wave's LDS tile so that global stores are whole 16-byte pieces of
+    // contiguous 64-256 byte row segments.
+    __syncthreads();  // every wave is done reading the staged activations
+    const bool wave_live = live0;
+    uint8_t *ep = lds_raw + wave * 32 * EROW;
+    const int col0 = ob[0] * 32;                         // first output feature of this wave
+    constexpr int CPR = C * EB / 16;                     // 16-byte chunks per row
+    constexpr int PER_LANE = 32 * CPR / 64;
 #pragma unroll
     for (int b = 0; b < TB; ++b) {
-        const int tok = b * 32 + brow;
-        if (tok >= n) continue;
-        const size_t p = (size_t)(p0 + tok);
-        if (kGateUp) {
-            if (!live0) continue;
+        if (!wave_live) break;
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int feat = ob[0] * 32 + 8 * q4 + 4 * bhalf;
+        for (int q4 = 0; q4 < 4; ++q4) {
+            if (kGateUp) {
                 uint2 v;
                 v.x = pk_bf16(silu_mul(acc[0][b][4 * q4 + 0], acc[1][b][4 * q4 + 0]),
                               silu_mul(acc[0][b][4 * q4 + 1], acc[1][b][4 * q4 + 1]));
                 v.y = pk_bf16(silu_mul(acc[0][b][4 * q4 + 2], acc[1][b][4 * q4 + 2]),
                               silu_mul(acc[0][b][4 * q4 + 3], acc[1][b][4 * q4 + 3]));
-                *reinterpret_cast<uint2 *>(a.hg + p * a.inter + feat) = v;
-            }
-        } else {
+                *reinterpret_cast<uint2 *>(ep + brow * EROW + (8 * q4 + 4 * bhalf) * 2) = v;
+            } else {
 #pragma unroll
-            for (int f = 0; f < 2; ++f) {
-                if (!(f ? live1 : live0)) continue;
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const int feat = ob[f] * 32 + 8 * q4 + 4 * bhalf;
+                for (int f = 0; f < 2; ++f) {
+                    const int col = f * 32 + 8 * q4 + 4 * bhalf;
                     if (MODE == DOWN_YE) {
                         uint2 v;
                         v.x = pk_bf16(acc[f][b][4 * q4 + 0], acc[f][b][4 * q4 + 1]);
                         v.y = pk_bf16(acc[f][b][4 * q4 + 2], acc[f][b][4 * q4 + 3]);
-                        *reinterpret_cast<uint2 *>(a.ye + p * a.hidden + feat) = v;
+                        *reinterpret_cast<uint2 *>(ep + brow * EROW + col * 2) = v;
                     } else {
-                        const float g = a.gate ? a.gate[p] : 1.0f;
-                        float4 *o = reinterpret_cast<float4 *>(a.out + p * a.hidden + feat);
-                        float4 v = make_float4(g * acc[f][b][4 * q4 + 0], g * acc[f][b][4 * q4 + 1],
-                                               g * acc[f][b][4 * q4 + 2], g * acc[f][b][4 * q4 + 3]);
-                        if (a.accumulate) {
-                            const float4 old = *o;
-                            v.x += old.x;
-                            v.y += old.y;
-                            v.z += old.z;
-                            v.w += old.w;
-                        }
-                        *o = v;
+                        *reinterpret_cast<float4 *>(ep + brow * EROW + col * 4) =
+                            make_float4(acc[f][b][4 * q4 + 0], acc[f][b][4 * q4 + 1], acc[f][b][4 * q4 + 2],
+                                        acc[f][b][4 * q4 + 3]);
                     }
                 }
             }
         }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+#pragma unroll
+        for (int i = 0; i < PER_LANE; ++i) {
+            const int idx = lane + 64 * i;
+            const int row = idx / CPR, ch = idx % CPR;
+            const int tok = b * 32 + row;
+            const int col = ch * 16 / EB;                // first column of the chunk
+            if (tok >= n || (!kGateUp && col >= 32 && !live1)) continue;
+            const size_t p = (size_t)(p0 + tok);
+            const uint4 v = *reinterpret_cast<const uint4 *>(ep + row * EROW + ch * 16);
+            if (MODE == GU_GATHER || MODE == GU_DENSE) {
+                *reinterpret_cast<uint4 *>(a.hg + p * a.inter + col0 + col) = v;
+            } else if (MODE == DOWN_YE) {
+                *reinterpret_cast<uint4 *>(a.ye + p * a.hidden + col0 + col) = v;
+            } else {
+                const float g = a.gate ? a.gate[p] : 1.0f;
+                float4 *o = reinterpret_cast<float4 *>(a.out + p * a.hidden + col0 + col);
+                float4 r = make_float4(g * __uint_as_float(v.x), g * __uint_as_float(v.y),
+                                       g * __uint_as_float(v.z), g * __uint_as_float(v.w));
+                if (a.accumulate) {
+                    const float4 old = *o;
+                    r.x += old.x;
+                    r.y += old.y;
+                    r.z += old.z;
+                    r.w += old.w;
+                }
+                *o = r;
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     }
 }
 
@@ -306,20 +432,32 @@ __global__ void __launch_bounds__(256) k_shared_gate(const uint16_t *__restrict_
     if (lane == 0) g[r] = 1.0f / (1.0f + expf(-s));
 }
 
+template <int MODE, int WAVES>
+hipError_t launch_waves(const GemmArgs &a, int bm, hipStream_t s) {
+    const bool gu = (MODE == GU_GATHER || MODE == GU_DENSE);
+    const bool dense = (MODE == GU_DENSE || MODE == DOWN_OUT);
+    const int n_out = gu ? a.inter : a.hidden;
+    const int feat = gu ? 32 * WAVES : 64 * WAVES;
+    const int nblk = (n_out + feat - 1) / feat;
+    const int tiles = dense ? (a.t + bm - 1) / bm : a.max_tiles;
+    // 1-D grid, rounded so every XCD slot of the remap exists
+    const int grid = ((tiles * nblk + 7) / 8) * 8 + 8;
+    switch (bm) {
+    case 32: hipLaunchKernelGGL((k_gemm<MODE, 32, WAVES>), dim3(grid), dim3(64 * WAVES), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((k_gemm<MODE, 64, WAVES>), dim3(grid), dim3(64 * WAVES), 0, s, a); break;
+    default: hipLaunchKernelGGL((k_gemm<MODE, 128, WAVES>), dim3(grid), dim3(64 * WAVES), 0, s, a); break;
+    }
+    return hipGetLastError();
+}
+
 template <int MODE>
 hipError_t launch_mode(const GemmArgs &a, int bm, hipStream_t s) {
     const bool gu = (MODE == GU_GATHER || MODE == GU_DENSE);
     const int n_out = gu ? a.inter : a.hidden;
-    const int per_wg = gu ? 128 : 256;
-    const bool dense = (MODE == GU_DENSE || MODE == DOWN_OUT);
-    const int tiles = dense ? (a.t + bm - 1) / bm : a.max_tiles;
-    const dim3 grid((n_out + per_wg - 1) / per_wg, tiles);
-    switch (bm) {
-    case 32: hipLaunchKernelGGL((k_gemm<MODE, 32>), grid, dim3(256), 0, s, a); break;
-    case 64: hipLaunchKernelGGL((k_gemm<MODE, 64>), grid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((k_gemm<MODE, 128>), grid, dim3(256), 0, s, a); break;
-    }
-    return hipGetLastError();
+    // 8 waves when the feature dimension fills them, so each staged activation
+    // tile serves 256 (gate/up) or 512 (down) features.
+    const bool wide = gu ? n_out >= 256 : n_out >= 512;
+    return wide ? launch_waves<MODE, 8>(a, bm, s) : launch_waves<MODE, 4>(a, bm, s);
 }
 
 }  // namespace

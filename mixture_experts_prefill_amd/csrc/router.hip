@@ -113,6 +113,111 @@ __global__ void __launch_bounds__(256) k_router(const uint16_t *__restrict__ x,
     }
 }
 
+// Large-t router: a workgroup of 8 waves owns 32 rows x 32 experts; every
+// 256-element step stages the rows' x chunks (16 KB) and the experts' W
+// chunks (32 KB) in LDS once, double-buffered, and each wave computes
+// 16 rows x 8 experts from LDS (lane l still owns partial l of every logit).
+constexpr int kLR = 32, kLE = 32;             // rows, experts per workgroup
+constexpr int kWR = 16, kWE = 8;              // rows, experts per wave
+constexpr int kXBytes = kLR * 512, kWBytes = kLE * 1024;
+
+__global__ void __launch_bounds__(512, 1) k_router_lds(const uint16_t *__restrict__ x,
+                                                       const float *__restrict__ w, int t, int h,
+                                                       int E, float *__restrict__ logits) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2][kXBytes + kWBytes];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int e_blocks = (E + kLE - 1) / kLE;
+    const int r0 = (blockIdx.x / e_blocks) * kLR, e0 = (blockIdx.x % e_blocks) * kLE;
+    const int wr = (wave >> 2) * kWR, we = (wave & 3) * kWE;   // this wave's rows / experts in the tile
+
+    // Staging: 16-byte chunks, x first (32 rows x 32 chunks) then W (32 x 64).
+    constexpr int kChunks = (kXBytes + kWBytes) / 16, kPer = kChunks / 512;
+    const uint8_t *src[kPer];
+    bool ok[kPer];
+#pragma unroll
+    for (int c = 0; c < kPer; ++c) {
+        const int ch = tid + 512 * c;
+        if (ch < kXBytes / 16) {
+            const int r = ch >> 5, q = ch & 31;
+            ok[c] = r0 + r < t;
+            src[c] = reinterpret_cast<const uint8_t *>(x + (size_t)min(r0 + r, t - 1) * h) + q * 16;
+        } else {
+            const int cw = ch - kXBytes / 16;
+            const int e = cw >> 6, q = cw & 63;
+            ok[c] = e0 + e < E;
+            src[c] = reinterpret_cast<const uint8_t *>(w + (size_t)min(e0 + e, E - 1) * h) + q * 16;
+        }
+    }
+    // step s covers elements [256 s, 256 s + 256): x bytes 512 s, W bytes 1024 s
+    auto load = [&](int s, uint4 *v) {
+#pragma unroll
+        for (int c = 0; c < kPer; ++c) {
+            const int ch = tid + 512 * c;
+            const size_t off = (ch < kXBytes / 16) ? (size_t)s * 512 : (size_t)s * 1024;
+            v[c] = ok[c] ? *reinterpret_cast<const uint4 *>(src[c] + off) : make_uint4(0, 0, 0, 0);
+        }
+    };
+
+    float p[kWR * kWE];
+#pragma unroll
+    for (int o = 0; o < kWR * kWE; ++o) p[o] = 0.0f;
+
+    uint4 v[kPer];
+    load(0, v);
+    const int steps = h >> 8;
+    for (int s = 0; s < steps; ++s) {
+        uint8_t *buf = lds[s & 1];
+#pragma unroll
+        for (int c = 0; c < kPer; ++c) *reinterpret_cast<uint4 *>(buf + (tid + 512 * c) * 16) = v[c];
+        __syncthreads();
+        if (s + 1 < steps) load(s + 1, v);
+        float wv[kWE][4];
+#pragma unroll
+        for (int j = 0; j < kWE; ++j) {
+            const float4 q = *reinterpret_cast<const float4 *>(buf + kXBytes + (we + j) * 1024 + lane * 16);
+            wv[j][0] = q.x;
+            wv[j][1] = q.y;
+            wv[j][2] = q.z;
+            wv[j][3] = q.w;
+        }
+#pragma unroll
+        for (int i = 0; i < kWR; ++i) {
+            const uint2 q = *reinterpret_cast<const uint2 *>(buf + (wr + i) * 512 + lane * 8);
+            const float x0 = bf16_lo(q.x), x1 = bf16_hi(q.x), x2 = bf16_lo(q.y), x3 = bf16_hi(q.y);
+#pragma unroll
+            for (int j = 0; j < kWE; ++j) {
+                float &acc = p[i * kWE + j];
+                acc = __builtin_fmaf(x0, wv[j][0], acc);
+                acc = __builtin_fmaf(x1, wv[j][1], acc);
+                acc = __builtin_fmaf(x2, wv[j][2], acc);
+                acc = __builtin_fmaf(x3, wv[j][3], acc);
+            }
+        }
+    }
+
+    // Transposed butterfly over the 64 partials: 6 splitting levels leave
+    // outputs 2*lane and 2*lane + 1 (row (2 lane)/8, experts (2 lane)%8, +1).
+#pragma unroll
+    for (int lvl = 0; lvl < 6; ++lvl) {
+        const int off = 32 >> lvl;
+        const int half = (kWR * kWE) >> (lvl + 1);
+        const uint32_t m = (lane & off) ? 0xffffffffu : 0u;
+#pragma unroll
+        for (int o = 0; o < half; ++o) {
+            const uint32_t lo = __float_as_uint(p[o]), hi = __float_as_uint(p[o + half]);
+            const float keep = __uint_as_float((lo & ~m) | (hi & m));
+            const float give = __uint_as_float((hi & ~m) | (lo & m));
+            p[o] = keep + __shfl_xor(give, off, 64);
+        }
+    }
+    const int o = 2 * lane, i = o / kWE, j = o % kWE;
+    const int r = r0 + wr + i, e = e0 + we + j;
+    if (r < t) {
+        if (e < E) logits[(size_t)r * E + e] = p[0];
+        if (e + 1 < E) logits[(size_t)r * E + e + 1] = p[1];
+    }
+}
+
 // Orderable key of a finite float: larger float -> larger key; -0 == +0.
 __device__ __forceinline__ uint32_t order_key(float f) {
     uint32_t u = __float_as_uint(f == 0.0f ? 0.0f : f);
@@ -179,7 +284,12 @@ hipError_t launch_router_logits(const uint16_t *x, const float *w, int t, int h,
                                 float *logits, hipStream_t s) {
     ProfileScope prof(MOE_PHASE_ROUTER, s);
     // Small t: one row block and one expert per wave keeps >= E waves busy
-    // streaming W; large t: 8 x 8 tiles reuse each loaded chunk 8 times.
+    // streaming W; large t: LDS-shared 32 x 32 tiles.
+    if (t >= 128 && E >= 32) {
+        const int blocks = ((t + kLR - 1) / kLR) * ((E + kLE - 1) / kLE);
+        hipLaunchKernelGGL(k_router_lds, dim3(blocks), dim3(512), 0, s, x, w, t, h, E, logits);
+        return hipGetLastError();
+    }
     if (t >= 64 && E >= 8) return launch_tile<8, 8>(x, w, t, h, E, logits, s);
     if (t >= 8) return launch_tile<8, 1>(x, w, t, h, E, logits, s);
     if (t >= 4) return launch_tile<4, 1>(x, w, t, h, E, logits, s);

@@ -99,6 +99,8 @@ SWEEP = [
     (6, 129, 512, 128, 12, 4, 32, True, False),   # several M-tiles per expert, ragged tail
     (7, 300, 256, 64, 3, 2, 64, True, False),     # > 100 rows per expert
     (8, 16, 1024, 320, 30, 6, 32, True, True),    # inter not a multiple of 128
+    (9, 161, 256, 64, 37, 4, 64, True, False),    # LDS router tile with ragged rows and experts
+    (10, 130, 768, 128, 96, 6, 32, False, False), # LDS router, 3 steps of 256
 ]
 
 

@@ -109,25 +109,75 @@ struct Stage {
     uint32_t sb[2];
 };
 
+// Staged activation rows are 128 bytes (8 chunks of 16 bytes); chunk c of row r
+// sits at position c ^ xswz(r).  For the 32 rows a B-fragment read touches at
+// one logical chunk this gives 32 distinct 16-byte bank groups modulo 8, 16
+// and 32, i.e. no bank conflicts for 32-, 64- or 128-bank LDS.
+__device__ __forceinline__ int xswz(int r) { return (r ^ (r >> 3)) & 7; }
+
+#define LOCAL __attribute__((address_space(3)))
+
+// Workgroup barrier without a memory fence.  __syncthreads() carries a
+// workgroup release fence, which makes the compiler wait for every
+// outstanding vector-memory operation (vmcnt(0)) -- that would drain the
+// prefetch pipeline at every K step.  Here the caller has already waited for
+// the loads it needs; lgkmcnt(0) completes this wave's LDS operations, and
+// the signal fences keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void barrier_no_fence() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt((15 << 0) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Direct global -> LDS loads (global_load_lds_dword[x4]): lane i's 4 or 16
+// bytes land at LDS byte m0 + 4i / 16i.  Issued from inline assembly so that
+// the compiler does not model them: its wait-count pass would otherwise make
+// every later LDS read wait for all of them (vmcnt(0)), which defeats the
+// prefetch.  Callers wait with explicit vmcnt counts before reading a slot;
+// the "memory" clobber keeps other memory accesses from moving across.
+__device__ __forceinline__ void dma16(uint32_t lds_addr, const void *src) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(src)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(uint32_t lds_addr, const void *src) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(src)
+                 : "memory", "m0");
+}
+
+// vmcnt(n) only (expcnt and lgkmcnt left at their no-wait maxima).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 template <int MODE, int BM, int WAVES>
-__global__ void __launch_bounds__(64 * WAVES, (WAVES >= 8) ? 1 : 2) k_gemm(const GemmArgs a) {
+__global__ void __launch_bounds__(64 * WAVES, (WAVES >= 8 || BM >= 256) ? 1 : 2) k_gemm(const GemmArgs a) {
     constexpr bool kGateUp = (MODE == GU_GATHER || MODE == GU_DENSE);
     constexpr bool kDense = (MODE == GU_DENSE || MODE == DOWN_OUT);
-    constexpr int NT = 64 * WAVES;
     constexpr int TB = BM / 32;                         // token blocks of 32
-    constexpr int CHUNKS = BM * 8;                      // 16-byte chunks per staged K step
-    constexpr int CH = (CHUNKS + NT - 1) / NT;          // chunks per thread
+    constexpr int XBLK = BM / 8;                        // 1 KB blocks (8 rows) per staged K step
+    constexpr int XPW = XBLK / WAVES;                   // direct-to-LDS loads per wave per K step
+    static_assert(BM % 32 == 0 && XBLK % WAVES == 0 && XPW >= 1, "every wave stages whole row blocks");
+    constexpr int XSTAGE = BM * 128;                    // staged activation rows of one K step
+    constexpr int WSTAGE = WAVES * 2 * (1024 + 256);    // per wave: 2 code tiles + 2 scale/bias blocks
+    constexpr int STAGE = XSTAGE + WSTAGE;
+    // ring depth: 3 K steps of lookahead when four stages fit in 160 KB of LDS, else 2
+    constexpr int NS = (4 * STAGE <= 160 * 1024) ? 4 : 3;
     constexpr int FEAT = kGateUp ? 32 * WAVES : 64 * WAVES;  // output features per workgroup
-    static_assert(BM % 32 == 0, "BM must be a multiple of 32");
-    constexpr int ROW = 144;                            // padded LDS row (bytes)
-    // Epilogue tile per wave: 32 token rows x C output columns, row padded by
-    // 16 bytes (an odd number of 16-byte bank groups).
-    constexpr int C = kGateUp ? 32 : 64;
+    constexpr int VM_PER_STEP = XPW + 4;                // vector-memory ops a wave issues per K step
+    // Epilogue: per wave 32 token rows x 32 columns, row padded by 16 bytes.
     constexpr int EB = (MODE == DOWN_OUT) ? 4 : 2;
-    constexpr int EROW = C * EB + 16;
-    constexpr int STAGE_BYTES = 2 * BM * ROW, EPI_BYTES = WAVES * 32 * EROW;
-    __shared__ __attribute__((aligned(16))) uint8_t lds_raw[STAGE_BYTES > EPI_BYTES ? STAGE_BYTES : EPI_BYTES];
-    uint8_t(*lds)[BM * ROW] = reinterpret_cast<uint8_t(*)[BM * ROW]>(lds_raw);
+    constexpr int EROW = 32 * EB + 16;
+    constexpr int RING = NS * STAGE, EPI = WAVES * 32 * EROW;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[RING > EPI ? RING : EPI];
+    // LDS byte address of the ring (wave-uniform, for the DMA's M0).
+    const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds_raw));
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
@@ -180,35 +230,46 @@ __global__ void __launch_bounds__(64 * WAVES, (WAVES >= 8) ? 1 : 2) k_gemm(const
         sbase[f] = rec + so + row0 * sb_tile_bytes + sb_entry * 4;
     }
 
-    // ---- activation rows this thread stages
-    const uint16_t *src[CH];
-    bool valid[CH];
-    int lds_off[CH];
+    // ---- activation rows this wave stages: block blk = wave*XPW + j covers
+    // rows 8*blk .. 8*blk+7; lane s writes LDS bytes 16 s of the block, which
+    // hold chunk (s%8) ^ xswz(row) of row 8*blk + s/8.  Rows past the tile
+    // load row 0 of the tile (never read back for a stored output).
+    const uint16_t *xsrc[XPW];
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-        const int ch = tid + NT * c;
-        const int i = ch >> 3, q = ch & 7;
-        valid[c] = ch < CHUNKS && i < n;
-        const int ii = valid[c] ? i : 0;
+    for (int j = 0; j < XPW; ++j) {
+        const int r = (wave * XPW + j) * 8 + (lane >> 3);
+        const int rr = r < n ? r : 0;
         size_t row;
         if (MODE == GU_GATHER)
-            row = a.rows[p0 + ii];
+            row = a.rows[p0 + rr];
         else
-            row = (size_t)(p0 + ii);
+            row = (size_t)(p0 + rr);
         const uint16_t *base = kGateUp ? a.x : a.act;
-        src[c] = base + row * (kGateUp ? a.hidden : a.inter) + q * 8;
-        lds_off[c] = (ch < CHUNKS) ? i * ROW + q * 16 : -1;
+        xsrc[j] = base + row * (kGateUp ? a.hidden : a.inter) + ((lane & 7) ^ xswz(r)) * 8;
     }
-
-    auto load_x = [&](int kb, uint4 *v) {
+    // Everything a K step needs goes straight from global memory into its
+    // ring slot by DMA (global_load_lds): the wave's share of the activation
+    // rows, its two 1 KB code tiles and their scale/bias entries.  No loop
+    // load has a register destination, so the only waits are the explicit
+    // vmcnt counts below.
+    auto wcode = [&](int slot, int f) { return (slot % NS) * STAGE + XSTAGE + (wave * 2 + f) * 1024; };
+    auto wsb = [&](int slot, int f) { return (slot % NS) * STAGE + XSTAGE + WAVES * 2048 + (wave * 2 + f) * 256; };
+    auto issue = [&](int ks, int slot) {
+        const uint32_t xd = lds_base + (slot % NS) * STAGE + wave * XPW * 1024;
 #pragma unroll
-        for (int c = 0; c < CH; ++c) v[c] = valid[c] ? ld_g16(src[c] + kb * 64) : make_uint4(0, 0, 0, 0);
-    };
-    auto load_w = [&](int kb, Stage &st) {
+        for (int j = 0; j < XPW; ++j) dma16(xd + j * 1024, xsrc[j] + ks * 64);
 #pragma unroll
         for (int f = 0; f < 2; ++f) {
-            st.c[f] = ld_g16(wbase[f] + (size_t)kb * 1024);
-            st.sb[f] = ld_g4(sbase[f] + (size_t)kb * sb_tile_bytes);
+            dma16(lds_base + wcode(slot, f), wbase[f] + (size_t)ks * 1024);
+            dma4(lds_base + wsb(slot, f), sbase[f] + (size_t)ks * sb_tile_bytes);
+        }
+    };
+    // This wave's weights of the K step in `slot`, from LDS.
+    auto read_w = [&](int slot, Stage &st) {
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+            st.c[f] = *reinterpret_cast<const uint4 *>(lds_raw + wcode(slot, f) + lane * 16);
+            st.sb[f] = *reinterpret_cast<const uint32_t *>(lds_raw + wsb(slot, f) + lane * 4);
         }
     };
 
@@ -222,44 +283,50 @@ __global__ void __launch_bounds__(64 * WAVES, (WAVES >= 8) ? 1 : 2) k_gemm(const
 
     const Masks msk = make_masks();
     const int brow = lane & 31, bhalf = lane >> 5;
+    int bsw[TB];                                           // xswz of this lane's B rows
+#pragma unroll
+    for (int b = 0; b < TB; ++b) bsw[b] = xswz(b * 32 + brow);
 
-    uint4 xv[CH];
-    Stage s0, s1, s2;
-    load_x(0, xv);
-    load_w(0, s0);
-    if (nk > 1) load_w(1, s1);
+    // prologue: K steps 0..2 in flight.  Every step issues the same loads --
+    // past the last step it reloads step nk-1 into a free slot -- so exactly
+    // two steps' loads are always newer than the one being consumed.
+#pragma unroll
+    for (int j = 0; j < NS - 1; ++j) issue(min(j, nk - 1), j);
 
-    // One K step: stage x[kb] into LDS, prefetch x[kb+1] and weights[kb+2]
-    // (into `nxt2`), then 4 MFMA steps per token block.  The weight fragments
-    // of MFMA step st+1 are dequantised while the MFMAs of step st run (the
-    // sched_group_barrier pattern interleaves them: one LDS read, two MFMAs,
-    // a slice of dequant VALU), and step 0 of the next K step is dequantised
-    // before the barrier, so the matrix core is fed as soon as LDS is ready.
     auto frag = [&](const Stage &sg, int st, const Deq &d0, const Deq &d1, bf16x8 *out) {
         const uint32_t w0 = st == 0 ? sg.c[0].x : st == 1 ? sg.c[0].y : st == 2 ? sg.c[0].z : sg.c[0].w;
         const uint32_t w1 = st == 0 ? sg.c[1].x : st == 1 ? sg.c[1].y : st == 2 ? sg.c[1].z : sg.c[1].w;
         out[0] = dequant8(w0, d0, msk);
         out[1] = dequant8(w1, d1, msk);
     };
+    // Step 0's own loads must have landed before its weights are read.
+    wait_vm<(NS - 2) * VM_PER_STEP>();
+    Stage cur;
+    read_w(0, cur);
     bf16x8 af[2];
     {
-        const Deq d0 = deq_consts(s0.sb[0]), d1 = deq_consts(s0.sb[1]);
-        frag(s0, 0, d0, d1, af);
-    }
-    auto step = [&](int kb, const Stage &cur, const Stage &nxt, Stage &nxt2) {
-        uint8_t *buf = lds[kb & 1];
-#pragma unroll
-        for (int c = 0; c < CH; ++c)
-            if (lds_off[c] >= 0) *reinterpret_cast<uint4 *>(buf + lds_off[c]) = xv[c];
-        __syncthreads();
-        if (kb + 1 < nk) load_x(kb + 1, xv);
-        if (kb + 2 < nk) load_w(kb + 2, nxt2);
         const Deq d0 = deq_consts(cur.sb[0]), d1 = deq_consts(cur.sb[1]);
-        // B fragments are read one MFMA step ahead of their use.
+        frag(cur, 0, d0, d1, af);
+    }
+
+    // K step kb (its loads have landed: waited for at the end of step kb-1).
+    // The barrier makes every wave's share of the activation block visible
+    // and frees the slot of step kb-1, which then receives step kb+3.  The
+    // weight fragments of MFMA step st+1 are dequantised while the MFMAs of
+    // step st run (sched_group_barrier interleaves one LDS read, two MFMAs
+    // and a slice of dequant VALU).  At the end, once step kb+1's loads have
+    // landed (two newer steps may still be in flight), its weights are read
+    // and its first fragment dequantised.
+    for (int kb = 0; kb < nk; ++kb) {
+        barrier_no_fence();
+        issue(min(kb + NS - 1, nk - 1), kb + NS - 1);
+        const uint8_t *buf = lds_raw + (kb % NS) * STAGE;
+        const Deq d0 = deq_consts(cur.sb[0]), d1 = deq_consts(cur.sb[1]);
+        Stage nxt;
         bf16x8 bcur[TB];
 #pragma unroll
         for (int b = 0; b < TB; ++b)
-            bcur[b] = *reinterpret_cast<const bf16x8 *>(buf + (b * 32 + brow) * ROW + (4 * bhalf) * 16);
+            bcur[b] = *reinterpret_cast<const bf16x8 *>(buf + (b * 32 + brow) * 128 + ((4 * bhalf) ^ bsw[b]) * 16);
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
             const bf16x8 a0 = af[0], a1 = af[1];
@@ -267,11 +334,12 @@ __global__ void __launch_bounds__(64 * WAVES, (WAVES >= 8) ? 1 : 2) k_gemm(const
             if (st < 3) {
 #pragma unroll
                 for (int b = 0; b < TB; ++b)
-                    bnxt[b] = *reinterpret_cast<const bf16x8 *>(buf + (b * 32 + brow) * ROW + (4 * bhalf + st + 1) * 16);
-            }
-            if (st < 3) {
+                    bnxt[b] = *reinterpret_cast<const bf16x8 *>(buf + (b * 32 + brow) * 128 +
+                                                                 ((4 * bhalf + st + 1) ^ bsw[b]) * 16);
                 frag(cur, st + 1, d0, d1, af);
-            } else if (kb + 1 < nk) {
+            } else {
+                wait_vm<(NS - 2) * VM_PER_STEP>();
+                read_w(kb + 1, nxt);                       // past the end: a reloaded step, unused
                 const Deq e0 = deq_consts(nxt.sb[0]), e1 = deq_consts(nxt.sb[1]);
                 frag(nxt, 0, e0, e1, af);
             }
@@ -291,87 +359,82 @@ __global__ void __launch_bounds__(64 * WAVES, (WAVES >= 8) ? 1 : 2) k_gemm(const
                 __builtin_amdgcn_sched_group_barrier(0x002, 36 / TB, 0);  // dequant VALU slice
             }
         }
-    };
-    // Unrolled by three so the weight stages rotate by renaming, not by copies.
-    for (int kb = 0; kb < nk; kb += 3) {
-        step(kb, s0, s1, s2);
-        if (kb + 1 < nk) step(kb + 1, s1, s2, s0);
-        if (kb + 2 < nk) step(kb + 2, s2, s0, s1);
+        cur = nxt;
     }
+    wait_vm<0>();  // retire the trailing (unused) loads before the ring is reused
 
     // ---- epilogue.  acc[f][b][r] holds feature 8*(r/4) + 4*(lane/32) + r%4 of
-    // fragment f for token b*32 + lane%32.  Each 32-token block goes through
-    // the wave's LDS tile so that global stores are whole 16-byte pieces of
-    // contiguous 64-256 byte row segments.
-    __syncthreads();  // every wave is done reading the staged activations
-    const bool wave_live = live0;
+    // fragment f for token b*32 + lane%32.  Each 32-token block of one
+    // fragment goes through the wave's LDS tile so that global stores are
+    // whole 16-byte pieces of contiguous 64 or 128 byte row segments.
+    __syncthreads();  // every wave is done reading the ring
+    if (!live0) return;
     uint8_t *ep = lds_raw + wave * 32 * EROW;
-    const int col0 = ob[0] * 32;                         // first output feature of this wave
-    constexpr int CPR = C * EB / 16;                     // 16-byte chunks per row
+    constexpr int CPR = 32 * EB / 16;                    // 16-byte chunks per row
     constexpr int PER_LANE = 32 * CPR / 64;
+    constexpr int PASSES = kGateUp ? 1 : 2;
 #pragma unroll
     for (int b = 0; b < TB; ++b) {
-        if (!wave_live) break;
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            if (kGateUp) {
-                uint2 v;
-                v.x = pk_bf16(silu_mul(acc[0][b][4 * q4 + 0], acc[1][b][4 * q4 + 0]),
-                              silu_mul(acc[0][b][4 * q4 + 1], acc[1][b][4 * q4 + 1]));
-                v.y = pk_bf16(silu_mul(acc[0][b][4 * q4 + 2], acc[1][b][4 * q4 + 2]),
-                              silu_mul(acc[0][b][4 * q4 + 3], acc[1][b][4 * q4 + 3]));
-                *reinterpret_cast<uint2 *>(ep + brow * EROW + (8 * q4 + 4 * bhalf) * 2) = v;
-            } else {
+        for (int f = 0; f < PASSES; ++f) {
+            if (f == 1 && !live1) break;
 #pragma unroll
-                for (int f = 0; f < 2; ++f) {
-                    const int col = f * 32 + 8 * q4 + 4 * bhalf;
-                    if (MODE == DOWN_YE) {
-                        uint2 v;
-                        v.x = pk_bf16(acc[f][b][4 * q4 + 0], acc[f][b][4 * q4 + 1]);
-                        v.y = pk_bf16(acc[f][b][4 * q4 + 2], acc[f][b][4 * q4 + 3]);
-                        *reinterpret_cast<uint2 *>(ep + brow * EROW + col * 2) = v;
-                    } else {
-                        *reinterpret_cast<float4 *>(ep + brow * EROW + col * 4) =
-                            make_float4(acc[f][b][4 * q4 + 0], acc[f][b][4 * q4 + 1], acc[f][b][4 * q4 + 2],
-                                        acc[f][b][4 * q4 + 3]);
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int col = 8 * q4 + 4 * bhalf;
+                if (kGateUp) {
+                    uint2 v;
+                    v.x = pk_bf16(silu_mul(acc[0][b][4 * q4 + 0], acc[1][b][4 * q4 + 0]),
+                                  silu_mul(acc[0][b][4 * q4 + 1], acc[1][b][4 * q4 + 1]));
+                    v.y = pk_bf16(silu_mul(acc[0][b][4 * q4 + 2], acc[1][b][4 * q4 + 2]),
+                                  silu_mul(acc[0][b][4 * q4 + 3], acc[1][b][4 * q4 + 3]));
+                    *reinterpret_cast<uint2 *>(ep + brow * EROW + col * 2) = v;
+                } else if (MODE == DOWN_YE) {
+                    uint2 v;
+                    v.x = pk_bf16(acc[f][b][4 * q4 + 0], acc[f][b][4 * q4 + 1]);
+                    v.y = pk_bf16(acc[f][b][4 * q4 + 2], acc[f][b][4 * q4 + 3]);
+                    *reinterpret_cast<uint2 *>(ep + brow * EROW + col * 2) = v;
+                } else {
+                    *reinterpret_cast<float4 *>(ep + brow * EROW + col * 4) =
+                        make_float4(acc[f][b][4 * q4 + 0], acc[f][b][4 * q4 + 1], acc[f][b][4 * q4 + 2],
+                                    acc[f][b][4 * q4 + 3]);
+                }
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+            const int colf = ob[f] * 32;                   // first feature of this fragment
+#pragma unroll
+            for (int i = 0; i < PER_LANE; ++i) {
+                const int idx = lane + 64 * i;
+                const int row = idx / CPR, ch = idx % CPR;
+                const int tok = b * 32 + row;
+                if (tok >= n) continue;
+                const int col = ch * 16 / EB;
+                const size_t p = (size_t)(p0 + tok);
+                const uint4 v = *reinterpret_cast<const uint4 *>(ep + row * EROW + ch * 16);
+                if (kGateUp) {
+                    *reinterpret_cast<uint4 *>(a.hg + p * a.inter + colf + col) = v;
+                } else if (MODE == DOWN_YE) {
+                    *reinterpret_cast<uint4 *>(a.ye + p * a.hidden + colf + col) = v;
+                } else {
+                    const float g = a.gate ? a.gate[p] : 1.0f;
+                    float4 *o = reinterpret_cast<float4 *>(a.out + p * a.hidden + colf + col);
+                    float4 r = make_float4(g * __uint_as_float(v.x), g * __uint_as_float(v.y),
+                                           g * __uint_as_float(v.z), g * __uint_as_float(v.w));
+                    if (a.accumulate) {
+                        const float4 old = *o;
+                        r.x += old.x;
+                        r.y += old.y;
+                        r.z += old.z;
+                        r.w += old.w;
                     }
+                    *o = r;
                 }
             }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-#pragma unroll
-        for (int i = 0; i < PER_LANE; ++i) {
-            const int idx = lane + 64 * i;
-            const int row = idx / CPR, ch = idx % CPR;
-            const int tok = b * 32 + row;
-            const int col = ch * 16 / EB;                // first column of the chunk
-            if (tok >= n || (!kGateUp && col >= 32 && !live1)) continue;
-            const size_t p = (size_t)(p0 + tok);
-            const uint4 v = *reinterpret_cast<const uint4 *>(ep + row * EROW + ch * 16);
-            if (MODE == GU_GATHER || MODE == GU_DENSE) {
-                *reinterpret_cast<uint4 *>(a.hg + p * a.inter + col0 + col) = v;
-            } else if (MODE == DOWN_YE) {
-                *reinterpret_cast<uint4 *>(a.ye + p * a.hidden + col0 + col) = v;
-            } else {
-                const float g = a.gate ? a.gate[p] : 1.0f;
-                float4 *o = reinterpret_cast<float4 *>(a.out + p * a.hidden + col0 + col);
-                float4 r = make_float4(g * __uint_as_float(v.x), g * __uint_as_float(v.y),
-                                       g * __uint_as_float(v.z), g * __uint_as_float(v.w));
-                if (a.accumulate) {
-                    const float4 old = *o;
-                    r.x += old.x;
-                    r.y += old.y;
-                    r.z += old.z;
-                    r.w += old.w;
-                }
-                *o = r;
-            }
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     }
 }
 
@@ -443,9 +506,20 @@ hipError_t launch_waves(const GemmArgs &a, int bm, hipStream_t s) {
     // 1-D grid, rounded so every XCD slot of the remap exists
     const int grid = ((tiles * nblk + 7) / 8) * 8 + 8;
     switch (bm) {
-    case 32: hipLaunchKernelGGL((k_gemm<MODE, 32, WAVES>), dim3(grid), dim3(64 * WAVES), 0, s, a); break;
+    case 32:
+        if constexpr (WAVES == 4)
+            hipLaunchKernelGGL((k_gemm<MODE, 32, 4>), dim3(grid), dim3(256), 0, s, a);
+        else
+            return hipErrorInvalidValue;  // a 32-row tile has 4 row blocks: 4 waves only
+        break;
     case 64: hipLaunchKernelGGL((k_gemm<MODE, 64, WAVES>), dim3(grid), dim3(64 * WAVES), 0, s, a); break;
-    default: hipLaunchKernelGGL((k_gemm<MODE, 128, WAVES>), dim3(grid), dim3(64 * WAVES), 0, s, a); break;
+    case 128: hipLaunchKernelGGL((k_gemm<MODE, 128, WAVES>), dim3(grid), dim3(64 * WAVES), 0, s, a); break;
+    default:
+        if constexpr (WAVES == 4)
+            hipLaunchKernelGGL((k_gemm<MODE, 256, 4>), dim3(grid), dim3(256), 0, s, a);
+        else
+            return hipErrorInvalidValue;  // 256-row tiles use 4 waves (one per SIMD)
+        break;
     }
     return hipGetLastError();
 }
@@ -456,7 +530,7 @@ hipError_t launch_mode(const GemmArgs &a, int bm, hipStream_t s) {
     const int n_out = gu ? a.inter : a.hidden;
     // 8 waves when the feature dimension fills them, so each staged activation
     // tile serves 256 (gate/up) or 512 (down) features.
-    const bool wide = gu ? n_out >= 256 : n_out >= 512;
+    const bool wide = (gu ? n_out >= 256 : n_out >= 512) && bm >= 64 && bm <= 128;
     return wide ? launch_waves<MODE, 8>(a, bm, s) : launch_waves<MODE, 4>(a, bm, s);
 }
 

@@ -56,17 +56,62 @@ def algorithmic(cfg, t, counts):
     )
 
 
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+DOMINANT_KERNEL = "k_gemm<0, 128, 8>"   # routed gate/up, 128-row tiles, 8 waves
+COPY_PROBE_BYTES = 512 << 20
+
+
 def traffic_for(kernel_key: str):
     """HBM bytes per launch from the committed counter runs, if they match this build."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    if not os.path.exists(path):
+    if not os.path.exists(TRAFFIC_JSON):
         return None
-    with open(path) as f:
+    with open(TRAFFIC_JSON) as f:
         data = json.load(f)
     ent = data.get(kernel_key)
     if not ent or ent.get("source_hash") != source_hash():
         return None
     return ent.get("bytes_per_launch")
+
+
+def ingest_pmc(fetch_csv: str, write_csv: str, key: str):
+    """Per-launch HBM bytes of the dominant kernel from two rocprofv3 --pmc runs.
+
+    Each counter (KiB per dispatch) is scaled by the ratio of known bytes to
+    what the same counter reads for the copy probe (a device-to-device copy of
+    COPY_PROBE_BYTES, which reads and writes that many bytes once).
+    """
+    import csv
+
+    def per_kernel(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    out = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        vals = per_kernel(path, counter)
+        dom = [v for k, vs in vals.items() if DOMINANT_KERNEL in k for v in vs]
+        cp = [v for k, vs in vals.items() if "copyBuffer" in k or "copy" in k.lower() for v in vs
+              if v * 1024 > COPY_PROBE_BYTES / 2]
+        if not dom or not cp:
+            raise SystemExit(f"{counter}: dominant kernel or copy probe missing from {path}")
+        factor = COPY_PROBE_BYTES / (max(cp) * 1024)
+        out[counter] = dict(kib_per_launch=sum(dom) / len(dom), copy_kib=max(cp), factor=factor,
+                            bytes_per_launch=sum(dom) / len(dom) * 1024 * factor)
+    entry = dict(kernel=DOMINANT_KERNEL, source_hash=source_hash(),
+                 fetch_bytes=round(out["FETCH_SIZE"]["bytes_per_launch"]),
+                 write_bytes=round(out["WRITE_SIZE"]["bytes_per_launch"]),
+                 bytes_per_launch=round(out["FETCH_SIZE"]["bytes_per_launch"] + out["WRITE_SIZE"]["bytes_per_launch"]),
+                 fetch_factor=round(out["FETCH_SIZE"]["factor"], 4), write_factor=round(out["WRITE_SIZE"]["factor"], 4),
+                 raw=out)
+    data = json.load(open(TRAFFIC_JSON)) if os.path.exists(TRAFFIC_JSON) else {}
+    data[key] = entry
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(data, f, indent=2)
+    print(json.dumps({key: {k: v for k, v in entry.items() if k != "raw"}}, indent=2))
 
 
 def cpu_baseline(cfg_name: str, rows: int):
@@ -93,9 +138,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="full")
     ap.add_argument("--copies", type=int, default=2, help="weight copies rotated per step (defeats the MALL)")
-    ap.add_argument("--cpu-rows", type=int, default=256, help="rows of the oracle CPU-baseline sample (0: skip)")
+    ap.add_argument("--cpu-rows", type=int, default=4096, help="rows of the oracle CPU-baseline sample (0: skip)")
     ap.add_argument("--phases", action="store_true", help="also time every phase in an extra pass")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after timing, copy 512 MiB device-to-device (calibrates HBM byte counters)")
+    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter_collection.csv files into profiles/traffic.json")
     args = ap.parse_args()
+    if args.ingest_pmc:
+        ingest_pmc(*args.ingest_pmc, key=f"gateup_{args.config}")
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the block is built and measured "
               f"on a single MI355X, with no sharding or collectives.", file=sys.stderr)
@@ -167,7 +219,7 @@ def main():
     achieved = work["flop_gateup"] / dom_avg_s / 1e12
     roofline = {"kernel": "k_gemm gate/up (routed, grouped int4 -> bf16 MFMA, SiLU*up epilogue)",
                 "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic_for(f"gateup_{cfg.name}"),
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic_for(f"gateup_{cfg.name}"), "algorithmic": round(work["flop_gateup"]),
                 "avg_launch_us": round(dom_avg_s * 1e6, 2)}
 
     block_flop = work["flop_gateup"] + work["flop_down"] + work["flop_shared"]
@@ -184,6 +236,13 @@ def main():
         torch.cuda.synchronize()
         ph = mep.moe_profile_end()
         extra["phase_us"] = {p: round(v[0] / v[1] * 1e3, 2) for p, v in ph.items()}
+
+    if args.copy_probe:
+        src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if args.cpu_rows > 0:

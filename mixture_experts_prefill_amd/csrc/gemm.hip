@@ -29,6 +29,8 @@
 //   - 4 MFMA steps of K = 16.  Inside a lane's 16 bytes the K order is
 //     permuted (lane half L/32 takes 32 consecutive columns), and the
 //     activation fragment uses the same permutation, so the products pair up.
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -157,10 +159,11 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 template <int MODE, int BM, int WAVES>
-__global__ void __launch_bounds__(64 * WAVES, (WAVES >= 8 || BM >= 256) ? 1 : 2) k_gemm(const GemmArgs a) {
+__global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const GemmArgs a) {
     constexpr bool kGateUp = (MODE == GU_GATHER || MODE == GU_DENSE);
     constexpr bool kDense = (MODE == GU_DENSE || MODE == DOWN_OUT);
     constexpr int TB = BM / 32;                         // token blocks of 32
+    static_assert(TB == 1 || TB == 2 || TB == 4, "M-tiles of 32, 64 or 128 rows");
     constexpr int XBLK = BM / 8;                        // 1 KB blocks (8 rows) per staged K step
     constexpr int XPW = XBLK / WAVES;                   // direct-to-LDS loads per wave per K step
     static_assert(BM % 32 == 0 && XBLK % WAVES == 0 && XPW >= 1, "every wave stages whole row blocks");
@@ -273,168 +276,195 @@ __global__ void __launch_bounds__(64 * WAVES, (WAVES >= 8 || BM >= 256) ? 1 : 2)
         }
     };
 
-    f32x16 acc[2][TB];
-#pragma unroll
-    for (int f = 0; f < 2; ++f)
-#pragma unroll
-        for (int b = 0; b < TB; ++b)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[f][b][r] = 0.0f;
+    // The tile's token blocks that hold rows: the K loop and epilogue below
+    // are compiled for each count, so MFMAs and LDS reads of empty blocks are
+    // skipped (row staging stays uniform).
+    auto body = [&](auto tbr_c) {
+        constexpr int TBR = decltype(tbr_c)::value;
+        f32x16 acc[2][TBR];
+    #pragma unroll
+        for (int f = 0; f < 2; ++f)
+    #pragma unroll
+            for (int b = 0; b < TBR; ++b)
+    #pragma unroll
+                for (int r = 0; r < 16; ++r) acc[f][b][r] = 0.0f;
 
-    const Masks msk = make_masks();
-    const int brow = lane & 31, bhalf = lane >> 5;
-    int bsw[TB];                                           // xswz of this lane's B rows
-#pragma unroll
-    for (int b = 0; b < TB; ++b) bsw[b] = xswz(b * 32 + brow);
+        const Masks msk = make_masks();
+        const int brow = lane & 31, bhalf = lane >> 5;
+        int bsw[TBR];                                           // xswz of this lane's B rows
+    #pragma unroll
+        for (int b = 0; b < TBR; ++b) bsw[b] = xswz(b * 32 + brow);
 
-    // prologue: K steps 0..2 in flight.  Every step issues the same loads --
-    // past the last step it reloads step nk-1 into a free slot -- so exactly
-    // two steps' loads are always newer than the one being consumed.
-#pragma unroll
-    for (int j = 0; j < NS - 1; ++j) issue(min(j, nk - 1), j);
+        // Prologue: one K step in flight per ring slot.  Every step issues the
+        // same loads -- past the last step it reloads step nk-1 into a free slot
+        // -- so the vmcnt counts below hold on every iteration.
+    #pragma unroll
+        for (int j = 0; j < NS; ++j) issue(min(j, nk - 1), j);
 
-    auto frag = [&](const Stage &sg, int st, const Deq &d0, const Deq &d1, bf16x8 *out) {
-        const uint32_t w0 = st == 0 ? sg.c[0].x : st == 1 ? sg.c[0].y : st == 2 ? sg.c[0].z : sg.c[0].w;
-        const uint32_t w1 = st == 0 ? sg.c[1].x : st == 1 ? sg.c[1].y : st == 2 ? sg.c[1].z : sg.c[1].w;
-        out[0] = dequant8(w0, d0, msk);
-        out[1] = dequant8(w1, d1, msk);
-    };
-    // Step 0's own loads must have landed before its weights are read.
-    wait_vm<(NS - 2) * VM_PER_STEP>();
-    Stage cur;
-    read_w(0, cur);
-    bf16x8 af[2];
-    {
-        const Deq d0 = deq_consts(cur.sb[0]), d1 = deq_consts(cur.sb[1]);
-        frag(cur, 0, d0, d1, af);
-    }
-
-    // K step kb (its loads have landed: waited for at the end of step kb-1).
-    // The barrier makes every wave's share of the activation block visible
-    // and frees the slot of step kb-1, which then receives step kb+3.  The
-    // weight fragments of MFMA step st+1 are dequantised while the MFMAs of
-    // step st run (sched_group_barrier interleaves one LDS read, two MFMAs
-    // and a slice of dequant VALU).  At the end, once step kb+1's loads have
-    // landed (two newer steps may still be in flight), its weights are read
-    // and its first fragment dequantised.
-    for (int kb = 0; kb < nk; ++kb) {
+        auto frag = [&](const Stage &sg, int st, const Deq &d0, const Deq &d1, bf16x8 *out) {
+            const uint32_t w0 = st == 0 ? sg.c[0].x : st == 1 ? sg.c[0].y : st == 2 ? sg.c[0].z : sg.c[0].w;
+            const uint32_t w1 = st == 0 ? sg.c[1].x : st == 1 ? sg.c[1].y : st == 2 ? sg.c[1].z : sg.c[1].w;
+            out[0] = dequant8(w0, d0, msk);
+            out[1] = dequant8(w1, d1, msk);
+        };
+        // B fragments (32 token rows x 8 K values per lane) of MFMA step st of the
+        // K step staged in `slot`.
+        auto read_b = [&](int slot, int st, bf16x8 *out) {
+            const uint8_t *buf = lds_raw + (slot % NS) * STAGE;
+    #pragma unroll
+            for (int b = 0; b < TBR; ++b)
+                out[b] = *reinterpret_cast<const bf16x8 *>(buf + (b * 32 + brow) * 128 + ((4 * bhalf + st) ^ bsw[b]) * 16);
+        };
+        // Step 0 has landed for every wave once each has waited for its own loads
+        // and all have met at the barrier.
+        wait_vm<(NS - 1) * VM_PER_STEP>();
         barrier_no_fence();
-        issue(min(kb + NS - 1, nk - 1), kb + NS - 1);
-        const uint8_t *buf = lds_raw + (kb % NS) * STAGE;
-        const Deq d0 = deq_consts(cur.sb[0]), d1 = deq_consts(cur.sb[1]);
-        Stage nxt;
-        bf16x8 bcur[TB];
-#pragma unroll
-        for (int b = 0; b < TB; ++b)
-            bcur[b] = *reinterpret_cast<const bf16x8 *>(buf + (b * 32 + brow) * 128 + ((4 * bhalf) ^ bsw[b]) * 16);
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            const bf16x8 a0 = af[0], a1 = af[1];
-            bf16x8 bnxt[TB];
-            if (st < 3) {
-#pragma unroll
-                for (int b = 0; b < TB; ++b)
-                    bnxt[b] = *reinterpret_cast<const bf16x8 *>(buf + (b * 32 + brow) * 128 +
-                                                                 ((4 * bhalf + st + 1) ^ bsw[b]) * 16);
-                frag(cur, st + 1, d0, d1, af);
-            } else {
-                wait_vm<(NS - 2) * VM_PER_STEP>();
-                read_w(kb + 1, nxt);                       // past the end: a reloaded step, unused
-                const Deq e0 = deq_consts(nxt.sb[0]), e1 = deq_consts(nxt.sb[1]);
-                frag(nxt, 0, e0, e1, af);
-            }
-#pragma unroll
-            for (int b = 0; b < TB; ++b) {
-                acc[0][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bcur[b], acc[0][b], 0, 0, 0);
-                acc[1][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bcur[b], acc[1][b], 0, 0, 0);
-            }
-            if (st < 3) {
-#pragma unroll
-                for (int b = 0; b < TB; ++b) bcur[b] = bnxt[b];
-            }
-#pragma unroll
-            for (int b = 0; b < TB; ++b) {
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
-                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // 2 MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 36 / TB, 0);  // dequant VALU slice
-            }
+        Stage cur;
+        read_w(0, cur);
+        bf16x8 af[2], bcur[TBR];
+        read_b(0, 0, bcur);
+        {
+            const Deq d0 = deq_consts(cur.sb[0]), d1 = deq_consts(cur.sb[1]);
+            frag(cur, 0, d0, d1, af);
         }
-        cur = nxt;
-    }
-    wait_vm<0>();  // retire the trailing (unused) loads before the ring is reused
 
-    // ---- epilogue.  acc[f][b][r] holds feature 8*(r/4) + 4*(lane/32) + r%4 of
-    // fragment f for token b*32 + lane%32.  Each 32-token block of one
-    // fragment goes through the wave's LDS tile so that global stores are
-    // whole 16-byte pieces of contiguous 64 or 128 byte row segments.
-    __syncthreads();  // every wave is done reading the ring
-    if (!live0) return;
-    uint8_t *ep = lds_raw + wave * 32 * EROW;
-    constexpr int CPR = 32 * EB / 16;                    // 16-byte chunks per row
-    constexpr int PER_LANE = 32 * CPR / 64;
-    constexpr int PASSES = kGateUp ? 1 : 2;
-#pragma unroll
-    for (int b = 0; b < TB; ++b) {
-#pragma unroll
-        for (int f = 0; f < PASSES; ++f) {
-            if (f == 1 && !live1) break;
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int col = 8 * q4 + 4 * bhalf;
-                if (kGateUp) {
-                    uint2 v;
-                    v.x = pk_bf16(silu_mul(acc[0][b][4 * q4 + 0], acc[1][b][4 * q4 + 0]),
-                                  silu_mul(acc[0][b][4 * q4 + 1], acc[1][b][4 * q4 + 1]));
-                    v.y = pk_bf16(silu_mul(acc[0][b][4 * q4 + 2], acc[1][b][4 * q4 + 2]),
-                                  silu_mul(acc[0][b][4 * q4 + 3], acc[1][b][4 * q4 + 3]));
-                    *reinterpret_cast<uint2 *>(ep + brow * EROW + col * 2) = v;
-                } else if (MODE == DOWN_YE) {
-                    uint2 v;
-                    v.x = pk_bf16(acc[f][b][4 * q4 + 0], acc[f][b][4 * q4 + 1]);
-                    v.y = pk_bf16(acc[f][b][4 * q4 + 2], acc[f][b][4 * q4 + 3]);
-                    *reinterpret_cast<uint2 *>(ep + brow * EROW + col * 2) = v;
+        // K step kb: four MFMA steps of K = 16, each a scheduling region of its
+        // own.  Region st issues the LDS reads of region st+1's operands (the next
+        // B fragments; in region 3 the first B fragments and the weights of step
+        // kb+1) ahead of its MFMAs and dequantises the next weight fragments
+        // between them, so no MFMA waits for an LDS read issued just before it.
+        // After region 2's MFMAs every wave waits for its own loads of step kb+1
+        // and meets the others at a barrier: step kb+1 is then complete in LDS,
+        // and slot kb, whose last reads were issued in region 2, is free for the
+        // loads of step kb+NS.
+        for (int kb = 0; kb < nk; ++kb) {
+            const Deq d0 = deq_consts(cur.sb[0]), d1 = deq_consts(cur.sb[1]);
+            Stage nxt;
+    #pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                const bf16x8 a0 = af[0], a1 = af[1];
+                bf16x8 bnxt[TBR];
+                if (st < 3) {
+                    read_b(kb, st + 1, bnxt);
+                    frag(cur, st + 1, d0, d1, af);
                 } else {
-                    *reinterpret_cast<float4 *>(ep + brow * EROW + col * 4) =
-                        make_float4(acc[f][b][4 * q4 + 0], acc[f][b][4 * q4 + 1], acc[f][b][4 * q4 + 2],
-                                    acc[f][b][4 * q4 + 3]);
+                    read_w(kb + 1, nxt);                       // past the end: a reloaded step, unused
+                    read_b(kb + 1, 0, bnxt);
+                    const Deq e0 = deq_consts(nxt.sb[0]), e1 = deq_consts(nxt.sb[1]);
+                    frag(nxt, 0, e0, e1, af);
                 }
-            }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-            const int colf = ob[f] * 32;                   // first feature of this fragment
-#pragma unroll
-            for (int i = 0; i < PER_LANE; ++i) {
-                const int idx = lane + 64 * i;
-                const int row = idx / CPR, ch = idx % CPR;
-                const int tok = b * 32 + row;
-                if (tok >= n) continue;
-                const int col = ch * 16 / EB;
-                const size_t p = (size_t)(p0 + tok);
-                const uint4 v = *reinterpret_cast<const uint4 *>(ep + row * EROW + ch * 16);
-                if (kGateUp) {
-                    *reinterpret_cast<uint4 *>(a.hg + p * a.inter + colf + col) = v;
-                } else if (MODE == DOWN_YE) {
-                    *reinterpret_cast<uint4 *>(a.ye + p * a.hidden + colf + col) = v;
-                } else {
-                    const float g = a.gate ? a.gate[p] : 1.0f;
-                    float4 *o = reinterpret_cast<float4 *>(a.out + p * a.hidden + colf + col);
-                    float4 r = make_float4(g * __uint_as_float(v.x), g * __uint_as_float(v.y),
-                                           g * __uint_as_float(v.z), g * __uint_as_float(v.w));
-                    if (a.accumulate) {
-                        const float4 old = *o;
-                        r.x += old.x;
-                        r.y += old.y;
-                        r.z += old.z;
-                        r.w += old.w;
-                    }
-                    *o = r;
+    #pragma unroll
+                for (int b = 0; b < TBR; ++b) {
+                    acc[0][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bcur[b], acc[0][b], 0, 0, 0);
+                    acc[1][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bcur[b], acc[1][b], 0, 0, 0);
                 }
+                if (st < 3)
+                    __builtin_amdgcn_sched_group_barrier(0x100, TBR, 0);       // the LDS reads first
+                else
+                    __builtin_amdgcn_sched_group_barrier(0x100, TBR + 4, 0);
+    #pragma unroll
+                for (int b = 0; b < TBR; ++b) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);            // 2 MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x002, 48 / TBR, 0);      // dequant VALU slice
+                }
+                if (st == 2) {
+                    wait_vm<(NS - 2) * VM_PER_STEP>();
+                    barrier_no_fence();
+                    issue(min(kb + NS, nk - 1), kb + NS);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+                for (int b = 0; b < TBR; ++b) bcur[b] = bnxt[b];
             }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+            cur = nxt;
         }
+        wait_vm<0>();  // retire the trailing (unused) loads before the ring is reused
+
+        // ---- epilogue.  acc[f][b][r] holds feature 8*(r/4) + 4*(lane/32) + r%4 of
+        // fragment f for token b*32 + lane%32.  Each 32-token block of one
+        // fragment goes through the wave's LDS tile so that global stores are
+        // whole 16-byte pieces of contiguous 64 or 128 byte row segments.
+        __syncthreads();  // every wave is done reading the ring
+        if (!live0) return;
+        uint8_t *ep = lds_raw + wave * 32 * EROW;
+        constexpr int CPR = 32 * EB / 16;                    // 16-byte chunks per row
+        constexpr int PER_LANE = 32 * CPR / 64;
+        constexpr int PASSES = kGateUp ? 1 : 2;
+    #pragma unroll
+        for (int b = 0; b < TBR; ++b) {
+    #pragma unroll
+            for (int f = 0; f < PASSES; ++f) {
+                if (f == 1 && !live1) break;
+    #pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int col = 8 * q4 + 4 * bhalf;
+                    if (kGateUp) {
+                        uint2 v;
+                        v.x = pk_bf16(silu_mul(acc[0][b][4 * q4 + 0], acc[1][b][4 * q4 + 0]),
+                                      silu_mul(acc[0][b][4 * q4 + 1], acc[1][b][4 * q4 + 1]));
+                        v.y = pk_bf16(silu_mul(acc[0][b][4 * q4 + 2], acc[1][b][4 * q4 + 2]),
+                                      silu_mul(acc[0][b][4 * q4 + 3], acc[1][b][4 * q4 + 3]));
+                        *reinterpret_cast<uint2 *>(ep + brow * EROW + col * 2) = v;
+                    } else if (MODE == DOWN_YE) {
+                        uint2 v;
+                        v.x = pk_bf16(acc[f][b][4 * q4 + 0], acc[f][b][4 * q4 + 1]);
+                        v.y = pk_bf16(acc[f][b][4 * q4 + 2], acc[f][b][4 * q4 + 3]);
+                        *reinterpret_cast<uint2 *>(ep + brow * EROW + col * 2) = v;
+                    } else {
+                        *reinterpret_cast<float4 *>(ep + brow * EROW + col * 4) =
+                            make_float4(acc[f][b][4 * q4 + 0], acc[f][b][4 * q4 + 1], acc[f][b][4 * q4 + 2],
+                                        acc[f][b][4 * q4 + 3]);
+                    }
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+                const int colf = ob[f] * 32;                   // first feature of this fragment
+    #pragma unroll
+                for (int i = 0; i < PER_LANE; ++i) {
+                    const int idx = lane + 64 * i;
+                    const int row = idx / CPR, ch = idx % CPR;
+                    const int tok = b * 32 + row;
+                    if (tok >= n) continue;
+                    const int col = ch * 16 / EB;
+                    const size_t p = (size_t)(p0 + tok);
+                    const uint4 v = *reinterpret_cast<const uint4 *>(ep + row * EROW + ch * 16);
+                    if (kGateUp) {
+                        *reinterpret_cast<uint4 *>(a.hg + p * a.inter + colf + col) = v;
+                    } else if (MODE == DOWN_YE) {
+                        *reinterpret_cast<uint4 *>(a.ye + p * a.hidden + colf + col) = v;
+                    } else {
+                        const float g = a.gate ? a.gate[p] : 1.0f;
+                        float4 *o = reinterpret_cast<float4 *>(a.out + p * a.hidden + colf + col);
+                        float4 r = make_float4(g * __uint_as_float(v.x), g * __uint_as_float(v.y),
+                                               g * __uint_as_float(v.z), g * __uint_as_float(v.w));
+                        if (a.accumulate) {
+                            const float4 old = *o;
+                            r.x += old.x;
+                            r.y += old.y;
+                            r.z += old.z;
+                            r.w += old.w;
+                        }
+                        *o = r;
+                    }
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+            }
+        }
+    };
+    const int tbr = (n + 31) >> 5;
+    if constexpr (TB >= 4) {
+        if (tbr >= 4) body(std::integral_constant<int, 4>{});
+        else if (tbr == 3) body(std::integral_constant<int, 3>{});
+        else if (tbr == 2) body(std::integral_constant<int, 2>{});
+        else body(std::integral_constant<int, 1>{});
+    } else if constexpr (TB == 2) {
+        if (tbr >= 2) body(std::integral_constant<int, 2>{});
+        else body(std::integral_constant<int, 1>{});
+    } else {
+        body(std::integral_constant<int, 1>{});
     }
 }
 
@@ -514,12 +544,7 @@ hipError_t launch_waves(const GemmArgs &a, int bm, hipStream_t s) {
         break;
     case 64: hipLaunchKernelGGL((k_gemm<MODE, 64, WAVES>), dim3(grid), dim3(64 * WAVES), 0, s, a); break;
     case 128: hipLaunchKernelGGL((k_gemm<MODE, 128, WAVES>), dim3(grid), dim3(64 * WAVES), 0, s, a); break;
-    default:
-        if constexpr (WAVES == 4)
-            hipLaunchKernelGGL((k_gemm<MODE, 256, 4>), dim3(grid), dim3(256), 0, s, a);
-        else
-            return hipErrorInvalidValue;  // 256-row tiles use 4 waves (one per SIMD)
-        break;
+    default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }

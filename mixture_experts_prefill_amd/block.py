@@ -6,8 +6,11 @@ workspace, output) and runs
     moe_shared(accumulate=0) -> moe_route -> moe_build_csr -> moe_prefill_experts(accumulate=1)
 
 the order of the cherenkov experts.rs page (fn pf_experts: shared expert into
-the zeroed output, then routed experts added in ascending id).  Only
-allocation and call sequencing live here; the arithmetic is in libmoe.
+the zeroed output, then routed experts added in ascending id).  The shared
+expert needs no routing, so forward() runs it on a second stream of the same
+(default) priority while routing and grouping run; the routed call waits for
+it, so every row still receives the shared term first.  Only allocation and
+call sequencing live here; the arithmetic is in libmoe.
 """
 from __future__ import annotations
 
@@ -49,6 +52,9 @@ class MoeBlock:
         self.x = self.w_router = self.pool = self.table = self.shared_record = self.gate_w = None
         self.host_records: Optional[Sequence[Optional[torch.Tensor]]] = None
         self.ring: Optional[MoeRing] = None
+        self._side = torch.cuda.Stream(device=d) if d.type == "cuda" else None
+        self._fork = torch.cuda.Event() if d.type == "cuda" else None
+        self._join = torch.cuda.Event() if d.type == "cuda" else None
 
     @classmethod
     def from_workload(cls, wl, device="cuda", resident: Optional[np.ndarray] = None, ring_slots: int = 64,
@@ -113,11 +119,24 @@ class MoeBlock:
                             self.table, self.out, accumulate, self.workspace, self.host_records, self.ring, stream)
 
     def forward(self, stream=None) -> torch.Tensor:
+        """One block.  `stream` (torch stream, raw handle or None for the current
+        stream) carries routing, grouping and the routed experts; the shared
+        expert forks off it and joins back before the routed call."""
         if self.Ls is not None:
-            self.shared(0, stream)
-            self.route(stream)
-            self.build_csr(stream)
-            self.experts(1, stream)
+            if stream is None:
+                main = torch.cuda.current_stream(self.device)
+            elif isinstance(stream, torch.cuda.Stream):
+                main = stream
+            else:
+                main = torch.cuda.ExternalStream(int(stream), device=self.device)
+            self._fork.record(main)
+            self._side.wait_event(self._fork)
+            self.shared(0, self._side)
+            self._join.record(self._side)
+            self.route(main)
+            self.build_csr(main)
+            main.wait_event(self._join)
+            self.experts(1, main)
         else:
             self.route(stream)
             self.build_csr(stream)

@@ -58,7 +58,8 @@ bool workspace_plan(int t, int k, int E, const moe_layout *routed, const moe_lay
     };
     w->csr_hist = take(tiles * E * 4);
     w->sched = take(max_mt * 16);
-    w->sched_n = take(16);
+    w->sched_n = take(64);
+    w->order = take(8 * max_mt * 4);
     w->jobs = take((size_t)E * 8);
     w->hg = take(P * routed->inter * 2);
     w->ye = take(P * routed->hidden * 2);
@@ -68,12 +69,22 @@ bool workspace_plan(int t, int k, int E, const moe_layout *routed, const moe_lay
     return true;
 }
 
-int pick_bm(int t, int k, int E) {
-    // mean rows per non-empty expert, assuming every expert gets some rows
+// Largest M-tile height.  Tiles only run their non-empty 32-row blocks, so a
+// taller tile costs no padding; it halves the dequantisation per MFMA each
+// time it doubles, but there must stay enough workgroups (about 1.5 per CU)
+// for the longest-first schedule to balance.  With about one token block per
+// expert (small chunks) 32-row tiles with 4 waves cover fewer features each
+// and so spread the weight stream over more workgroups.
+int pick_bm(int t, int k, int E, int inter, int hidden) {
     const long P = (long)t * k;
-    const long used = P < E ? P : E;
+    const long used = P < E ? P : E;  // at most this many non-empty experts
     const long mean = P / (used > 0 ? used : 1);
-    return mean >= 96 ? 128 : mean >= 48 ? 64 : 32;
+    if (mean < 48) return 32;
+    (void)hidden;
+    const long nblk = (inter + 255) / 256;  // gate/up workgroups cover 256 features
+    for (int bm = kMaxBM; bm >= 64; bm /= 2)
+        if ((P / bm + used) * nblk >= 384) return bm;
+    return 64;
 }
 
 static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
@@ -239,13 +250,15 @@ moe_status moe_prefill_experts(const uint16_t *x, int32_t t, int32_t k, int32_t 
     a.records = records;
     a.sched = reinterpret_cast<int4 *>(ws + w.sched);
     a.sched_n = reinterpret_cast<uint32_t *>(ws + w.sched_n);
+    a.order = reinterpret_cast<int *>(ws + w.order);
+    a.xcap = (int)((size_t)t * k / kMinBM + (size_t)E + 1);
     a.t = t;
     a.hidden = L->hidden;
     a.inter = L->inter;
     a.group = L->group;
     a.hg = reinterpret_cast<uint16_t *>(ws + w.hg);
     a.ye = reinterpret_cast<uint16_t *>(ws + w.ye);
-    const int bm = pick_bm(t, k, E);
+    const int bm = pick_bm(t, k, E, L->inter, L->hidden);
     a.max_tiles = (int)((size_t)t * k / bm + (size_t)E + 1);
 
     if (ring || host_records) {
@@ -254,7 +267,7 @@ moe_status moe_prefill_experts(const uint16_t *x, int32_t t, int32_t k, int32_t 
     }
 
     hipError_t e = launch_schedule(offsets, 0, E, bm, const_cast<int4 *>(a.sched),
-                                   const_cast<uint32_t *>(a.sched_n), s);
+                                   const_cast<uint32_t *>(a.sched_n), const_cast<int *>(a.order), a.xcap, s);
     if (e != hipSuccess) return hip_fail(e, "schedule");
     a.w_off = L->gate_w;
     a.sb_off = L->gate_sb;

@@ -7,7 +7,7 @@
 //   1. k_csr_count: per tile of 64 rows, a 64-bit mask per expert of the
 //      tile's rows that chose it (LDS atomics), and its popcount.
 //   2. k_csr_scan:  one workgroup turns the per-tile counts into the
-//      segment start of every (tile, expert) and the offsets array.
+//      segment start of every (expert, tile) and the offsets array.
 //   3. k_csr_place: every (row, slot) entry goes to
 //      segment base + number of earlier rows of its tile in the mask.
 // A row's k experts are distinct, so "earlier entries of expert e" are the
@@ -18,6 +18,30 @@ namespace moe {
 namespace {
 
 constexpr int TR = kCsrTileRows;
+
+// Inclusive scan of one value per thread over a workgroup of 1024 threads
+// (16 waves): shuffle scan in each wave, then the wave totals.  `wsum` is
+// 16 words of LDS.  Returns the inclusive prefix; *total gets the sum.
+__device__ __forceinline__ uint32_t block_scan_1024(uint32_t v, uint32_t *wsum, uint32_t *total) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t o = __shfl_up(v, d, 64);
+        if (lane >= d) v += o;
+    }
+    if (lane == 63) wsum[wave] = v;
+    __syncthreads();
+    uint32_t before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+        const uint32_t x = wsum[w];
+        before += (w < wave) ? x : 0u;
+        all += x;
+    }
+    __syncthreads();  // wsum may be reused by the caller's next scan
+    *total = all;
+    return v + before;
+}
 
 // Block of 256 threads per tile of 64 rows.
 __global__ void __launch_bounds__(256) k_csr_count(const uint32_t *__restrict__ idx, int t, int k,
@@ -34,27 +58,31 @@ __global__ void __launch_bounds__(256) k_csr_count(const uint32_t *__restrict__ 
         if (e < (uint32_t)E) atomicOr(&mask[e], 1ull << r);
     }
     __syncthreads();
+    const int tiles = gridDim.x;
     for (int e = threadIdx.x; e < E; e += blockDim.x)
-        hist[(size_t)tile * E + e] = (uint32_t)__popcll(mask[e]);
+        hist[(size_t)e * tiles + tile] = (uint32_t)__popcll(mask[e]);
 }
 
 // One workgroup of 1024 threads (16 waves).  Row tiles number at most
-// 4096 / 64 = 64, so a wave scans one expert's per-tile counts with lane =
-// tile (shuffle scan), 8 experts per pass with their loads issued together.
-// A block scan over the expert totals then gives the offsets, and every
-// (tile, expert) entry becomes its absolute segment start.
+// 4096 / 64 = 64, so a wave scans one expert's per-tile counts (contiguous in
+// hist) with lane = tile, 8 experts per pass with their loads issued
+// together.  A block scan over the expert totals then gives the offsets, and
+// every (expert, tile) entry becomes its absolute segment start.  With at most
+// 128 experts (one pass) the per-tile prefixes stay in registers; beyond
+// that they are re-read and re-scanned.
 __global__ void __launch_bounds__(1024) k_csr_scan(int tiles, int E, int total,
                                                    uint32_t *__restrict__ hist,
                                                    uint32_t *__restrict__ offsets) {
-    __shared__ uint32_t tot[1024];
-    __shared__ uint32_t part[1024];
+    __shared__ uint32_t tot[MOE_MAX_EXPERTS];
+    __shared__ uint32_t wsum[16];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     constexpr int kPass = 8;
-    for (int e0 = wave * kPass; e0 < E; e0 += 16 * kPass) {
+    uint32_t ex[kPass];  // exclusive per-tile prefix of the last pass
+    auto pass = [&](int e0, bool totals) {
         uint32_t v[kPass];
 #pragma unroll
         for (int j = 0; j < kPass; ++j)
-            v[j] = (lane < tiles && e0 + j < E) ? hist[(size_t)lane * E + e0 + j] : 0u;
+            v[j] = (lane < tiles && e0 + j < E) ? hist[(size_t)(e0 + j) * tiles + lane] : 0u;
 #pragma unroll
         for (int j = 0; j < kPass; ++j) {
             uint32_t incl = v[j];
@@ -63,32 +91,28 @@ __global__ void __launch_bounds__(1024) k_csr_scan(int tiles, int E, int total,
                 const uint32_t o = __shfl_up(incl, d, 64);
                 if (lane >= d) incl += o;
             }
-            if (e0 + j < E) {
-                if (lane < tiles) hist[(size_t)lane * E + e0 + j] = incl - v[j];
-                if (lane == 63) tot[e0 + j] = incl;
-            }
+            ex[j] = incl - v[j];
+            if (totals && e0 + j < E && lane == 63) tot[e0 + j] = incl;
         }
-    }
+    };
+    for (int e0 = wave * kPass; e0 < E; e0 += 16 * kPass) pass(e0, true);
     __syncthreads();
+    uint32_t all;
     const uint32_t mine = tid < E ? tot[tid] : 0u;
-    part[tid] = mine;
-    __syncthreads();
-    for (int d = 1; d < 1024; d <<= 1) {  // Hillis-Steele inclusive scan
-        const uint32_t o = tid >= d ? part[tid - d] : 0u;
-        __syncthreads();
-        part[tid] += o;
-        __syncthreads();
-    }
+    const uint32_t incl = block_scan_1024(mine, wsum, &all);
     if (tid < E) {
-        tot[tid] = part[tid] - mine;  // exclusive: segment start of expert tid
-        offsets[tid] = part[tid] - mine;
+        tot[tid] = incl - mine;  // exclusive: segment start of expert tid
+        offsets[tid] = incl - mine;
     }
     if (tid == 0) offsets[E] = (uint32_t)total;
     __syncthreads();
-    for (int e0 = wave * kPass; e0 < E; e0 += 16 * kPass)
+    const bool one_pass = E <= 16 * kPass;
+    for (int e0 = wave * kPass; e0 < E; e0 += 16 * kPass) {
+        if (!one_pass) pass(e0, false);
 #pragma unroll
         for (int j = 0; j < kPass; ++j)
-            if (lane < tiles && e0 + j < E) hist[(size_t)lane * E + e0 + j] += tot[e0 + j];
+            if (lane < tiles && e0 + j < E) hist[(size_t)(e0 + j) * tiles + lane] = tot[e0 + j] + ex[j];
+    }
 }
 
 __global__ void __launch_bounds__(256) k_csr_place(const uint32_t *__restrict__ idx,
@@ -115,40 +139,84 @@ __global__ void __launch_bounds__(256) k_csr_place(const uint32_t *__restrict__ 
         const uint32_t e = idx[src];
         if (e >= (uint32_t)E) continue;
         const unsigned long long below = (r == 0) ? 0ull : (mask[e] & ((1ull << r) - 1ull));
-        const uint32_t p = base[(size_t)tile * E + e] + (uint32_t)__popcll(below);
+        const uint32_t p = base[(size_t)e * gridDim.x + tile] + (uint32_t)__popcll(below);
         rows[p] = (uint32_t)(r0 + r);
         csr_w[p] = wts[src];
         pos[src] = p;
     }
 }
 
-// One workgroup: tiles of bm rows for experts [e0, e1), in ascending expert id.
+// One workgroup builds the M-tile schedule of experts [e0, e1):
+//   1. tiles of up to bm rows per expert, in ascending expert id (sched);
+//   2. each XCD gets a contiguous run of those tiles of about one eighth of
+//      the total cost (kTileCostBase + token blocks per tile), so an expert's
+//      tiles share one L2;
+//   3. within its run, an XCD's tiles are listed by token blocks, largest
+//      first and in expert order among equals (order[x * xcap + j]), so the
+//      long tiles start first and the short ones fill the end.
+// xcnt[x] is the number of tiles of XCD x, sched_n[0] the total.
 __global__ void __launch_bounds__(1024) k_schedule(const uint32_t *__restrict__ offsets, int e0,
                                                    int e1, int bm, int4 *__restrict__ sched,
-                                                   uint32_t *__restrict__ sched_n) {
-    __shared__ uint32_t part[1024];
-    const int tid = threadIdx.x;
+                                                   uint32_t *__restrict__ sched_n, int *__restrict__ order,
+                                                   int xcap) {
+    __shared__ uint32_t wsum[16];
+    __shared__ uint8_t tbl[kSchedMaxTiles];   // token blocks of each tile
+    __shared__ uint8_t xof[kSchedMaxTiles];   // XCD of each tile
+    __shared__ uint32_t xstart[9];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // 1. tiles in expert order; each thread owns a contiguous run of experts
     const int n_e = e1 - e0;
-    // each thread owns a contiguous run of experts
     const int per = (n_e + 1023) / 1024;
     const int a = e0 + tid * per, b = min(e1, a + per);
     uint32_t cnt = 0;
     for (int e = a; e < b; ++e) cnt += (offsets[e + 1] - offsets[e] + bm - 1) / bm;
-    part[tid] = cnt;
-    __syncthreads();
-    for (int d = 1; d < 1024; d <<= 1) {
-        uint32_t v = (tid >= d) ? part[tid - d] : 0;
-        __syncthreads();
-        part[tid] += v;
-        __syncthreads();
-    }
-    uint32_t w = part[tid] - cnt;
+    uint32_t T;
+    uint32_t w = block_scan_1024(cnt, wsum, &T) - cnt;
     for (int e = a; e < b; ++e) {
         const uint32_t p0 = offsets[e], n = offsets[e + 1] - p0;
-        for (uint32_t m = 0; m < n; m += bm)
-            sched[w++] = make_int4(e, (int)(p0 + m), (int)min((uint32_t)bm, n - m), 0);
+        for (uint32_t m = 0; m < n; m += bm) {
+            const uint32_t rows = min((uint32_t)bm, n - m);
+            sched[w] = make_int4(e, (int)(p0 + m), (int)rows, 0);
+            tbl[w++] = (uint8_t)((rows + 31) / 32);
+        }
     }
-    if (tid == 1023) sched_n[0] = part[1023];
+    __syncthreads();
+    // 2. cost prefix over tiles; tile i goes to XCD floor(8 (S_i + c_i / 2) / C)
+    const uint32_t per2 = (T + 1023) / 1024;
+    const uint32_t a2 = min(T, tid * per2), b2 = min(T, a2 + per2);
+    uint32_t csum = 0;
+    for (uint32_t i = a2; i < b2; ++i) csum += kTileCostBase + tbl[i];
+    uint32_t Ctot;
+    uint64_t S = block_scan_1024(csum, wsum, &Ctot) - csum;
+    const uint64_t C = Ctot;
+    for (uint32_t i = a2; i < b2; ++i) {
+        const uint32_t c = kTileCostBase + tbl[i];
+        xof[i] = (uint8_t)min<uint64_t>(7, (8 * (2 * S + c)) / (2 * C));
+        S += c;
+    }
+    if (tid < 9) xstart[tid] = T;
+    __syncthreads();
+    // run starts: tile i opens every XCD in (x of tile i-1, x of tile i]
+    for (uint32_t i = a2; i < b2; ++i) {
+        const int lo = i ? (int)xof[i - 1] + 1 : 0;
+        for (int x = lo; x <= (int)xof[i]; ++x) xstart[x] = i;
+    }
+    __syncthreads();
+    // 3. wave x lists XCD x's tiles by token blocks, descending, stable
+    if (wave < 8) {
+        const uint32_t s0 = xstart[wave], s1 = xstart[wave + 1];
+        uint32_t o = 0;
+        for (int tb = bm / 32; tb >= 1; --tb)
+            for (uint32_t base = s0; base < s1; base += 64) {
+                const uint32_t i = base + lane;
+                const bool hit = i < s1 && tbl[i] == tb;
+                const unsigned long long m = __ballot(hit);
+                if (hit) order[(size_t)wave * xcap + o + __popcll(m & ((1ull << lane) - 1ull))] = (int)i;
+                o += (uint32_t)__popcll(m);
+            }
+        if (lane == 0) sched_n[kSchedXcnt + wave] = s1 - s0;
+    }
+    if (tid == 0) sched_n[0] = T;
 }
 
 }  // namespace
@@ -166,9 +234,10 @@ hipError_t launch_csr(const uint32_t *idx, const float *wts, int t, int k, int E
 }
 
 hipError_t launch_schedule(const uint32_t *offsets, int e0, int e1, int bm, int4 *sched,
-                           uint32_t *sched_n, hipStream_t s) {
+                           uint32_t *sched_n, int *order, int xcap, hipStream_t s) {
     ProfileScope prof(MOE_PHASE_SCHEDULE, s);
-    hipLaunchKernelGGL(k_schedule, dim3(1), dim3(1024), 0, s, offsets, e0, e1, bm, sched, sched_n);
+    hipLaunchKernelGGL(k_schedule, dim3(1), dim3(1024), 0, s, offsets, e0, e1, bm, sched, sched_n, order,
+                       xcap);
     return hipGetLastError();
 }
 

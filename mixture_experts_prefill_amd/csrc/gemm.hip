@@ -29,6 +29,7 @@
 //   - 4 MFMA steps of K = 16.  Inside a lane's 16 bytes the K order is
 //     permuted (lane half L/32 takes 32 consecutive columns), and the
 //     activation fragment uses the same permutation, so the products pair up.
+#include <algorithm>
 #include <type_traits>
 
 #include "moe_internal.h"
@@ -163,6 +164,9 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
     constexpr bool kGateUp = (MODE == GU_GATHER || MODE == GU_DENSE);
     constexpr bool kDense = (MODE == GU_DENSE || MODE == DOWN_OUT);
     constexpr int TB = BM / 32;                         // token blocks of 32
+    // Two waves per SIMD leave 256 registers per wave: 128 accumulators
+    // (two fragments x 4 token blocks) is the most that fits beside the
+    // pipeline's operands, so tiles stop at 128 rows.
     static_assert(TB == 1 || TB == 2 || TB == 4, "M-tiles of 32, 64 or 128 rows");
     constexpr int XBLK = BM / 8;                        // 1 KB blocks (8 rows) per staged K step
     constexpr int XPW = XBLK / WAVES;                   // direct-to-LDS loads per wave per K step
@@ -184,17 +188,28 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-    // ---- which (M-tile, feature block): tiles of one XCD are contiguous in
-    // the logical order (expert-major, then M-tile, then feature block), so
-    // the CUs of an XCD share an expert's weights and rows in their L2.
+    // ---- which (M-tile, feature block).  Workgroups are dispatched to the 8
+    // XCDs round-robin (XCD = blockIdx % 8) and in order within an XCD.
+    // Routed: XCD x runs the tiles of its list (its share of the experts,
+    // longest tiles first), each with all its feature blocks in a row.
+    // Dense: each XCD runs a contiguous eighth of the (M-tile, feature block)
+    // pairs.  Either way an XCD's CUs share the weights and rows in its L2.
     const int n_out = kGateUp ? a.inter : a.hidden;
     const int nblk = (n_out + FEAT - 1) / FEAT;
-    const int m_tiles = kDense ? (a.t + BM - 1) / BM : (int)*a.sched_n;
-    const int total = m_tiles * nblk;
-    const int chunk = (total + 7) >> 3;
-    const int logical = (blockIdx.x & 7) * chunk + (blockIdx.x >> 3);
-    if ((int)(blockIdx.x >> 3) >= chunk || logical >= total) return;
-    const int mt = logical / nblk, nb = logical % nblk;
+    const int xcd = blockIdx.x & 7, slot_in_xcd = blockIdx.x >> 3;
+    int mt, nb;
+    if (kDense) {
+        const int total = ((a.t + BM - 1) / BM) * nblk;
+        const int chunk = (total + 7) >> 3;
+        const int logical = xcd * chunk + slot_in_xcd;
+        if (slot_in_xcd >= chunk || logical >= total) return;
+        mt = logical / nblk;
+        nb = logical % nblk;
+    } else {
+        if (slot_in_xcd >= (int)a.sched_n[kSchedXcnt + xcd] * nblk) return;
+        mt = a.order[xcd * a.xcap + slot_in_xcd / nblk];
+        nb = slot_in_xcd % nblk;
+    }
 
     int expert = 0, p0, n;
     if (kDense) {
@@ -455,7 +470,7 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
         }
     };
     const int tbr = (n + 31) >> 5;
-    if constexpr (TB >= 4) {
+    if constexpr (TB == 4) {
         if (tbr >= 4) body(std::integral_constant<int, 4>{});
         else if (tbr == 3) body(std::integral_constant<int, 3>{});
         else if (tbr == 2) body(std::integral_constant<int, 2>{});
@@ -532,9 +547,17 @@ hipError_t launch_waves(const GemmArgs &a, int bm, hipStream_t s) {
     const int n_out = gu ? a.inter : a.hidden;
     const int feat = gu ? 32 * WAVES : 64 * WAVES;
     const int nblk = (n_out + feat - 1) / feat;
-    const int tiles = dense ? (a.t + bm - 1) / bm : a.max_tiles;
-    // 1-D grid, rounded so every XCD slot of the remap exists
-    const int grid = ((tiles * nblk + 7) / 8) * 8 + 8;
+    int grid;
+    if (dense) {
+        // 1-D grid, rounded so every XCD slot of the remap exists
+        grid = (((a.t + bm - 1) / bm * nblk + 7) / 8) * 8 + 8;
+    } else {
+        // An XCD's tiles cost at most an eighth of the total plus one tile,
+        // and each costs at least kTileCostBase + 1, which bounds their count.
+        const long T = a.max_tiles, cmax = kTileCostBase + bm / 32, cmin = kTileCostBase + 1;
+        const long per_xcd = std::min<long>(T, (T * cmax / 8 + cmax) / cmin + 1);
+        grid = (int)(8 * per_xcd * nblk);
+    }
     switch (bm) {
     case 32:
         if constexpr (WAVES == 4)
@@ -553,9 +576,9 @@ template <int MODE>
 hipError_t launch_mode(const GemmArgs &a, int bm, hipStream_t s) {
     const bool gu = (MODE == GU_GATHER || MODE == GU_DENSE);
     const int n_out = gu ? a.inter : a.hidden;
-    // 8 waves when the feature dimension fills them, so each staged activation
-    // tile serves 256 (gate/up) or 512 (down) features.
-    const bool wide = (gu ? n_out >= 256 : n_out >= 512) && bm >= 64 && bm <= 128;
+    // 8 waves (two per SIMD) when the feature dimension fills them, so each
+    // staged activation tile serves 256 (gate/up) or 512 (down) features.
+    const bool wide = (gu ? n_out >= 256 : n_out >= 512) && bm >= 64;
     return wide ? launch_waves<MODE, 8>(a, bm, s) : launch_waves<MODE, 4>(a, bm, s);
 }
 

@@ -17,7 +17,8 @@ namespace moe {
 struct Workspace {
     size_t csr_hist;   // u32 [row_tiles][E]: per-tile expert counts, then segment bases
     size_t sched;      // int4 [max_tiles]: (expert, first CSR position, rows, 0) per M-tile
-    size_t sched_n;    // u32 [4]: number of M-tiles
+    size_t sched_n;    // u32 [16]: number of M-tiles; [kSchedXcnt + x]: tiles of XCD x
+    size_t order;      // i32 [8][max_tiles]: per XCD, its tiles largest first
     size_t jobs;       // u64 [E]: record address per expert for the ring path
     size_t hg;         // bf16 [t*k][I]: SiLU(gate)*up of every CSR entry
     size_t ye;         // bf16 [t*k][h]: down projection of every CSR entry
@@ -28,6 +29,13 @@ struct Workspace {
 
 constexpr int kCsrTileRows = 64;  // rows per CSR tile (one 64-bit mask per expert)
 constexpr int kMinBM = 32;        // smallest GEMM M-tile
+constexpr int kMaxBM = 128;       // largest GEMM M-tile
+constexpr int kSchedMaxTiles = 8192;  // tiles one schedule can hold (>= t*k/kMinBM + E + 1)
+constexpr int kSchedXcnt = 8;     // sched_n[kSchedXcnt + x] = tiles of XCD x
+// Relative cost of an M-tile with b token blocks of 32 rows: kTileCostBase + b
+// (the weight dequantisation of a K step costs about as much as five token
+// blocks of MFMAs).
+constexpr int kTileCostBase = 5;
 
 bool workspace_plan(int t, int k, int E, const moe_layout *routed, const moe_layout *shared,
                     Workspace *out);
@@ -44,9 +52,10 @@ hipError_t launch_csr(const uint32_t *idx, const float *wts, int t, int k, int E
                       uint32_t *hist, hipStream_t s);
 
 // M-tile schedule of the grouped GEMMs: for experts [e0, e1) with rows, tiles of
-// bm rows; written to sched/sched_n.
+// up to bm rows (sched, sched_n[0]), split over the 8 XCDs by cost and listed
+// per XCD largest first (order[x * xcap ..], sched_n[kSchedXcnt + x]).
 hipError_t launch_schedule(const uint32_t *offsets, int e0, int e1, int bm, int4 *sched,
-                           uint32_t *sched_n, hipStream_t s);
+                           uint32_t *sched_n, int *order, int xcap, hipStream_t s);
 
 struct GemmArgs {
     // B-operand rows (tokens): x rows gathered through `rows` (routed gate/up),
@@ -58,7 +67,9 @@ struct GemmArgs {
     const void *record;      // the one record (shared expert) when records == nullptr
     const int4 *sched;       // M-tiles (routed) or nullptr (dense rows 0..t)
     const uint32_t *sched_n;
-    int max_tiles;           // grid bound on M-tiles
+    const int *order;        // per-XCD tile lists (routed)
+    int xcap;                // stride of order between XCDs
+    int max_tiles;           // bound on M-tiles of the call
     int t;                   // rows (dense mode)
     int hidden, inter, group;
     uint64_t w_off, sb_off, w2_off, sb2_off;  // sections: gate & up (gate/up), down (down)

@@ -225,14 +225,16 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 }
 
 // One wave per row: k rounds of a 64-lane arg-max over (value desc, id asc).
-// Round j's winner is kept by lane j, which then writes slot j.
+// Round j's winner is kept by lane j, which then writes slot j.  Lane l holds
+// experts l, l + 64, ... (KPL of them, E <= 64 KPL).
+template <int KPL>
 __global__ void __launch_bounds__(256) k_topk(const float *__restrict__ logits, int t, int E, int k,
                                               uint32_t *__restrict__ idx, float *__restrict__ wts) {
     const int lane = threadIdx.x & 63;
     const int r = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     if (r >= t) return;
     const float *l = logits + (size_t)r * E;
-    constexpr int kMaxPerLane = MOE_MAX_EXPERTS / 64;
+    constexpr int kMaxPerLane = KPL;
     uint64_t key[kMaxPerLane];
 #pragma unroll
     for (int i = 0; i < kMaxPerLane; ++i) {
@@ -300,7 +302,12 @@ hipError_t launch_router_logits(const uint16_t *x, const float *w, int t, int h,
 hipError_t launch_topk(const float *logits, int t, int E, int k, uint32_t *idx, float *wts,
                        hipStream_t s) {
     ProfileScope prof(MOE_PHASE_TOPK, s);
-    hipLaunchKernelGGL(k_topk, dim3((t + 3) / 4), dim3(256), 0, s, logits, t, E, k, idx, wts);
+    const dim3 grid((t + 3) / 4), block(256);
+    if (E <= 64) hipLaunchKernelGGL(k_topk<1>, grid, block, 0, s, logits, t, E, k, idx, wts);
+    else if (E <= 128) hipLaunchKernelGGL(k_topk<2>, grid, block, 0, s, logits, t, E, k, idx, wts);
+    else if (E <= 256) hipLaunchKernelGGL(k_topk<4>, grid, block, 0, s, logits, t, E, k, idx, wts);
+    else if (E <= 512) hipLaunchKernelGGL(k_topk<8>, grid, block, 0, s, logits, t, E, k, idx, wts);
+    else hipLaunchKernelGGL(k_topk<MOE_MAX_EXPERTS / 64>, grid, block, 0, s, logits, t, E, k, idx, wts);
     return hipGetLastError();
 }
 

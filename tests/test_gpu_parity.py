@@ -42,6 +42,9 @@ def run(mep, wl, resident=None, ring_slots=64, group=8, shared=True, force_ring=
     blk = mep.MoeBlock.from_workload(wl, resident=resident, ring_slots=ring_slots, group=group, shared=shared)
     if force_ring:
         blk.use_ring(ring_slots, group)
+    # NaN bytes in every intermediate: a GEMM tile or feature block that the
+    # schedule skipped would leave NaN rows in the output.
+    blk.workspace.fill_(0xFF)
     blk.forward()
     torch.cuda.synchronize()
     g = dict(
@@ -54,6 +57,7 @@ def run(mep, wl, resident=None, ring_slots=64, group=8, shared=True, force_ring=
         out=blk.out.cpu().numpy(),
     )
     g["ring_stats"] = blk.ring.stats() if blk.ring is not None else None
+    assert np.isfinite(g["out"]).all(), "non-finite outputs: some rows were never computed"
     del blk
     return g
 

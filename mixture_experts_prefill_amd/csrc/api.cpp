@@ -132,6 +132,9 @@ moe_status moe_layout_make(int32_t hidden, int32_t inter, int32_t group, moe_lay
         off = (off + sb + 255) / 256 * 256;
     }
     L.stride = (off + 4095) / 4096 * 4096;
+    // The GEMMs address a record with 32-bit byte offsets.
+    if (L.stride > 0xffffffffull)
+        return fail(MOE_ERR_INVALID, "layout: record of %llu bytes exceeds 4 GiB", (unsigned long long)L.stride);
     *out = L;
     return MOE_OK;
 }
@@ -181,6 +184,8 @@ moe_status moe_shared(const uint16_t *x, int32_t t, const moe_layout *Ls, const 
     if (!x || !record || !out || !workspace) return fail(MOE_ERR_INVALID, "shared: null pointer");
     if (!aligned16(x) || !aligned16(record) || !aligned16(out))
         return fail(MOE_ERR_INVALID, "shared: x, record and out must be 16-byte aligned");
+    if ((uint64_t)t * Ls->inter * 2 > 0xffffffffull || (uint64_t)t * Ls->hidden * 2 > 0xffffffffull)
+        return fail(MOE_ERR_CAPACITY, "shared: t*inter or t*hidden too large for 32-bit offsets");
     // The shared expert's scratch is the end of the workspace: [.. | hs | gate].
     const size_t g_bytes = align256((size_t)t * 4), hs_bytes = align256((size_t)t * Ls->inter * 2);
     const size_t end = workspace_bytes & ~size_t(255);
@@ -235,6 +240,9 @@ moe_status moe_prefill_experts(const uint16_t *x, int32_t t, int32_t k, int32_t 
     if (!x || !offsets || !csr_rows || !csr_w || !csr_pos || !records || !out || !workspace)
         return fail(MOE_ERR_INVALID, "experts: null pointer");
     if (!aligned16(x) || !aligned16(out)) return fail(MOE_ERR_INVALID, "experts: x and out must be 16-byte aligned");
+    // The GEMMs address x and the intermediate rows with 32-bit byte offsets.
+    if ((uint64_t)t * k * L->inter * 2 > 0xffffffffull || (uint64_t)t * L->hidden * 2 > 0xffffffffull)
+        return fail(MOE_ERR_CAPACITY, "experts: t*k*inter or t*hidden too large for 32-bit offsets");
     Workspace w;
     workspace_plan(t, k, E, L, nullptr, &w);
     const size_t need = w.gate;  // everything before the shared scratch

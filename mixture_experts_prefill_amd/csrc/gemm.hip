@@ -62,13 +62,16 @@ __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
 // Per-lane dequantisation constants of one (row, group): codes at nibble
 // positions 0-3 / 16-19 become fp16 1024 + q, codes at 4-7 / 20-23 become
 // 1024 + 16 q, so  w = v * s + (b - 1024 s)  or  w = v * (s/16) + (b - 64 s).
+// The scale stays fp16 (v_fma_mix_f32 widens it exactly); the other three
+// constants are fp32, each one v_fma_mix_f32 from the fp16 pair.
 struct Deq {
-    float s, c, s16, c16;
+    _Float16 s;
+    float c, s16, c16;
 };
 __device__ __forceinline__ Deq deq_consts(uint32_t sb) {
     const half2_t h = __builtin_bit_cast(half2_t, sb);
-    const float s = (float)h.x, b = (float)h.y;
-    return Deq{s, __builtin_fmaf(-1024.0f, s, b), s * 0.0625f, __builtin_fmaf(-64.0f, s, b)};
+    return Deq{h.x, __builtin_fmaf(-1024.0f, (float)h.x, (float)h.y), __builtin_fmaf((float)h.x, 0.0625f, 0.0f),
+               __builtin_fmaf(-64.0f, (float)h.x, (float)h.y)};
 }
 
 // Loop-invariant bit masks kept in VGPRs: VOP3 on gfx950 takes no literal, so
@@ -94,9 +97,9 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t w, const Deq &d, const Masks
     const half2_t p2 = __builtin_bit_cast(half2_t, and_or(w8, m.lo, m.magic));  // q4, q5
     const half2_t p3 = __builtin_bit_cast(half2_t, and_or(w8, m.hi, m.magic));  // 16 q6, 16 q7
     uint4 u;
-    u.x = pk_bf16(__builtin_fmaf((float)p0.x, d.s, d.c), __builtin_fmaf((float)p0.y, d.s, d.c));
+    u.x = pk_bf16(__builtin_fmaf((float)p0.x, (float)d.s, d.c), __builtin_fmaf((float)p0.y, (float)d.s, d.c));
     u.y = pk_bf16(__builtin_fmaf((float)p1.x, d.s16, d.c16), __builtin_fmaf((float)p1.y, d.s16, d.c16));
-    u.z = pk_bf16(__builtin_fmaf((float)p2.x, d.s, d.c), __builtin_fmaf((float)p2.y, d.s, d.c));
+    u.z = pk_bf16(__builtin_fmaf((float)p2.x, (float)d.s, d.c), __builtin_fmaf((float)p2.y, (float)d.s, d.c));
     u.w = pk_bf16(__builtin_fmaf((float)p3.x, d.s16, d.c16), __builtin_fmaf((float)p3.y, d.s16, d.c16));
     return __builtin_bit_cast(bf16x8, u);
 }
@@ -133,22 +136,37 @@ __device__ __forceinline__ void barrier_no_fence() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// Direct global -> LDS loads (global_load_lds_dword[x4]): lane i's 4 or 16
-// bytes land at LDS byte m0 + 4i / 16i.  Issued from inline assembly so that
-// the compiler does not model them: its wait-count pass would otherwise make
-// every later LDS read wait for all of them (vmcnt(0)), which defeats the
-// prefetch.  Callers wait with explicit vmcnt counts before reading a slot;
-// the "memory" clobber keeps other memory accesses from moving across.
-__device__ __forceinline__ void dma16(uint32_t lds_addr, const void *src) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+// Direct memory -> LDS loads through a buffer resource
+// (buffer_load_dword[x4] ... lds): lane i reads base + soffset + voffset_i and
+// its 4 or 16 bytes land at LDS byte m0 + 4i / 16i.  The per-lane offset is
+// fixed for the tile and the per-step offset is a scalar, so a K step's loads
+// need no vector address arithmetic.  Issued from inline assembly so that the
+// compiler does not model them: its wait-count pass would otherwise make every
+// later LDS read wait for all of them (vmcnt(0)), which defeats the prefetch.
+// Callers wait with explicit vmcnt counts before reading a slot; the "memory"
+// clobber keeps other memory accesses from moving across.
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+// Raw buffer over [p, p + 4 GiB): the offsets computed below stay inside
+// the caller's buffers, as the former flat addresses did.
+__device__ __forceinline__ i32x4 buffer_rsrc(const void *p) {
+    const uint64_t b = (uint64_t)(uintptr_t)p;
+    i32x4 r;
+    r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(b >> 32) & 0xffffu));  // stride 0
+    r.z = -1;                                                                       // num_records
+    r.w = 0x00020000;                                                               // 32-bit raw data
+    return r;
+}
+__device__ __forceinline__ void dma16(uint32_t lds_addr, uint32_t voff, i32x4 rsrc, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                  :
-                 : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(src)
+                 : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
                  : "memory", "m0");
 }
-__device__ __forceinline__ void dma4(uint32_t lds_addr, const void *src) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
+__device__ __forceinline__ void dma4(uint32_t lds_addr, uint32_t voff, i32x4 rsrc, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
                  :
-                 : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(src)
+                 : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
                  : "memory", "m0");
 }
 
@@ -176,6 +194,8 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
     constexpr int STAGE = XSTAGE + WSTAGE;
     // ring depth: 3 K steps of lookahead when four stages fit in 160 KB of LDS, else 2
     constexpr int NS = (4 * STAGE <= 160 * 1024) ? 4 : 3;
+    // LDS: the NS activation stages, then the NS weight stages.
+    constexpr int WRING = NS * XSTAGE;
     constexpr int FEAT = kGateUp ? 32 * WAVES : 64 * WAVES;  // output features per workgroup
     constexpr int VM_PER_STEP = XPW + 4;                // vector-memory ops a wave issues per K step
     // Epilogue: per wave 32 token rows x 32 columns, row padded by 16 bytes.
@@ -186,7 +206,8 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
     // LDS byte address of the ring (wave-uniform, for the DMA's M0).
     const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds_raw));
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar
 
     // ---- which (M-tile, feature block).  Workgroups are dispatched to the 8
     // XCDs round-robin (XCD = blockIdx % 8) and in order within an XCD.
@@ -235,51 +256,52 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
         ob[1] = ob[0] + 1;
     }
     const bool live0 = ob[0] < obs, live1 = ob[1] < obs;
-    const uint8_t *wbase[2], *sbase[2];
+    const i32x4 rrec = buffer_rsrc(rec);
+    uint32_t wvo[2], svo[2];                              // per-lane byte offsets in the record
     const int sb_tile_bytes = (64 / a.group) * 32 * 4;
     const int sb_entry = (a.group == 64) ? (lane & 31) : lane;
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
         const bool live = f ? live1 : live0;
-        const size_t row0 = (size_t)(live ? ob[f] : 0) * nk;
-        const uint64_t wo = (kGateUp && f) ? a.w2_off : a.w_off;
-        const uint64_t so = (kGateUp && f) ? a.sb2_off : a.sb_off;
-        wbase[f] = rec + wo + row0 * 1024 + lane * 16;
-        sbase[f] = rec + so + row0 * sb_tile_bytes + sb_entry * 4;
+        const uint32_t row0 = (uint32_t)(live ? ob[f] : 0) * nk;
+        const uint32_t wo = (uint32_t)((kGateUp && f) ? a.w2_off : a.w_off);
+        const uint32_t so = (uint32_t)((kGateUp && f) ? a.sb2_off : a.sb_off);
+        wvo[f] = wo + row0 * 1024 + lane * 16;
+        svo[f] = so + row0 * sb_tile_bytes + sb_entry * 4;
     }
 
     // ---- activation rows this wave stages: block blk = wave*XPW + j covers
     // rows 8*blk .. 8*blk+7; lane s writes LDS bytes 16 s of the block, which
     // hold chunk (s%8) ^ xswz(row) of row 8*blk + s/8.  Rows past the tile
     // load row 0 of the tile (never read back for a stored output).
-    const uint16_t *xsrc[XPW];
+    const i32x4 rx = buffer_rsrc(kGateUp ? a.x : a.act);
+    uint32_t xvo[XPW];                                    // per-lane byte offsets of the staged rows
 #pragma unroll
     for (int j = 0; j < XPW; ++j) {
         const int r = (wave * XPW + j) * 8 + (lane >> 3);
         const int rr = r < n ? r : 0;
-        size_t row;
+        uint32_t row;
         if (MODE == GU_GATHER)
             row = a.rows[p0 + rr];
         else
-            row = (size_t)(p0 + rr);
-        const uint16_t *base = kGateUp ? a.x : a.act;
-        xsrc[j] = base + row * (kGateUp ? a.hidden : a.inter) + ((lane & 7) ^ xswz(r)) * 8;
+            row = (uint32_t)(p0 + rr);
+        xvo[j] = row * (uint32_t)(kGateUp ? a.hidden : a.inter) * 2u + (uint32_t)(((lane & 7) ^ xswz(r)) * 16);
     }
-    // Everything a K step needs goes straight from global memory into its
-    // ring slot by DMA (global_load_lds): the wave's share of the activation
-    // rows, its two 1 KB code tiles and their scale/bias entries.  No loop
-    // load has a register destination, so the only waits are the explicit
-    // vmcnt counts below.
-    auto wcode = [&](int slot, int f) { return (slot % NS) * STAGE + XSTAGE + (wave * 2 + f) * 1024; };
-    auto wsb = [&](int slot, int f) { return (slot % NS) * STAGE + XSTAGE + WAVES * 2048 + (wave * 2 + f) * 256; };
+    // Everything a K step needs goes straight from memory into its ring slot
+    // by DMA: the wave's share of the activation rows, its two 1 KB code tiles
+    // and their scale/bias entries.  No loop load has a register destination,
+    // so the only waits are the explicit vmcnt counts below.
+    auto wcode = [&](int slot, int f) { return WRING + (slot % NS) * WSTAGE + (wave * 2 + f) * 1024; };
+    auto wsb = [&](int slot, int f) { return WRING + (slot % NS) * WSTAGE + WAVES * 2048 + (wave * 2 + f) * 256; };
     auto issue = [&](int ks, int slot) {
-        const uint32_t xd = lds_base + (slot % NS) * STAGE + wave * XPW * 1024;
+        const uint32_t xd = lds_base + (slot % NS) * XSTAGE + wave * XPW * 1024;
+        const uint32_t xs = (uint32_t)ks * 128u;
 #pragma unroll
-        for (int j = 0; j < XPW; ++j) dma16(xd + j * 1024, xsrc[j] + ks * 64);
+        for (int j = 0; j < XPW; ++j) dma16(xd + j * 1024, xvo[j], rx, xs);
 #pragma unroll
         for (int f = 0; f < 2; ++f) {
-            dma16(lds_base + wcode(slot, f), wbase[f] + (size_t)ks * 1024);
-            dma4(lds_base + wsb(slot, f), sbase[f] + (size_t)ks * sb_tile_bytes);
+            dma16(lds_base + wcode(slot, f), wvo[f], rrec, (uint32_t)ks * 1024u);
+            dma4(lds_base + wsb(slot, f), svo[f], rrec, (uint32_t)(ks * sb_tile_bytes));
         }
     };
     // This wave's weights of the K step in `slot`, from LDS.
@@ -306,9 +328,16 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
 
         const Masks msk = make_masks();
         const int brow = lane & 31, bhalf = lane >> 5;
-        int bsw[TBR];                                           // xswz of this lane's B rows
+        // Lane offset of the B fragment of token block b at MFMA step st:
+        // row b*32 + brow, chunk (4*bhalf + st) ^ xswz(row).  Since
+        // xswz(b*32 + brow) = xswz(brow) ^ 4*(b&1), the offset is
+        // b*4096 + boff[b&1][st]: eight lane offsets plus immediates.
+        uint32_t boff[2][4];
     #pragma unroll
-        for (int b = 0; b < TBR; ++b) bsw[b] = xswz(b * 32 + brow);
+        for (int p = 0; p < 2; ++p)
+    #pragma unroll
+            for (int st = 0; st < 4; ++st)
+                boff[p][st] = brow * 128 + (((4 * bhalf + st) ^ xswz(brow) ^ (4 * p)) & 7) * 16;
 
         // Prologue: one K step in flight per ring slot.  Every step issues the
         // same loads -- past the last step it reloads step nk-1 into a free slot
@@ -325,10 +354,11 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
         // B fragments (32 token rows x 8 K values per lane) of MFMA step st of the
         // K step staged in `slot`.
         auto read_b = [&](int slot, int st, bf16x8 *out) {
-            const uint8_t *buf = lds_raw + (slot % NS) * STAGE;
+            const uint32_t sx = (uint32_t)((slot % NS) * XSTAGE);
+            const uint32_t o0 = sx + boff[0][st], o1 = sx + boff[1][st];
     #pragma unroll
             for (int b = 0; b < TBR; ++b)
-                out[b] = *reinterpret_cast<const bf16x8 *>(buf + (b * 32 + brow) * 128 + ((4 * bhalf + st) ^ bsw[b]) * 16);
+                out[b] = *reinterpret_cast<const bf16x8 *>(lds_raw + ((b & 1) ? o1 : o0) + b * 4096);
         };
         // Step 0 has landed for every wave once each has waited for its own loads
         // and all have met at the barrier.
@@ -378,9 +408,12 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
                 else
                     __builtin_amdgcn_sched_group_barrier(0x100, TBR + 4, 0);
     #pragma unroll
-                for (int b = 0; b < TBR; ++b) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);            // 2 MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x002, 48 / TBR, 0);      // dequant VALU slice
+                for (int m = 0; m < 2 * TBR; ++m) {
+                    // one MFMA, then a slice of VALU that issues during its
+                    // 32 cycles (an MFMA pair would block the wave at the
+                    // second MFMA with no VALU in between)
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 24 / TBR, 0);
                 }
                 if (st == 2) {
                     wait_vm<(NS - 2) * VM_PER_STEP>();

@@ -517,7 +517,10 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
 }
 
 // out[r, :] (+)= sum over the row's k CSR entries, in ascending CSR position
-// (= ascending expert id), of csr_w[p] * ye[p, :].  One workgroup per row.
+// (= ascending expert id), of csr_w[p] * ye[p, :].  One workgroup per row;
+// each thread owns 8 columns.  The loads of up to 8 entries are issued
+// before their FMAs so a thread waits for memory once per 8 entries, not
+// once per entry; the FMAs still run in ascending position.
 __global__ void __launch_bounds__(256) k_combine(const uint16_t *__restrict__ ye,
                                                  const uint32_t *__restrict__ pos,
                                                  const float *__restrict__ csr_w, int t, int k,
@@ -544,13 +547,21 @@ __global__ void __launch_bounds__(256) k_combine(const uint16_t *__restrict__ ye
 #pragma unroll
             for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
         }
-        for (int j = 0; j < k; ++j) {
-            const uint4 v = *reinterpret_cast<const uint4 *>(ye + (size_t)ps[j] * h + c);
-            const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+        for (int j0 = 0; j0 < k; j0 += 8) {
+            uint4 v[8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                acc[2 * i] = __builtin_fmaf(ws[j], __uint_as_float(u[i] << 16), acc[2 * i]);
-                acc[2 * i + 1] = __builtin_fmaf(ws[j], __uint_as_float(u[i] & 0xffff0000u), acc[2 * i + 1]);
+            for (int j = 0; j < 8; ++j)
+                if (j0 + j < k) v[j] = *reinterpret_cast<const uint4 *>(ye + (size_t)ps[j0 + j] * h + c);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (j0 + j >= k) break;
+                const float wj = ws[j0 + j];
+                const uint32_t u[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    acc[2 * i] = __builtin_fmaf(wj, __uint_as_float(u[i] << 16), acc[2 * i]);
+                    acc[2 * i + 1] = __builtin_fmaf(wj, __uint_as_float(u[i] & 0xffff0000u), acc[2 * i + 1]);
+                }
             }
         }
         o[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);

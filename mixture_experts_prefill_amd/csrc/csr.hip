@@ -151,9 +151,10 @@ __global__ void __launch_bounds__(256) k_csr_place(const uint32_t *__restrict__ 
 //   2. each XCD gets a contiguous run of those tiles of about one eighth of
 //      the total cost (kTileCostBase + token blocks per tile), so an expert's
 //      tiles share one L2;
-//   3. within its run, an XCD's tiles are listed by token blocks, largest
-//      first and in expert order among equals (order[x * xcap + j]), so the
-//      long tiles start first and the short ones fill the end.
+//   3. within its share, an XCD lists each expert's tiles together (they
+//      reuse its weights from L2), experts with more tiles first and in
+//      expert order among equals (order[x * xcap + j]): the long runs start
+//      first and the short ones fill the end.
 // xcnt[x] is the number of tiles of XCD x, sched_n[0] the total.
 __global__ void __launch_bounds__(1024) k_schedule(const uint32_t *__restrict__ offsets, int e0,
                                                    int e1, int bm, int4 *__restrict__ sched,
@@ -162,6 +163,8 @@ __global__ void __launch_bounds__(1024) k_schedule(const uint32_t *__restrict__ 
     __shared__ uint32_t wsum[16];
     __shared__ uint8_t tbl[kSchedMaxTiles];   // token blocks of each tile
     __shared__ uint8_t xof[kSchedMaxTiles];   // XCD of each tile
+    __shared__ uint8_t tin[kSchedMaxTiles];   // index of the tile within its expert
+    __shared__ uint8_t tne[kSchedMaxTiles];   // tiles of its expert
     __shared__ uint32_t xstart[9];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     // 1. tiles in expert order; each thread owns a contiguous run of experts
@@ -174,9 +177,12 @@ __global__ void __launch_bounds__(1024) k_schedule(const uint32_t *__restrict__ 
     uint32_t w = block_scan_1024(cnt, wsum, &T) - cnt;
     for (int e = a; e < b; ++e) {
         const uint32_t p0 = offsets[e], n = offsets[e + 1] - p0;
+        const uint32_t ne = (n + bm - 1) / bm;
         for (uint32_t m = 0; m < n; m += bm) {
             const uint32_t rows = min((uint32_t)bm, n - m);
             sched[w] = make_int4(e, (int)(p0 + m), (int)rows, 0);
+            tin[w] = (uint8_t)(m / bm);
+            tne[w] = (uint8_t)ne;
             tbl[w++] = (uint8_t)((rows + 31) / 32);
         }
     }
@@ -202,17 +208,26 @@ __global__ void __launch_bounds__(1024) k_schedule(const uint32_t *__restrict__ 
         for (int x = lo; x <= (int)xof[i]; ++x) xstart[x] = i;
     }
     __syncthreads();
-    // 3. wave x lists XCD x's tiles by token blocks, descending, stable
+    // 3. wave x lists XCD x's expert runs (an expert's tiles inside the
+    // share, cut at the share's ends) by length, descending, stable
     if (wave < 8) {
         const uint32_t s0 = xstart[wave], s1 = xstart[wave + 1];
+        uint32_t maxlen = 0;
+        for (uint32_t i = s0 + lane; i < s1; i += 64)
+            if (i == s0 || tin[i] == 0) maxlen = max(maxlen, min((uint32_t)(tne[i] - tin[i]), s1 - i));
+        for (int off = 32; off >= 1; off >>= 1) maxlen = max(maxlen, (uint32_t)__shfl_xor((int)maxlen, off, 64));
         uint32_t o = 0;
-        for (int tb = bm / 32; tb >= 1; --tb)
+        for (uint32_t len = maxlen; len >= 1; --len)
             for (uint32_t base = s0; base < s1; base += 64) {
                 const uint32_t i = base + lane;
-                const bool hit = i < s1 && tbl[i] == tb;
+                const bool start = i < s1 && (i == s0 || tin[i] == 0);
+                const bool hit = start && min((uint32_t)(tne[i] - tin[i]), s1 - i) == len;
+                // position of this run: len times the hits on lower lanes
                 const unsigned long long m = __ballot(hit);
-                if (hit) order[(size_t)wave * xcap + o + __popcll(m & ((1ull << lane) - 1ull))] = (int)i;
-                o += (uint32_t)__popcll(m);
+                const uint32_t at = o + len * (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
+                if (hit)
+                    for (uint32_t j = 0; j < len; ++j) order[(size_t)wave * xcap + at + j] = (int)(i + j);
+                o += len * (uint32_t)__popcll(m);
             }
         if (lane == 0) sched_n[kSchedXcnt + wave] = s1 - s0;
     }

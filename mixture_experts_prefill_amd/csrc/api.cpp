@@ -57,9 +57,8 @@ bool workspace_plan(int t, int k, int E, const moe_layout *routed, const moe_lay
         return at;
     };
     w->csr_hist = take(tiles * E * 4);
-    w->sched = take(max_mt * 16);
     w->sched_n = take(64);
-    w->order = take(8 * max_mt * 4);
+    w->order = take(8 * max_mt * sizeof(TileEntry));
     w->jobs = take((size_t)E * 8);
     w->hg = take(P * routed->inter * 2);
     w->ye = take(P * routed->hidden * 2);
@@ -256,9 +255,8 @@ moe_status moe_prefill_experts(const uint16_t *x, int32_t t, int32_t k, int32_t 
     a.x = x;
     a.rows = csr_rows;
     a.records = records;
-    a.sched = reinterpret_cast<int4 *>(ws + w.sched);
     a.sched_n = reinterpret_cast<uint32_t *>(ws + w.sched_n);
-    a.order = reinterpret_cast<int *>(ws + w.order);
+    a.order = reinterpret_cast<TileEntry *>(ws + w.order);
     a.xcap = (int)((size_t)t * k / kMinBM + (size_t)E + 1);
     a.t = t;
     a.hidden = L->hidden;
@@ -274,8 +272,8 @@ moe_status moe_prefill_experts(const uint16_t *x, int32_t t, int32_t k, int32_t 
                         accumulate, reinterpret_cast<uint64_t *>(ws + w.jobs), s);
     }
 
-    hipError_t e = launch_schedule(offsets, 0, E, bm, const_cast<int4 *>(a.sched),
-                                   const_cast<uint32_t *>(a.sched_n), const_cast<int *>(a.order), a.xcap, s);
+    hipError_t e = launch_schedule(offsets, 0, E, bm, records, const_cast<uint32_t *>(a.sched_n),
+                                   const_cast<TileEntry *>(a.order), a.xcap, s);
     if (e != hipSuccess) return hip_fail(e, "schedule");
     a.w_off = L->gate_w;
     a.sb_off = L->gate_sb;

@@ -147,24 +147,31 @@ __global__ void __launch_bounds__(256) k_csr_place(const uint32_t *__restrict__ 
 }
 
 // One workgroup builds the M-tile schedule of experts [e0, e1):
-//   1. tiles of up to bm rows per expert, in ascending expert id (sched);
-//   2. each XCD gets a contiguous run of those tiles of about one eighth of
+//   1. tiles of up to bm rows per expert, in ascending expert id (kept in LDS);
+//   2. each XCD gets a contiguous share of those tiles of about one eighth of
 //      the total cost (kTileCostBase + token blocks per tile), so an expert's
 //      tiles share one L2;
 //   3. within its share, an XCD lists each expert's tiles together (they
 //      reuse its weights from L2), experts with more tiles first and in
-//      expert order among equals (order[x * xcap + j]): the long runs start
-//      first and the short ones fill the end.
-// xcnt[x] is the number of tiles of XCD x, sched_n[0] the total.
+//      expert order among equals: the long runs start first and the short
+//      ones fill the end;
+//   4. every listed tile is written as a TileEntry (rows, expert, record
+//      address) to order[x * xcap + j].
+// sched_n[kSchedXcnt + x] is the number of tiles of XCD x, sched_n[0] the total.
 __global__ void __launch_bounds__(1024) k_schedule(const uint32_t *__restrict__ offsets, int e0,
-                                                   int e1, int bm, int4 *__restrict__ sched,
-                                                   uint32_t *__restrict__ sched_n, int *__restrict__ order,
-                                                   int xcap) {
+                                                   int e1, int bm, const uint64_t *__restrict__ records,
+                                                   uint32_t *__restrict__ sched_n,
+                                                   TileEntry *__restrict__ order, int xcap) {
     __shared__ uint32_t wsum[16];
-    __shared__ uint8_t tbl[kSchedMaxTiles];   // token blocks of each tile
-    __shared__ uint8_t xof[kSchedMaxTiles];   // XCD of each tile
-    __shared__ uint8_t tin[kSchedMaxTiles];   // index of the tile within its expert
-    __shared__ uint8_t tne[kSchedMaxTiles];   // tiles of its expert
+    __shared__ uint32_t tp0[kSchedMaxTiles];   // first CSR position of each tile
+    __shared__ uint16_t tex[kSchedMaxTiles];   // expert of each tile
+    __shared__ uint8_t tbl[kSchedMaxTiles];    // token blocks (32 rows) of each tile
+    __shared__ uint8_t trows[kSchedMaxTiles];  // rows of each tile - 1
+    __shared__ uint8_t xof[kSchedMaxTiles];    // XCD of each tile
+    __shared__ uint8_t tin[kSchedMaxTiles];    // index of the tile within its expert
+    __shared__ uint8_t tne[kSchedMaxTiles];    // tiles of its expert
+    __shared__ uint16_t perm[kSchedMaxTiles];  // listing position -> tile
+    __shared__ uint64_t erec[MOE_MAX_EXPERTS]; // record address of each expert
     __shared__ uint32_t xstart[9];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     // 1. tiles in expert order; each thread owns a contiguous run of experts
@@ -172,18 +179,23 @@ __global__ void __launch_bounds__(1024) k_schedule(const uint32_t *__restrict__ 
     const int per = (n_e + 1023) / 1024;
     const int a = e0 + tid * per, b = min(e1, a + per);
     uint32_t cnt = 0;
-    for (int e = a; e < b; ++e) cnt += (offsets[e + 1] - offsets[e] + bm - 1) / bm;
+    for (int e = a; e < b; ++e) {
+        cnt += (offsets[e + 1] - offsets[e] + bm - 1) / bm;
+        erec[e - e0] = records[e];
+    }
     uint32_t T;
     uint32_t w = block_scan_1024(cnt, wsum, &T) - cnt;
     for (int e = a; e < b; ++e) {
         const uint32_t p0 = offsets[e], n = offsets[e + 1] - p0;
         const uint32_t ne = (n + bm - 1) / bm;
-        for (uint32_t m = 0; m < n; m += bm) {
+        for (uint32_t m = 0; m < n; m += bm, ++w) {
             const uint32_t rows = min((uint32_t)bm, n - m);
-            sched[w] = make_int4(e, (int)(p0 + m), (int)rows, 0);
+            tp0[w] = p0 + m;
+            tex[w] = (uint16_t)(e - e0);
+            trows[w] = (uint8_t)(rows - 1);
             tin[w] = (uint8_t)(m / bm);
             tne[w] = (uint8_t)ne;
-            tbl[w++] = (uint8_t)((rows + 31) / 32);
+            tbl[w] = (uint8_t)((rows + 31) / 32);
         }
     }
     __syncthreads();
@@ -202,7 +214,7 @@ __global__ void __launch_bounds__(1024) k_schedule(const uint32_t *__restrict__ 
     }
     if (tid < 9) xstart[tid] = T;
     __syncthreads();
-    // run starts: tile i opens every XCD in (x of tile i-1, x of tile i]
+    // share starts: tile i opens every XCD in (x of tile i-1, x of tile i]
     for (uint32_t i = a2; i < b2; ++i) {
         const int lo = i ? (int)xof[i - 1] + 1 : 0;
         for (int x = lo; x <= (int)xof[i]; ++x) xstart[x] = i;
@@ -226,10 +238,25 @@ __global__ void __launch_bounds__(1024) k_schedule(const uint32_t *__restrict__ 
                 const unsigned long long m = __ballot(hit);
                 const uint32_t at = o + len * (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
                 if (hit)
-                    for (uint32_t j = 0; j < len; ++j) order[(size_t)wave * xcap + at + j] = (int)(i + j);
+                    for (uint32_t j = 0; j < len; ++j) perm[s0 + at + j] = (uint16_t)(i + j);
                 o += len * (uint32_t)__popcll(m);
             }
         if (lane == 0) sched_n[kSchedXcnt + wave] = s1 - s0;
+    }
+    __syncthreads();
+    // 4. position q of the listing belongs to the XCD of its tile, at index
+    // q - xstart of that XCD.
+    for (uint32_t q = tid; q < T; q += 1024) {
+        const uint32_t i = perm[q];
+        const uint32_t x = xof[i];
+        TileEntry te;
+        te.p0 = (int)tp0[i];
+        te.n = (int)trows[i] + 1;
+        te.expert = e0 + (int)tex[i];
+        te.pad = 0;
+        te.rec = reinterpret_cast<const void *>(erec[tex[i]]);
+        te.pad2 = 0;
+        order[(size_t)x * xcap + (q - xstart[x])] = te;
     }
     if (tid == 0) sched_n[0] = T;
 }
@@ -248,10 +275,10 @@ hipError_t launch_csr(const uint32_t *idx, const float *wts, int t, int k, int E
     return hipGetLastError();
 }
 
-hipError_t launch_schedule(const uint32_t *offsets, int e0, int e1, int bm, int4 *sched,
-                           uint32_t *sched_n, int *order, int xcap, hipStream_t s) {
+hipError_t launch_schedule(const uint32_t *offsets, int e0, int e1, int bm, const uint64_t *records,
+                           uint32_t *sched_n, TileEntry *order, int xcap, hipStream_t s) {
     ProfileScope prof(MOE_PHASE_SCHEDULE, s);
-    hipLaunchKernelGGL(k_schedule, dim3(1), dim3(1024), 0, s, offsets, e0, e1, bm, sched, sched_n, order,
+    hipLaunchKernelGGL(k_schedule, dim3(1), dim3(1024), 0, s, offsets, e0, e1, bm, records, sched_n, order,
                        xcap);
     return hipGetLastError();
 }

@@ -218,32 +218,29 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
     const int n_out = kGateUp ? a.inter : a.hidden;
     const int nblk = (n_out + FEAT - 1) / FEAT;
     const int xcd = blockIdx.x & 7, slot_in_xcd = blockIdx.x >> 3;
-    int mt, nb;
+    int nb, expert = 0, p0, n;
+    const uint8_t *rec;
     if (kDense) {
         const int total = ((a.t + BM - 1) / BM) * nblk;
         const int chunk = (total + 7) >> 3;
         const int logical = xcd * chunk + slot_in_xcd;
         if (slot_in_xcd >= chunk || logical >= total) return;
-        mt = logical / nblk;
         nb = logical % nblk;
-    } else {
-        if (slot_in_xcd >= (int)a.sched_n[kSchedXcnt + xcd] * nblk) return;
-        mt = a.order[xcd * a.xcap + slot_in_xcd / nblk];
-        nb = slot_in_xcd % nblk;
-    }
-
-    int expert = 0, p0, n;
-    if (kDense) {
-        p0 = mt * BM;
+        p0 = (logical / nblk) * BM;
         n = min(BM, a.t - p0);
+        rec = static_cast<const uint8_t *>(a.record);
     } else {
-        const int4 tl = a.sched[mt];
-        expert = tl.x;
-        p0 = tl.y;
-        n = tl.z;
+        // The entry is loaded together with the count (the grid never
+        // exceeds xcap slots per XCD, so the read stays inside the list).
+        const TileEntry te = a.order[xcd * a.xcap + slot_in_xcd / nblk];
+        if (slot_in_xcd >= (int)a.sched_n[kSchedXcnt + xcd] * nblk) return;
+        nb = slot_in_xcd % nblk;
+        expert = te.expert;
+        p0 = te.p0;
+        n = te.n;
+        rec = static_cast<const uint8_t *>(te.rec);
     }
-    const uint8_t *rec = static_cast<const uint8_t *>(
-        a.records ? reinterpret_cast<const void *>(a.records[expert]) : a.record);
+    (void)expert;
 
     const int K = kGateUp ? a.hidden : a.inter;
     const int nk = K >> 6;
@@ -629,13 +626,13 @@ hipError_t launch_mode(const GemmArgs &a, int bm, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_gateup(const GemmArgs &a, int bm, hipStream_t s) {
-    ProfileScope prof(a.sched ? MOE_PHASE_GATEUP : MOE_PHASE_SHARED_GU, s);
-    return a.sched ? launch_mode<GU_GATHER>(a, bm, s) : launch_mode<GU_DENSE>(a, bm, s);
+    ProfileScope prof(a.order ? MOE_PHASE_GATEUP : MOE_PHASE_SHARED_GU, s);
+    return a.order ? launch_mode<GU_GATHER>(a, bm, s) : launch_mode<GU_DENSE>(a, bm, s);
 }
 
 hipError_t launch_down(const GemmArgs &a, int bm, hipStream_t s) {
-    ProfileScope prof(a.sched ? MOE_PHASE_DOWN : MOE_PHASE_SHARED_DOWN, s);
-    return a.sched ? launch_mode<DOWN_YE>(a, bm, s) : launch_mode<DOWN_OUT>(a, bm, s);
+    ProfileScope prof(a.order ? MOE_PHASE_DOWN : MOE_PHASE_SHARED_DOWN, s);
+    return a.order ? launch_mode<DOWN_YE>(a, bm, s) : launch_mode<DOWN_OUT>(a, bm, s);
 }
 
 hipError_t launch_shared_gate(const uint16_t *x, const uint16_t *gate_w, int t, int h, float *g,

@@ -16,9 +16,8 @@ namespace moe {
 // Disjoint regions of the caller's workspace, 256-byte aligned.
 struct Workspace {
     size_t csr_hist;   // u32 [row_tiles][E]: per-tile expert counts, then segment bases
-    size_t sched;      // int4 [max_tiles]: (expert, first CSR position, rows, 0) per M-tile
     size_t sched_n;    // u32 [16]: number of M-tiles; [kSchedXcnt + x]: tiles of XCD x
-    size_t order;      // i32 [8][max_tiles]: per XCD, its tiles largest first
+    size_t order;      // TileEntry [8][max_tiles]: per XCD, its tiles in run order
     size_t jobs;       // u64 [E]: record address per expert for the ring path
     size_t hg;         // bf16 [t*k][I]: SiLU(gate)*up of every CSR entry
     size_t ye;         // bf16 [t*k][h]: down projection of every CSR entry
@@ -51,11 +50,21 @@ hipError_t launch_csr(const uint32_t *idx, const float *wts, int t, int k, int E
                       uint32_t *offsets, uint32_t *rows, float *csr_w, uint32_t *pos,
                       uint32_t *hist, hipStream_t s);
 
+// One M-tile of a grouped GEMM as the kernel reads it: one 32-byte load
+// gives the rows and the expert's record.
+struct TileEntry {
+    int p0, n, expert, pad;
+    const void *rec;
+    uint64_t pad2;
+};
+static_assert(sizeof(TileEntry) == 32, "one 32-byte load per tile");
+
 // M-tile schedule of the grouped GEMMs: for experts [e0, e1) with rows, tiles of
 // up to bm rows (sched, sched_n[0]), split over the 8 XCDs by cost and listed
-// per XCD largest first (order[x * xcap ..], sched_n[kSchedXcnt + x]).
-hipError_t launch_schedule(const uint32_t *offsets, int e0, int e1, int bm, int4 *sched,
-                           uint32_t *sched_n, int *order, int xcap, hipStream_t s);
+// per XCD (order[x * xcap ..], sched_n[kSchedXcnt + x]) with each entry's
+// record address taken from records[expert].
+hipError_t launch_schedule(const uint32_t *offsets, int e0, int e1, int bm, const uint64_t *records,
+                           uint32_t *sched_n, TileEntry *order, int xcap, hipStream_t s);
 
 struct GemmArgs {
     // B-operand rows (tokens): x rows gathered through `rows` (routed gate/up),
@@ -65,9 +74,8 @@ struct GemmArgs {
     const uint16_t *act;     // bf16 activations for the down projection
     const uint64_t *records; // device table of record addresses, per expert
     const void *record;      // the one record (shared expert) when records == nullptr
-    const int4 *sched;       // M-tiles (routed) or nullptr (dense rows 0..t)
     const uint32_t *sched_n;
-    const int *order;        // per-XCD tile lists (routed)
+    const TileEntry *order;  // per-XCD tile lists (routed) or nullptr (dense rows 0..t)
     int xcap;                // stride of order between XCDs
     int max_tiles;           // bound on M-tiles of the call
     int t;                   // rows (dense mode)

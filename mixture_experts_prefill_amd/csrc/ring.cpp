@@ -138,8 +138,8 @@ moe_status ring_run(moe_ring *ring, const void *const *host_records, GemmArgs a,
         if (e != hipSuccess) return hip_fail(e, "experts: fetched event");
 
         const int e0 = plan.jobs[j0].expert, e1 = plan.jobs[j1 - 1].expert + 1;
-        e = launch_schedule(offsets, e0, e1, bm, const_cast<int4 *>(a.sched), const_cast<uint32_t *>(a.sched_n),
-                            const_cast<int *>(a.order), a.xcap, s);
+        e = launch_schedule(offsets, e0, e1, bm, a.records, const_cast<uint32_t *>(a.sched_n),
+                            const_cast<TileEntry *>(a.order), a.xcap, s);
         if (e != hipSuccess) return hip_fail(e, "experts: schedule");
         int rows = 0;
         for (int j = j0; j < j1; ++j) rows += plan.jobs[j].rows;

@@ -257,7 +257,7 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
     uint32_t wvo[2], svo[2];                              // per-lane byte offsets in the record
     const int sb_tile_bytes = (64 / a.group) * 32 * 4;
     const int sb_entry = (a.group == 64) ? (lane & 31) : lane;
-#pragma unroll
+    #pragma unroll
     for (int f = 0; f < 2; ++f) {
         const bool live = f ? live1 : live0;
         const uint32_t row0 = (uint32_t)(live ? ob[f] : 0) * nk;
@@ -273,7 +273,7 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
     // load row 0 of the tile (never read back for a stored output).
     const i32x4 rx = buffer_rsrc(kGateUp ? a.x : a.act);
     uint32_t xvo[XPW];                                    // per-lane byte offsets of the staged rows
-#pragma unroll
+    #pragma unroll
     for (int j = 0; j < XPW; ++j) {
         const int r = (wave * XPW + j) * 8 + (lane >> 3);
         const int rr = r < n ? r : 0;
@@ -293,9 +293,9 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
     auto issue = [&](int ks, int slot) {
         const uint32_t xd = lds_base + (slot % NS) * XSTAGE + wave * XPW * 1024;
         const uint32_t xs = (uint32_t)ks * 128u;
-#pragma unroll
+        #pragma unroll
         for (int j = 0; j < XPW; ++j) dma16(xd + j * 1024, xvo[j], rx, xs);
-#pragma unroll
+        #pragma unroll
         for (int f = 0; f < 2; ++f) {
             dma16(lds_base + wcode(slot, f), wvo[f], rrec, (uint32_t)ks * 1024u);
             dma4(lds_base + wsb(slot, f), svo[f], rrec, (uint32_t)(ks * sb_tile_bytes));
@@ -303,7 +303,7 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
     };
     // This wave's weights of the K step in `slot`, from LDS.
     auto read_w = [&](int slot, Stage &st) {
-#pragma unroll
+        #pragma unroll
         for (int f = 0; f < 2; ++f) {
             st.c[f] = *reinterpret_cast<const uint4 *>(lds_raw + wcode(slot, f) + lane * 16);
             st.sb[f] = *reinterpret_cast<const uint32_t *>(lds_raw + wsb(slot, f) + lane * 4);
@@ -316,11 +316,11 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
     auto body = [&](auto tbr_c) {
         constexpr int TBR = decltype(tbr_c)::value;
         f32x16 acc[2][TBR];
-    #pragma unroll
+        #pragma unroll
         for (int f = 0; f < 2; ++f)
-    #pragma unroll
+            #pragma unroll
             for (int b = 0; b < TBR; ++b)
-    #pragma unroll
+                #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[f][b][r] = 0.0f;
 
         const Masks msk = make_masks();
@@ -330,16 +330,16 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
         // xswz(b*32 + brow) = xswz(brow) ^ 4*(b&1), the offset is
         // b*4096 + boff[b&1][st]: eight lane offsets plus immediates.
         uint32_t boff[2][4];
-    #pragma unroll
+        #pragma unroll
         for (int p = 0; p < 2; ++p)
-    #pragma unroll
+            #pragma unroll
             for (int st = 0; st < 4; ++st)
                 boff[p][st] = brow * 128 + (((4 * bhalf + st) ^ xswz(brow) ^ (4 * p)) & 7) * 16;
 
         // Prologue: one K step in flight per ring slot.  Every step issues the
         // same loads -- past the last step it reloads step nk-1 into a free slot
         // -- so the vmcnt counts below hold on every iteration.
-    #pragma unroll
+        #pragma unroll
         for (int j = 0; j < NS; ++j) issue(min(j, nk - 1), j);
 
         auto frag = [&](const Stage &sg, int st, const Deq &d0, const Deq &d1, bf16x8 *out) {
@@ -353,7 +353,7 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
         auto read_b = [&](int slot, int st, bf16x8 *out) {
             const uint32_t sx = (uint32_t)((slot % NS) * XSTAGE);
             const uint32_t o0 = sx + boff[0][st], o1 = sx + boff[1][st];
-    #pragma unroll
+            #pragma unroll
             for (int b = 0; b < TBR; ++b)
                 out[b] = *reinterpret_cast<const bf16x8 *>(lds_raw + ((b & 1) ? o1 : o0) + b * 4096);
         };
@@ -382,7 +382,7 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
         for (int kb = 0; kb < nk; ++kb) {
             const Deq d0 = deq_consts(cur.sb[0]), d1 = deq_consts(cur.sb[1]);
             Stage nxt;
-    #pragma unroll
+            #pragma unroll
             for (int st = 0; st < 4; ++st) {
                 const bf16x8 a0 = af[0], a1 = af[1];
                 bf16x8 bnxt[TBR];
@@ -395,7 +395,7 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
                     const Deq e0 = deq_consts(nxt.sb[0]), e1 = deq_consts(nxt.sb[1]);
                     frag(nxt, 0, e0, e1, af);
                 }
-    #pragma unroll
+                #pragma unroll
                 for (int b = 0; b < TBR; ++b) {
                     acc[0][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bcur[b], acc[0][b], 0, 0, 0);
                     acc[1][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bcur[b], acc[1][b], 0, 0, 0);
@@ -404,7 +404,7 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
                     __builtin_amdgcn_sched_group_barrier(0x100, TBR, 0);       // the LDS reads first
                 else
                     __builtin_amdgcn_sched_group_barrier(0x100, TBR + 4, 0);
-    #pragma unroll
+                #pragma unroll
                 for (int m = 0; m < 2 * TBR; ++m) {
                     // one MFMA, then a slice of VALU that issues during its
                     // 32 cycles (an MFMA pair would block the wave at the
@@ -418,7 +418,7 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
                     issue(min(kb + NS, nk - 1), kb + NS);
                 }
                 __builtin_amdgcn_sched_barrier(0);
-    #pragma unroll
+                #pragma unroll
                 for (int b = 0; b < TBR; ++b) bcur[b] = bnxt[b];
             }
             cur = nxt;
@@ -435,12 +435,12 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
         constexpr int CPR = 32 * EB / 16;                    // 16-byte chunks per row
         constexpr int PER_LANE = 32 * CPR / 64;
         constexpr int PASSES = kGateUp ? 1 : 2;
-    #pragma unroll
+        #pragma unroll
         for (int b = 0; b < TBR; ++b) {
-    #pragma unroll
+            #pragma unroll
             for (int f = 0; f < PASSES; ++f) {
                 if (f == 1 && !live1) break;
-    #pragma unroll
+                #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
                     const int col = 8 * q4 + 4 * bhalf;
                     if (kGateUp) {
@@ -465,7 +465,7 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
                 __builtin_amdgcn_wave_barrier();
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
                 const int colf = ob[f] * 32;                   // first feature of this fragment
-    #pragma unroll
+                #pragma unroll
                 for (int i = 0; i < PER_LANE; ++i) {
                     const int idx = lane + 64 * i;
                     const int row = idx / CPR, ch = idx % CPR;
@@ -541,20 +541,20 @@ __global__ void __launch_bounds__(256) k_combine(const uint16_t *__restrict__ ye
             acc[0] = o0.x; acc[1] = o0.y; acc[2] = o0.z; acc[3] = o0.w;
             acc[4] = o1.x; acc[5] = o1.y; acc[6] = o1.z; acc[7] = o1.w;
         } else {
-#pragma unroll
+            #pragma unroll
             for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
         }
         for (int j0 = 0; j0 < k; j0 += 8) {
             uint4 v[8];
-#pragma unroll
+            #pragma unroll
             for (int j = 0; j < 8; ++j)
                 if (j0 + j < k) v[j] = *reinterpret_cast<const uint4 *>(ye + (size_t)ps[j0 + j] * h + c);
-#pragma unroll
+            #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 if (j0 + j >= k) break;
                 const float wj = ws[j0 + j];
                 const uint32_t u[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
-#pragma unroll
+                #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     acc[2 * i] = __builtin_fmaf(wj, __uint_as_float(u[i] << 16), acc[2 * i]);
                     acc[2 * i + 1] = __builtin_fmaf(wj, __uint_as_float(u[i] & 0xffff0000u), acc[2 * i + 1]);

@@ -112,6 +112,21 @@ def test_null_and_alignment_checks(lib):
     assert lib.moe_shared(P(FAKE), 0, ctypes.byref(L), P(FAKE), None, P(FAKE), 0, P(FAKE), 1 << 20, None) == 2
 
 
+def test_32bit_offset_limits(lib):
+    """The GEMMs address records, x and the intermediate rows with 32-bit byte
+    offsets; shapes beyond that are refused before anything is enqueued."""
+    with pytest.raises(mep.MoeError) as e:
+        mep.moe_layout_make(65536, 65536, 64)          # three 2 GiB code sections
+    assert e.value.status == 1 and "4 GiB" in e.value.message
+    L = mep.moe_layout_make(256, 16384, 64)            # t*k*I*2 = 4096*32*16384*2 = 4 GiB
+    rc = lib.moe_prefill_experts(P(FAKE), 4096, 32, 64, ctypes.byref(L), P(FAKE), P(FAKE), P(FAKE), P(FAKE),
+                                 P(FAKE), None, None, P(FAKE), 1, P(FAKE), 1 << 40, None)
+    assert rc == 2 and "32-bit" in lib.moe_last_error().decode()
+    Ls = mep.moe_layout_make(256, 524352, 64)          # t*Is*2 > 4 GiB at t = 4096
+    rc = lib.moe_shared(P(FAKE), 4096, ctypes.byref(Ls), P(FAKE), None, P(FAKE), 0, P(FAKE), 1 << 40, None)
+    assert rc == 2 and "32-bit" in lib.moe_last_error().decode()
+
+
 def test_workspace_too_small(lib):
     L = mep.moe_layout_make(256, 128, 32)
     need = mep.moe_workspace_bytes(16, 2, 8, L, L)

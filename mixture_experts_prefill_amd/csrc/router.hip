@@ -114,12 +114,14 @@ __global__ void __launch_bounds__(256) k_router(const uint16_t *__restrict__ x,
 }
 
 // Large-t router: a workgroup of 8 waves owns 32 rows x 32 experts; every
-// 256-element step stages the rows' x chunks (16 KB) and the experts' W
-// chunks (32 KB) in LDS once, double-buffered, and each wave computes
-// 16 rows x 8 experts from LDS (lane l still owns partial l of every logit).
+// 256-element step stages the rows' x chunks (widened once to fp32 on the way
+// in, 32 KB) and the experts' W chunks (32 KB) in LDS, double-buffered, and
+// each wave computes 16 rows x 8 experts from LDS (lane l still owns partial
+// l of every logit).
 constexpr int kLR = 32, kLE = 32;             // rows, experts per workgroup
 constexpr int kWR = 16, kWE = 8;              // rows, experts per wave
-constexpr int kXBytes = kLR * 512, kWBytes = kLE * 1024;
+constexpr int kXSrc = kLR * 512;              // x bytes (bf16) per step
+constexpr int kXBytes = kLR * 1024, kWBytes = kLE * 1024;  // staged bytes (x as fp32)
 
 __global__ void __launch_bounds__(512, 1) k_router_lds(const uint16_t *__restrict__ x,
                                                        const float *__restrict__ w, int t, int h,
@@ -130,19 +132,20 @@ __global__ void __launch_bounds__(512, 1) k_router_lds(const uint16_t *__restric
     const int r0 = (blockIdx.x / e_blocks) * kLR, e0 = (blockIdx.x % e_blocks) * kLE;
     const int wr = (wave >> 2) * kWR, we = (wave & 3) * kWE;   // this wave's rows / experts in the tile
 
-    // Staging: 16-byte chunks, x first (32 rows x 32 chunks) then W (32 x 64).
-    constexpr int kChunks = (kXBytes + kWBytes) / 16, kPer = kChunks / 512;
+    // Staging: 16-byte source chunks, x first (32 rows x 32 chunks of 8 bf16,
+    // each stored as 32 bytes of fp32) then W (32 x 64).
+    constexpr int kChunks = (kXSrc + kWBytes) / 16, kPer = kChunks / 512;
     const uint8_t *src[kPer];
     bool ok[kPer];
 #pragma unroll
     for (int c = 0; c < kPer; ++c) {
         const int ch = tid + 512 * c;
-        if (ch < kXBytes / 16) {
+        if (ch < kXSrc / 16) {
             const int r = ch >> 5, q = ch & 31;
             ok[c] = r0 + r < t;
             src[c] = reinterpret_cast<const uint8_t *>(x + (size_t)min(r0 + r, t - 1) * h) + q * 16;
         } else {
-            const int cw = ch - kXBytes / 16;
+            const int cw = ch - kXSrc / 16;
             const int e = cw >> 6, q = cw & 63;
             ok[c] = e0 + e < E;
             src[c] = reinterpret_cast<const uint8_t *>(w + (size_t)min(e0 + e, E - 1) * h) + q * 16;
@@ -153,7 +156,7 @@ __global__ void __launch_bounds__(512, 1) k_router_lds(const uint16_t *__restric
 #pragma unroll
         for (int c = 0; c < kPer; ++c) {
             const int ch = tid + 512 * c;
-            const size_t off = (ch < kXBytes / 16) ? (size_t)s * 512 : (size_t)s * 1024;
+            const size_t off = (ch < kXSrc / 16) ? (size_t)s * 512 : (size_t)s * 1024;
             v[c] = ok[c] ? *reinterpret_cast<const uint4 *>(src[c] + off) : make_uint4(0, 0, 0, 0);
         }
     };
@@ -168,7 +171,16 @@ __global__ void __launch_bounds__(512, 1) k_router_lds(const uint16_t *__restric
     for (int s = 0; s < steps; ++s) {
         uint8_t *buf = lds[s & 1];
 #pragma unroll
-        for (int c = 0; c < kPer; ++c) *reinterpret_cast<uint4 *>(buf + (tid + 512 * c) * 16) = v[c];
+        for (int c = 0; c < kPer; ++c) {
+            const int ch = tid + 512 * c;
+            if (ch < kXSrc / 16) {  // 8 bf16 -> 8 fp32 (exact)
+                const uint4 q = v[c];
+                *reinterpret_cast<float4 *>(buf + ch * 32) = make_float4(bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.y), bf16_hi(q.y));
+                *reinterpret_cast<float4 *>(buf + ch * 32 + 16) = make_float4(bf16_lo(q.z), bf16_hi(q.z), bf16_lo(q.w), bf16_hi(q.w));
+            } else {
+                *reinterpret_cast<uint4 *>(buf + kXBytes + (ch - kXSrc / 16) * 16) = v[c];
+            }
+        }
         __syncthreads();
         if (s + 1 < steps) load(s + 1, v);
         float wv[kWE][4];
@@ -182,8 +194,8 @@ __global__ void __launch_bounds__(512, 1) k_router_lds(const uint16_t *__restric
         }
 #pragma unroll
         for (int i = 0; i < kWR; ++i) {
-            const uint2 q = *reinterpret_cast<const uint2 *>(buf + (wr + i) * 512 + lane * 8);
-            const float x0 = bf16_lo(q.x), x1 = bf16_hi(q.x), x2 = bf16_lo(q.y), x3 = bf16_hi(q.y);
+            const float4 q = *reinterpret_cast<const float4 *>(buf + (wr + i) * 1024 + lane * 16);
+            const float x0 = q.x, x1 = q.y, x2 = q.z, x3 = q.w;
 #pragma unroll
             for (int j = 0; j < kWE; ++j) {
                 float &acc = p[i * kWE + j];
@@ -197,8 +209,22 @@ __global__ void __launch_bounds__(512, 1) k_router_lds(const uint16_t *__restric
 
     // Transposed butterfly over the 64 partials: 6 splitting levels leave
     // outputs 2*lane and 2*lane + 1 (row (2 lane)/8, experts (2 lane)%8, +1).
+    // Levels off = 32 and 16 use v_permlane32/16_swap: swapping the upper
+    // lanes of p[o] with the lower lanes of p[o + half] hands each lane its
+    // partner's copy of the output it keeps, so one add finishes the pair
+    // (lane l < off: p_l + p_(l+off); lane l >= off: p_(l-off) + p_l).
 #pragma unroll
-    for (int lvl = 0; lvl < 6; ++lvl) {
+    for (int o = 0; o < 64; ++o) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[o]), __float_as_uint(p[o + 64]), false, false);
+        p[o] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+#pragma unroll
+    for (int o = 0; o < 32; ++o) {
+        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(p[o]), __float_as_uint(p[o + 32]), false, false);
+        p[o] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+#pragma unroll
+    for (int lvl = 2; lvl < 6; ++lvl) {
         const int off = 32 >> lvl;
         const int half = (kWR * kWE) >> (lvl + 1);
         const uint32_t m = (lane & off) ? 0xffffffffu : 0u;

@@ -146,6 +146,62 @@ __global__ void __launch_bounds__(256) k_csr_place(const uint32_t *__restrict__ 
     }
 }
 
+// Small chunks (t <= kCsrSmallTiles * 64 rows): the same three steps in one
+// workgroup of 1024 threads, with the masks, counts and segment starts in
+// LDS, so a decode-sized chunk costs one launch instead of three.  Thread e
+// owns expert e (E <= 1024).
+constexpr int kCsrSmallTiles = 4;
+__global__ void __launch_bounds__(1024) k_csr_small(const uint32_t *__restrict__ idx,
+                                                    const float *__restrict__ wts, int t, int k, int E,
+                                                    uint32_t *__restrict__ offsets,
+                                                    uint32_t *__restrict__ rows,
+                                                    float *__restrict__ csr_w,
+                                                    uint32_t *__restrict__ pos) {
+    __shared__ unsigned long long mask[kCsrSmallTiles][MOE_MAX_EXPERTS];
+    __shared__ uint32_t base[kCsrSmallTiles][MOE_MAX_EXPERTS];
+    __shared__ uint32_t wsum[16];
+    const int tid = threadIdx.x;
+    const int tiles = (t + TR - 1) / TR;
+    for (int i = tid; i < kCsrSmallTiles * MOE_MAX_EXPERTS; i += 1024) (&mask[0][0])[i] = 0ull;
+    __syncthreads();
+    for (int i = tid; i < t * k; i += 1024) {
+        const int r = i / k;
+        const uint32_t e = idx[i];
+        if (e < (uint32_t)E) atomicOr(&mask[r / TR][e], 1ull << (r % TR));
+    }
+    __syncthreads();
+    // expert tid: counts per tile, total, then its segment start
+    uint32_t cnt[kCsrSmallTiles], tot = 0;
+#pragma unroll
+    for (int j = 0; j < kCsrSmallTiles; ++j) {
+        cnt[j] = (tid < E && j < tiles) ? (uint32_t)__popcll(mask[j][tid]) : 0u;
+        tot += cnt[j];
+    }
+    uint32_t all;
+    const uint32_t start = block_scan_1024(tot, wsum, &all) - tot;
+    if (tid < E) {
+        offsets[tid] = start;
+        uint32_t b = start;
+#pragma unroll
+        for (int j = 0; j < kCsrSmallTiles; ++j) {
+            base[j][tid] = b;
+            b += cnt[j];
+        }
+    }
+    if (tid == 0) offsets[E] = (uint32_t)(t * k);
+    __syncthreads();
+    for (int i = tid; i < t * k; i += 1024) {
+        const int r = i / k, tile = r / TR, rr = r % TR;
+        const uint32_t e = idx[i];
+        if (e >= (uint32_t)E) continue;
+        const unsigned long long below = (rr == 0) ? 0ull : (mask[tile][e] & ((1ull << rr) - 1ull));
+        const uint32_t p = base[tile][e] + (uint32_t)__popcll(below);
+        rows[p] = (uint32_t)r;
+        csr_w[p] = wts[i];
+        pos[i] = p;
+    }
+}
+
 // One workgroup builds the M-tile schedule of experts [e0, e1):
 //   1. tiles of up to bm rows per expert, in ascending expert id (kept in LDS);
 //   2. each XCD gets a contiguous share of those tiles of about one eighth of
@@ -268,6 +324,10 @@ hipError_t launch_csr(const uint32_t *idx, const float *wts, int t, int k, int E
                       uint32_t *hist, hipStream_t s) {
     const int tiles = (t + TR - 1) / TR;
     ProfileScope prof(MOE_PHASE_CSR, s);
+    if (tiles <= kCsrSmallTiles) {
+        hipLaunchKernelGGL(k_csr_small, dim3(1), dim3(1024), 0, s, idx, wts, t, k, E, offsets, rows, csr_w, pos);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(k_csr_count, dim3(tiles), dim3(256), 0, s, idx, t, k, E, hist);
     hipLaunchKernelGGL(k_csr_scan, dim3(1), dim3(1024), 0, s, tiles, E, t * k, hist, offsets);
     hipLaunchKernelGGL(k_csr_place, dim3(tiles), dim3(256), 0, s, idx, wts, t, k, E, hist, rows,

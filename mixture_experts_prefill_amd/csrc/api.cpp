@@ -5,6 +5,7 @@
 // chunk" and capacity checks up front, errors returned with a message).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -34,6 +35,38 @@ moe_status hip_fail(hipError_t e, const char *what) {
 
 static size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
+int shared_ksplit(int t, int ksteps, int nblk) {
+    if (t > 64) return 1;
+    const int mt = (t + 31) / 32;
+    for (int d = 1; d <= ksteps; ++d)
+        if (ksteps % d == 0 && mt * nblk * d >= 128) return d;
+    return ksteps;
+}
+
+// How the shared expert runs for t rows: tile height, K splits of its two
+// GEMMs (workgroup counts follow the GEMM's launch rule) and the bytes of
+// split partial sums it needs.
+struct SharedPlan {
+    int bm, s_gu, s_dn;
+    size_t part_bytes;
+};
+static SharedPlan shared_plan(int t, const moe_layout *Ls) {
+    SharedPlan sp;
+    sp.bm = t >= 512 ? 128 : t >= 64 ? 64 : 32;
+    const int mt = (t + sp.bm - 1) / sp.bm;
+    const bool wide_gu = Ls->inter >= 256 && sp.bm >= 64, wide_dn = Ls->hidden >= 512 && sp.bm >= 64;
+    const int nblk_gu = (Ls->inter + (wide_gu ? 255 : 127)) / (wide_gu ? 256 : 128);
+    const int nblk_dn = (Ls->hidden + (wide_dn ? 511 : 255)) / (wide_dn ? 512 : 256);
+    (void)mt;
+    sp.s_gu = shared_ksplit(t, Ls->hidden / 64, nblk_gu);
+    sp.s_dn = shared_ksplit(t, Ls->inter / 64, nblk_dn);
+    size_t pb = 0;
+    if (sp.s_gu > 1) pb = (size_t)sp.s_gu * t * 2 * Ls->inter * 4;
+    if (sp.s_dn > 1) pb = std::max(pb, (size_t)sp.s_dn * t * Ls->hidden * 4);
+    sp.part_bytes = pb;
+    return sp;
+}
+
 static bool layout_ok(const moe_layout *L) {
     if (!L) return false;
     moe_layout ref;
@@ -62,6 +95,7 @@ bool workspace_plan(int t, int k, int E, const moe_layout *routed, const moe_lay
     w->jobs = take((size_t)E * 8);
     w->hg = take(P * routed->inter * 2);
     w->ye = take(P * routed->hidden * 2);
+    w->part = take(shared ? shared_plan(t, shared).part_bytes : 0);
     w->hs = take(shared ? (size_t)t * shared->inter * 2 : 0);
     w->gate = take((size_t)t * 4);
     w->total = off;
@@ -185,15 +219,18 @@ moe_status moe_shared(const uint16_t *x, int32_t t, const moe_layout *Ls, const 
         return fail(MOE_ERR_INVALID, "shared: x, record and out must be 16-byte aligned");
     if ((uint64_t)t * Ls->inter * 2 > 0xffffffffull || (uint64_t)t * Ls->hidden * 2 > 0xffffffffull)
         return fail(MOE_ERR_CAPACITY, "shared: t*inter or t*hidden too large for 32-bit offsets");
-    // The shared expert's scratch is the end of the workspace: [.. | hs | gate].
+    // The shared expert's scratch is the end of the workspace: [.. | part | hs | gate].
+    const SharedPlan sp = shared_plan(t, Ls);
     const size_t g_bytes = align256((size_t)t * 4), hs_bytes = align256((size_t)t * Ls->inter * 2);
+    const size_t p_bytes = align256(sp.part_bytes);
     const size_t end = workspace_bytes & ~size_t(255);
-    if (end < g_bytes + hs_bytes)
+    if (end < g_bytes + hs_bytes + p_bytes)
         return fail(MOE_ERR_WORKSPACE, "shared: workspace %zu bytes < %zu needed", workspace_bytes,
-                    g_bytes + hs_bytes);
+                    g_bytes + hs_bytes + p_bytes);
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     uint16_t *hs = reinterpret_cast<uint16_t *>(ws + end - g_bytes - hs_bytes);
     float *g = reinterpret_cast<float *>(ws + end - g_bytes);
+    float *part = reinterpret_cast<float *>(ws + end - g_bytes - hs_bytes - p_bytes);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
     if (gate_w) {
@@ -213,8 +250,13 @@ moe_status moe_shared(const uint16_t *x, int32_t t, const moe_layout *Ls, const 
     a.w2_off = Ls->up_w;
     a.sb2_off = Ls->up_sb;
     a.hg = hs;
-    const int bm = t >= 512 ? 128 : t >= 64 ? 64 : 32;
+    a.part = part;
+    const int bm = sp.bm;
+    // Small chunks split K over workgroups (partial sums reduced in a fixed
+    // order by k_reduce_*); larger ones run the GEMM with its epilogue.
+    a.ksplit = sp.s_gu;
     e = launch_gateup(a, bm, s);
+    if (e == hipSuccess && sp.s_gu > 1) e = launch_reduce_gu(part, sp.s_gu, t, Ls->inter, hs, s);
     if (e != hipSuccess) return hip_fail(e, "shared gate/up");
     a.act = hs;
     a.w_off = Ls->down_w;
@@ -222,7 +264,10 @@ moe_status moe_shared(const uint16_t *x, int32_t t, const moe_layout *Ls, const 
     a.out = out;
     a.gate = gate_w ? g : nullptr;
     a.accumulate = accumulate;
+    a.ksplit = sp.s_dn;
     e = launch_down(a, bm, s);
+    if (e == hipSuccess && sp.s_dn > 1)
+        e = launch_reduce_down(part, sp.s_dn, t, Ls->hidden, gate_w ? g : nullptr, out, accumulate, s);
     if (e != hipSuccess) return hip_fail(e, "shared down");
     return MOE_OK;
 }

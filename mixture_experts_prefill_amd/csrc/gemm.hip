@@ -52,7 +52,9 @@ __device__ __forceinline__ uint32_t ld_g4(const void *p) {
     return *reinterpret_cast<const GLOBAL uint32_t *>(reinterpret_cast<uintptr_t>(p));
 }
 
-enum Mode { GU_GATHER = 0, GU_DENSE = 1, DOWN_YE = 2, DOWN_OUT = 3 };
+// GU_PART / DOWN_PART: dense rows, one K range (split) per workgroup, raw
+// fp32 accumulators written to a.part for k_reduce_gu / k_reduce_down.
+enum Mode { GU_GATHER = 0, GU_DENSE = 1, DOWN_YE = 2, DOWN_OUT = 3, GU_PART = 4, DOWN_PART = 5 };
 
 __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
     bf16x2 v = {(__bf16)a, (__bf16)b};
@@ -179,8 +181,9 @@ __device__ __forceinline__ void wait_vm() {
 
 template <int MODE, int BM, int WAVES>
 __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const GemmArgs a) {
-    constexpr bool kGateUp = (MODE == GU_GATHER || MODE == GU_DENSE);
-    constexpr bool kDense = (MODE == GU_DENSE || MODE == DOWN_OUT);
+    constexpr bool kGateUp = (MODE == GU_GATHER || MODE == GU_DENSE || MODE == GU_PART);
+    constexpr bool kPart = (MODE == GU_PART || MODE == DOWN_PART);
+    constexpr bool kDense = (MODE == GU_DENSE || MODE == DOWN_OUT || kPart);
     constexpr int TB = BM / 32;                         // token blocks of 32
     // Two waves per SIMD leave 256 registers per wave: 128 accumulators
     // (two fragments x 4 token blocks) is the most that fits beside the
@@ -199,7 +202,7 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
     constexpr int FEAT = kGateUp ? 32 * WAVES : 64 * WAVES;  // output features per workgroup
     constexpr int VM_PER_STEP = XPW + 4;                // vector-memory ops a wave issues per K step
     // Epilogue: per wave 32 token rows x 32 columns, row padded by 16 bytes.
-    constexpr int EB = (MODE == DOWN_OUT) ? 4 : 2;
+    constexpr int EB = (MODE == DOWN_OUT || kPart) ? 4 : 2;
     constexpr int EROW = 32 * EB + 16;
     constexpr int RING = NS * STAGE, EPI = WAVES * 32 * EROW;
     __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[RING > EPI ? RING : EPI];
@@ -218,15 +221,18 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
     const int n_out = kGateUp ? a.inter : a.hidden;
     const int nblk = (n_out + FEAT - 1) / FEAT;
     const int xcd = blockIdx.x & 7, slot_in_xcd = blockIdx.x >> 3;
-    int nb, expert = 0, p0, n;
+    int nb, expert = 0, p0, n, split = 0;
     const uint8_t *rec;
     if (kDense) {
-        const int total = ((a.t + BM - 1) / BM) * nblk;
+        const int per_split = ((a.t + BM - 1) / BM) * nblk;
+        const int total = per_split * (kPart ? a.ksplit : 1);
         const int chunk = (total + 7) >> 3;
         const int logical = xcd * chunk + slot_in_xcd;
         if (slot_in_xcd >= chunk || logical >= total) return;
-        nb = logical % nblk;
-        p0 = (logical / nblk) * BM;
+        split = logical / per_split;
+        const int rest = logical % per_split;
+        nb = rest % nblk;
+        p0 = (rest / nblk) * BM;
         n = min(BM, a.t - p0);
         rec = static_cast<const uint8_t *>(a.record);
     } else {
@@ -243,7 +249,11 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
     (void)expert;
 
     const int K = kGateUp ? a.hidden : a.inter;
-    const int nk = K >> 6;
+    // K steps of this workgroup: all of them, or one split's range
+    // (the host picks splits that divide the step count)
+    const int nk_all = K >> 6;                            // K steps of the record's rows
+    const int nk = kPart ? nk_all / a.ksplit : nk_all;
+    const int kbase = split * nk;
     const int obs = n_out >> 5;
     int ob[2];
     if (kGateUp) {
@@ -260,7 +270,7 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
     #pragma unroll
     for (int f = 0; f < 2; ++f) {
         const bool live = f ? live1 : live0;
-        const uint32_t row0 = (uint32_t)(live ? ob[f] : 0) * nk;
+        const uint32_t row0 = (uint32_t)(live ? ob[f] : 0) * nk_all;  // first tile of the row block
         const uint32_t wo = (uint32_t)((kGateUp && f) ? a.w2_off : a.w_off);
         const uint32_t so = (uint32_t)((kGateUp && f) ? a.sb2_off : a.sb_off);
         wvo[f] = wo + row0 * 1024 + lane * 16;
@@ -292,13 +302,14 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
     auto wsb = [&](int slot, int f) { return WRING + (slot % NS) * WSTAGE + WAVES * 2048 + (wave * 2 + f) * 256; };
     auto issue = [&](int ks, int slot) {
         const uint32_t xd = lds_base + (slot % NS) * XSTAGE + wave * XPW * 1024;
-        const uint32_t xs = (uint32_t)ks * 128u;
+        const int kg = kbase + ks;
+        const uint32_t xs = (uint32_t)kg * 128u;
         #pragma unroll
         for (int j = 0; j < XPW; ++j) dma16(xd + j * 1024, xvo[j], rx, xs);
         #pragma unroll
         for (int f = 0; f < 2; ++f) {
-            dma16(lds_base + wcode(slot, f), wvo[f], rrec, (uint32_t)ks * 1024u);
-            dma4(lds_base + wsb(slot, f), svo[f], rrec, (uint32_t)(ks * sb_tile_bytes));
+            dma16(lds_base + wcode(slot, f), wvo[f], rrec, (uint32_t)kg * 1024u);
+            dma4(lds_base + wsb(slot, f), svo[f], rrec, (uint32_t)(kg * sb_tile_bytes));
         }
     };
     // This wave's weights of the K step in `slot`, from LDS.
@@ -434,7 +445,7 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
         uint8_t *ep = lds_raw + wave * 32 * EROW;
         constexpr int CPR = 32 * EB / 16;                    // 16-byte chunks per row
         constexpr int PER_LANE = 32 * CPR / 64;
-        constexpr int PASSES = kGateUp ? 1 : 2;
+        constexpr int PASSES = (kGateUp && !kPart) ? 1 : 2;
         #pragma unroll
         for (int b = 0; b < TBR; ++b) {
             #pragma unroll
@@ -443,7 +454,7 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
                 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
                     const int col = 8 * q4 + 4 * bhalf;
-                    if (kGateUp) {
+                    if (kGateUp && !kPart) {
                         uint2 v;
                         v.x = pk_bf16(silu_mul(acc[0][b][4 * q4 + 0], acc[1][b][4 * q4 + 0]),
                                       silu_mul(acc[0][b][4 * q4 + 1], acc[1][b][4 * q4 + 1]));
@@ -474,7 +485,12 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
                     const int col = ch * 16 / EB;
                     const size_t p = (size_t)(p0 + tok);
                     const uint4 v = *reinterpret_cast<const uint4 *>(ep + row * EROW + ch * 16);
-                    if (kGateUp) {
+                    if (kPart) {
+                        // gate/up partials: gate in [0, I), up in [I, 2I) of each row
+                        const size_t nf = kGateUp ? 2 * (size_t)a.inter : (size_t)a.hidden;
+                        const size_t f0 = (kGateUp && f) ? (size_t)a.inter : 0;
+                        *reinterpret_cast<uint4 *>(a.part + ((size_t)split * a.t + p) * nf + f0 + colf + col) = v;
+                    } else if (kGateUp) {
                         *reinterpret_cast<uint4 *>(a.hg + p * a.inter + colf + col) = v;
                     } else if (MODE == DOWN_YE) {
                         *reinterpret_cast<uint4 *>(a.ye + p * a.hidden + colf + col) = v;
@@ -566,6 +582,50 @@ __global__ void __launch_bounds__(256) k_combine(const uint16_t *__restrict__ ye
     }
 }
 
+// Split-K reductions of the shared expert (small chunks): partial sums of
+// the S K ranges added in ascending range order, then the epilogue of the
+// unsplit kernel (SiLU(g)*u to bf16, or gate * d (+ out) in fp32).
+// One thread per 4 consecutive features of one row.
+__global__ void __launch_bounds__(256) k_reduce_gu(const float *__restrict__ part, int S, int t, int I,
+                                                   uint16_t *__restrict__ hs) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= t * (I / 4)) return;
+    const int r = i / (I / 4), c = (i % (I / 4)) * 4;
+    float4 g = make_float4(0.f, 0.f, 0.f, 0.f), u = g;
+    for (int sp = 0; sp < S; ++sp) {
+        const float *row = part + ((size_t)sp * t + r) * 2 * I;
+        const float4 a = *reinterpret_cast<const float4 *>(row + c);
+        const float4 b = *reinterpret_cast<const float4 *>(row + I + c);
+        g.x += a.x; g.y += a.y; g.z += a.z; g.w += a.w;
+        u.x += b.x; u.y += b.y; u.z += b.z; u.w += b.w;
+    }
+    uint2 v;
+    v.x = pk_bf16(silu_mul(g.x, u.x), silu_mul(g.y, u.y));
+    v.y = pk_bf16(silu_mul(g.z, u.z), silu_mul(g.w, u.w));
+    *reinterpret_cast<uint2 *>(hs + (size_t)r * I + c) = v;
+}
+
+__global__ void __launch_bounds__(256) k_reduce_down(const float *__restrict__ part, int S, int t, int h,
+                                                     const float *__restrict__ gate, float *__restrict__ out,
+                                                     int accumulate) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= t * (h / 4)) return;
+    const int r = i / (h / 4), c = (i % (h / 4)) * 4;
+    float4 d = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int sp = 0; sp < S; ++sp) {
+        const float4 a = *reinterpret_cast<const float4 *>(part + ((size_t)sp * t + r) * h + c);
+        d.x += a.x; d.y += a.y; d.z += a.z; d.w += a.w;
+    }
+    const float gr = gate ? gate[r] : 1.0f;
+    float4 *o = reinterpret_cast<float4 *>(out + (size_t)r * h + c);
+    float4 res = make_float4(gr * d.x, gr * d.y, gr * d.z, gr * d.w);
+    if (accumulate) {
+        const float4 old = *o;
+        res.x += old.x; res.y += old.y; res.z += old.z; res.w += old.w;
+    }
+    *o = res;
+}
+
 // g[r] = sigmoid(x_r . gate_w), one wave per row, fp32.
 __global__ void __launch_bounds__(256) k_shared_gate(const uint16_t *__restrict__ x,
                                                      const uint16_t *__restrict__ gw, int t, int h,
@@ -583,15 +643,16 @@ __global__ void __launch_bounds__(256) k_shared_gate(const uint16_t *__restrict_
 
 template <int MODE, int WAVES>
 hipError_t launch_waves(const GemmArgs &a, int bm, hipStream_t s) {
-    const bool gu = (MODE == GU_GATHER || MODE == GU_DENSE);
-    const bool dense = (MODE == GU_DENSE || MODE == DOWN_OUT);
+    const bool gu = (MODE == GU_GATHER || MODE == GU_DENSE || MODE == GU_PART);
+    const bool part = (MODE == GU_PART || MODE == DOWN_PART);
+    const bool dense = (MODE == GU_DENSE || MODE == DOWN_OUT || part);
     const int n_out = gu ? a.inter : a.hidden;
     const int feat = gu ? 32 * WAVES : 64 * WAVES;
     const int nblk = (n_out + feat - 1) / feat;
     int grid;
     if (dense) {
         // 1-D grid, rounded so every XCD slot of the remap exists
-        grid = (((a.t + bm - 1) / bm * nblk + 7) / 8) * 8 + 8;
+        grid = (((a.t + bm - 1) / bm * nblk * (part ? a.ksplit : 1) + 7) / 8) * 8 + 8;
     } else {
         // An XCD's tiles cost at most an eighth of the total plus one tile,
         // and each costs at least kTileCostBase + 1, which bounds their count.
@@ -615,7 +676,7 @@ hipError_t launch_waves(const GemmArgs &a, int bm, hipStream_t s) {
 
 template <int MODE>
 hipError_t launch_mode(const GemmArgs &a, int bm, hipStream_t s) {
-    const bool gu = (MODE == GU_GATHER || MODE == GU_DENSE);
+    const bool gu = (MODE == GU_GATHER || MODE == GU_DENSE || MODE == GU_PART);
     const int n_out = gu ? a.inter : a.hidden;
     // 8 waves (two per SIMD) when the feature dimension fills them, so each
     // staged activation tile serves 256 (gate/up) or 512 (down) features.
@@ -627,12 +688,29 @@ hipError_t launch_mode(const GemmArgs &a, int bm, hipStream_t s) {
 
 hipError_t launch_gateup(const GemmArgs &a, int bm, hipStream_t s) {
     ProfileScope prof(a.order ? MOE_PHASE_GATEUP : MOE_PHASE_SHARED_GU, s);
-    return a.order ? launch_mode<GU_GATHER>(a, bm, s) : launch_mode<GU_DENSE>(a, bm, s);
+    if (a.order) return launch_mode<GU_GATHER>(a, bm, s);
+    return a.ksplit > 1 ? launch_mode<GU_PART>(a, bm, s) : launch_mode<GU_DENSE>(a, bm, s);
 }
 
 hipError_t launch_down(const GemmArgs &a, int bm, hipStream_t s) {
     ProfileScope prof(a.order ? MOE_PHASE_DOWN : MOE_PHASE_SHARED_DOWN, s);
-    return a.order ? launch_mode<DOWN_YE>(a, bm, s) : launch_mode<DOWN_OUT>(a, bm, s);
+    if (a.order) return launch_mode<DOWN_YE>(a, bm, s);
+    return a.ksplit > 1 ? launch_mode<DOWN_PART>(a, bm, s) : launch_mode<DOWN_OUT>(a, bm, s);
+}
+
+hipError_t launch_reduce_gu(const float *part, int S, int t, int I, uint16_t *hs, hipStream_t s) {
+    ProfileScope prof(MOE_PHASE_SHARED_GU, s);
+    const int n = t * (I / 4);
+    hipLaunchKernelGGL(k_reduce_gu, dim3((n + 255) / 256), dim3(256), 0, s, part, S, t, I, hs);
+    return hipGetLastError();
+}
+
+hipError_t launch_reduce_down(const float *part, int S, int t, int h, const float *gate, float *out,
+                              int accumulate, hipStream_t s) {
+    ProfileScope prof(MOE_PHASE_SHARED_DOWN, s);
+    const int n = t * (h / 4);
+    hipLaunchKernelGGL(k_reduce_down, dim3((n + 255) / 256), dim3(256), 0, s, part, S, t, h, gate, out, accumulate);
+    return hipGetLastError();
 }
 
 hipError_t launch_shared_gate(const uint16_t *x, const uint16_t *gate_w, int t, int h, float *g,

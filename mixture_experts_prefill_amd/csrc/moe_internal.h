@@ -22,6 +22,7 @@ struct Workspace {
     size_t hg;         // bf16 [t*k][I]: SiLU(gate)*up of every CSR entry
     size_t ye;         // bf16 [t*k][h]: down projection of every CSR entry
     size_t hs;         // bf16 [t][I_s]: shared expert's SiLU(gate)*up
+    size_t part;       // f32 split-K partial sums of the shared expert (small t only)
     size_t gate;       // f32 [t]: shared-expert gate factors
     size_t total;
 };
@@ -87,10 +88,18 @@ struct GemmArgs {
     float *out;              // down shared: fp32 [t][hidden]
     const float *gate;       // shared gate factors or nullptr
     int accumulate;
+    int ksplit;              // dense calls: K ranges run by separate workgroups (1 = none)
+    float *part;             // split partial sums [ksplit][t][2 I or h]
 };
 
 hipError_t launch_gateup(const GemmArgs &a, int bm, hipStream_t s);
 hipError_t launch_down(const GemmArgs &a, int bm, hipStream_t s);
+hipError_t launch_reduce_gu(const float *part, int S, int t, int I, uint16_t *hs, hipStream_t s);
+hipError_t launch_reduce_down(const float *part, int S, int t, int h, const float *gate, float *out,
+                              int accumulate, hipStream_t s);
+// K splits of the shared expert's dense GEMMs: for small chunks, so that
+// enough workgroups stream the weights; a divisor of the K step count.
+int shared_ksplit(int t, int ksteps, int nblk);
 hipError_t launch_shared_gate(const uint16_t *x, const uint16_t *gate_w, int t, int h, float *g,
                               hipStream_t s);
 hipError_t launch_combine(const uint16_t *ye, const uint32_t *pos, const float *csr_w, int t,

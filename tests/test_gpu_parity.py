@@ -254,6 +254,27 @@ def test_accumulate_semantics(mep, orc):
     check_out(experts_only.cpu().numpy(), r0["out"])
 
 
+@pytest.mark.parametrize("name,t", [("decode", 8), ("decode", 1), ("mid", 64), ("mid", 200)])
+def test_shared_expert_gate(mep, orc, name, t):
+    """The shared expert alone with its sigmoid gate, on chunks that split K
+    over workgroups (t <= 64, partial sums reduced in a fixed order) and on a
+    chunk that does not; accumulate=1 adds onto what out holds."""
+    wl = ms.make_workload(name, centred=True, with_gate=True, t=t)
+    c = wl.cfg
+    blk = mep.MoeBlock.from_workload(wl)
+    blk.workspace.fill_(0xFF)
+    blk.out.fill_(float("nan"))
+    blk.shared(accumulate=0)
+    torch.cuda.synchronize()
+    got = blk.out.cpu().numpy()
+    ref = orc.shared(wl.shared_record, c.hidden, c.inter_shared, c.group, wl.x, wl.gate_w)
+    check_out(got, ref)
+    blk.out.fill_(1.0)
+    blk.shared(accumulate=1)
+    torch.cuda.synchronize()
+    check_out(blk.out.cpu().numpy(), ref + 1.0)
+
+
 def test_bad_arguments_leave_outputs_untouched(mep):
     wl = ms.make_workload("tiny")
     blk = mep.MoeBlock.from_workload(wl)

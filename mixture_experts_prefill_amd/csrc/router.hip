@@ -250,6 +250,32 @@ __device__ __forceinline__ uint32_t order_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Maximum of a 64-bit key over the wave, with DPP moves only (no LDS
+// crossbar): row_shr 1, 2, 4, 8 leave each 16-lane row's maximum in its lane
+// 15, row_bcast 15 and 31 carry it up, so lane 63 holds the wave's maximum,
+// read back as a scalar.  Lanes whose DPP source is missing see 0, the
+// smallest key.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void dpp_max_step(uint32_t &hi, uint32_t &lo) {
+    const uint32_t h2 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hi, CTRL, ROW_MASK, 0xf, false);
+    const uint32_t l2 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)lo, CTRL, ROW_MASK, 0xf, false);
+    const bool gt = (h2 > hi) || (h2 == hi && l2 > lo);
+    hi = gt ? h2 : hi;
+    lo = gt ? l2 : lo;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
+    uint32_t hi = (uint32_t)(k >> 32), lo = (uint32_t)k;
+    dpp_max_step<0x111, 0xf>(hi, lo);  // row_shr:1
+    dpp_max_step<0x112, 0xf>(hi, lo);  // row_shr:2
+    dpp_max_step<0x114, 0xf>(hi, lo);  // row_shr:4
+    dpp_max_step<0x118, 0xf>(hi, lo);  // row_shr:8
+    dpp_max_step<0x142, 0xa>(hi, lo);  // row_bcast:15 into rows 1, 3
+    dpp_max_step<0x143, 0xc>(hi, lo);  // row_bcast:31 into rows 2, 3
+    const uint32_t H = (uint32_t)__builtin_amdgcn_readlane((int)hi, 63);
+    const uint32_t L = (uint32_t)__builtin_amdgcn_readlane((int)lo, 63);
+    return ((uint64_t)H << 32) | L;
+}
+
 // One wave per row: k rounds of a 64-lane arg-max over (value desc, id asc).
 // Round j's winner is kept by lane j, which then writes slot j.  Lane l holds
 // experts l, l + 64, ... (KPL of them, E <= 64 KPL).
@@ -260,10 +286,9 @@ __global__ void __launch_bounds__(256) k_topk(const float *__restrict__ logits, 
     const int r = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     if (r >= t) return;
     const float *l = logits + (size_t)r * E;
-    constexpr int kMaxPerLane = KPL;
-    uint64_t key[kMaxPerLane];
+    uint64_t key[KPL];
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {
+    for (int i = 0; i < KPL; ++i) {
         const int e = lane + 64 * i;
         key[i] = (e < E) ? ((uint64_t)order_key(l[e]) << 32) | (uint32_t)(0xffffffffu - e) : 0;
     }
@@ -271,15 +296,11 @@ __global__ void __launch_bounds__(256) k_topk(const float *__restrict__ logits, 
     for (int j = 0; j < k; ++j) {
         uint64_t best = 0;
 #pragma unroll
-        for (int i = 0; i < kMaxPerLane; ++i) best = key[i] > best ? key[i] : best;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const uint64_t o = __shfl_xor(best, off, 64);
-            best = o > best ? o : best;
-        }
+        for (int i = 0; i < KPL; ++i) best = key[i] > best ? key[i] : best;
+        best = wave_max_u64(best);
         const uint32_t e = 0xffffffffu - (uint32_t)(best & 0xffffffffu);
 #pragma unroll
-        for (int i = 0; i < kMaxPerLane; ++i)
+        for (int i = 0; i < KPL; ++i)
             if ((uint32_t)(lane + 64 * i) == e) key[i] = 0;   // remove the winner
         if (lane == j) my_e = e;
     }

@@ -106,6 +106,22 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t w, const Deq &d, const Masks
     return __builtin_bit_cast(bf16x8, u);
 }
 
+// Few-row path: the 8 codes of one word (code j at bit 4*(j/2) + 16*(j%2))
+// become four bf16 pairs 128 + q (a nibble moved to bits 0-3 / 16-19 and
+// OR'ed into bf16 128.0, exact) dotted with the matching x pairs, so
+// P = sum_j (128 + q_j) x_j and sum_j q_j x_j = P - 128 X.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+__device__ __forceinline__ float dot8(uint32_t w, const uint4 &xp, uint32_t mask, uint32_t mag, float p) {
+    p = dot2bf(and_or(w, mask, mag), xp.x, p);          // codes 0, 1
+    p = dot2bf(and_or(w >> 4, mask, mag), xp.y, p);     // codes 2, 3
+    p = dot2bf(and_or(w >> 8, mask, mag), xp.z, p);     // codes 4, 5
+    p = dot2bf(and_or(w >> 12, mask, mag), xp.w, p);    // codes 6, 7
+    return p;
+}
+
 // SiLU(g) * u with the hardware exp and reciprocal (about 1 ulp each).
 __device__ __forceinline__ float silu_mul(float g, float u) {
     return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
@@ -515,6 +531,118 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
             }
         }
     };
+    // ---- few-row path (routed tiles of 1 or 2 rows): no MFMA; each lane
+    // dots its 32 codes per K step with the rows' x values (read from the
+    // staged activation tile) and applies the group's scale and bias once per
+    // step:  w.x summed over the lane's columns = s P + (b - 128 s) X, with
+    // X the sum of those x.  The weights are never rounded to bf16.  Lanes L
+    // and L+32 hold the two column halves of feature row 32 ob + L%32 and are
+    // added at the end.  Same ring, waits and barriers as the MFMA loop; the
+    // reads of step kb+1 overlap step kb's math.
+    auto gemv = [&](auto nr_c) {
+        constexpr int NR = decltype(nr_c)::value;
+        uint32_t mask, mag, one2;
+        asm volatile("v_mov_b32 %0, 0xf000f" : "=v"(mask));
+        asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(mag));      // bf16 128.0 pair
+        asm volatile("v_mov_b32 %0, 0x3f803f80" : "=v"(one2));     // bf16 1.0 pair
+        const int half = lane >> 5;
+        auto read_x = [&](int slot, uint4 (&xw)[NR][4]) {
+            const uint8_t *buf = lds_raw + (slot % NS) * XSTAGE;
+            #pragma unroll
+            for (int r = 0; r < NR; ++r)
+                #pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    xw[r][c] = *reinterpret_cast<const uint4 *>(buf + r * 128 + (((4 * half + c) ^ xswz(r)) & 7) * 16);
+        };
+        float acc[2][NR];
+        #pragma unroll
+        for (int f = 0; f < 2; ++f)
+            #pragma unroll
+            for (int r = 0; r < NR; ++r) acc[f][r] = 0.0f;
+        #pragma unroll
+        for (int j = 0; j < NS; ++j) issue(min(j, nk - 1), j);
+        wait_vm<(NS - 1) * VM_PER_STEP>();
+        barrier_no_fence();
+        Stage cur;
+        uint4 xc[NR][4];
+        read_w(0, cur);
+        read_x(0, xc);
+        for (int kb = 0; kb < nk; ++kb) {
+            // step kb+1 landed for every wave; step kb's slot is free
+            wait_vm<(NS - 2) * VM_PER_STEP>();
+            barrier_no_fence();
+            issue(min(kb + NS, nk - 1), kb + NS);
+            Stage nxt;
+            uint4 xn[NR][4];
+            read_w(kb + 1, nxt);                          // past the end: a reloaded step, unused
+            read_x(kb + 1, xn);
+            #pragma unroll
+            for (int r = 0; r < NR; ++r) {
+                float X = 0.0f;
+                #pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    X = dot2bf(one2, xc[r][c].x, X);
+                    X = dot2bf(one2, xc[r][c].y, X);
+                    X = dot2bf(one2, xc[r][c].z, X);
+                    X = dot2bf(one2, xc[r][c].w, X);
+                }
+                #pragma unroll
+                for (int f = 0; f < 2; ++f) {
+                    float P = 0.0f;
+                    P = dot8(cur.c[f].x, xc[r][0], mask, mag, P);
+                    P = dot8(cur.c[f].y, xc[r][1], mask, mag, P);
+                    P = dot8(cur.c[f].z, xc[r][2], mask, mag, P);
+                    P = dot8(cur.c[f].w, xc[r][3], mask, mag, P);
+                    const half2_t sb = __builtin_bit_cast(half2_t, cur.sb[f]);
+                    const float cc = __builtin_fmaf(-128.0f, (float)sb.x, (float)sb.y);
+                    acc[f][r] = __builtin_fmaf(cc, X, __builtin_fmaf((float)sb.x, P, acc[f][r]));
+                }
+            }
+            cur = nxt;
+            #pragma unroll
+            for (int r = 0; r < NR; ++r)
+                #pragma unroll
+                for (int c = 0; c < 4; ++c) xc[r][c] = xn[r][c];
+        }
+        wait_vm<0>();  // retire the trailing (unused) loads
+        // both column halves of a feature: lane l and l +- 32
+        #pragma unroll
+        for (int f = 0; f < 2; ++f)
+            #pragma unroll
+            for (int r = 0; r < NR; ++r) {
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[f][r]), __float_as_uint(acc[f][r]),
+                                                                 false, false);
+                acc[f][r] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+            }
+        if (!live0) return;
+        const int feat = lane & 31;
+        #pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            if (r >= n) break;
+            const size_t p = (size_t)(p0 + r);
+            if (kGateUp) {
+                if (half == 0) {
+                    const float v = silu_mul(acc[0][r], acc[1][r]);
+                    a.hg[p * a.inter + ob[0] * 32 + feat] = (uint16_t)(pk_bf16(v, 0.0f) & 0xffffu);
+                }
+            } else {
+                // lanes 0-31 store fragment 0, lanes 32-63 fragment 1
+                const int f = half;
+                if (f == 0 || live1) {
+                    const float v = f ? acc[1][r] : acc[0][r];
+                    a.ye[p * a.hidden + ob[f] * 32 + feat] = (uint16_t)(pk_bf16(v, 0.0f) & 0xffffu);
+                }
+            }
+        }
+    };
+    if constexpr (!kDense) {
+        if (n <= 2) {
+            if (n == 1) gemv(std::integral_constant<int, 1>{});
+            else gemv(std::integral_constant<int, 2>{});
+            return;
+        }
+    }
+
     const int tbr = (n + 31) >> 5;
     if constexpr (TB == 4) {
         if (tbr >= 4) body(std::integral_constant<int, 4>{});

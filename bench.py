@@ -46,8 +46,11 @@ def algorithmic(cfg, t, counts):
     R = ms.layout(h, I, cfg.group).stride
     Rs = ms.layout(h, Is, cfg.group).stride
     touched = int((np.asarray(counts) > 0).sum())
+    gu_weights = 2 * (h * I // 2 + h * I // cfg.group * 4)   # gate + up codes and scale/bias of one record
     return dict(
         flop_gateup=4.0 * t * k * h * I,
+        # gate/up kernel: weights of the touched experts, x rows once, SiLU*up written once
+        bytes_gateup=touched * gu_weights + 2.0 * t * h + 2.0 * t * k * I,
         flop_down=2.0 * t * k * h * I,
         flop_shared=6.0 * t * h * Is,
         flop_router=2.0 * t * h * E,
@@ -216,11 +219,22 @@ def main():
     work = algorithmic(cfg, t, counts)
     dom_ms, dom_n = prof[dominant]
     dom_avg_s = dom_ms / dom_n / 1e3
-    achieved = work["flop_gateup"] / dom_avg_s / 1e12
-    roofline = {"kernel": "k_gemm gate/up (routed, grouped int4 -> bf16 MFMA, SiLU*up epilogue)",
-                "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic_for(f"gateup_{cfg.name}"), "algorithmic": round(work["flop_gateup"]),
-                "avg_launch_us": round(dom_avg_s * 1e6, 2)}
+    # The kernel is MFMA-bound when its arithmetic intensity exceeds the
+    # machine balance (2500 TFLOP/s / 8 TB/s = 312 FLOP/B), else HBM-bound.
+    intensity = work["flop_gateup"] / work["bytes_gateup"]
+    kname = "k_gemm gate/up (routed, grouped int4 -> bf16 MFMA, SiLU*up epilogue)"
+    if intensity >= PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+        achieved = work["flop_gateup"] / dom_avg_s / 1e12
+        roofline = {"kernel": kname, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                    "traffic": traffic_for(f"gateup_{cfg.name}"), "algorithmic": round(work["flop_gateup"]),
+                    "avg_launch_us": round(dom_avg_s * 1e6, 2)}
+    else:
+        achieved = work["bytes_gateup"] / dom_avg_s / 1e9
+        roofline = {"kernel": kname, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                    "traffic": traffic_for(f"gateup_{cfg.name}"), "algorithmic": round(work["bytes_gateup"]),
+                    "avg_launch_us": round(dom_avg_s * 1e6, 2)}
 
     block_flop = work["flop_gateup"] + work["flop_down"] + work["flop_shared"]
     step_s = ms_per_step / 1e3

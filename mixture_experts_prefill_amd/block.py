@@ -118,11 +118,27 @@ class MoeBlock:
         moe_prefill_experts(self.x, self.k, self.E, self.L, self.offsets, self.csr_rows, self.csr_w, self.csr_pos,
                             self.table, self.out, accumulate, self.workspace, self.host_records, self.ring, stream)
 
-    def forward(self, stream=None) -> torch.Tensor:
+    # Rows from which the shared expert runs on a second stream beside the
+    # routing calls.  The fork and join cost about 10 us each of cross-queue
+    # latency on MI355X, while below this the two chains are short
+    # latency-bound kernels (measured: t = 1 and 8 run faster in one stream,
+    # t = 512 and 4096 faster forked).
+    FORK_MIN_ROWS = 64
+
+    def forward(self, stream=None, fork: Optional[bool] = None) -> torch.Tensor:
         """One block.  `stream` (torch stream, raw handle or None for the current
-        stream) carries routing, grouping and the routed experts; the shared
-        expert forks off it and joins back before the routed call."""
-        if self.Ls is not None:
+        stream) carries routing, grouping and the routed experts.  With `fork`
+        (default: t >= FORK_MIN_ROWS) the shared expert forks off it onto a
+        second stream and joins back before the routed call; otherwise it runs
+        first on the same stream."""
+        if fork is None:
+            fork = self.t >= self.FORK_MIN_ROWS
+        if self.Ls is not None and not fork:
+            self.shared(0, stream)
+            self.route(stream)
+            self.build_csr(stream)
+            self.experts(1, stream)
+        elif self.Ls is not None:
             if stream is None:
                 main = torch.cuda.current_stream(self.device)
             elif isinstance(stream, torch.cuda.Stream):

@@ -32,6 +32,8 @@
 #include <algorithm>
 #include <type_traits>
 
+#include <hip/hip_ext.h>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -658,56 +660,63 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
 }
 
 // out[r, :] (+)= sum over the row's k CSR entries, in ascending CSR position
-// (= ascending expert id), of csr_w[p] * ye[p, :].  One workgroup per row;
-// each thread owns 8 columns.  The loads of up to 8 entries are issued
-// before their FMAs so a thread waits for memory once per 8 entries, not
-// once per entry; the FMAs still run in ascending position.
-__global__ void __launch_bounds__(256) k_combine(const uint16_t *__restrict__ ye,
-                                                 const uint32_t *__restrict__ pos,
-                                                 const float *__restrict__ csr_w, int t, int k,
-                                                 int h, float *__restrict__ out, int accumulate) {
-    const int r = blockIdx.x;
-    uint32_t ps[MOE_MAX_K];
-    float ws[MOE_MAX_K];
-    for (int j = 0; j < k; ++j) ps[j] = pos[(size_t)r * k + j];
-    for (int j = 1; j < k; ++j)  // insertion sort, k <= 32
-        for (int i = j; i > 0 && ps[i] < ps[i - 1]; --i) {
-            uint32_t tmp = ps[i];
-            ps[i] = ps[i - 1];
-            ps[i - 1] = tmp;
-        }
-    for (int j = 0; j < k; ++j) ws[j] = csr_w[ps[j]];
-    for (int c = threadIdx.x * 8; c < h; c += blockDim.x * 8) {
-        float acc[8];
-        float4 *o = reinterpret_cast<float4 *>(out + (size_t)r * h + c);
-        if (accumulate) {
-            const float4 o0 = o[0], o1 = o[1];
-            acc[0] = o0.x; acc[1] = o0.y; acc[2] = o0.z; acc[3] = o0.w;
-            acc[4] = o1.x; acc[5] = o1.y; acc[6] = o1.z; acc[7] = o1.w;
-        } else {
-            #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-        }
-        for (int j0 = 0; j0 < k; j0 += 8) {
-            uint4 v[8];
-            #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                if (j0 + j < k) v[j] = *reinterpret_cast<const uint4 *>(ye + (size_t)ps[j0 + j] * h + c);
-            #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                if (j0 + j >= k) break;
-                const float wj = ws[j0 + j];
+// (= ascending expert id), of csr_w[p] * ye[p, :].  One workgroup of CT
+// threads per (row, 8 CT columns); each thread owns 8 columns.  The first
+// wave ranks the row's k positions (distinct, k <= 32) into LDS; then every
+// thread issues the loads of up to 16 entries and their weights before the
+// FMAs, so it waits for memory once per 16 entries; the FMAs still run in
+// ascending position.
+template <int CT>
+__global__ void __launch_bounds__(CT) k_combine(const uint16_t *__restrict__ ye,
+                                                const uint32_t *__restrict__ pos,
+                                                const float *__restrict__ csr_w, int t, int k,
+                                                int h, float *__restrict__ out, int accumulate) {
+    __shared__ uint32_t ps[MOE_MAX_K];
+    const int r = blockIdx.x, tid = threadIdx.x;
+    const int c = (blockIdx.y * CT + tid) * 8;
+    const bool live = c < h;
+    float acc[8];
+    float4 *o = reinterpret_cast<float4 *>(out + (size_t)r * h + (live ? c : 0));
+    if (accumulate && live) {
+        const float4 o0 = o[0], o1 = o[1];
+        acc[0] = o0.x; acc[1] = o0.y; acc[2] = o0.z; acc[3] = o0.w;
+        acc[4] = o1.x; acc[5] = o1.y; acc[6] = o1.z; acc[7] = o1.w;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+    }
+    if (tid < 64) {
+        const uint32_t mine = tid < k ? pos[(size_t)r * k + tid] : 0xffffffffu;
+        int rank = 0;
+        for (int i = 0; i < k; ++i) rank += (uint32_t)__builtin_amdgcn_readlane((int)mine, i) < mine;
+        if (tid < k) ps[rank] = mine;
+    }
+    __syncthreads();
+    if (!live) return;
+    for (int j0 = 0; j0 < k; j0 += 16) {
+        uint4 v[16];
+        float wj[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            if (j0 + j < k) {
+                const uint32_t p = ps[j0 + j];
+                v[j] = *reinterpret_cast<const uint4 *>(ye + (size_t)p * h + c);
+                wj[j] = csr_w[p];
+            }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            if (j0 + j < k) {
                 const uint32_t u[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
-                #pragma unroll
+#pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    acc[2 * i] = __builtin_fmaf(wj, __uint_as_float(u[i] << 16), acc[2 * i]);
-                    acc[2 * i + 1] = __builtin_fmaf(wj, __uint_as_float(u[i] & 0xffff0000u), acc[2 * i + 1]);
+                    acc[2 * i] = __builtin_fmaf(wj[j], __uint_as_float(u[i] << 16), acc[2 * i]);
+                    acc[2 * i + 1] = __builtin_fmaf(wj[j], __uint_as_float(u[i] & 0xffff0000u), acc[2 * i + 1]);
                 }
             }
         }
-        o[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-        o[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
     }
+    o[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    o[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
 }
 
 // Split-K reductions of the shared expert (small chunks): partial sums of
@@ -720,12 +729,22 @@ __global__ void __launch_bounds__(256) k_reduce_gu(const float *__restrict__ par
     if (i >= t * (I / 4)) return;
     const int r = i / (I / 4), c = (i % (I / 4)) * 4;
     float4 g = make_float4(0.f, 0.f, 0.f, 0.f), u = g;
-    for (int sp = 0; sp < S; ++sp) {
-        const float *row = part + ((size_t)sp * t + r) * 2 * I;
-        const float4 a = *reinterpret_cast<const float4 *>(row + c);
-        const float4 b = *reinterpret_cast<const float4 *>(row + I + c);
-        g.x += a.x; g.y += a.y; g.z += a.z; g.w += a.w;
-        u.x += b.x; u.y += b.y; u.z += b.z; u.w += b.w;
+    // splits in ascending order; the loads of 16 splits go out together
+    for (int s0 = 0; s0 < S; s0 += 16) {
+        float4 a[16], b[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            if (s0 + j < S) {
+                const float *row = part + ((size_t)(s0 + j) * t + r) * 2 * I;
+                a[j] = *reinterpret_cast<const float4 *>(row + c);
+                b[j] = *reinterpret_cast<const float4 *>(row + I + c);
+            }
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            if (s0 + j < S) {
+                g.x += a[j].x; g.y += a[j].y; g.z += a[j].z; g.w += a[j].w;
+                u.x += b[j].x; u.y += b[j].y; u.z += b[j].z; u.w += b[j].w;
+            }
     }
     uint2 v;
     v.x = pk_bf16(silu_mul(g.x, u.x), silu_mul(g.y, u.y));
@@ -740,9 +759,16 @@ __global__ void __launch_bounds__(256) k_reduce_down(const float *__restrict__ p
     if (i >= t * (h / 4)) return;
     const int r = i / (h / 4), c = (i % (h / 4)) * 4;
     float4 d = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int sp = 0; sp < S; ++sp) {
-        const float4 a = *reinterpret_cast<const float4 *>(part + ((size_t)sp * t + r) * h + c);
-        d.x += a.x; d.y += a.y; d.z += a.z; d.w += a.w;
+    for (int s0 = 0; s0 < S; s0 += 16) {
+        float4 a[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            if (s0 + j < S) a[j] = *reinterpret_cast<const float4 *>(part + ((size_t)(s0 + j) * t + r) * h + c);
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            if (s0 + j < S) {
+                d.x += a[j].x; d.y += a[j].y; d.z += a[j].z; d.w += a[j].w;
+            }
     }
     const float gr = gate ? gate[r] : 1.0f;
     float4 *o = reinterpret_cast<float4 *>(out + (size_t)r * h + c);
@@ -770,7 +796,7 @@ __global__ void __launch_bounds__(256) k_shared_gate(const uint16_t *__restrict_
 }
 
 template <int MODE, int WAVES>
-hipError_t launch_waves(const GemmArgs &a, int bm, hipStream_t s) {
+hipError_t launch_waves(const GemmArgs &a, int bm, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     const bool gu = (MODE == GU_GATHER || MODE == GU_DENSE || MODE == GU_PART);
     const bool part = (MODE == GU_PART || MODE == DOWN_PART);
     const bool dense = (MODE == GU_DENSE || MODE == DOWN_OUT || part);
@@ -791,39 +817,41 @@ hipError_t launch_waves(const GemmArgs &a, int bm, hipStream_t s) {
     switch (bm) {
     case 32:
         if constexpr (WAVES == 4)
-            hipLaunchKernelGGL((k_gemm<MODE, 32, 4>), dim3(grid), dim3(256), 0, s, a);
+            hipExtLaunchKernelGGL((k_gemm<MODE, 32, 4>), dim3(grid), dim3(256), 0, s, e0, e1, 0, a);
         else
             return hipErrorInvalidValue;  // a 32-row tile has 4 row blocks: 4 waves only
         break;
-    case 64: hipLaunchKernelGGL((k_gemm<MODE, 64, WAVES>), dim3(grid), dim3(64 * WAVES), 0, s, a); break;
-    case 128: hipLaunchKernelGGL((k_gemm<MODE, 128, WAVES>), dim3(grid), dim3(64 * WAVES), 0, s, a); break;
+    case 64: hipExtLaunchKernelGGL((k_gemm<MODE, 64, WAVES>), dim3(grid), dim3(64 * WAVES), 0, s, e0, e1, 0, a); break;
+    case 128: hipExtLaunchKernelGGL((k_gemm<MODE, 128, WAVES>), dim3(grid), dim3(64 * WAVES), 0, s, e0, e1, 0, a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
 template <int MODE>
-hipError_t launch_mode(const GemmArgs &a, int bm, hipStream_t s) {
+hipError_t launch_mode(const GemmArgs &a, int bm, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     const bool gu = (MODE == GU_GATHER || MODE == GU_DENSE || MODE == GU_PART);
     const int n_out = gu ? a.inter : a.hidden;
     // 8 waves (two per SIMD) when the feature dimension fills them, so each
     // staged activation tile serves 256 (gate/up) or 512 (down) features.
     const bool wide = (gu ? n_out >= 256 : n_out >= 512) && bm >= 64;
-    return wide ? launch_waves<MODE, 8>(a, bm, s) : launch_waves<MODE, 4>(a, bm, s);
+    return wide ? launch_waves<MODE, 8>(a, bm, s, e0, e1) : launch_waves<MODE, 4>(a, bm, s, e0, e1);
 }
 
 }  // namespace
 
 hipError_t launch_gateup(const GemmArgs &a, int bm, hipStream_t s) {
-    ProfileScope prof(a.order ? MOE_PHASE_GATEUP : MOE_PHASE_SHARED_GU, s);
-    if (a.order) return launch_mode<GU_GATHER>(a, bm, s);
-    return a.ksplit > 1 ? launch_mode<GU_PART>(a, bm, s) : launch_mode<GU_DENSE>(a, bm, s);
+    ProfileScope prof(a.order ? MOE_PHASE_GATEUP : MOE_PHASE_SHARED_GU, s, true);
+    const hipEvent_t e0 = prof.start(), e1 = prof.stop();
+    if (a.order) return launch_mode<GU_GATHER>(a, bm, s, e0, e1);
+    return a.ksplit > 1 ? launch_mode<GU_PART>(a, bm, s, e0, e1) : launch_mode<GU_DENSE>(a, bm, s, e0, e1);
 }
 
 hipError_t launch_down(const GemmArgs &a, int bm, hipStream_t s) {
-    ProfileScope prof(a.order ? MOE_PHASE_DOWN : MOE_PHASE_SHARED_DOWN, s);
-    if (a.order) return launch_mode<DOWN_YE>(a, bm, s);
-    return a.ksplit > 1 ? launch_mode<DOWN_PART>(a, bm, s) : launch_mode<DOWN_OUT>(a, bm, s);
+    ProfileScope prof(a.order ? MOE_PHASE_DOWN : MOE_PHASE_SHARED_DOWN, s, true);
+    const hipEvent_t e0 = prof.start(), e1 = prof.stop();
+    if (a.order) return launch_mode<DOWN_YE>(a, bm, s, e0, e1);
+    return a.ksplit > 1 ? launch_mode<DOWN_PART>(a, bm, s, e0, e1) : launch_mode<DOWN_OUT>(a, bm, s, e0, e1);
 }
 
 hipError_t launch_reduce_gu(const float *part, int S, int t, int I, uint16_t *hs, hipStream_t s) {
@@ -850,7 +878,15 @@ hipError_t launch_shared_gate(const uint16_t *x, const uint16_t *gate_w, int t, 
 hipError_t launch_combine(const uint16_t *ye, const uint32_t *pos, const float *csr_w, int t,
                           int k, int h, float *out, int accumulate, hipStream_t s) {
     ProfileScope prof(MOE_PHASE_COMBINE, s);
-    hipLaunchKernelGGL(k_combine, dim3(t), dim3(256), 0, s, ye, pos, csr_w, t, k, h, out, accumulate);
+    // few rows: 64-thread workgroups over 512 columns spread one row over
+    // h / 512 workgroups; many rows: 256 threads cover 2048 columns.
+    if (t < 256) {
+        hipLaunchKernelGGL(k_combine<64>, dim3(t, (h + 511) / 512), dim3(64), 0, s, ye, pos, csr_w, t, k, h,
+                           out, accumulate);
+    } else {
+        hipLaunchKernelGGL(k_combine<256>, dim3(t, (h + 2047) / 2048), dim3(256), 0, s, ye, pos, csr_w, t, k, h,
+                           out, accumulate);
+    }
     return hipGetLastError();
 }
 

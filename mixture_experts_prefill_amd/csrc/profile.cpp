@@ -28,16 +28,23 @@ hipEvent_t take() {
 }
 }  // namespace
 
-ProfileScope::ProfileScope(int phase, hipStream_t s) : phase_(phase), s_(s) {
+ProfileScope::ProfileScope(int phase, hipStream_t s, bool attached)
+    : phase_(phase), s_(s), attached_(attached) {
     if (!(g_mask & (1u << phase))) return;
     a_ = take();
     b_ = take();
-    if (a_ && b_) hipEventRecord(a_, s_);
+    if (!a_ || !b_) {
+        if (a_) g_pool.push_back(a_);
+        if (b_) g_pool.push_back(b_);
+        a_ = b_ = nullptr;
+        return;
+    }
+    if (!attached_) hipEventRecord(a_, s_);
 }
 
 ProfileScope::~ProfileScope() {
     if (!a_ || !b_) return;
-    hipEventRecord(b_, s_);
+    if (!attached_) hipEventRecord(b_, s_);
     g_marks.push_back(Mark{phase_, a_, b_});
 }
 

@@ -22,6 +22,41 @@ namespace {
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 
+// Transposed butterfly over the 64 partials of N outputs (N a power of two,
+// at most 64).  While a lane holds n > 1 outputs it keeps the half selected
+// by its lane bit and receives the partner's copy of that half; once n == 1
+// it plain-reduces.  Selects are done on bit patterns (mask blend) so the
+// compiler keeps p[] in registers instead of selecting an address into a
+// stack copy.  The output index is formed by the lane bits used for
+// splitting (MSB first): with N = 2^a, lanes whose low 6 - a bits are zero
+// hold output lane >> (6 - a).
+constexpr int tree_shift(int n) {
+    return n == 64 ? 0 : n == 32 ? 1 : n == 16 ? 2 : n == 8 ? 3 : n == 4 ? 4 : n == 2 ? 5 : 6;
+}
+template <int N>
+__device__ __forceinline__ float tree64(float (&p)[N], int lane) {
+    static_assert(N >= 1 && N <= 64 && (N & (N - 1)) == 0, "a power of two <= 64");
+#pragma unroll
+    for (int lvl = 0; lvl < 6; ++lvl) {
+        const int off = 32 >> lvl;
+        const int cnt = N >> lvl;  // outputs held before this level (compile-time)
+        if (cnt > 1) {
+            const int half = cnt >> 1;
+            const uint32_t m = (lane & off) ? 0xffffffffu : 0u;
+#pragma unroll
+            for (int o = 0; o < half; ++o) {
+                const uint32_t lo = __float_as_uint(p[o]), hi = __float_as_uint(p[o + half]);
+                const float keep = __uint_as_float((lo & ~m) | (hi & m));
+                const float give = __uint_as_float((hi & ~m) | (lo & m));
+                p[o] = keep + __shfl_xor(give, off, 64);
+            }
+        } else {
+            p[0] = p[0] + __shfl_xor(p[0], off, 64);
+        }
+    }
+    return p[0];
+}
+
 // One wave computes an RT x ET tile of logits (RT * ET outputs, a power of two <= 64).
 template <int RT, int ET>
 __global__ void __launch_bounds__(256) k_router(const uint16_t *__restrict__ x,
@@ -78,38 +113,73 @@ __global__ void __launch_bounds__(256) k_router(const uint16_t *__restrict__ x,
         }
     }
 
-    // Transposed butterfly over the 64 partials.  While a lane holds n > 1
-    // outputs it keeps the half selected by its lane bit and receives the
-    // partner's copy of that half; once n == 1 it plain-reduces.
-    // Selects are done on bit patterns (mask blend) so the compiler keeps p[]
-    // in registers instead of selecting an address into a stack copy.
-#pragma unroll
-    for (int lvl = 0; lvl < 6; ++lvl) {
-        const int off = 32 >> lvl;
-        const int cnt = N >> lvl;  // outputs held before this level (compile-time)
-        if (cnt > 1) {
-            const int half = cnt >> 1;
-            const uint32_t m = (lane & off) ? 0xffffffffu : 0u;
-#pragma unroll
-            for (int o = 0; o < half; ++o) {
-                const uint32_t lo = __float_as_uint(p[o]), hi = __float_as_uint(p[o + half]);
-                const float keep = __uint_as_float((lo & ~m) | (hi & m));
-                const float give = __uint_as_float((hi & ~m) | (lo & m));
-                p[o] = keep + __shfl_xor(give, off, 64);
-            }
-        } else {
-            p[0] = p[0] + __shfl_xor(p[0], off, 64);
-        }
-    }
-    // Output index o is formed by the lane bits used for splitting (MSB first);
-    // with N = 2^a splits at off = 32 .. 2^(6-a), o = lane >> (6 - a).
-    constexpr int shift = (N == 64) ? 0 : (N == 32) ? 1 : (N == 16) ? 2 : (N == 8) ? 3
-                        : (N == 4) ? 4 : (N == 2) ? 5 : 6;
+    const float v = tree64(p, lane);
+    constexpr int shift = tree_shift(N);
     if ((lane & ((1 << shift) - 1)) == 0) {
         const int o = lane >> shift;
         const int i = o / ET, j = o % ET;
         const int r = r0 + i, e = e0 + j;
-        if (r < t && e < E) logits[(size_t)r * E + e] = p[0];
+        if (r < t && e < E) logits[(size_t)r * E + e] = v;
+    }
+}
+
+// Few-row router (t <= 8, h <= 4096): a workgroup of 4 waves owns every row
+// of the chunk and 4 experts, one per wave.  Each wave loads its expert's
+// whole W row into registers (h/64 floats per lane) while the workgroup
+// stages the rows' x in LDS (at most 64 KB), so the kernel waits on memory
+// about twice instead of once per 256-element step.  Lane l still owns
+// partial l of every logit and runs the same fma chains and tree.
+constexpr int kFewRows = 8, kFewSteps = 16;
+template <int RT>
+__global__ void __launch_bounds__(256) k_router_few(const uint16_t *__restrict__ x,
+                                                    const float *__restrict__ w, int t, int h, int E,
+                                                    float *__restrict__ logits) {
+    __shared__ __attribute__((aligned(16))) uint16_t xs[RT * kFewSteps * 256];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int e = blockIdx.x * 4 + (tid >> 6);
+    const int steps = h >> 8;
+    const float4 *wr = reinterpret_cast<const float4 *>(w + (size_t)min(e, E - 1) * h) + lane;
+    // Loads are unconditional, at clamped (in-bounds) addresses, so that they
+    // all go out before the first wait; clamped copies are never used.
+    float4 wv[kFewSteps];
+#pragma unroll
+    for (int s = 0; s < kFewSteps; ++s) wv[s] = wr[min(s, steps - 1) * 64];
+    // rows 0 .. t-1 are contiguous: t * h / 8 chunks of 16 bytes
+    constexpr int kCh = RT * kFewSteps * 256 / 8 / 256;
+    const int nch = t * (h >> 3);
+    const uint4 *xg = reinterpret_cast<const uint4 *>(x);
+    uint4 xv[kCh];
+#pragma unroll
+    for (int j = 0; j < kCh; ++j) xv[j] = xg[min(tid + 256 * j, nch - 1)];
+    // (a clamped chunk is stored again where its own thread stores it, with
+    // the same bytes; the stores have no branch, so the loads are not sunk
+    // into one wait each)
+#pragma unroll
+    for (int j = 0; j < kCh; ++j) reinterpret_cast<uint4 *>(xs)[min(tid + 256 * j, nch - 1)] = xv[j];
+    __syncthreads();
+
+    float p[RT];
+#pragma unroll
+    for (int i = 0; i < RT; ++i) p[i] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < kFewSteps; ++s) {
+        if (s < steps) {
+#pragma unroll
+            for (int i = 0; i < RT; ++i) {
+                const int r = i < t ? i : t - 1;  // rows past t repeat the last row, never stored
+                const uint2 v = *reinterpret_cast<const uint2 *>(xs + r * h + s * 256 + 4 * lane);
+                p[i] = __builtin_fmaf(bf16_lo(v.x), wv[s].x, p[i]);
+                p[i] = __builtin_fmaf(bf16_hi(v.x), wv[s].y, p[i]);
+                p[i] = __builtin_fmaf(bf16_lo(v.y), wv[s].z, p[i]);
+                p[i] = __builtin_fmaf(bf16_hi(v.y), wv[s].w, p[i]);
+            }
+        }
+    }
+    const float v = tree64(p, lane);
+    constexpr int shift = tree_shift(RT);
+    if ((lane & ((1 << shift) - 1)) == 0) {
+        const int r = lane >> shift;
+        if (r < t && e < E) logits[(size_t)r * E + e] = v;
     }
 }
 
@@ -250,35 +320,38 @@ __device__ __forceinline__ uint32_t order_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Maximum of a 64-bit key over the wave, with DPP moves only (no LDS
+// Value of an order_key (the inverse map, with -0 read back as +0).
+__device__ __forceinline__ float key_value(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// Maximum of a 32-bit key over the wave, with DPP moves only (no LDS
 // crossbar): row_shr 1, 2, 4, 8 leave each 16-lane row's maximum in its lane
 // 15, row_bcast 15 and 31 carry it up, so lane 63 holds the wave's maximum,
 // read back as a scalar.  Lanes whose DPP source is missing see 0, the
 // smallest key.
 template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ void dpp_max_step(uint32_t &hi, uint32_t &lo) {
-    const uint32_t h2 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hi, CTRL, ROW_MASK, 0xf, false);
-    const uint32_t l2 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)lo, CTRL, ROW_MASK, 0xf, false);
-    const bool gt = (h2 > hi) || (h2 == hi && l2 > lo);
-    hi = gt ? h2 : hi;
-    lo = gt ? l2 : lo;
+__device__ __forceinline__ uint32_t dpp_max_step(uint32_t v) {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xf, false);
+    return o > v ? o : v;
 }
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
-    uint32_t hi = (uint32_t)(k >> 32), lo = (uint32_t)k;
-    dpp_max_step<0x111, 0xf>(hi, lo);  // row_shr:1
-    dpp_max_step<0x112, 0xf>(hi, lo);  // row_shr:2
-    dpp_max_step<0x114, 0xf>(hi, lo);  // row_shr:4
-    dpp_max_step<0x118, 0xf>(hi, lo);  // row_shr:8
-    dpp_max_step<0x142, 0xa>(hi, lo);  // row_bcast:15 into rows 1, 3
-    dpp_max_step<0x143, 0xc>(hi, lo);  // row_bcast:31 into rows 2, 3
-    const uint32_t H = (uint32_t)__builtin_amdgcn_readlane((int)hi, 63);
-    const uint32_t L = (uint32_t)__builtin_amdgcn_readlane((int)lo, 63);
-    return ((uint64_t)H << 32) | L;
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = dpp_max_step<0x111, 0xf>(v);  // row_shr:1
+    v = dpp_max_step<0x112, 0xf>(v);  // row_shr:2
+    v = dpp_max_step<0x114, 0xf>(v);  // row_shr:4
+    v = dpp_max_step<0x118, 0xf>(v);  // row_shr:8
+    v = dpp_max_step<0x142, 0xa>(v);  // row_bcast:15 into rows 1, 3
+    v = dpp_max_step<0x143, 0xc>(v);  // row_bcast:31 into rows 2, 3
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 // One wave per row: k rounds of a 64-lane arg-max over (value desc, id asc).
-// Round j's winner is kept by lane j, which then writes slot j.  Lane l holds
-// experts l, l + 64, ... (KPL of them, E <= 64 KPL).
+// Lane l holds the keys of experts l, l + 64, ... (KPL of them, E <= 64 KPL).
+// A round takes the wave maximum of the keys, then the lowest expert id that
+// holds it from one ballot per key slot (slot i before i + 1, then the lowest
+// lane), and clears that key.  Round j's winner is kept by lane j, which then
+// writes slot j; the winning key gives the logit back, so the softmax needs
+// no second read of the row.
 template <int KPL>
 __global__ void __launch_bounds__(256) k_topk(const float *__restrict__ logits, int t, int E, int k,
                                               uint32_t *__restrict__ idx, float *__restrict__ wts) {
@@ -286,29 +359,37 @@ __global__ void __launch_bounds__(256) k_topk(const float *__restrict__ logits, 
     const int r = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     if (r >= t) return;
     const float *l = logits + (size_t)r * E;
-    uint64_t key[KPL];
+    uint32_t key[KPL];
 #pragma unroll
     for (int i = 0; i < KPL; ++i) {
         const int e = lane + 64 * i;
-        key[i] = (e < E) ? ((uint64_t)order_key(l[e]) << 32) | (uint32_t)(0xffffffffu - e) : 0;
+        key[i] = (e < E) ? order_key(l[e]) : 0u;
     }
-    uint32_t my_e = 0;
+    uint32_t my_e = 0, my_key = 0, top = 0;
     for (int j = 0; j < k; ++j) {
-        uint64_t best = 0;
+        uint32_t best = key[0];
 #pragma unroll
-        for (int i = 0; i < KPL; ++i) best = key[i] > best ? key[i] : best;
-        best = wave_max_u64(best);
-        const uint32_t e = 0xffffffffu - (uint32_t)(best & 0xffffffffu);
+        for (int i = 1; i < KPL; ++i) best = key[i] > best ? key[i] : best;
+        best = wave_max_u32(best);
+        int e = 0;
+#pragma unroll
+        for (int i = KPL - 1; i >= 0; --i) {
+            const uint64_t m = __ballot(key[i] == best);
+            if (m) e = 64 * i + __builtin_ctzll(m);
+        }
 #pragma unroll
         for (int i = 0; i < KPL; ++i)
-            if ((uint32_t)(lane + 64 * i) == e) key[i] = 0;   // remove the winner
-        if (lane == j) my_e = e;
+            if (lane + 64 * i == e) key[i] = 0u;   // remove the winner
+        if (j == 0) top = best;
+        if (lane == j) {
+            my_e = (uint32_t)e;
+            my_key = best;
+        }
     }
     // softmax over the selected logits (renormalised top-k), fp32
     const bool mine = lane < k;
-    const float my_l = mine ? l[my_e] : 0.0f;
-    const float lmax = __shfl(my_l, 0, 64);
-    const float ex = mine ? expf(my_l - lmax) : 0.0f;
+    const float lmax = key_value(top);
+    const float ex = mine ? expf(key_value(my_key) - lmax) : 0.0f;
     float sum = ex;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
@@ -332,11 +413,20 @@ hipError_t launch_tile(const uint16_t *x, const float *w, int t, int h, int E, f
 hipError_t launch_router_logits(const uint16_t *x, const float *w, int t, int h, int E,
                                 float *logits, hipStream_t s) {
     ProfileScope prof(MOE_PHASE_ROUTER, s);
-    // Small t: one row block and one expert per wave keeps >= E waves busy
+    // t <= 8: rows staged once per workgroup, W rows held in registers;
+    // small t: one row block and one expert per wave keeps >= E waves busy
     // streaming W; large t: LDS-shared 32 x 32 tiles.
     if (t >= 128 && E >= 32) {
         const int blocks = ((t + kLR - 1) / kLR) * ((E + kLE - 1) / kLE);
         hipLaunchKernelGGL(k_router_lds, dim3(blocks), dim3(512), 0, s, x, w, t, h, E, logits);
+        return hipGetLastError();
+    }
+    if (t <= kFewRows && h <= kFewSteps * 256) {
+        const dim3 grid((E + 3) / 4), block(256);
+        if (t == 1) hipLaunchKernelGGL(k_router_few<1>, grid, block, 0, s, x, w, t, h, E, logits);
+        else if (t == 2) hipLaunchKernelGGL(k_router_few<2>, grid, block, 0, s, x, w, t, h, E, logits);
+        else if (t <= 4) hipLaunchKernelGGL(k_router_few<4>, grid, block, 0, s, x, w, t, h, E, logits);
+        else hipLaunchKernelGGL(k_router_few<8>, grid, block, 0, s, x, w, t, h, E, logits);
         return hipGetLastError();
     }
     if (t >= 64 && E >= 8) return launch_tile<8, 8>(x, w, t, h, E, logits, s);

@@ -223,7 +223,8 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
     constexpr int EB = (MODE == DOWN_OUT || kPart) ? 4 : 2;
     constexpr int EROW = 32 * EB + 16;
     constexpr int RING = NS * STAGE, EPI = WAVES * 32 * EROW;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[RING > EPI ? RING : EPI];
+    constexpr int LDS_BYTES = RING > EPI ? RING : EPI;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[LDS_BYTES];
     // LDS byte address of the ring (wave-uniform, for the DMA's M0).
     const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds_raw));
 
@@ -318,17 +319,21 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
     // so the only waits are the explicit vmcnt counts below.
     auto wcode = [&](int slot, int f) { return WRING + (slot % NS) * WSTAGE + (wave * 2 + f) * 1024; };
     auto wsb = [&](int slot, int f) { return WRING + (slot % NS) * WSTAGE + WAVES * 2048 + (wave * 2 + f) * 256; };
-    auto issue = [&](int ks, int slot) {
-        const uint32_t xd = lds_base + (slot % NS) * XSTAGE + wave * XPW * 1024;
+    // The wave's weights of K step ks (code tiles and scale/bias), 4 loads.
+    auto issue_w = [&](int ks, int slot) {
         const int kg = kbase + ks;
-        const uint32_t xs = (uint32_t)kg * 128u;
-        #pragma unroll
-        for (int j = 0; j < XPW; ++j) dma16(xd + j * 1024, xvo[j], rx, xs);
         #pragma unroll
         for (int f = 0; f < 2; ++f) {
             dma16(lds_base + wcode(slot, f), wvo[f], rrec, (uint32_t)kg * 1024u);
             dma4(lds_base + wsb(slot, f), svo[f], rrec, (uint32_t)(kg * sb_tile_bytes));
         }
+    };
+    auto issue = [&](int ks, int slot) {
+        const uint32_t xd = lds_base + (slot % NS) * XSTAGE + wave * XPW * 1024;
+        const uint32_t xs = (uint32_t)(kbase + ks) * 128u;
+        #pragma unroll
+        for (int j = 0; j < XPW; ++j) dma16(xd + j * 1024, xvo[j], rx, xs);
+        issue_w(ks, slot);
     };
     // This wave's weights of the K step in `slot`, from LDS.
     auto read_w = [&](int slot, Stage &st) {
@@ -534,27 +539,72 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
         }
     };
     // ---- few-row path (routed tiles of 1 or 2 rows): no MFMA; each lane
-    // dots its 32 codes per K step with the rows' x values (read from the
-    // staged activation tile) and applies the group's scale and bias once per
-    // step:  w.x summed over the lane's columns = s P + (b - 128 s) X, with
-    // X the sum of those x.  The weights are never rounded to bf16.  Lanes L
-    // and L+32 hold the two column halves of feature row 32 ob + L%32 and are
-    // added at the end.  Same ring, waits and barriers as the MFMA loop; the
-    // reads of step kb+1 overlap step kb's math.
+    // dots its 32 codes per K step with the rows' x values and applies the
+    // group's scale and bias once per step:  w.x summed over the lane's
+    // columns = s P + (b - 128 s) X, with X the sum of those x.  The weights
+    // are never rounded to bf16.  Lanes L and L+32 hold the two column halves
+    // of feature row 32 ob + L%32 and are added at the end.
+    // The NR rows are staged whole, once, at the start of the row ring (the
+    // caller checks that they fit); after that every wave streams only its
+    // own weight slots, so the K loop has no barrier: a wave waits for its
+    // own loads and for its own LDS reads of a slot before refilling it.
     auto gemv = [&](auto nr_c) {
         constexpr int NR = decltype(nr_c)::value;
+        constexpr int VMW = 4;                            // weight loads per K step
+        // weight ring: the LDS after the staged rows (as many stages as the
+        // MFMA path's ring; six stages measured no faster)
+        constexpr int WR0 = NS * XSTAGE;
+        constexpr int NSG = (LDS_BYTES - WR0) / WSTAGE < 8 ? (LDS_BYTES - WR0) / WSTAGE : 8;
+        static_assert(NSG >= 3, "a weight ring of at least three stages");
+        auto gcode = [&](int slot, int f) { return WR0 + (slot % NSG) * WSTAGE + (wave * 2 + f) * 1024; };
+        auto gsb = [&](int slot, int f) { return WR0 + (slot % NSG) * WSTAGE + WAVES * 2048 + (wave * 2 + f) * 256; };
+        auto issue_g = [&](int ks, int slot) {
+            #pragma unroll
+            for (int f = 0; f < 2; ++f) {
+                dma16(lds_base + gcode(slot, f), wvo[f], rrec, (uint32_t)ks * 1024u);
+                dma4(lds_base + gsb(slot, f), svo[f], rrec, (uint32_t)(ks * sb_tile_bytes));
+            }
+        };
+        auto read_g = [&](int slot, Stage &st) {
+            #pragma unroll
+            for (int f = 0; f < 2; ++f) {
+                st.c[f] = *reinterpret_cast<const uint4 *>(lds_raw + gcode(slot, f) + lane * 16);
+                st.sb[f] = *reinterpret_cast<const uint32_t *>(lds_raw + gsb(slot, f) + lane * 4);
+            }
+        };
         uint32_t mask, mag, one2;
         asm volatile("v_mov_b32 %0, 0xf000f" : "=v"(mask));
         asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(mag));      // bf16 128.0 pair
         asm volatile("v_mov_b32 %0, 0x3f803f80" : "=v"(one2));     // bf16 1.0 pair
         const int half = lane >> 5;
-        auto read_x = [&](int slot, uint4 (&xw)[NR][4]) {
-            const uint8_t *buf = lds_raw + (slot % NS) * XSTAGE;
+        const int rowb = K * 2;                           // bytes of one staged row
+        {
+            // rows r < NR at LDS byte r * rowb; 1 KB DMA chunks, lane i of
+            // chunk j carries bytes 1024 j + 16 i (rows are 128-byte multiples,
+            // so a 16-byte piece never straddles two rows; pieces past the end
+            // reload the first piece and land inside the row ring).
+            uint32_t rowbase[NR];
+            #pragma unroll
+            for (int r = 0; r < NR; ++r) {
+                const int q = p0 + min(r, n - 1);
+                const uint32_t row = (MODE == GU_GATHER) ? __builtin_nontemporal_load(a.rows + q) : (uint32_t)q;
+                rowbase[r] = __builtin_amdgcn_readfirstlane(row) * (uint32_t)rowb;
+            }
+            const int total = NR * rowb;
+            const int chunks = (total + 1023) >> 10;
+            for (int j = wave; j < chunks; j += WAVES) {
+                const int bt = j * 1024 + lane * 16;
+                const int r = (NR == 2 && bt >= rowb) ? 1 : 0;
+                const uint32_t voff = bt < total ? rowbase[r] + (uint32_t)(bt - r * rowb) : rowbase[0];
+                dma16(lds_base + j * 1024, voff, rx, 0);
+            }
+        }
+        auto read_x = [&](int kb, uint4 (&xw)[NR][4]) {
             #pragma unroll
             for (int r = 0; r < NR; ++r)
                 #pragma unroll
                 for (int c = 0; c < 4; ++c)
-                    xw[r][c] = *reinterpret_cast<const uint4 *>(buf + r * 128 + (((4 * half + c) ^ xswz(r)) & 7) * 16);
+                    xw[r][c] = *reinterpret_cast<const uint4 *>(lds_raw + r * rowb + kb * 128 + half * 64 + c * 16);
         };
         float acc[2][NR];
         #pragma unroll
@@ -562,22 +612,24 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
             #pragma unroll
             for (int r = 0; r < NR; ++r) acc[f][r] = 0.0f;
         #pragma unroll
-        for (int j = 0; j < NS; ++j) issue(min(j, nk - 1), j);
-        wait_vm<(NS - 1) * VM_PER_STEP>();
+        for (int j = 0; j < NSG; ++j) issue_g(min(j, nk - 1), j);
+        // the rows (issued first) and step 0 of this wave have landed; the
+        // barrier makes every wave's rows visible
+        wait_vm<(NSG - 1) * VMW>();
         barrier_no_fence();
         Stage cur;
         uint4 xc[NR][4];
-        read_w(0, cur);
+        read_g(0, cur);
         read_x(0, xc);
         for (int kb = 0; kb < nk; ++kb) {
-            // step kb+1 landed for every wave; step kb's slot is free
-            wait_vm<(NS - 2) * VM_PER_STEP>();
-            barrier_no_fence();
-            issue(min(kb + NS, nk - 1), kb + NS);
+            // step kb+1 of this wave has landed; its reads of slot kb are done
+            wait_vm<(NSG - 2) * VMW>();
+            __builtin_amdgcn_s_waitcnt((15 << 0) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+            issue_g(min(kb + NSG, nk - 1), kb + NSG);
             Stage nxt;
             uint4 xn[NR][4];
-            read_w(kb + 1, nxt);                          // past the end: a reloaded step, unused
-            read_x(kb + 1, xn);
+            read_g(kb + 1, nxt);                          // past the end: a reloaded step, unused
+            read_x(min(kb + 1, nk - 1), xn);
             #pragma unroll
             for (int r = 0; r < NR; ++r) {
                 float X = 0.0f;
@@ -606,7 +658,7 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
                 #pragma unroll
                 for (int c = 0; c < 4; ++c) xc[r][c] = xn[r][c];
         }
-        wait_vm<0>();  // retire the trailing (unused) loads
+        wait_vm<0>();  // retire the trailing (unused) loads before the workgroup's LDS goes away
         // both column halves of a feature: lane l and l +- 32
         #pragma unroll
         for (int f = 0; f < 2; ++f)
@@ -638,7 +690,8 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
         }
     };
     if constexpr (!kDense) {
-        if (n <= 2) {
+        // few rows whose whole K fits in the row ring: the no-MFMA path
+        if (n <= 2 && ((n * K * 2 + 1023) >> 10) * 1024 <= NS * XSTAGE) {
             if (n == 1) gemv(std::integral_constant<int, 1>{});
             else gemv(std::integral_constant<int, 2>{});
             return;

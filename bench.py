@@ -219,22 +219,25 @@ def main():
     work = algorithmic(cfg, t, counts)
     dom_ms, dom_n = prof[dominant]
     dom_avg_s = dom_ms / dom_n / 1e3
+    # Launches per step: one, except with streamed experts, where the ring
+    # runs the GEMMs once per batch; each launch then does its share.
+    per_launch = args.steps / dom_n
     # The kernel is MFMA-bound when its arithmetic intensity exceeds the
     # machine balance (2500 TFLOP/s / 8 TB/s = 312 FLOP/B), else HBM-bound.
     intensity = work["flop_gateup"] / work["bytes_gateup"]
     kname = "k_gemm gate/up (routed, grouped int4 -> bf16 MFMA, SiLU*up epilogue)"
     if intensity >= PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
-        achieved = work["flop_gateup"] / dom_avg_s / 1e12
+        achieved = work["flop_gateup"] * per_launch / dom_avg_s / 1e12
         roofline = {"kernel": kname, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                    "traffic": traffic_for(f"gateup_{cfg.name}"), "algorithmic": round(work["flop_gateup"]),
-                    "avg_launch_us": round(dom_avg_s * 1e6, 2)}
+                    "traffic": traffic_for(f"gateup_{cfg.name}"), "algorithmic": round(work["flop_gateup"] * per_launch),
+                    "avg_launch_us": round(dom_avg_s * 1e6, 2), "launches_per_step": round(1 / per_launch, 2)}
     else:
-        achieved = work["bytes_gateup"] / dom_avg_s / 1e9
+        achieved = work["bytes_gateup"] * per_launch / dom_avg_s / 1e9
         roofline = {"kernel": kname, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                    "traffic": traffic_for(f"gateup_{cfg.name}"), "algorithmic": round(work["bytes_gateup"]),
-                    "avg_launch_us": round(dom_avg_s * 1e6, 2)}
+                    "traffic": traffic_for(f"gateup_{cfg.name}"), "algorithmic": round(work["bytes_gateup"] * per_launch),
+                    "avg_launch_us": round(dom_avg_s * 1e6, 2), "launches_per_step": round(1 / per_launch, 2)}
 
     block_flop = work["flop_gateup"] + work["flop_down"] + work["flop_shared"]
     step_s = ms_per_step / 1e3
@@ -242,6 +245,30 @@ def main():
              "block_hbm_frac": round(work["bytes_total"] / step_s / 1e9 / PEAK_HBM_GBS, 4),
              "touched_experts": work["touched"], "max_rows_per_expert": int(counts.max()),
              "weight_copies": len(tables)}
+    if blk.ring is not None:
+        # streamed experts: the host link is the bound; the ring counters are
+        # those of the last call (one step)
+        rs = blk.ring.stats()
+        extra["ring"] = {"streamed_experts": rs["streamed"], "batches": rs["batches"],
+                         "fetched_bytes_per_step": rs["fetched_bytes"],
+                         "h2d_GBps": round(rs["fetched_bytes"] / step_s / 1e9, 2),
+                         "host_wait_ms": round(rs["wait_ms"], 3)}
+        # the link itself: pinned host -> device copies of 512 MiB
+        hsrc = torch.empty(1 << 29, dtype=torch.uint8).pin_memory()
+        ddst = torch.empty(1 << 29, dtype=torch.uint8, device="cuda")
+        ddst.copy_(hsrc, non_blocking=True)
+        torch.cuda.synchronize()
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        c0.record()
+        for _ in range(3):
+            ddst.copy_(hsrc, non_blocking=True)
+        c1.record()
+        torch.cuda.synchronize()
+        probe = 3 * (1 << 29) / (c0.elapsed_time(c1) / 1e3) / 1e9
+        extra["ring"]["h2d_probe_GBps"] = round(probe, 2)
+        extra["ring"]["h2d_frac_of_probe"] = round(extra["ring"]["h2d_GBps"] / probe, 4)
+        del hsrc, ddst
 
     if args.phases:
         mep.moe_profile_begin(mep.PHASES)

@@ -54,9 +54,9 @@ static SharedPlan shared_plan(int t, const moe_layout *Ls) {
     SharedPlan sp;
     sp.bm = t >= 512 ? 128 : t >= 64 ? 64 : 32;
     const int mt = (t + sp.bm - 1) / sp.bm;
-    const bool wide_gu = Ls->inter >= 256 && sp.bm >= 64, wide_dn = Ls->hidden >= 512 && sp.bm >= 64;
-    const int nblk_gu = (Ls->inter + (wide_gu ? 255 : 127)) / (wide_gu ? 256 : 128);
-    const int nblk_dn = (Ls->hidden + (wide_dn ? 511 : 255)) / (wide_dn ? 512 : 256);
+    // feature blocks of the 4-wave GEMM workgroups: 128 (gate/up), 256 (down)
+    const int nblk_gu = (Ls->inter + 127) / 128;
+    const int nblk_dn = (Ls->hidden + 255) / 256;
     (void)mt;
     sp.s_gu = shared_ksplit(t, Ls->hidden / 64, nblk_gu);
     sp.s_dn = shared_ksplit(t, Ls->inter / 64, nblk_dn);
@@ -105,7 +105,7 @@ bool workspace_plan(int t, int k, int E, const moe_layout *routed, const moe_lay
 // Largest M-tile height.  Tiles only run their non-empty 32-row blocks, so a
 // taller tile costs no padding; it halves the dequantisation per MFMA each
 // time it doubles, but there must stay enough workgroups (about 1.5 per CU)
-// for the longest-first schedule to balance.  With about one token block per
+// for the cost-ordered schedule to balance.  With about one token block per
 // expert (small chunks) 32-row tiles with 4 waves cover fewer features each
 // and so spread the weight stream over more workgroups.
 int pick_bm(int t, int k, int E, int inter, int hidden) {
@@ -114,7 +114,7 @@ int pick_bm(int t, int k, int E, int inter, int hidden) {
     const long mean = P / (used > 0 ? used : 1);
     if (mean < 48) return 32;
     (void)hidden;
-    const long nblk = (inter + 255) / 256;  // gate/up workgroups cover 256 features
+    const long nblk = (inter + 127) / 128;  // gate/up workgroups cover 128 features
     for (int bm = kMaxBM; bm >= 64; bm /= 2)
         if ((P / bm + used) * nblk >= 384) return bm;
     return 64;

@@ -207,10 +207,10 @@ __global__ void __launch_bounds__(1024) k_csr_small(const uint32_t *__restrict__
 //   2. each XCD gets a contiguous share of those tiles of about one eighth of
 //      the total cost (kTileCostBase + token blocks per tile), so an expert's
 //      tiles share one L2;
-//   3. within its share, an XCD lists each expert's tiles together (they
-//      reuse its weights from L2), experts with more tiles first and in
-//      expert order among equals: the long runs start first and the short
-//      ones fill the end;
+//   3. within its share, an XCD lists its tiles by token blocks, descending,
+//      in expert order within a count, so an expert's full tiles run back to
+//      back (they reuse its weights from L2) and the cheapest tiles fill the
+//      end of the launch;
 //   4. every listed tile is written as a TileEntry (rows, expert, record
 //      address) to order[x * xcap + j].
 // sched_n[kSchedXcnt + x] is the number of tiles of XCD x, sched_n[0] the total.
@@ -276,26 +276,21 @@ __global__ void __launch_bounds__(1024) k_schedule(const uint32_t *__restrict__ 
         for (int x = lo; x <= (int)xof[i]; ++x) xstart[x] = i;
     }
     __syncthreads();
-    // 3. wave x lists XCD x's expert runs (an expert's tiles inside the
-    // share, cut at the share's ends) by length, descending, stable
+    // 3. wave x lists XCD x's tiles by token blocks, descending, and in
+    // expert order within a count (a stable partition): an expert's full
+    // tiles still run back to back, and the last workgroups an XCD starts
+    // are its cheapest, so the launch ends with short tiles instead of long
+    // ones (the tail was up to one full tile long).
     if (wave < 8) {
         const uint32_t s0 = xstart[wave], s1 = xstart[wave + 1];
-        uint32_t maxlen = 0;
-        for (uint32_t i = s0 + lane; i < s1; i += 64)
-            if (i == s0 || tin[i] == 0) maxlen = max(maxlen, min((uint32_t)(tne[i] - tin[i]), s1 - i));
-        for (int off = 32; off >= 1; off >>= 1) maxlen = max(maxlen, (uint32_t)__shfl_xor((int)maxlen, off, 64));
         uint32_t o = 0;
-        for (uint32_t len = maxlen; len >= 1; --len)
+        for (int c = 8; c >= 1; --c)
             for (uint32_t base = s0; base < s1; base += 64) {
                 const uint32_t i = base + lane;
-                const bool start = i < s1 && (i == s0 || tin[i] == 0);
-                const bool hit = start && min((uint32_t)(tne[i] - tin[i]), s1 - i) == len;
-                // position of this run: len times the hits on lower lanes
+                const bool hit = i < s1 && tbl[i] == c;
                 const unsigned long long m = __ballot(hit);
-                const uint32_t at = o + len * (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
-                if (hit)
-                    for (uint32_t j = 0; j < len; ++j) perm[s0 + at + j] = (uint16_t)(i + j);
-                o += len * (uint32_t)__popcll(m);
+                if (hit) perm[s0 + o + (uint32_t)__popcll(m & ((1ull << lane) - 1ull))] = (uint16_t)i;
+                o += (uint32_t)__popcll(m);
             }
         if (lane == 0) sched_n[kSchedXcnt + wave] = s1 - s0;
     }

@@ -236,7 +236,7 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
     // ---- which (M-tile, feature block).  Workgroups are dispatched to the 8
     // XCDs round-robin (XCD = blockIdx % 8) and in order within an XCD.
     // Routed: XCD x runs the tiles of its list (its share of the experts,
-    // longest tiles first), each with all its feature blocks in a row.
+    // costliest tiles first), each with all its feature blocks in a row.
     // Dense: each XCD runs a contiguous eighth of the (M-tile, feature block)
     // pairs.  Either way an XCD's CUs share the weights and rows in its L2.
     const int n_out = kGateUp ? a.inter : a.hidden;

@@ -60,7 +60,7 @@ def algorithmic(cfg, t, counts):
 
 
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
-DOMINANT_KERNEL = "k_gemm<0, 128, 8>"   # routed gate/up, 128-row tiles, 8 waves
+DOMINANT_KERNEL = "k_gemm<0, 128, 4>"   # routed gate/up, 128-row tiles, 4 waves
 COPY_PROBE_BYTES = 512 << 20
 
 

@@ -105,6 +105,11 @@ SWEEP = [
     (8, 16, 1024, 320, 30, 6, 32, True, True),    # inter not a multiple of 128
     (9, 161, 256, 64, 37, 4, 64, True, False),    # LDS router tile with ragged rows and experts
     (10, 130, 768, 128, 96, 6, 32, False, False), # LDS router, 3 steps of 256
+    (11, 3, 8192, 128, 64, 4, 64, False, False),  # t <= 8 with h > 4096: tiled router; wide few-row rows
+    (12, 5, 256, 64, 130, 7, 32, True, True),     # few-row router with t < 8 and E % 4 != 0
+    (13, 2, 512, 192, 9, 2, 32, False, False),    # few-row router, 2 rows
+    (14, 8, 1024, 256, 300, 10, 64, True, False), # decode-like: ~1 row per expert, E % 64 != 0
+    (15, 200, 512, 128, 16, 6, 64, True, True),   # 64-row tiles, forked shared expert, 64-thread combine
 ]
 
 
@@ -116,6 +121,21 @@ def test_small_sweep(mep, orc, case):
     r = orc.block(wl)
     check_routing(g, r)
     check_out(g["out"], r["out"])
+
+
+def test_fork_matches_one_stream(mep):
+    """The shared expert on a second stream (fork) or first on the same
+    stream gives the same bits: the order of additions into out is the same."""
+    wl = ms.small_case(16, 100, 512, 128, 24, 4, 64, centred=True, with_gate=True)
+    outs = []
+    for fork in (True, False):
+        blk = mep.MoeBlock.from_workload(wl)
+        blk.workspace.fill_(0xFF)
+        blk.forward(fork=fork)
+        torch.cuda.synchronize()
+        outs.append(blk.out.cpu().numpy())
+        del blk
+    assert np.array_equal(outs[0], outs[1])
 
 
 def test_max_rows_small_dims(mep, orc):

@@ -22,8 +22,11 @@ hipEvent_t take() {
         g_pool.pop_back();
         return e;
     }
+    // Timing only: no system-scope fence when the event completes (the host
+    // synchronises the stream before it reads the times), which would
+    // otherwise hold back the next kernel on the stream.
     hipEvent_t e = nullptr;
-    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
     return e;
 }
 }  // namespace

@@ -110,6 +110,8 @@ SWEEP = [
     (13, 2, 512, 192, 9, 2, 32, False, False),    # few-row router, 2 rows
     (14, 8, 1024, 256, 300, 10, 64, True, False), # decode-like: ~1 row per expert, E % 64 != 0
     (15, 200, 512, 128, 16, 6, 64, True, True),   # 64-row tiles, forked shared expert, 64-thread combine
+    (17, 64, 256, 64, 1024, 32, 32, True, False), # the expert and top-k caps: E = 1024, k = 32
+    (18, 4096, 256, 64, 64, 32, 64, False, True), # the row cap with k = 32: 131072 CSR entries
 ]
 
 

@@ -36,8 +36,10 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic(cfg, t, counts):
-    """FLOPs and bytes the method itself must do (no padding, no intermediates)."""
+def algorithmic(cfg, t, counts, fused=False):
+    """FLOPs and bytes the method itself must do (no padding, no intermediates).
+    With `fused` the shared expert's gate/up and down run inside the routed
+    launches, so their work is counted there (and flop_shared is 0)."""
     import numpy as np
 
     h, I, Is, E, k = cfg.hidden, cfg.inter, cfg.inter_shared, cfg.experts, cfg.k
@@ -47,12 +49,15 @@ def algorithmic(cfg, t, counts):
     Rs = ms.layout(h, Is, cfg.group).stride
     touched = int((np.asarray(counts) > 0).sum())
     gu_weights = 2 * (h * I // 2 + h * I // cfg.group * 4)   # gate + up codes and scale/bias of one record
+    gu_weights_s = 2 * (h * Is // 2 + h * Is // cfg.group * 4)
+    sh = 1.0 if fused else 0.0
     return dict(
-        flop_gateup=4.0 * t * k * h * I,
-        # gate/up kernel: weights of the touched experts, x rows once, SiLU*up written once
-        bytes_gateup=touched * gu_weights + 2.0 * t * h + 2.0 * t * k * I,
-        flop_down=2.0 * t * k * h * I,
-        flop_shared=6.0 * t * h * Is,
+        flop_gateup=4.0 * t * k * h * I + sh * 4.0 * t * h * Is,
+        # gate/up kernel: weights of the touched experts (and the shared
+        # expert's when fused), x rows once, SiLU*up written once
+        bytes_gateup=touched * gu_weights + sh * gu_weights_s + 2.0 * t * h + 2.0 * t * k * I + sh * 2.0 * t * Is,
+        flop_down=2.0 * t * k * h * I + sh * 2.0 * t * h * Is,
+        flop_shared=(1.0 - sh) * 6.0 * t * h * Is,
         flop_router=2.0 * t * h * E,
         bytes_total=touched * R + Rs + 4.0 * E * h + 2.0 * t * h + 4.0 * t * h,
         touched=touched,
@@ -143,13 +148,15 @@ def main():
     ap.add_argument("--copies", type=int, default=2, help="weight copies rotated per step (defeats the MALL)")
     ap.add_argument("--cpu-rows", type=int, default=4096, help="rows of the oracle CPU-baseline sample (0: skip)")
     ap.add_argument("--phases", action="store_true", help="also time every phase in an extra pass")
+    ap.add_argument("--separate", action="store_true",
+                    help="run the shared expert as its own call (moe_shared) instead of inside the routed launches")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, copy 512 MiB device-to-device (calibrates HBM byte counters)")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter_collection.csv files into profiles/traffic.json")
     args = ap.parse_args()
     if args.ingest_pmc:
-        ingest_pmc(*args.ingest_pmc, key=f"gateup_{args.config}")
+        ingest_pmc(*args.ingest_pmc, key=f"gateup_{args.config}" + ("_separate" if args.separate else ""))
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the block is built and measured "
@@ -188,9 +195,11 @@ def main():
         tab[nz] = tab[nz] - blk.pool.data_ptr() + pool.data_ptr()
         tables.append(tab)
 
+    fused = blk.can_fuse and not args.separate
+
     def step(i):
         blk.table = tables[i % len(tables)]
-        blk.forward()
+        blk.forward(fused=fused)
 
     log(f"[bench] warmup {args.warmup}")
     for i in range(args.warmup):
@@ -216,7 +225,7 @@ def main():
     value = t * args.steps / (gpu_ms / 1e3)
     log(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f} ms/step)")
 
-    work = algorithmic(cfg, t, counts)
+    work = algorithmic(cfg, t, counts, fused)
     dom_ms, dom_n = prof[dominant]
     dom_avg_s = dom_ms / dom_n / 1e3
     # Launches per step: one, except with streamed experts, where the ring
@@ -225,18 +234,20 @@ def main():
     # The kernel is MFMA-bound when its arithmetic intensity exceeds the
     # machine balance (2500 TFLOP/s / 8 TB/s = 312 FLOP/B), else HBM-bound.
     intensity = work["flop_gateup"] / work["bytes_gateup"]
-    kname = "k_gemm gate/up (routed, grouped int4 -> bf16 MFMA, SiLU*up epilogue)"
+    kname = ("k_gemm gate/up (routed experts and the shared expert in one grouped launch, int4 -> bf16 MFMA, "
+             "SiLU*up epilogue)" if fused else "k_gemm gate/up (routed, grouped int4 -> bf16 MFMA, SiLU*up epilogue)")
+    tkey = f"gateup_{cfg.name}" + ("" if fused else "_separate")
     if intensity >= PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
         achieved = work["flop_gateup"] * per_launch / dom_avg_s / 1e12
         roofline = {"kernel": kname, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                    "traffic": traffic_for(f"gateup_{cfg.name}"), "algorithmic": round(work["flop_gateup"] * per_launch),
+                    "traffic": traffic_for(tkey), "algorithmic": round(work["flop_gateup"] * per_launch),
                     "avg_launch_us": round(dom_avg_s * 1e6, 2), "launches_per_step": round(1 / per_launch, 2)}
     else:
         achieved = work["bytes_gateup"] * per_launch / dom_avg_s / 1e9
         roofline = {"kernel": kname, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                    "traffic": traffic_for(f"gateup_{cfg.name}"), "algorithmic": round(work["bytes_gateup"] * per_launch),
+                    "traffic": traffic_for(tkey), "algorithmic": round(work["bytes_gateup"] * per_launch),
                     "avg_launch_us": round(dom_avg_s * 1e6, 2), "launches_per_step": round(1 / per_launch, 2)}
 
     block_flop = work["flop_gateup"] + work["flop_down"] + work["flop_shared"]
@@ -244,7 +255,8 @@ def main():
     extra = {"block_mfma_frac": round(block_flop / step_s / 1e12 / PEAK_BF16_TFLOPS, 4),
              "block_hbm_frac": round(work["bytes_total"] / step_s / 1e9 / PEAK_HBM_GBS, 4),
              "touched_experts": work["touched"], "max_rows_per_expert": int(counts.max()),
-             "weight_copies": len(tables)}
+             "weight_copies": len(tables),
+             "shared_expert": "in the routed launches (moe_prefill_fused)" if fused else "own call (moe_shared)"}
     if blk.ring is not None:
         # streamed experts: the host link is the bound; the ring counters are
         # those of the last call (one step)

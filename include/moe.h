@@ -202,7 +202,9 @@ moe_status moe_ring_get_stats(const moe_ring *ring, moe_ring_stats *out);
  *   host_records [host] array of E pinned host pointers (hipHostMalloc or
  *              torch pin_memory) to each streamed expert's record; may be
  *              NULL when every used expert is resident
- *   ring       required when a used expert has records[e] == 0
+ *   ring       required when a used expert has records[e] == 0 (without
+ *              one, such an expert's entries get unspecified values; its
+ *              record is never dereferenced)
  *   out        fp32 [t][h]; accumulate = 0 overwrites, 1 adds
  * Experts with no rows cost nothing and are never read.  The sum over a
  * row's entries is taken in a fixed order, so results are bitwise
@@ -215,6 +217,38 @@ moe_status moe_prefill_experts(const uint16_t *x, int32_t t, int32_t k, int32_t 
                                const void *const *host_records, moe_ring *ring, float *out,
                                int32_t accumulate, void *workspace, size_t workspace_bytes,
                                void *stream);
+
+/*
+ * The shared expert and the routed experts in the same two grouped launches
+ * (experts.rs page, fn pf_experts: the shared expert's qmm/silu_mul over all
+ * rows, shared_add_rows, then the routed experts).  The result is that of
+ * moe_shared(accumulate) followed by moe_prefill_experts(accumulate = 1) with
+ * every expert resident, up to rounding: each row sums, in this order,
+ *
+ *   out[r] (if accumulate) + g_r * shared(x_r) + the routed terms in ascending
+ *   expert id,
+ *
+ * where the shared expert's down output is rounded to bf16 like a routed
+ * one's.  Its t rows are scheduled as one more segment beside the routed
+ * experts' rows, so the shared expert streams its weights in the same
+ * launches instead of four or two of its own.
+ *
+ *   x, t, k, E, L, offsets, csr_rows, csr_w, csr_pos, records
+ *              as for moe_prefill_experts; every used expert resident
+ *              (records[e] != 0 for each expert with rows)
+ *   Ls         [host] shared layout; must equal *L in hidden, inter and group
+ *   shared_record  the shared expert's record (Ls->stride bytes, 16-byte aligned)
+ *   shared_gate_w  bf16 [h] or NULL, as gate_w of moe_shared
+ *   out        fp32 [t][h]; accumulate = 0 overwrites, 1 adds
+ *   workspace  at least moe_workspace_bytes(t, k, E, L, Ls) bytes
+ * Returns MOE_ERR_INVALID for a shared layout other than the routed one, and
+ * MOE_ERR_CAPACITY when t*(k+1)*inter*2 or t*h*2 bytes exceed 2^32.
+ */
+moe_status moe_prefill_fused(const uint16_t *x, int32_t t, int32_t k, int32_t E, const moe_layout *L,
+                             const uint32_t *offsets, const uint32_t *csr_rows, const float *csr_w,
+                             const uint32_t *csr_pos, const uint64_t *records, const moe_layout *Ls,
+                             const void *shared_record, const uint16_t *shared_gate_w, float *out,
+                             int32_t accumulate, void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

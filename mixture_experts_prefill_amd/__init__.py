@@ -50,7 +50,7 @@ class moe_ring_stats(ctypes.Structure):
 _lib = None
 EXPORTS = ["moe_last_error", "moe_layout_make", "moe_workspace_bytes", "moe_route", "moe_build_csr",
            "moe_shared", "moe_ring_create", "moe_ring_destroy", "moe_ring_get_stats", "moe_prefill_experts",
-           "moe_ring_plan_debug", "moe_profile_begin", "moe_profile_end"]
+           "moe_ring_plan_debug", "moe_profile_begin", "moe_profile_end", "moe_prefill_fused"]
 PHASES = ["router", "topk", "csr", "shared_gateup", "shared_down", "schedule", "gateup", "down", "combine"]
 
 
@@ -76,13 +76,14 @@ def lib():
     L.moe_ring_destroy.restype = None
     L.moe_ring_get_stats.argtypes = [P, ctypes.POINTER(moe_ring_stats)]
     L.moe_prefill_experts.argtypes = [P, I, I, I, LP, P, P, P, P, P, P, P, P, I, P, Z, P]
+    L.moe_prefill_fused.argtypes = [P, I, I, I, LP, P, P, P, P, P, LP, P, P, P, I, P, Z, P]
     L.moe_ring_plan_debug.argtypes = [P, P, I, I, I, P, P, P]
     L.moe_profile_begin.argtypes = [ctypes.c_uint32]
     L.moe_profile_begin.restype = None
     L.moe_profile_end.argtypes = [P, P]
     L.moe_profile_end.restype = ctypes.c_int
     for f in ("moe_layout_make", "moe_route", "moe_build_csr", "moe_shared", "moe_ring_create",
-              "moe_ring_get_stats", "moe_prefill_experts"):
+              "moe_ring_get_stats", "moe_prefill_experts", "moe_prefill_fused"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -188,6 +189,18 @@ def moe_prefill_experts(x: torch.Tensor, k: int, E: int, layout: moe_layout, off
                                      ring.handle if ring is not None else None, _ptr(out), accumulate,
                                      _ptr(workspace), workspace.numel() * workspace.element_size(),
                                      _stream(stream)))
+
+
+def moe_prefill_fused(x: torch.Tensor, k: int, E: int, layout: moe_layout, offsets: torch.Tensor,
+                      csr_rows: torch.Tensor, csr_w: torch.Tensor, csr_pos: torch.Tensor, records: torch.Tensor,
+                      shared_layout: moe_layout, shared_record: torch.Tensor, shared_gate_w: Optional[torch.Tensor],
+                      out: torch.Tensor, accumulate: int, workspace: torch.Tensor, stream=None) -> None:
+    t = x.shape[0]
+    _check(lib().moe_prefill_fused(_ptr(x), t, k, E, ctypes.byref(layout), _ptr(offsets), _ptr(csr_rows),
+                                   _ptr(csr_w), _ptr(csr_pos), _ptr(records), ctypes.byref(shared_layout),
+                                   _ptr(shared_record), _ptr(shared_gate_w), _ptr(out), accumulate,
+                                   _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                   _stream(stream)))
 
 
 def moe_ring_plan_debug(offsets, resident, n_slots: int = 64, group: int = 8):

@@ -6,8 +6,14 @@ workspace, output) and runs
     moe_shared(accumulate=0) -> moe_route -> moe_build_csr -> moe_prefill_experts(accumulate=1)
 
 the order of the cherenkov experts.rs page (fn pf_experts: shared expert into
-the zeroed output, then routed experts added in ascending id).  The shared
-expert needs no routing, so forward() runs it on a second stream of the same
+the zeroed output, then routed experts added in ascending id), or, when the
+shared record has the routed layout and every expert is resident,
+
+    moe_route -> moe_build_csr -> moe_prefill_fused(accumulate=0)
+
+which runs the shared expert inside the routed experts' grouped launches and
+adds its term first in the combine.  In the separate form the shared expert
+needs no routing, so forward() can run it on a second stream of the same
 (default) priority while routing and grouping run; the routed call waits for
 it, so every row still receives the shared term first.  Only allocation and
 call sequencing live here; the arithmetic is in libmoe.
@@ -19,8 +25,8 @@ from typing import Optional, Sequence
 import numpy as np
 import torch
 
-from . import (MoeRing, moe_build_csr, moe_layout_make, moe_prefill_experts, moe_route, moe_shared,
-               moe_workspace_bytes)
+from . import (MoeRing, moe_build_csr, moe_layout_make, moe_prefill_experts, moe_prefill_fused, moe_route,
+               moe_shared, moe_workspace_bytes)
 
 
 def bf16_tensor(bits: np.ndarray, device) -> torch.Tensor:
@@ -114,6 +120,17 @@ class MoeBlock:
     def shared(self, accumulate: int = 0, stream=None):
         moe_shared(self.x, self.Ls, self.shared_record, self.gate_w, self.out, accumulate, self.workspace, stream)
 
+    def fused(self, accumulate: int = 0, stream=None):
+        moe_prefill_fused(self.x, self.k, self.E, self.L, self.offsets, self.csr_rows, self.csr_w, self.csr_pos,
+                          self.table, self.Ls, self.shared_record, self.gate_w, self.out, accumulate, self.workspace,
+                          stream)
+
+    @property
+    def can_fuse(self) -> bool:
+        """The shared record has the routed layout and no expert streams through a ring."""
+        return (self.Ls is not None and self.ring is None and self.host_records is None
+                and (self.Ls.hidden, self.Ls.inter, self.Ls.group) == (self.L.hidden, self.L.inter, self.L.group))
+
     def experts(self, accumulate: int = 1, stream=None):
         moe_prefill_experts(self.x, self.k, self.E, self.L, self.offsets, self.csr_rows, self.csr_w, self.csr_pos,
                             self.table, self.out, accumulate, self.workspace, self.host_records, self.ring, stream)
@@ -125,15 +142,25 @@ class MoeBlock:
     # t = 512 and 4096 faster forked).
     FORK_MIN_ROWS = 64
 
-    def forward(self, stream=None, fork: Optional[bool] = None) -> torch.Tensor:
+    def forward(self, stream=None, fork: Optional[bool] = None, fused: Optional[bool] = None) -> torch.Tensor:
         """One block.  `stream` (torch stream, raw handle or None for the current
-        stream) carries routing, grouping and the routed experts.  With `fork`
-        (default: t >= FORK_MIN_ROWS) the shared expert forks off it onto a
-        second stream and joins back before the routed call; otherwise it runs
-        first on the same stream."""
+        stream) carries routing, grouping and the routed experts.  With `fused`
+        (default: whenever can_fuse) the shared expert runs inside the routed
+        launches (moe_prefill_fused).  Otherwise, with `fork` (default:
+        t >= FORK_MIN_ROWS) the shared expert forks off the stream onto a
+        second one and joins back before the routed call, or runs first on the
+        same stream."""
+        if fused is None:
+            fused = self.can_fuse
         if fork is None:
             fork = self.t >= self.FORK_MIN_ROWS
-        if self.Ls is not None and not fork:
+        if fused:
+            if not self.can_fuse:
+                raise ValueError("fused block needs a shared record of the routed layout and resident experts")
+            self.route(stream)
+            self.build_csr(stream)
+            self.fused(0, stream)
+        elif self.Ls is not None and not fork:
             self.shared(0, stream)
             self.route(stream)
             self.build_csr(stream)

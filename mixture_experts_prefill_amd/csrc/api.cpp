@@ -74,6 +74,13 @@ static bool layout_ok(const moe_layout *L) {
     return std::memcmp(&ref, L, sizeof ref) == 0;
 }
 
+// The shared expert can share the routed experts' grouped launches when its
+// record has the routed layout (same hidden, inter and group).
+static bool fusable(const moe_layout *routed, const moe_layout *shared) {
+    return shared && routed && shared->hidden == routed->hidden && shared->inter == routed->inter &&
+           shared->group == routed->group;
+}
+
 bool workspace_plan(int t, int k, int E, const moe_layout *routed, const moe_layout *shared,
                     Workspace *w) {
     if (t < 1 || t > MOE_MAX_ROWS || k < 1 || k > MOE_MAX_K || E < k || E > MOE_MAX_EXPERTS)
@@ -82,7 +89,11 @@ bool workspace_plan(int t, int k, int E, const moe_layout *routed, const moe_lay
     if (shared && shared->hidden != routed->hidden) return false;
     const size_t P = (size_t)t * k;
     const size_t tiles = (size_t)(t + kCsrTileRows - 1) / kCsrTileRows;
-    const size_t max_mt = P / kMinBM + (size_t)E + 1;
+    // A shared expert of the routed shape can run inside the routed launches
+    // (moe_prefill_fused): its t rows follow the t*k CSR positions in hg / ye
+    // and its tiles join the schedule.
+    const size_t Q = P + (fusable(routed, shared) ? (size_t)t : 0);
+    const size_t max_mt = Q / kMinBM + (size_t)E + 2;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         size_t at = off;
@@ -93,8 +104,8 @@ bool workspace_plan(int t, int k, int E, const moe_layout *routed, const moe_lay
     w->sched_n = take(64);
     w->order = take(8 * max_mt * sizeof(TileEntry));
     w->jobs = take((size_t)E * 8);
-    w->hg = take(P * routed->inter * 2);
-    w->ye = take(P * routed->hidden * 2);
+    w->hg = take(Q * routed->inter * 2);
+    w->ye = take(Q * routed->hidden * 2);
     w->part = take(shared ? shared_plan(t, shared).part_bytes : 0);
     w->hs = take(shared ? (size_t)t * shared->inter * 2 : 0);
     w->gate = take((size_t)t * 4);
@@ -332,6 +343,74 @@ moe_status moe_prefill_experts(const uint16_t *x, int32_t t, int32_t k, int32_t 
     e = launch_down(a, bm, s);
     if (e != hipSuccess) return hip_fail(e, "experts down");
     e = launch_combine(a.ye, csr_pos, csr_w, t, k, L->hidden, out, accumulate, s);
+    if (e != hipSuccess) return hip_fail(e, "combine");
+    return MOE_OK;
+}
+
+moe_status moe_prefill_fused(const uint16_t *x, int32_t t, int32_t k, int32_t E, const moe_layout *L,
+                             const uint32_t *offsets, const uint32_t *csr_rows, const float *csr_w,
+                             const uint32_t *csr_pos, const uint64_t *records, const moe_layout *Ls,
+                             const void *shared_record, const uint16_t *shared_gate_w, float *out,
+                             int32_t accumulate, void *workspace, size_t workspace_bytes, void *stream) {
+    if (moe_status st = check_routing(t, k, E)) return st;
+    if (!layout_ok(L) || !layout_ok(Ls)) return fail(MOE_ERR_INVALID, "fused: layout not made by moe_layout_make");
+    if (!fusable(L, Ls))
+        return fail(MOE_ERR_INVALID, "fused: the shared layout (h %d, inter %d, group %d) must equal the routed one "
+                    "(h %d, inter %d, group %d)", Ls->hidden, Ls->inter, Ls->group, L->hidden, L->inter, L->group);
+    if (!x || !offsets || !csr_rows || !csr_w || !csr_pos || !records || !shared_record || !out || !workspace)
+        return fail(MOE_ERR_INVALID, "fused: null pointer");
+    if (!aligned16(x) || !aligned16(out) || !aligned16(shared_record))
+        return fail(MOE_ERR_INVALID, "fused: x, out and the shared record must be 16-byte aligned");
+    const uint64_t Q = (uint64_t)t * (k + 1);
+    if (Q * L->inter * 2 > 0xffffffffull || (uint64_t)t * L->hidden * 2 > 0xffffffffull)
+        return fail(MOE_ERR_CAPACITY, "fused: t*(k+1)*inter or t*hidden too large for 32-bit offsets");
+    Workspace w;
+    workspace_plan(t, k, E, L, Ls, &w);
+    if (workspace_bytes < w.total)
+        return fail(MOE_ERR_WORKSPACE, "fused: workspace %zu bytes < %zu needed", workspace_bytes, w.total);
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    float *g = reinterpret_cast<float *>(ws + w.gate);
+    hipError_t e;
+    if (shared_gate_w) {
+        e = launch_shared_gate(x, shared_gate_w, t, L->hidden, g, s);
+        if (e != hipSuccess) return hip_fail(e, "shared gate");
+    }
+    const int P = t * k;
+    GemmArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.x = x;
+    a.rows = csr_rows;
+    a.records = records;
+    a.sched_n = reinterpret_cast<uint32_t *>(ws + w.sched_n);
+    a.order = reinterpret_cast<TileEntry *>(ws + w.order);
+    a.xcap = (int)(Q / kMinBM + (size_t)E + 2);
+    a.t = t;
+    a.hidden = L->hidden;
+    a.inter = L->inter;
+    a.group = L->group;
+    a.hg = reinterpret_cast<uint16_t *>(ws + w.hg);
+    a.ye = reinterpret_cast<uint16_t *>(ws + w.ye);
+    a.shared_rows = 1;
+    a.shared_p0 = P;
+    const int bm = pick_bm(t, k, E, L->inter, L->hidden);
+    a.max_tiles = (int)(Q / bm + (size_t)E + 2);
+    e = launch_schedule(offsets, 0, E, bm, records, const_cast<uint32_t *>(a.sched_n),
+                        const_cast<TileEntry *>(a.order), a.xcap, s, SharedSeg{shared_record, P, t});
+    if (e != hipSuccess) return hip_fail(e, "schedule");
+    a.w_off = L->gate_w;
+    a.sb_off = L->gate_sb;
+    a.w2_off = L->up_w;
+    a.sb2_off = L->up_sb;
+    e = launch_gateup(a, bm, s);
+    if (e != hipSuccess) return hip_fail(e, "experts gate/up");
+    a.act = a.hg;
+    a.w_off = L->down_w;
+    a.sb_off = L->down_sb;
+    e = launch_down(a, bm, s);
+    if (e != hipSuccess) return hip_fail(e, "experts down");
+    e = launch_combine(a.ye, csr_pos, csr_w, t, k, L->hidden, out, accumulate, s, a.ye + (size_t)P * L->hidden,
+                       shared_gate_w ? g : nullptr);
     if (e != hipSuccess) return hip_fail(e, "combine");
     return MOE_OK;
 }

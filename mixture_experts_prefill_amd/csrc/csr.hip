@@ -217,7 +217,8 @@ __global__ void __launch_bounds__(1024) k_csr_small(const uint32_t *__restrict__
 __global__ void __launch_bounds__(1024) k_schedule(const uint32_t *__restrict__ offsets, int e0,
                                                    int e1, int bm, const uint64_t *__restrict__ records,
                                                    uint32_t *__restrict__ sched_n,
-                                                   TileEntry *__restrict__ order, int xcap) {
+                                                   TileEntry *__restrict__ order, int xcap,
+                                                   SharedSeg sh) {
     __shared__ uint32_t wsum[16];
     __shared__ uint32_t tp0[kSchedMaxTiles];   // first CSR position of each tile
     __shared__ uint16_t tex[kSchedMaxTiles];   // expert of each tile
@@ -227,27 +228,42 @@ __global__ void __launch_bounds__(1024) k_schedule(const uint32_t *__restrict__ 
     __shared__ uint8_t tin[kSchedMaxTiles];    // index of the tile within its expert
     __shared__ uint8_t tne[kSchedMaxTiles];    // tiles of its expert
     __shared__ uint16_t perm[kSchedMaxTiles];  // listing position -> tile
-    __shared__ uint64_t erec[MOE_MAX_EXPERTS]; // record address of each expert
+    __shared__ uint64_t erec[MOE_MAX_EXPERTS + 1]; // record address of each expert (+ shared)
     __shared__ uint32_t xstart[9];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    // 1. tiles in expert order; each thread owns a contiguous run of experts
+    // 1. tiles in expert order; each thread owns a contiguous run of experts.
+    // Local index n_e (after the routed experts) is the shared expert's segment
+    // when the call has one.
     const int n_e = e1 - e0;
-    const int per = (n_e + 1023) / 1024;
-    const int a = e0 + tid * per, b = min(e1, a + per);
+    const int n_all = n_e + (sh.rec ? 1 : 0);
+    const int per = (n_all + 1023) / 1024;
+    const int a = tid * per, b = min(n_all, a + per);
+    auto seg = [&](int le, uint32_t &p0, uint32_t &n) {
+        if (le < n_e) {
+            p0 = offsets[e0 + le];
+            n = offsets[e0 + le + 1] - p0;
+        } else {
+            p0 = (uint32_t)sh.p0;
+            n = (uint32_t)sh.n;
+        }
+    };
     uint32_t cnt = 0;
-    for (int e = a; e < b; ++e) {
-        cnt += (offsets[e + 1] - offsets[e] + bm - 1) / bm;
-        erec[e - e0] = records[e];
+    for (int le = a; le < b; ++le) {
+        uint32_t p0, n;
+        seg(le, p0, n);
+        cnt += (n + bm - 1) / bm;
+        erec[le] = le < n_e ? records[e0 + le] : (uint64_t)(uintptr_t)sh.rec;
     }
     uint32_t T;
     uint32_t w = block_scan_1024(cnt, wsum, &T) - cnt;
-    for (int e = a; e < b; ++e) {
-        const uint32_t p0 = offsets[e], n = offsets[e + 1] - p0;
+    for (int le = a; le < b; ++le) {
+        uint32_t p0, n;
+        seg(le, p0, n);
         const uint32_t ne = (n + bm - 1) / bm;
         for (uint32_t m = 0; m < n; m += bm, ++w) {
             const uint32_t rows = min((uint32_t)bm, n - m);
             tp0[w] = p0 + m;
-            tex[w] = (uint16_t)(e - e0);
+            tex[w] = (uint16_t)le;
             trows[w] = (uint8_t)(rows - 1);
             tin[w] = (uint8_t)(m / bm);
             tne[w] = (uint8_t)ne;
@@ -280,14 +296,17 @@ __global__ void __launch_bounds__(1024) k_schedule(const uint32_t *__restrict__ 
     // expert order within a count (a stable partition): an expert's full
     // tiles still run back to back, and the last workgroups an XCD starts
     // are its cheapest, so the launch ends with short tiles instead of long
-    // ones (the tail was up to one full tile long).
+    // ones (the tail was up to one full tile long).  The shared expert's
+    // tiles come first (class 9): its rows are dense and, in small chunks,
+    // its tiles stream far more weight bytes than a routed tile.
     if (wave < 8) {
         const uint32_t s0 = xstart[wave], s1 = xstart[wave + 1];
         uint32_t o = 0;
-        for (int c = 8; c >= 1; --c)
+        for (int c = 9; c >= 1; --c)
             for (uint32_t base = s0; base < s1; base += 64) {
                 const uint32_t i = base + lane;
-                const bool hit = i < s1 && tbl[i] == c;
+                const int cls = i < s1 ? ((int)tex[i] == n_e ? 9 : (int)tbl[i]) : 0;
+                const bool hit = cls == c;
                 const unsigned long long m = __ballot(hit);
                 if (hit) perm[s0 + o + (uint32_t)__popcll(m & ((1ull << lane) - 1ull))] = (uint16_t)i;
                 o += (uint32_t)__popcll(m);
@@ -331,10 +350,10 @@ hipError_t launch_csr(const uint32_t *idx, const float *wts, int t, int k, int E
 }
 
 hipError_t launch_schedule(const uint32_t *offsets, int e0, int e1, int bm, const uint64_t *records,
-                           uint32_t *sched_n, TileEntry *order, int xcap, hipStream_t s) {
+                           uint32_t *sched_n, TileEntry *order, int xcap, hipStream_t s, SharedSeg sh) {
     ProfileScope prof(MOE_PHASE_SCHEDULE, s);
     hipLaunchKernelGGL(k_schedule, dim3(1), dim3(1024), 0, s, offsets, e0, e1, bm, records, sched_n, order,
-                       xcap);
+                       xcap, sh);
     return hipGetLastError();
 }
 

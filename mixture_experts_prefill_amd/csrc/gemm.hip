@@ -266,6 +266,7 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
         p0 = te.p0;
         n = te.n;
         rec = static_cast<const uint8_t *>(te.rec);
+        if (!rec) return;   // a used expert left without a record: no read of address 0
     }
     (void)expert;
 
@@ -310,7 +311,7 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
         const int rr = r < n ? r : 0;
         uint32_t row;
         if (MODE == GU_GATHER)
-            row = a.rows[p0 + rr];
+            row = (a.shared_rows && p0 >= a.shared_p0) ? (uint32_t)(p0 + rr - a.shared_p0) : a.rows[p0 + rr];
         else
             row = (uint32_t)(p0 + rr);
         xvo[j] = row * (uint32_t)(kGateUp ? a.hidden : a.inter) * 2u + (uint32_t)(((lane & 7) ^ xswz(r)) * 16);
@@ -600,7 +601,9 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
             #pragma unroll
             for (int r = 0; r < NR; ++r) {
                 const int q = p0 + min(r, n - 1);
-                const uint32_t row = (MODE == GU_GATHER) ? __builtin_nontemporal_load(a.rows + q) : (uint32_t)q;
+                const bool sh = a.shared_rows && p0 >= a.shared_p0;   // shared expert: dense rows
+                const uint32_t row = (MODE == GU_GATHER && !sh) ? __builtin_nontemporal_load(a.rows + q)
+                                     : (MODE == GU_GATHER) ? (uint32_t)(q - a.shared_p0) : (uint32_t)q;
                 rowbase[r] = __builtin_amdgcn_readfirstlane(row) * (uint32_t)rowb;
             }
             const int total = NR * rowb;
@@ -736,7 +739,9 @@ template <int CT>
 __global__ void __launch_bounds__(CT) k_combine(const uint16_t *__restrict__ ye,
                                                 const uint32_t *__restrict__ pos,
                                                 const float *__restrict__ csr_w, int t, int k,
-                                                int h, float *__restrict__ out, int accumulate) {
+                                                int h, float *__restrict__ out, int accumulate,
+                                                const uint16_t *__restrict__ ys,
+                                                const float *__restrict__ gate) {
     __shared__ uint32_t ps[MOE_MAX_K];
     const int r = blockIdx.x, tid = threadIdx.x;
     const int c = (blockIdx.y * CT + tid) * 8;
@@ -750,6 +755,18 @@ __global__ void __launch_bounds__(CT) k_combine(const uint16_t *__restrict__ ye,
     } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+    }
+    if (ys && live) {
+        // the shared expert's row first (scaled by its gate), as the separate
+        // shared call would have left it in out
+        const uint4 v = *reinterpret_cast<const uint4 *>(ys + (size_t)r * h + c);
+        const float g = gate ? gate[r] : 1.0f;
+        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[2 * i] = acc[2 * i] + g * __uint_as_float(u[i] << 16);
+            acc[2 * i + 1] = acc[2 * i + 1] + g * __uint_as_float(u[i] & 0xffff0000u);
+        }
     }
     if (tid < 64) {
         const uint32_t mine = tid < k ? pos[(size_t)r * k + tid] : 0xffffffffu;
@@ -951,16 +968,17 @@ hipError_t launch_shared_gate(const uint16_t *x, const uint16_t *gate_w, int t, 
 }
 
 hipError_t launch_combine(const uint16_t *ye, const uint32_t *pos, const float *csr_w, int t,
-                          int k, int h, float *out, int accumulate, hipStream_t s) {
+                          int k, int h, float *out, int accumulate, hipStream_t s, const uint16_t *ys,
+                          const float *gate) {
     ProfileScope prof(MOE_PHASE_COMBINE, s);
     // few rows: 64-thread workgroups over 512 columns spread one row over
     // h / 512 workgroups; many rows: 256 threads cover 2048 columns.
     if (t < 256) {
         hipLaunchKernelGGL(k_combine<64>, dim3(t, (h + 511) / 512), dim3(64), 0, s, ye, pos, csr_w, t, k, h,
-                           out, accumulate);
+                           out, accumulate, ys, gate);
     } else {
         hipLaunchKernelGGL(k_combine<256>, dim3(t, (h + 2047) / 2048), dim3(256), 0, s, ye, pos, csr_w, t, k, h,
-                           out, accumulate);
+                           out, accumulate, ys, gate);
     }
     return hipGetLastError();
 }

@@ -64,8 +64,16 @@ static_assert(sizeof(TileEntry) == 32, "one 32-byte load per tile");
 // up to bm rows (sched, sched_n[0]), split over the 8 XCDs by cost and listed
 // per XCD (order[x * xcap ..], sched_n[kSchedXcnt + x]) with each entry's
 // record address taken from records[expert].
+// Optional extra segment of dense rows (the shared expert) scheduled with the
+// routed experts: n rows at CSR-like positions p0 .. p0+n-1, record rec
+// (rec == nullptr: none).  Its tiles are listed first on their XCD.
+struct SharedSeg {
+    const void *rec;
+    int p0, n;
+};
 hipError_t launch_schedule(const uint32_t *offsets, int e0, int e1, int bm, const uint64_t *records,
-                           uint32_t *sched_n, TileEntry *order, int xcap, hipStream_t s);
+                           uint32_t *sched_n, TileEntry *order, int xcap, hipStream_t s,
+                           SharedSeg sh = SharedSeg{nullptr, 0, 0});
 
 struct GemmArgs {
     // B-operand rows (tokens): x rows gathered through `rows` (routed gate/up),
@@ -90,6 +98,10 @@ struct GemmArgs {
     int accumulate;
     int ksplit;              // dense calls: K ranges run by separate workgroups (1 = none)
     float *part;             // split partial sums [ksplit][t][2 I or h]
+    // Routed gate/up with the shared expert in the same launch: positions
+    // p >= shared_p0 are the shared expert's rows, x row p - shared_p0
+    // (only when shared_rows != 0).
+    int shared_rows, shared_p0;
 };
 
 hipError_t launch_gateup(const GemmArgs &a, int bm, hipStream_t s);
@@ -102,7 +114,10 @@ hipError_t launch_reduce_down(const float *part, int S, int t, int h, const floa
 int shared_ksplit(int t, int ksteps, int nblk);
 hipError_t launch_shared_gate(const uint16_t *x, const uint16_t *gate_w, int t, int h, float *g,
                               hipStream_t s);
+// ys (optional): bf16 [t][h] shared-expert rows added first, scaled by gate[r]
+// when gate is given.
 hipError_t launch_combine(const uint16_t *ye, const uint32_t *pos, const float *csr_w, int t,
-                          int k, int h, float *out, int accumulate, hipStream_t s);
+                          int k, int h, float *out, int accumulate, hipStream_t s,
+                          const uint16_t *ys = nullptr, const float *gate = nullptr);
 
 }  // namespace moe

@@ -70,10 +70,18 @@ def test_workspace_plan(lib):
     t, k, E = 4096, 8, 128
     n = mep.moe_workspace_bytes(t, k, E, L, Ls)
     P = t * k
-    # hg and ye (bf16) dominate: P*I*2 + P*h*2, plus shared scratch t*Is*2
-    assert n >= P * 768 * 2 + P * 2048 * 2 + t * 768 * 2
-    assert n < P * 768 * 2 + P * 2048 * 2 + t * 768 * 2 + 8 * 2**20
+    # hg and ye (bf16) dominate: with a shared expert of the routed layout they
+    # hold t more rows (moe_prefill_fused), plus the shared scratch t*Is*2
+    Q = P + t
+    assert n >= Q * 768 * 2 + Q * 2048 * 2 + t * 768 * 2
+    assert n < Q * 768 * 2 + Q * 2048 * 2 + t * 768 * 2 + 8 * 2**20
     assert n % 256 == 0
+    # no shared expert, or one of another shape: t*k rows only
+    n0 = mep.moe_workspace_bytes(t, k, E, L, None)
+    assert P * 768 * 2 + P * 2048 * 2 <= n0 < P * 768 * 2 + P * 2048 * 2 + 8 * 2**20
+    Ls2 = mep.moe_layout_make(2048, 1536, 64)
+    n2 = mep.moe_workspace_bytes(t, k, E, L, Ls2)
+    assert n2 < P * 768 * 2 + P * 2048 * 2 + t * 1536 * 2 + 8 * 2**20
     assert mep.moe_workspace_bytes(0, k, E, L, Ls) == 0
     assert mep.moe_workspace_bytes(4097, k, E, L, Ls) == 0
     assert mep.moe_workspace_bytes(t, 9, 8, L, Ls) == 0
@@ -181,3 +189,24 @@ def test_ring_schedule_reuse_rule(lib, seed, n_slots, group):
             assert prev_b < b
             assert wait[b] >= prev_b
         last_user[s] = b
+
+
+def test_fused_validation(lib):
+    """moe_prefill_fused refuses a shared layout other than the routed one, null
+    pointers, a short workspace and shapes beyond its 32-bit offsets, all before
+    anything is enqueued."""
+    L = mep.moe_layout_make(256, 128, 32)
+    Ls_other = mep.moe_layout_make(256, 192, 32)
+    need = mep.moe_workspace_bytes(16, 2, 8, L, L)
+    args = lambda Ls, rec, ws: (P(FAKE), 16, 2, 8, ctypes.byref(L), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE),
+                                ctypes.byref(Ls), rec, None, P(FAKE), 0, P(FAKE), ws, None)
+    assert lib.moe_prefill_fused(*args(Ls_other, P(FAKE), need)) == 1
+    assert "must equal" in lib.moe_last_error().decode()
+    assert lib.moe_prefill_fused(*args(L, None, need)) == 1
+    assert lib.moe_prefill_fused(*args(L, P(FAKE + 8), need)) == 1          # misaligned record
+    assert lib.moe_prefill_fused(*args(L, P(FAKE), need - 256)) == 3
+    # the shared rows follow the t*k routed rows: t*(k+1)*I*2 > 4 GiB is refused
+    Lb = mep.moe_layout_make(256, 16384, 64)
+    rc = lib.moe_prefill_fused(P(FAKE), 4096, 31, 64, ctypes.byref(Lb), P(FAKE), P(FAKE), P(FAKE), P(FAKE),
+                               P(FAKE), ctypes.byref(Lb), P(FAKE), None, P(FAKE), 0, P(FAKE), 1 << 40, None)
+    assert rc == 2 and "32-bit" in lib.moe_last_error().decode()

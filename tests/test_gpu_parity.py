@@ -38,14 +38,19 @@ def mep():
     return m
 
 
-def run(mep, wl, resident=None, ring_slots=64, group=8, shared=True, force_ring=False):
+def run(mep, wl, resident=None, ring_slots=64, group=8, shared=True, force_ring=False, fused=None):
+    """One block; `fused` None takes forward()'s default (the shared expert
+    inside the routed launches whenever its layout allows), False the separate
+    moe_shared + moe_prefill_experts calls."""
     blk = mep.MoeBlock.from_workload(wl, resident=resident, ring_slots=ring_slots, group=group, shared=shared)
     if force_ring:
         blk.use_ring(ring_slots, group)
+    if fused:
+        assert blk.can_fuse
     # NaN bytes in every intermediate: a GEMM tile or feature block that the
     # schedule skipped would leave NaN rows in the output.
     blk.workspace.fill_(0xFF)
-    blk.forward()
+    blk.forward(fused=fused)
     torch.cuda.synchronize()
     g = dict(
         topk_idx=blk.topk_idx.cpu().numpy().view(np.uint32),
@@ -83,10 +88,15 @@ def check_out(got, ref):
 
 # ------------------------------------------------------------------ small shapes, full oracle
 
+PATHS = [True, False]
+PATH_IDS = ["fused", "separate"]
+
+
+@pytest.mark.parametrize("fused", PATHS, ids=PATH_IDS)
 @pytest.mark.parametrize("centred", [False, True])
-def test_tiny_config(mep, orc, centred):
+def test_tiny_config(mep, orc, centred, fused):
     wl = ms.make_workload("tiny", centred=centred)
-    g = run(mep, wl)
+    g = run(mep, wl, fused=fused)
     r = orc.block(wl)
     check_routing(g, r)
     check_out(g["out"], r["out"])
@@ -115,14 +125,40 @@ SWEEP = [
 ]
 
 
+@pytest.mark.parametrize("fused", PATHS, ids=PATH_IDS)
 @pytest.mark.parametrize("case", SWEEP, ids=[f"s{c[0]}-t{c[1]}-h{c[2]}-I{c[3]}-E{c[4]}-k{c[5]}" for c in SWEEP])
-def test_small_sweep(mep, orc, case):
+def test_small_sweep(mep, orc, case, fused):
     seed, t, h, I, E, k, G, centred, gate = case
     wl = ms.small_case(seed, t, h, I, E, k, G, centred=centred, with_gate=gate)
+    g = run(mep, wl, fused=fused)
+    r = orc.block(wl)
+    check_routing(g, r)
+    check_out(g["out"], r["out"])
+
+
+@pytest.mark.parametrize("t", [1, 8, 100])
+def test_shared_of_another_shape(mep, orc, t):
+    """A shared expert whose inter differs from the routed one cannot join the
+    routed launches: forward() takes the separate calls."""
+    wl = ms.small_case(19, t, 512, 128, 12, 3, 64, inter_shared=192, centred=True, with_gate=t == 8)
+    blk = mep.MoeBlock.from_workload(wl)
+    assert not blk.can_fuse
+    del blk
     g = run(mep, wl)
     r = orc.block(wl)
     check_routing(g, r)
     check_out(g["out"], r["out"])
+
+
+def test_fused_matches_separate(mep):
+    """The two paths add the same terms in the same order; they differ only in
+    the shared expert's output being rounded to bf16 on the fused path."""
+    wl = ms.small_case(20, 150, 512, 128, 24, 4, 64, centred=True, with_gate=True)
+    a = run(mep, wl, fused=True)
+    b = run(mep, wl, fused=False)
+    for key in ("topk_idx", "offsets", "csr_rows", "csr_pos"):
+        assert np.array_equal(a[key], b[key]), key
+    check_out(a["out"], b["out"].astype(np.float64))
 
 
 def test_fork_matches_one_stream(mep):
@@ -133,7 +169,7 @@ def test_fork_matches_one_stream(mep):
     for fork in (True, False):
         blk = mep.MoeBlock.from_workload(wl)
         blk.workspace.fill_(0xFF)
-        blk.forward(fork=fork)
+        blk.forward(fork=fork, fused=False)
         torch.cuda.synchronize()
         outs.append(blk.out.cpu().numpy())
         del blk
@@ -159,19 +195,21 @@ def test_no_shared_expert(mep, orc):
 
 # ------------------------------------------------------------------ the five workloads
 
-def test_mid_config(mep, orc):
+@pytest.mark.parametrize("fused", PATHS, ids=PATH_IDS)
+def test_mid_config(mep, orc, fused):
     wl = ms.make_workload("mid")
-    g = run(mep, wl)
+    g = run(mep, wl, fused=fused)
     say("  oracle mid ...")
     r = orc.block(wl)
     check_routing(g, r)
     check_out(g["out"], r["out"])
 
 
+@pytest.mark.parametrize("fused", PATHS, ids=PATH_IDS)
 @pytest.mark.parametrize("name", ["decode", "decode1"])
-def test_decode_configs(mep, orc, name):
+def test_decode_configs(mep, orc, name, fused):
     wl = ms.make_workload(name)
-    g = run(mep, wl)
+    g = run(mep, wl, fused=fused)
     say(f"  oracle {name} ...")
     r = orc.block(wl)
     check_routing(g, r)
@@ -190,9 +228,10 @@ def full_routing_ref(orc, wl):
     return dict(topk_idx=idx, topk_w=w, offsets=offsets, csr_rows=rows, csr_w=cw, csr_pos=pos)
 
 
-def test_full_config(mep, orc):
+@pytest.mark.parametrize("fused", PATHS, ids=PATH_IDS)
+def test_full_config(mep, orc, fused):
     wl = ms.make_workload("full")
-    g = run(mep, wl)
+    g = run(mep, wl, fused=fused)
     say("  oracle routing full ...")
     r = full_routing_ref(orc, wl)
     check_routing(g, r)
@@ -213,7 +252,7 @@ def test_large_config_streamed(mep, orc):
     st = g["ring_stats"]
     n_streamed = int(((np.diff(r["offsets"].astype(np.int64)) > 0) & ~resident).sum())
     assert st["streamed"] == n_streamed and st["fetched_bytes"] == n_streamed * wl.layout.stride
-    g_res = run(mep, wl)
+    g_res = run(mep, wl, fused=False)
     assert np.array_equal(g["out"], g_res["out"]), "ring output differs from all-resident output"
     s = sample_rows(wl.cfg.t, 10, 2)
     say(f"  oracle brute force on {s.size} rows ...")
@@ -226,7 +265,7 @@ def test_large_config_streamed(mep, orc):
 def test_ring_equals_resident_with_poison(mep, monkeypatch):
     """A small ring (4 slots, batches of 2) with released slots poisoned must not change a bit."""
     wl = ms.make_workload("mid")
-    base = run(mep, wl)
+    base = run(mep, wl, fused=False)
     resident = np.zeros(wl.cfg.experts, dtype=bool)
     resident[::5] = True
     monkeypatch.setenv("MOE_RING_POISON", "1")
@@ -240,17 +279,38 @@ def test_ring_equals_resident_with_poison(mep, monkeypatch):
 
 def test_ring_with_everything_resident(mep):
     wl = ms.make_workload("tiny")
-    a = run(mep, wl)
+    a = run(mep, wl, fused=False)
     b = run(mep, wl, force_ring=True, ring_slots=2, group=1)
     assert np.array_equal(a["out"], b["out"])
 
 
-def test_deterministic(mep):
+@pytest.mark.parametrize("fused", PATHS, ids=PATH_IDS)
+def test_deterministic(mep, fused):
     wl = ms.small_case(11, 200, 512, 128, 16, 4, 64, centred=True)
-    a = run(mep, wl)
-    b = run(mep, wl)
+    a = run(mep, wl, fused=fused)
+    b = run(mep, wl, fused=fused)
     for key in ("topk_idx", "topk_w", "offsets", "csr_rows", "csr_w", "csr_pos", "out"):
         assert np.array_equal(a[key], b[key]), key
+
+
+def test_fused_accumulate(mep, orc):
+    """moe_prefill_fused: accumulate=0 overwrites whatever out holds (NaN
+    here), accumulate=1 adds the whole block onto it."""
+    wl = ms.small_case(21, 40, 256, 128, 8, 3, 64, centred=True, with_gate=True)
+    blk = mep.MoeBlock.from_workload(wl)
+    blk.workspace.fill_(0xFF)
+    blk.route()
+    blk.build_csr()
+    blk.out.fill_(float("nan"))
+    blk.fused(accumulate=0)
+    torch.cuda.synchronize()
+    first = blk.out.cpu().numpy()
+    r = orc.block(wl)
+    check_out(first, r["out"])
+    blk.out.fill_(1.0)
+    blk.fused(accumulate=1)
+    torch.cuda.synchronize()
+    check_out(blk.out.cpu().numpy(), r["out"] + 1.0)
 
 
 def test_accumulate_semantics(mep, orc):

@@ -45,6 +45,12 @@ enum {
 };
 void moe_profile_begin(uint32_t mask);
 int moe_profile_end(double *ms, int64_t *launches);
+/*
+ * Changes which phases later launches time, keeping the events already
+ * recorded since moe_profile_begin (mask 0 pauses timing), so that a
+ * benchmark can time a sample of its steps' launches.
+ */
+void moe_profile_set_mask(uint32_t mask);
 #ifdef __cplusplus
 }
 #endif

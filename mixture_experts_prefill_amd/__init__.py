@@ -50,7 +50,8 @@ class moe_ring_stats(ctypes.Structure):
 _lib = None
 EXPORTS = ["moe_last_error", "moe_layout_make", "moe_workspace_bytes", "moe_route", "moe_build_csr",
            "moe_shared", "moe_ring_create", "moe_ring_destroy", "moe_ring_get_stats", "moe_prefill_experts",
-           "moe_ring_plan_debug", "moe_profile_begin", "moe_profile_end", "moe_prefill_fused"]
+           "moe_ring_plan_debug", "moe_profile_begin", "moe_profile_end", "moe_profile_set_mask",
+           "moe_prefill_fused"]
 PHASES = ["router", "topk", "csr", "shared_gateup", "shared_down", "schedule", "gateup", "down", "combine"]
 
 
@@ -80,6 +81,8 @@ def lib():
     L.moe_ring_plan_debug.argtypes = [P, P, I, I, I, P, P, P]
     L.moe_profile_begin.argtypes = [ctypes.c_uint32]
     L.moe_profile_begin.restype = None
+    L.moe_profile_set_mask.argtypes = [ctypes.c_uint32]
+    L.moe_profile_set_mask.restype = None
     L.moe_profile_end.argtypes = [P, P]
     L.moe_profile_end.restype = ctypes.c_int
     for f in ("moe_layout_make", "moe_route", "moe_build_csr", "moe_shared", "moe_ring_create",
@@ -224,6 +227,14 @@ def moe_profile_begin(phases: Sequence[str]) -> None:
     for p in phases:
         mask |= 1 << PHASES.index(p)
     lib().moe_profile_begin(mask)
+
+
+def moe_profile_set_mask(phases: Sequence[str]) -> None:
+    """Time the named phases from now on, keeping what was recorded so far ([] pauses)."""
+    mask = 0
+    for p in phases:
+        mask |= 1 << PHASES.index(p)
+    lib().moe_profile_set_mask(mask)
 
 
 def moe_profile_end() -> dict:

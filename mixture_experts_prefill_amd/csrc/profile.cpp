@@ -66,6 +66,8 @@ void moe_profile_begin(uint32_t mask) {
     g_marks.clear();
 }
 
+void moe_profile_set_mask(uint32_t mask) { g_mask = mask; }
+
 int moe_profile_end(double *ms, int64_t *launches) {
     g_mask = 0;
     if (ms)

@@ -235,10 +235,14 @@ __global__ void __launch_bounds__(512, 1) k_router_lds(const uint16_t *__restric
 #pragma unroll
     for (int o = 0; o < kWR * kWE; ++o) p[o] = 0.0f;
 
-    uint4 v[kPer];
-    load(0, v);
+    // Staged chunks are loaded two steps ahead into two register sets (the
+    // step's compute is shorter than a load's latency from L2 or HBM), so the
+    // loop is unrolled by two to keep each set in fixed registers.
+    uint4 va[kPer], vb[kPer];
     const int steps = h >> 8;
-    for (int s = 0; s < steps; ++s) {
+    load(0, va);
+    if (steps > 1) load(1, vb);
+    auto step = [&](int s, uint4 (&v)[kPer]) {
         uint8_t *buf = lds[s & 1];
 #pragma unroll
         for (int c = 0; c < kPer; ++c) {
@@ -252,7 +256,7 @@ __global__ void __launch_bounds__(512, 1) k_router_lds(const uint16_t *__restric
             }
         }
         __syncthreads();
-        if (s + 1 < steps) load(s + 1, v);
+        if (s + 2 < steps) load(s + 2, v);
         float wv[kWE][4];
 #pragma unroll
         for (int j = 0; j < kWE; ++j) {
@@ -275,6 +279,10 @@ __global__ void __launch_bounds__(512, 1) k_router_lds(const uint16_t *__restric
                 acc = __builtin_fmaf(x3, wv[j][3], acc);
             }
         }
+    };
+    for (int s = 0; s < steps; s += 2) {
+        step(s, va);
+        if (s + 1 < steps) step(s + 1, vb);
     }
 
     // Transposed butterfly over the 64 partials: 6 splitting levels leave

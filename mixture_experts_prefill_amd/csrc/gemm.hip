@@ -449,9 +449,11 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
                 for (int m = 0; m < 2 * TBR; ++m) {
                     // one MFMA, then a slice of VALU that issues during its
                     // 32 cycles (an MFMA pair would block the wave at the
-                    // second MFMA with no VALU in between)
+                    // second MFMA with no VALU in between); slices of about
+                    // 40 / (2 TBR) spread a region's ~37 VALU over all its
+                    // MFMAs (same box: 1% faster than 48 / (2 TBR))
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x002, 24 / TBR, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 20 / TBR, 0);
                 }
                 if (st == 2) {
                     wait_vm<(NS - 2) * VM_PER_STEP>();

@@ -183,33 +183,38 @@ __global__ void __launch_bounds__(256) k_router_few(const uint16_t *__restrict__
     }
 }
 
-// Large-t router: a workgroup of 8 waves owns 32 rows x 32 experts; every
-// 256-element step stages the rows' x chunks (widened once to fp32 on the way
-// in, 32 KB) and the experts' W chunks (32 KB) in LDS, double-buffered, and
-// each wave computes 16 rows x 8 experts from LDS (lane l still owns partial
-// l of every logit).
-constexpr int kLR = 32, kLE = 32;             // rows, experts per workgroup
-constexpr int kWR = 16, kWE = 8;              // rows, experts per wave
-constexpr int kXSrc = kLR * 512;              // x bytes (bf16) per step
-constexpr int kXBytes = kLR * 1024, kWBytes = kLE * 1024;  // staged bytes (x as fp32)
-
-__global__ void __launch_bounds__(512, 1) k_router_lds(const uint16_t *__restrict__ x,
-                                                       const float *__restrict__ w, int t, int h,
-                                                       int E, float *__restrict__ logits) {
+// Large-t router: a workgroup of 4 or 8 waves owns LR rows x LE experts;
+// every 256-element step stages the rows' x chunks (widened once to fp32 on
+// the way in) and the experts' W chunks in LDS, double-buffered, and each
+// wave computes WR rows x WE experts from LDS (lane l still owns partial l
+// of every logit).  Two shapes: 32 x 32 with 8 waves of 16 x 8 (128 KB of
+// LDS, one workgroup per CU) where the chunk gives at least one workgroup
+// per CU, else 16 x 16 with 4 waves of 8 x 8 (64 KB, two per CU), whose 4x
+// more workgroups fill the GPU for mid-sized chunks (t = 512, E = 64:
+// 20.5 -> 12.0 us; at t = 4096, E = 128 the 32 x 32 shape is faster, 47 vs 57 us).
+template <int LR, int LE, int WR, int WE>
+__global__ void __launch_bounds__(64 * (LR / WR) * (LE / WE), (LR * LE >= 1024) ? 1 : 2)
+k_router_lds(const uint16_t *__restrict__ x, const float *__restrict__ w, int t, int h, int E,
+             float *__restrict__ logits) {
+    constexpr int kThreads = 64 * (LR / WR) * (LE / WE);
+    constexpr int kXSrc = LR * 512;                         // x bytes (bf16) per step
+    constexpr int kXBytes = LR * 1024, kWBytes = LE * 1024; // staged bytes (x as fp32)
+    constexpr int kWavesE = LE / WE;                        // waves along the experts
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][kXBytes + kWBytes];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int e_blocks = (E + kLE - 1) / kLE;
-    const int r0 = (blockIdx.x / e_blocks) * kLR, e0 = (blockIdx.x % e_blocks) * kLE;
-    const int wr = (wave >> 2) * kWR, we = (wave & 3) * kWE;   // this wave's rows / experts in the tile
+    const int e_blocks = (E + LE - 1) / LE;
+    const int r0 = (blockIdx.x / e_blocks) * LR, e0 = (blockIdx.x % e_blocks) * LE;
+    const int wr = (wave / kWavesE) * WR, we = (wave % kWavesE) * WE;   // this wave's rows / experts
 
-    // Staging: 16-byte source chunks, x first (32 rows x 32 chunks of 8 bf16,
-    // each stored as 32 bytes of fp32) then W (32 x 64).
-    constexpr int kChunks = (kXSrc + kWBytes) / 16, kPer = kChunks / 512;
+    // Staging: 16-byte source chunks, x first (LR rows x 32 chunks of 8 bf16,
+    // each stored as 32 bytes of fp32) then W (LE x 64).
+    constexpr int kChunks = (kXSrc + kWBytes) / 16, kPer = kChunks / kThreads;
+    static_assert(kChunks % kThreads == 0, "whole chunks per thread");
     const uint8_t *src[kPer];
     bool ok[kPer];
 #pragma unroll
     for (int c = 0; c < kPer; ++c) {
-        const int ch = tid + 512 * c;
+        const int ch = tid + kThreads * c;
         if (ch < kXSrc / 16) {
             const int r = ch >> 5, q = ch & 31;
             ok[c] = r0 + r < t;
@@ -225,15 +230,17 @@ __global__ void __launch_bounds__(512, 1) k_router_lds(const uint16_t *__restric
     auto load = [&](int s, uint4 *v) {
 #pragma unroll
         for (int c = 0; c < kPer; ++c) {
-            const int ch = tid + 512 * c;
+            const int ch = tid + kThreads * c;
             const size_t off = (ch < kXSrc / 16) ? (size_t)s * 512 : (size_t)s * 1024;
             v[c] = ok[c] ? *reinterpret_cast<const uint4 *>(src[c] + off) : make_uint4(0, 0, 0, 0);
         }
     };
 
-    float p[kWR * kWE];
+    constexpr int N = WR * WE;  // outputs of the wave
+    static_assert(N == 64 || N == 128, "one or two outputs per lane");
+    float p[N];
 #pragma unroll
-    for (int o = 0; o < kWR * kWE; ++o) p[o] = 0.0f;
+    for (int o = 0; o < N; ++o) p[o] = 0.0f;
 
     // Staged chunks are loaded two steps ahead into two register sets (the
     // step's compute is shorter than a load's latency from L2 or HBM), so the
@@ -246,7 +253,7 @@ __global__ void __launch_bounds__(512, 1) k_router_lds(const uint16_t *__restric
         uint8_t *buf = lds[s & 1];
 #pragma unroll
         for (int c = 0; c < kPer; ++c) {
-            const int ch = tid + 512 * c;
+            const int ch = tid + kThreads * c;
             if (ch < kXSrc / 16) {  // 8 bf16 -> 8 fp32 (exact)
                 const uint4 q = v[c];
                 *reinterpret_cast<float4 *>(buf + ch * 32) = make_float4(bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.y), bf16_hi(q.y));
@@ -257,9 +264,9 @@ __global__ void __launch_bounds__(512, 1) k_router_lds(const uint16_t *__restric
         }
         __syncthreads();
         if (s + 2 < steps) load(s + 2, v);
-        float wv[kWE][4];
+        float wv[WE][4];
 #pragma unroll
-        for (int j = 0; j < kWE; ++j) {
+        for (int j = 0; j < WE; ++j) {
             const float4 q = *reinterpret_cast<const float4 *>(buf + kXBytes + (we + j) * 1024 + lane * 16);
             wv[j][0] = q.x;
             wv[j][1] = q.y;
@@ -267,12 +274,12 @@ __global__ void __launch_bounds__(512, 1) k_router_lds(const uint16_t *__restric
             wv[j][3] = q.w;
         }
 #pragma unroll
-        for (int i = 0; i < kWR; ++i) {
+        for (int i = 0; i < WR; ++i) {
             const float4 q = *reinterpret_cast<const float4 *>(buf + (wr + i) * 1024 + lane * 16);
             const float x0 = q.x, x1 = q.y, x2 = q.z, x3 = q.w;
 #pragma unroll
-            for (int j = 0; j < kWE; ++j) {
-                float &acc = p[i * kWE + j];
+            for (int j = 0; j < WE; ++j) {
+                float &acc = p[i * WE + j];
                 acc = __builtin_fmaf(x0, wv[j][0], acc);
                 acc = __builtin_fmaf(x1, wv[j][1], acc);
                 acc = __builtin_fmaf(x2, wv[j][2], acc);
@@ -286,25 +293,26 @@ __global__ void __launch_bounds__(512, 1) k_router_lds(const uint16_t *__restric
     }
 
     // Transposed butterfly over the 64 partials: 6 splitting levels leave
-    // outputs 2*lane and 2*lane + 1 (row (2 lane)/8, experts (2 lane)%8, +1).
+    // N / 64 outputs per lane: output `lane` (N = 64), or outputs 2 lane and
+    // 2 lane + 1 (N = 128); output o is row o / WE, expert o % WE.
     // Levels off = 32 and 16 use v_permlane32/16_swap: swapping the upper
     // lanes of p[o] with the lower lanes of p[o + half] hands each lane its
     // partner's copy of the output it keeps, so one add finishes the pair
     // (lane l < off: p_l + p_(l+off); lane l >= off: p_(l-off) + p_l).
 #pragma unroll
-    for (int o = 0; o < 64; ++o) {
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[o]), __float_as_uint(p[o + 64]), false, false);
+    for (int o = 0; o < N / 2; ++o) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[o]), __float_as_uint(p[o + N / 2]), false, false);
         p[o] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
     }
 #pragma unroll
-    for (int o = 0; o < 32; ++o) {
-        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(p[o]), __float_as_uint(p[o + 32]), false, false);
+    for (int o = 0; o < N / 4; ++o) {
+        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(p[o]), __float_as_uint(p[o + N / 4]), false, false);
         p[o] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
     }
 #pragma unroll
     for (int lvl = 2; lvl < 6; ++lvl) {
         const int off = 32 >> lvl;
-        const int half = (kWR * kWE) >> (lvl + 1);
+        const int half = N >> (lvl + 1);
         const uint32_t m = (lane & off) ? 0xffffffffu : 0u;
 #pragma unroll
         for (int o = 0; o < half; ++o) {
@@ -314,11 +322,13 @@ __global__ void __launch_bounds__(512, 1) k_router_lds(const uint16_t *__restric
             p[o] = keep + __shfl_xor(give, off, 64);
         }
     }
-    const int o = 2 * lane, i = o / kWE, j = o % kWE;
+    constexpr int PER = N / 64;
+    const int o = PER * lane, i = o / WE, j = o % WE;
     const int r = r0 + wr + i, e = e0 + we + j;
     if (r < t) {
-        if (e < E) logits[(size_t)r * E + e] = p[0];
-        if (e + 1 < E) logits[(size_t)r * E + e + 1] = p[1];
+#pragma unroll
+        for (int q = 0; q < PER; ++q)
+            if (e + q < E) logits[(size_t)r * E + e + q] = p[q];
     }
 }
 
@@ -425,8 +435,13 @@ hipError_t launch_router_logits(const uint16_t *x, const float *w, int t, int h,
     // small t: one row block and one expert per wave keeps >= E waves busy
     // streaming W; large t: LDS-shared 32 x 32 tiles.
     if (t >= 128 && E >= 32) {
-        const int blocks = ((t + kLR - 1) / kLR) * ((E + kLE - 1) / kLE);
-        hipLaunchKernelGGL(k_router_lds, dim3(blocks), dim3(512), 0, s, x, w, t, h, E, logits);
+        const int big = ((t + 31) / 32) * ((E + 31) / 32);
+        if (big >= 256) {
+            hipLaunchKernelGGL((k_router_lds<32, 32, 16, 8>), dim3(big), dim3(512), 0, s, x, w, t, h, E, logits);
+        } else {
+            const int blocks = ((t + 15) / 16) * ((E + 15) / 16);
+            hipLaunchKernelGGL((k_router_lds<16, 16, 8, 8>), dim3(blocks), dim3(256), 0, s, x, w, t, h, E, logits);
+        }
         return hipGetLastError();
     }
     if (t <= kFewRows && h <= kFewSteps * 256) {

@@ -123,6 +123,7 @@ SWEEP = [
     (17, 64, 256, 64, 1024, 32, 32, True, False), # the expert and top-k caps: E = 1024, k = 32
     (18, 4096, 256, 64, 64, 32, 64, False, True), # the row cap with k = 32: 131072 CSR entries
     (22, 4000, 256, 64, 1024, 8, 64, True, False),# 63 CSR tiles (ragged last) with E = 1024 counts each
+    (23, 1000, 256, 64, 300, 4, 32, False, False),# 32 x 32 LDS router tiles with ragged rows and experts
 ]
 
 

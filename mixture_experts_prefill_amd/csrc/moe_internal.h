@@ -33,9 +33,10 @@ constexpr int kMaxBM = 128;       // largest GEMM M-tile
 constexpr int kSchedMaxTiles = 8192;  // tiles one schedule can hold (>= t*k/kMinBM + E + 1)
 constexpr int kSchedXcnt = 8;     // sched_n[kSchedXcnt + x] = tiles of XCD x
 // Relative cost of an M-tile with b token blocks of 32 rows: kTileCostBase + b
-// (the weight dequantisation of a K step costs about as much as five token
-// blocks of MFMAs).
-constexpr int kTileCostBase = 5;
+// (per-workgroup timestamps put a gate/up tile at about 28 + 7.3 b us: the
+// weight dequantisation of the tile costs about as much as four token blocks
+// of MFMAs; 4 measured 1% faster than 5 for the full chunk).
+constexpr int kTileCostBase = 4;
 
 bool workspace_plan(int t, int k, int E, const moe_layout *routed, const moe_layout *shared,
                     Workspace *out);

@@ -385,3 +385,32 @@ def test_bad_arguments_leave_outputs_untouched(mep):
         ring.close()
     torch.cuda.synchronize()
     assert bool((blk.out == 7.0).all())
+
+
+def test_missing_record_does_not_fault(mep):
+    """A used expert whose record address is 0 (and no ring) is never
+    dereferenced: its entries get unspecified values, every other row is
+    unchanged, on both paths."""
+    wl = ms.small_case(24, 64, 256, 128, 8, 2, 64, centred=True)
+    for fused in (True, False):
+        ref = run(mep, wl, fused=fused)
+        blk = mep.MoeBlock.from_workload(wl)
+        blk.workspace.fill_(0xFF)
+        blk.route()
+        blk.build_csr()
+        torch.cuda.synchronize()
+        table = blk.table.clone()
+        table[3] = 0
+        blk.table = table
+        if fused:
+            blk.fused(accumulate=0)
+        else:
+            blk.shared(accumulate=0)
+            blk.experts(accumulate=1)
+        torch.cuda.synchronize()
+        out = blk.out.cpu().numpy()
+        idx = blk.topk_idx.cpu().numpy()
+        clean = ~(idx == 3).any(axis=1)
+        assert clean.any() and (~clean).any()
+        assert np.array_equal(out[clean], ref["out"][clean])
+        del blk

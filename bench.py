@@ -28,11 +28,18 @@ def log(*a):
 
 
 def source_hash() -> str:
+    """Hash of the library's sources with comments and blank space removed, so
+    that counters stay attached to the code they were taken on, not its prose."""
+    import re
+
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "mixture_experts_prefill_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(f.encode() + " ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

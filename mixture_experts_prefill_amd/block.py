@@ -1,4 +1,4 @@
-"""Device buffers for one MoE block and the four calls in their order.
+"""Device buffers for one MoE block and its calls in their order.
 
 Owns the GPU tensors of one layer shape (inputs, routing outputs, CSR,
 workspace, output) and runs

@@ -15,20 +15,22 @@
 // fragments (gate and up of the same features, or two adjacent down
 // features) for all BM tokens, so every activation fragment read from LDS
 // feeds two MFMAs.  Per 64-wide K step:
-//   - the workgroup stages BM activation rows x 128 bytes into LDS (gathered
-//     through csr_rows for the routed gate/up projection), double-buffered,
-//     each row padded to 144 bytes: 9 sixteen-byte bank groups per row is
-//     coprime with any power-of-two bank count, so the B-fragment reads of 32
+//   - the workgroup stages BM activation rows x 128 bytes (gathered through
+//     csr_rows for the routed gate/up projection) and each wave its two 1 KB
+//     code tiles and their fp16 scale/bias pairs straight from memory into
+//     an LDS ring of 3-4 K steps (buffer loads with the lds modifier); rows
+//     are XOR-swizzled in 16-byte chunks so that the B-fragment reads of 32
 //     rows at one column hit distinct banks;
-//   - each wave loads its two 1 KB code tiles (one 16-byte load per lane,
-//     fully coalesced thanks to the record's tile order) and their fp16
-//     scale/bias pairs, and dequantises in registers: a nibble pair OR'ed
+//   - each wave dequantises its code tiles in registers: a nibble pair OR'ed
 //     into the fp16 pattern 0x6400 (= 1024 + q) feeds v_fma_mix_f32 with
 //     scale s and offset (bias - 1024 s) kept in fp32, then
 //     v_cvt_pk_bf16_f32 packs the MFMA operand;
 //   - 4 MFMA steps of K = 16.  Inside a lane's 16 bytes the K order is
 //     permuted (lane half L/32 takes 32 consecutive columns), and the
 //     activation fragment uses the same permutation, so the products pair up.
+// The shared expert can ride in the routed launches as one more segment of
+// dense rows (moe_prefill_fused), and tiles of one or two rows take a
+// matrix-core-free path (see gemv below).
 #include <algorithm>
 #include <type_traits>
 

@@ -138,6 +138,36 @@ def test_small_sweep(mep, orc, case, fused):
     check_out(g["out"], r["out"])
 
 
+def random_cases(n, seed=7):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        t = int(rng.choice([1, 2, 3, 8, 17, 64, 65, 130, 257, 600]))
+        h = int(rng.choice([256, 512, 768, 1024]))
+        I = int(rng.choice([64, 128, 192, 320]))
+        E = int(rng.integers(1, 300))
+        k = int(rng.integers(1, min(E, 12) + 1))
+        G = int(rng.choice([32, 64]))
+        cases.append((100 + i, t, h, I, E, k, G, bool(rng.integers(2)), bool(rng.integers(2))))
+    return cases
+
+
+RANDOM = random_cases(12)
+
+
+@pytest.mark.parametrize("fused", PATHS, ids=PATH_IDS)
+@pytest.mark.parametrize("case", RANDOM, ids=[f"r{c[0]}-t{c[1]}-h{c[2]}-I{c[3]}-E{c[4]}-k{c[5]}-G{c[6]}" for c in RANDOM])
+def test_random_shapes(mep, orc, case, fused):
+    """Seeded random shapes (row counts around the tile and CSR-tile edges,
+    any E and k, both group sizes, gated or not) on both paths."""
+    seed, t, h, I, E, k, G, centred, gate = case
+    wl = ms.small_case(seed, t, h, I, E, k, G, centred=centred, with_gate=gate)
+    g = run(mep, wl, fused=fused)
+    r = orc.block(wl)
+    check_routing(g, r)
+    check_out(g["out"], r["out"])
+
+
 @pytest.mark.parametrize("t", [1, 8, 100])
 def test_shared_of_another_shape(mep, orc, t):
     """A shared expert whose inter differs from the routed one cannot join the

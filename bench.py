@@ -151,9 +151,11 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    # 20 warm-up steps: after only 5 the timed steps still ran 5% slower
-    # (full chunk 0.513 vs 0.483-0.487 ms per step for 20, 50 or 200).
-    ap.add_argument("--warmup", type=int, default=20)
+    # Default warm-up: at least 20 steps and 30 ms of GPU work.  After only 5
+    # steps the timed ones still ran 5% slower (full chunk 0.513 vs
+    # 0.483-0.487 ms per step for 20, 50 or 200 warm-up steps; decode-shaped
+    # chunk 0.189 vs 0.180 ms for 5 and 50).
+    ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--config", default="full")
     ap.add_argument("--copies", type=int, default=0,
                     help="weight copies rotated per step (0: enough that a step's weights have left the "
@@ -221,10 +223,17 @@ def main():
         blk.table = tables[i % len(tables)]
         blk.forward(fused=fused)
 
-    log(f"[bench] warmup {args.warmup}")
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    warmup = 0
+    w_start = time.perf_counter()
+    while True:
+        n = args.warmup if args.warmup is not None else 20
+        for _ in range(n if warmup == 0 else 10):
+            step(warmup)
+            warmup += 1
+        torch.cuda.synchronize()
+        if args.warmup is not None or time.perf_counter() - w_start >= 0.03:
+            break
+    log(f"[bench] warmup {warmup} steps")
 
     dominant = "gateup"
     # The dominant kernel's launches are timed with HIP events attached to
@@ -342,7 +351,7 @@ def main():
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "warmup": warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"{cfg.name}: {cfg.description}", "t": t, "hidden": cfg.hidden, "inter": cfg.inter,
                    "inter_shared": cfg.inter_shared, "experts": cfg.experts, "top_k": cfg.k, "group": cfg.group,

@@ -222,11 +222,14 @@ def main():
         tab[nz] = tab[nz] - blk.pool.data_ptr() + pool.data_ptr()
         tables.append(tab)
 
-    fused = blk.can_fuse and not args.separate
+    # the whole block in one call (moe_block) unless the shared expert must run
+    # in its own call (--separate, or experts streamed through the ring)
+    path = "block" if blk.can_block and not args.separate else "separate"
+    fused = path == "block" and blk.Ls is not None
 
     def step(i):
         blk.table = tables[i % len(tables)]
-        blk.forward(fused=fused)
+        blk.forward(path=path)
 
     warmup = 0
     w_start = time.perf_counter()
@@ -296,7 +299,8 @@ def main():
              "block_hbm_frac": round(work["bytes_total"] / step_s / 1e9 / PEAK_HBM_GBS, 4),
              "touched_experts": work["touched"], "max_rows_per_expert": int(counts.max()),
              "weight_copies": len(tables),
-             "shared_expert": "in the routed launches (moe_prefill_fused)" if fused else "own call (moe_shared)"}
+             "calls": "moe_block (shared expert in the routed launches)" if path == "block"
+                      else "moe_shared, moe_route, moe_build_csr, moe_prefill_experts"}
     if blk.ring is not None:
         # streamed experts: the host link is the bound; the ring counters are
         # those of the last call (one step)

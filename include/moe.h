@@ -250,6 +250,29 @@ moe_status moe_prefill_fused(const uint16_t *x, int32_t t, int32_t k, int32_t E,
                              const void *shared_record, const uint16_t *shared_gate_w, float *out,
                              int32_t accumulate, void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * The whole block in one call: moe_route, moe_build_csr and
+ * moe_prefill_fused (or moe_prefill_experts when Ls is NULL) in this order,
+ * on one stream, with the same outputs and the same arithmetic.  Being one
+ * call lets it merge launches that the separate calls cannot: for chunks of
+ * up to 512 rows the grouping (CSR) and the experts' tile schedule run in
+ * one workgroup and one launch.
+ *
+ *   x, w_router, t, k, E, logits, topk_idx, topk_w   as for moe_route (h = L->hidden)
+ *   offsets, csr_rows, csr_w, csr_pos                outputs, as for moe_build_csr
+ *   L, records, Ls, shared_record, shared_gate_w,
+ *   out, accumulate                                  as for moe_prefill_fused; Ls may be
+ *                                                    NULL (no shared expert)
+ *   workspace  at least moe_workspace_bytes(t, k, E, L, Ls) bytes
+ * Every used expert must be resident.  Errors as for the separate calls.
+ */
+moe_status moe_block(const uint16_t *x, const float *w_router, int32_t t, int32_t k, int32_t E,
+                     const moe_layout *L, const uint64_t *records, const moe_layout *Ls,
+                     const void *shared_record, const uint16_t *shared_gate_w, float *logits,
+                     uint32_t *topk_idx, float *topk_w, uint32_t *offsets, uint32_t *csr_rows,
+                     float *csr_w, uint32_t *csr_pos, float *out, int32_t accumulate, void *workspace,
+                     size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

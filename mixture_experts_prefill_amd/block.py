@@ -25,8 +25,8 @@ from typing import Optional, Sequence
 import numpy as np
 import torch
 
-from . import (MoeRing, moe_build_csr, moe_layout_make, moe_prefill_experts, moe_prefill_fused, moe_route,
-               moe_shared, moe_workspace_bytes)
+from . import (MoeRing, moe_block, moe_build_csr, moe_layout_make, moe_prefill_experts, moe_prefill_fused,
+               moe_route, moe_shared, moe_workspace_bytes)
 
 
 def bf16_tensor(bits: np.ndarray, device) -> torch.Tensor:
@@ -125,6 +125,16 @@ class MoeBlock:
                           self.table, self.Ls, self.shared_record, self.gate_w, self.out, accumulate, self.workspace,
                           stream)
 
+    def block(self, accumulate: int = 0, stream=None):
+        moe_block(self.x, self.w_router, self.k, self.L, self.table, self.Ls, self.shared_record, self.gate_w,
+                  self.logits, self.topk_idx, self.topk_w, self.offsets, self.csr_rows, self.csr_w, self.csr_pos,
+                  self.out, accumulate, self.workspace, stream)
+
+    @property
+    def can_block(self) -> bool:
+        """Every expert resident, and no shared expert or one of the routed layout."""
+        return self.ring is None and self.host_records is None and (self.Ls is None or self.can_fuse)
+
     @property
     def can_fuse(self) -> bool:
         """The shared record has the routed layout and no expert streams through a ring."""
@@ -142,18 +152,31 @@ class MoeBlock:
     # t = 512 and 4096 faster forked).
     FORK_MIN_ROWS = 64
 
-    def forward(self, stream=None, fork: Optional[bool] = None, fused: Optional[bool] = None) -> torch.Tensor:
+    def forward(self, stream=None, fork: Optional[bool] = None, fused: Optional[bool] = None,
+                path: Optional[str] = None) -> torch.Tensor:
         """One block.  `stream` (torch stream, raw handle or None for the current
-        stream) carries routing, grouping and the routed experts.  With `fused`
-        (default: whenever can_fuse) the shared expert runs inside the routed
-        launches (moe_prefill_fused).  Otherwise, with `fork` (default:
-        t >= FORK_MIN_ROWS) the shared expert forks off the stream onto a
-        second one and joins back before the routed call, or runs first on the
-        same stream."""
-        if fused is None:
-            fused = self.can_fuse
+        stream) carries routing, grouping and the routed experts.  `path`:
+          "block"    the whole block in one call (moe_block), the default
+                     whenever can_block;
+          "fused"    moe_route, moe_build_csr, moe_prefill_fused (fused=True);
+          "separate" the shared expert in its own call (fused=False, and the
+                     default with a ring): with `fork` (default:
+                     t >= FORK_MIN_ROWS) it forks off the stream onto a second
+                     one and joins back before the routed call, otherwise it
+                     runs first on the same stream."""
+        if path is None:
+            if fused is None:
+                path = "block" if self.can_block else "separate"
+            else:
+                path = "fused" if fused else "separate"
         if fork is None:
             fork = self.t >= self.FORK_MIN_ROWS
+        if path == "block":
+            if not self.can_block:
+                raise ValueError("one-call block needs resident experts and a shared record of the routed layout")
+            self.block(0, stream)
+            return self.out
+        fused = path == "fused"
         if fused:
             if not self.can_fuse:
                 raise ValueError("fused block needs a shared record of the routed layout and resident experts")

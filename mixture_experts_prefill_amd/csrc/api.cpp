@@ -146,6 +146,87 @@ static moe_status check_routing(int t, int k, int E) {
     return MOE_OK;
 }
 
+// Checks shared by moe_prefill_fused and moe_block: the routed layout, the
+// shared layout (optional for moe_block, required for the fused call) equal
+// to it, the inputs, the 32-bit offsets and the workspace.
+static moe_status check_fused(const uint16_t *x, int t, int k, int E, const moe_layout *L,
+                              const uint64_t *records, const moe_layout *Ls, const void *shared_record,
+                              const float *out, const void *workspace, size_t workspace_bytes,
+                              const char *who) {
+    const bool block = who[0] == 'b';
+    if (!layout_ok(L) || (Ls && !layout_ok(Ls)) || (!Ls && !block))
+        return fail(MOE_ERR_INVALID, "%s: layout not made by moe_layout_make", who);
+    if (Ls && !fusable(L, Ls))
+        return fail(MOE_ERR_INVALID, "%s: the shared layout (h %d, inter %d, group %d) must equal the routed one "
+                    "(h %d, inter %d, group %d)", who, Ls->hidden, Ls->inter, Ls->group, L->hidden, L->inter, L->group);
+    if (!x || !records || (Ls && !shared_record) || !out || !workspace)
+        return fail(MOE_ERR_INVALID, "%s: null pointer", who);
+    if (!aligned16(x) || !aligned16(out) || (Ls && !aligned16(shared_record)))
+        return fail(MOE_ERR_INVALID, "%s: x, out and the shared record must be 16-byte aligned", who);
+    const uint64_t Q = (uint64_t)t * (k + (Ls ? 1 : 0));
+    if (Q * L->inter * 2 > 0xffffffffull || (uint64_t)t * L->hidden * 2 > 0xffffffffull)
+        return fail(MOE_ERR_CAPACITY, "%s: t*(k+1)*inter or t*hidden too large for 32-bit offsets", who);
+    Workspace w;
+    workspace_plan(t, k, E, L, Ls, &w);
+    if (workspace_bytes < w.total)
+        return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", who, workspace_bytes, w.total);
+    return MOE_OK;
+}
+
+// GEMM arguments of the grouped launches, with the shared expert's t rows
+// after the t*k CSR positions when `shared`.
+static GemmArgs fused_args(const uint16_t *x, int t, int k, int E, const moe_layout *L, const uint32_t *csr_rows,
+                           const uint64_t *records, uint8_t *ws, const Workspace &w, bool shared) {
+    const size_t Q = (size_t)t * (k + (shared ? 1 : 0));
+    GemmArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.x = x;
+    a.rows = csr_rows;
+    a.records = records;
+    a.sched_n = reinterpret_cast<uint32_t *>(ws + w.sched_n);
+    a.order = reinterpret_cast<TileEntry *>(ws + w.order);
+    a.xcap = (int)(Q / kMinBM + (size_t)E + 2);
+    a.t = t;
+    a.hidden = L->hidden;
+    a.inter = L->inter;
+    a.group = L->group;
+    a.hg = reinterpret_cast<uint16_t *>(ws + w.hg);
+    a.ye = reinterpret_cast<uint16_t *>(ws + w.ye);
+    a.shared_rows = shared ? 1 : 0;
+    a.shared_p0 = t * k;
+    return a;
+}
+
+static moe_status shared_gate(const uint16_t *x, int t, const moe_layout *L, const uint16_t *gate_w, uint8_t *g,
+                              hipStream_t s) {
+    if (!gate_w) return MOE_OK;
+    hipError_t e = launch_shared_gate(x, gate_w, t, L->hidden, reinterpret_cast<float *>(g), s);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "shared gate");
+}
+
+// Gate/up, down and combine of a scheduled call (the schedule already enqueued).
+static moe_status fused_gemms(GemmArgs a, int bm, const moe_layout *L, int t, int k, int E,
+                              const uint32_t *csr_pos, const float *csr_w, float *out, int accumulate,
+                              const float *g, bool shared, hipStream_t s) {
+    const size_t Q = (size_t)t * (k + (shared ? 1 : 0));
+    a.max_tiles = (int)(Q / bm + (size_t)E + 2);
+    a.w_off = L->gate_w;
+    a.sb_off = L->gate_sb;
+    a.w2_off = L->up_w;
+    a.sb2_off = L->up_sb;
+    hipError_t e = launch_gateup(a, bm, s);
+    if (e != hipSuccess) return hip_fail(e, "experts gate/up");
+    a.act = a.hg;
+    a.w_off = L->down_w;
+    a.sb_off = L->down_sb;
+    e = launch_down(a, bm, s);
+    if (e != hipSuccess) return hip_fail(e, "experts down");
+    e = launch_combine(a.ye, csr_pos, csr_w, t, k, L->hidden, out, accumulate, s,
+                       shared ? a.ye + (size_t)t * k * L->hidden : nullptr, g);
+    if (e != hipSuccess) return hip_fail(e, "combine");
+    return MOE_OK;
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -353,66 +434,65 @@ moe_status moe_prefill_fused(const uint16_t *x, int32_t t, int32_t k, int32_t E,
                              const void *shared_record, const uint16_t *shared_gate_w, float *out,
                              int32_t accumulate, void *workspace, size_t workspace_bytes, void *stream) {
     if (moe_status st = check_routing(t, k, E)) return st;
-    if (!layout_ok(L) || !layout_ok(Ls)) return fail(MOE_ERR_INVALID, "fused: layout not made by moe_layout_make");
-    if (!fusable(L, Ls))
-        return fail(MOE_ERR_INVALID, "fused: the shared layout (h %d, inter %d, group %d) must equal the routed one "
-                    "(h %d, inter %d, group %d)", Ls->hidden, Ls->inter, Ls->group, L->hidden, L->inter, L->group);
-    if (!x || !offsets || !csr_rows || !csr_w || !csr_pos || !records || !shared_record || !out || !workspace)
-        return fail(MOE_ERR_INVALID, "fused: null pointer");
-    if (!aligned16(x) || !aligned16(out) || !aligned16(shared_record))
-        return fail(MOE_ERR_INVALID, "fused: x, out and the shared record must be 16-byte aligned");
-    const uint64_t Q = (uint64_t)t * (k + 1);
-    if (Q * L->inter * 2 > 0xffffffffull || (uint64_t)t * L->hidden * 2 > 0xffffffffull)
-        return fail(MOE_ERR_CAPACITY, "fused: t*(k+1)*inter or t*hidden too large for 32-bit offsets");
-    Workspace w;
-    workspace_plan(t, k, E, L, Ls, &w);
-    if (workspace_bytes < w.total)
-        return fail(MOE_ERR_WORKSPACE, "fused: workspace %zu bytes < %zu needed", workspace_bytes, w.total);
+    if (!offsets || !csr_rows || !csr_w || !csr_pos) return fail(MOE_ERR_INVALID, "fused: null pointer");
+    if (moe_status st = check_fused(x, t, k, E, L, records, Ls, shared_record, out, workspace, workspace_bytes, "fused"))
+        return st;
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    float *g = reinterpret_cast<float *>(ws + w.gate);
-    hipError_t e;
-    if (shared_gate_w) {
-        e = launch_shared_gate(x, shared_gate_w, t, L->hidden, g, s);
-        if (e != hipSuccess) return hip_fail(e, "shared gate");
-    }
-    const int P = t * k;
-    GemmArgs a;
-    std::memset(&a, 0, sizeof a);
-    a.x = x;
-    a.rows = csr_rows;
-    a.records = records;
-    a.sched_n = reinterpret_cast<uint32_t *>(ws + w.sched_n);
-    a.order = reinterpret_cast<TileEntry *>(ws + w.order);
-    a.xcap = (int)(Q / kMinBM + (size_t)E + 2);
-    a.t = t;
-    a.hidden = L->hidden;
-    a.inter = L->inter;
-    a.group = L->group;
-    a.hg = reinterpret_cast<uint16_t *>(ws + w.hg);
-    a.ye = reinterpret_cast<uint16_t *>(ws + w.ye);
-    a.shared_rows = 1;
-    a.shared_p0 = P;
+    Workspace w;
+    workspace_plan(t, k, E, L, Ls, &w);
+    GemmArgs a = fused_args(x, t, k, E, L, csr_rows, records, ws, w, true);
     const int bm = pick_bm(t, k, E, L->inter, L->hidden);
-    a.max_tiles = (int)(Q / bm + (size_t)E + 2);
-    e = launch_schedule(offsets, 0, E, bm, records, const_cast<uint32_t *>(a.sched_n),
-                        const_cast<TileEntry *>(a.order), a.xcap, s, SharedSeg{shared_record, P, t});
+    if (moe_status st = shared_gate(x, t, L, shared_gate_w, ws + w.gate, s)) return st;
+    hipError_t e = launch_schedule(offsets, 0, E, bm, records, const_cast<uint32_t *>(a.sched_n),
+                                   const_cast<TileEntry *>(a.order), a.xcap, s,
+                                   SharedSeg{shared_record, a.shared_p0, t});
     if (e != hipSuccess) return hip_fail(e, "schedule");
-    a.w_off = L->gate_w;
-    a.sb_off = L->gate_sb;
-    a.w2_off = L->up_w;
-    a.sb2_off = L->up_sb;
-    e = launch_gateup(a, bm, s);
-    if (e != hipSuccess) return hip_fail(e, "experts gate/up");
-    a.act = a.hg;
-    a.w_off = L->down_w;
-    a.sb_off = L->down_sb;
-    e = launch_down(a, bm, s);
-    if (e != hipSuccess) return hip_fail(e, "experts down");
-    e = launch_combine(a.ye, csr_pos, csr_w, t, k, L->hidden, out, accumulate, s, a.ye + (size_t)P * L->hidden,
-                       shared_gate_w ? g : nullptr);
-    if (e != hipSuccess) return hip_fail(e, "combine");
-    return MOE_OK;
+    return fused_gemms(a, bm, L, t, k, E, csr_pos, csr_w, out, accumulate,
+                       shared_gate_w ? reinterpret_cast<float *>(ws + w.gate) : nullptr, true, s);
+}
+
+moe_status moe_block(const uint16_t *x, const float *w_router, int32_t t, int32_t k, int32_t E,
+                     const moe_layout *L, const uint64_t *records, const moe_layout *Ls,
+                     const void *shared_record, const uint16_t *shared_gate_w, float *logits,
+                     uint32_t *topk_idx, float *topk_w, uint32_t *offsets, uint32_t *csr_rows,
+                     float *csr_w, uint32_t *csr_pos, float *out, int32_t accumulate, void *workspace,
+                     size_t workspace_bytes, void *stream) {
+    if (moe_status st = check_routing(t, k, E)) return st;
+    if (!w_router || !logits || !topk_idx || !topk_w || !offsets || !csr_rows || !csr_w || !csr_pos)
+        return fail(MOE_ERR_INVALID, "block: null pointer");
+    if (!aligned16(w_router)) return fail(MOE_ERR_INVALID, "block: w_router must be 16-byte aligned");
+    const bool shared = Ls != nullptr;
+    if (moe_status st = check_fused(x, t, k, E, L, records, Ls, shared_record, out, workspace, workspace_bytes, "block"))
+        return st;
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Workspace w;
+    workspace_plan(t, k, E, L, Ls, &w);
+    const int h = L->hidden;
+    hipError_t e = launch_router_logits(x, w_router, t, h, E, logits, s);
+    if (e != hipSuccess) return hip_fail(e, "router logits");
+    e = launch_topk(logits, t, E, k, topk_idx, topk_w, s);
+    if (e != hipSuccess) return hip_fail(e, "top-k");
+    if (shared)
+        if (moe_status st = shared_gate(x, t, L, shared_gate_w, ws + w.gate, s)) return st;
+    GemmArgs a = fused_args(x, t, k, E, L, csr_rows, records, ws, w, shared);
+    const int bm = pick_bm(t, k, E, L->inter, L->hidden);
+    const SharedSeg sh{shared ? shared_record : nullptr, a.shared_p0, shared ? t : 0};
+    if (csr_schedule_fits(t)) {
+        e = launch_csr_schedule(topk_idx, topk_w, t, k, E, offsets, csr_rows, csr_w, csr_pos, bm, records,
+                                const_cast<uint32_t *>(a.sched_n), const_cast<TileEntry *>(a.order), a.xcap, sh, s);
+        if (e != hipSuccess) return hip_fail(e, "grouping and schedule");
+    } else {
+        e = launch_csr(topk_idx, topk_w, t, k, E, offsets, csr_rows, csr_w, csr_pos,
+                       reinterpret_cast<uint32_t *>(ws + w.csr_hist), s);
+        if (e != hipSuccess) return hip_fail(e, "build_csr");
+        e = launch_schedule(offsets, 0, E, bm, records, const_cast<uint32_t *>(a.sched_n),
+                            const_cast<TileEntry *>(a.order), a.xcap, s, sh);
+        if (e != hipSuccess) return hip_fail(e, "schedule");
+    }
+    return fused_gemms(a, bm, L, t, k, E, csr_pos, csr_w, out, accumulate,
+                       (shared && shared_gate_w) ? reinterpret_cast<float *>(ws + w.gate) : nullptr, shared, s);
 }
 
 }  // extern "C"

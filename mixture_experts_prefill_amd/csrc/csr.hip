@@ -152,12 +152,14 @@ __global__ void __launch_bounds__(256) k_csr_place(const uint32_t *__restrict__ 
 // chunk, t = 512: 13.7 -> 10.4 us; 96 KB of LDS).  Thread e
 // owns expert e (E <= 1024).
 constexpr int kCsrSmallTiles = 8;
-__global__ void __launch_bounds__(1024) k_csr_small(const uint32_t *__restrict__ idx,
-                                                    const float *__restrict__ wts, int t, int k, int E,
-                                                    uint32_t *__restrict__ offsets,
-                                                    uint32_t *__restrict__ rows,
-                                                    float *__restrict__ csr_w,
-                                                    uint32_t *__restrict__ pos) {
+// The body, also run by k_csr_schedule; `soff` (LDS, or nullptr) receives a
+// copy of the offsets for the caller's next phase.
+__device__ __forceinline__ void csr_small_body(const uint32_t *__restrict__ idx,
+                                               const float *__restrict__ wts, int t, int k, int E,
+                                               uint32_t *__restrict__ offsets,
+                                               uint32_t *__restrict__ rows,
+                                               float *__restrict__ csr_w,
+                                               uint32_t *__restrict__ pos, uint32_t *soff) {
     __shared__ unsigned long long mask[kCsrSmallTiles][MOE_MAX_EXPERTS];
     __shared__ uint32_t base[kCsrSmallTiles][MOE_MAX_EXPERTS];
     __shared__ uint32_t wsum[16];
@@ -182,6 +184,7 @@ __global__ void __launch_bounds__(1024) k_csr_small(const uint32_t *__restrict__
     const uint32_t start = block_scan_1024(tot, wsum, &all) - tot;
     if (tid < E) {
         offsets[tid] = start;
+        if (soff) soff[tid] = start;
         uint32_t b = start;
 #pragma unroll
         for (int j = 0; j < kCsrSmallTiles; ++j) {
@@ -189,7 +192,10 @@ __global__ void __launch_bounds__(1024) k_csr_small(const uint32_t *__restrict__
             b += cnt[j];
         }
     }
-    if (tid == 0) offsets[E] = (uint32_t)(t * k);
+    if (tid == 0) {
+        offsets[E] = (uint32_t)(t * k);
+        if (soff) soff[E] = (uint32_t)(t * k);
+    }
     __syncthreads();
     for (int i = tid; i < t * k; i += 1024) {
         const int r = i / k, tile = r / TR, rr = r % TR;
@@ -201,6 +207,15 @@ __global__ void __launch_bounds__(1024) k_csr_small(const uint32_t *__restrict__
         csr_w[p] = wts[i];
         pos[i] = p;
     }
+}
+
+__global__ void __launch_bounds__(1024) k_csr_small(const uint32_t *__restrict__ idx,
+                                                    const float *__restrict__ wts, int t, int k, int E,
+                                                    uint32_t *__restrict__ offsets,
+                                                    uint32_t *__restrict__ rows,
+                                                    float *__restrict__ csr_w,
+                                                    uint32_t *__restrict__ pos) {
+    csr_small_body(idx, wts, t, k, E, offsets, rows, csr_w, pos, nullptr);
 }
 
 // One workgroup builds the M-tile schedule of experts [e0, e1):
@@ -215,20 +230,20 @@ __global__ void __launch_bounds__(1024) k_csr_small(const uint32_t *__restrict__
 //   4. every listed tile is written as a TileEntry (rows, expert, record
 //      address) to order[x * xcap + j].
 // sched_n[kSchedXcnt + x] is the number of tiles of XCD x, sched_n[0] the total.
-__global__ void __launch_bounds__(1024) k_schedule(const uint32_t *__restrict__ offsets, int e0,
-                                                   int e1, int bm, const uint64_t *__restrict__ records,
-                                                   uint32_t *__restrict__ sched_n,
-                                                   TileEntry *__restrict__ order, int xcap,
-                                                   SharedSeg sh) {
+template <int MAXT>
+__device__ __forceinline__ void schedule_body(const uint32_t *offsets, int e0, int e1, int bm,
+                                              const uint64_t *__restrict__ records,
+                                              uint32_t *__restrict__ sched_n,
+                                              TileEntry *__restrict__ order, int xcap, SharedSeg sh) {
     __shared__ uint32_t wsum[16];
-    __shared__ uint32_t tp0[kSchedMaxTiles];   // first CSR position of each tile
-    __shared__ uint16_t tex[kSchedMaxTiles];   // expert of each tile
-    __shared__ uint8_t tbl[kSchedMaxTiles];    // token blocks (32 rows) of each tile
-    __shared__ uint8_t trows[kSchedMaxTiles];  // rows of each tile - 1
-    __shared__ uint8_t xof[kSchedMaxTiles];    // XCD of each tile
-    __shared__ uint8_t tin[kSchedMaxTiles];    // index of the tile within its expert
-    __shared__ uint8_t tne[kSchedMaxTiles];    // tiles of its expert
-    __shared__ uint16_t perm[kSchedMaxTiles];  // listing position -> tile
+    __shared__ uint32_t tp0[MAXT];   // first CSR position of each tile
+    __shared__ uint16_t tex[MAXT];   // expert of each tile
+    __shared__ uint8_t tbl[MAXT];    // token blocks (32 rows) of each tile
+    __shared__ uint8_t trows[MAXT];  // rows of each tile - 1
+    __shared__ uint8_t xof[MAXT];    // XCD of each tile
+    __shared__ uint8_t tin[MAXT];    // index of the tile within its expert
+    __shared__ uint8_t tne[MAXT];    // tiles of its expert
+    __shared__ uint16_t perm[MAXT];  // listing position -> tile
     __shared__ uint64_t erec[MOE_MAX_EXPERTS + 1]; // record address of each expert (+ shared)
     __shared__ uint32_t xstart[9];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -332,6 +347,36 @@ __global__ void __launch_bounds__(1024) k_schedule(const uint32_t *__restrict__ 
     if (tid == 0) sched_n[0] = T;
 }
 
+__global__ void __launch_bounds__(1024) k_schedule(const uint32_t *__restrict__ offsets, int e0,
+                                                   int e1, int bm, const uint64_t *__restrict__ records,
+                                                   uint32_t *__restrict__ sched_n,
+                                                   TileEntry *__restrict__ order, int xcap,
+                                                   SharedSeg sh) {
+    schedule_body<kSchedMaxTiles>(offsets, e0, e1, bm, records, sched_n, order, xcap, sh);
+}
+
+// Chunks of up to kCsrSmallTiles * 64 rows: grouping and schedule in one
+// workgroup and one launch (the offsets pass from one phase to the next in
+// LDS); the schedule's tile arrays are sized for such chunks.
+constexpr int kSchedSmallTiles = 2048;
+static_assert(kCsrSmallTiles * 64 * MOE_MAX_K / kMinBM + MOE_MAX_EXPERTS + kCsrSmallTiles * 64 / kMinBM + 2 <=
+                  kSchedSmallTiles, "tiles of a small chunk");
+__global__ void __launch_bounds__(1024) k_csr_schedule(const uint32_t *__restrict__ idx,
+                                                       const float *__restrict__ wts, int t, int k, int E,
+                                                       uint32_t *__restrict__ offsets,
+                                                       uint32_t *__restrict__ rows,
+                                                       float *__restrict__ csr_w,
+                                                       uint32_t *__restrict__ pos, int bm,
+                                                       const uint64_t *__restrict__ records,
+                                                       uint32_t *__restrict__ sched_n,
+                                                       TileEntry *__restrict__ order, int xcap,
+                                                       SharedSeg sh) {
+    __shared__ uint32_t soff[MOE_MAX_EXPERTS + 1];
+    csr_small_body(idx, wts, t, k, E, offsets, rows, csr_w, pos, soff);
+    __syncthreads();
+    schedule_body<kSchedSmallTiles>(soff, 0, E, bm, records, sched_n, order, xcap, sh);
+}
+
 }  // namespace
 
 hipError_t launch_csr(const uint32_t *idx, const float *wts, int t, int k, int E,
@@ -347,6 +392,17 @@ hipError_t launch_csr(const uint32_t *idx, const float *wts, int t, int k, int E
     hipLaunchKernelGGL(k_csr_scan, dim3(1), dim3(1024), 0, s, tiles, E, t * k, hist, offsets);
     hipLaunchKernelGGL(k_csr_place, dim3(tiles), dim3(256), 0, s, idx, wts, t, k, E, hist, rows,
                        csr_w, pos);
+    return hipGetLastError();
+}
+
+bool csr_schedule_fits(int t) { return (t + TR - 1) / TR <= kCsrSmallTiles; }
+
+hipError_t launch_csr_schedule(const uint32_t *idx, const float *wts, int t, int k, int E, uint32_t *offsets,
+                               uint32_t *rows, float *csr_w, uint32_t *pos, int bm, const uint64_t *records,
+                               uint32_t *sched_n, TileEntry *order, int xcap, SharedSeg sh, hipStream_t s) {
+    ProfileScope prof(MOE_PHASE_CSR, s);
+    hipLaunchKernelGGL(k_csr_schedule, dim3(1), dim3(1024), 0, s, idx, wts, t, k, E, offsets, rows, csr_w, pos, bm,
+                       records, sched_n, order, xcap, sh);
     return hipGetLastError();
 }
 

@@ -76,6 +76,13 @@ hipError_t launch_schedule(const uint32_t *offsets, int e0, int e1, int bm, cons
                            uint32_t *sched_n, TileEntry *order, int xcap, hipStream_t s,
                            SharedSeg sh = SharedSeg{nullptr, 0, 0});
 
+// Grouping and schedule in one workgroup and one launch, for chunks whose
+// CSR fits the one-workgroup path (csr_schedule_fits).
+bool csr_schedule_fits(int t);
+hipError_t launch_csr_schedule(const uint32_t *idx, const float *wts, int t, int k, int E, uint32_t *offsets,
+                               uint32_t *rows, float *csr_w, uint32_t *pos, int bm, const uint64_t *records,
+                               uint32_t *sched_n, TileEntry *order, int xcap, SharedSeg sh, hipStream_t s);
+
 struct GemmArgs {
     // B-operand rows (tokens): x rows gathered through `rows` (routed gate/up),
     // identity rows (shared gate/up), or consecutive rows of `act` (down).

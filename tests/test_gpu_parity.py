@@ -38,19 +38,20 @@ def mep():
     return m
 
 
-def run(mep, wl, resident=None, ring_slots=64, group=8, shared=True, force_ring=False, fused=None):
-    """One block; `fused` None takes forward()'s default (the shared expert
-    inside the routed launches whenever its layout allows), False the separate
-    moe_shared + moe_prefill_experts calls."""
+def run(mep, wl, resident=None, ring_slots=64, group=8, shared=True, force_ring=False, path=None):
+    """One block; `path` None takes forward()'s default (moe_block whenever
+    every expert is resident), else "block", "fused" (moe_route,
+    moe_build_csr, moe_prefill_fused) or "separate" (moe_shared +
+    moe_prefill_experts)."""
     blk = mep.MoeBlock.from_workload(wl, resident=resident, ring_slots=ring_slots, group=group, shared=shared)
     if force_ring:
         blk.use_ring(ring_slots, group)
-    if fused:
+    if path == "fused":
         assert blk.can_fuse
     # NaN bytes in every intermediate: a GEMM tile or feature block that the
     # schedule skipped would leave NaN rows in the output.
     blk.workspace.fill_(0xFF)
-    blk.forward(fused=fused)
+    blk.forward(path=path)
     torch.cuda.synchronize()
     g = dict(
         topk_idx=blk.topk_idx.cpu().numpy().view(np.uint32),
@@ -88,15 +89,14 @@ def check_out(got, ref):
 
 # ------------------------------------------------------------------ small shapes, full oracle
 
-PATHS = [True, False]
-PATH_IDS = ["fused", "separate"]
+PATHS = ["block", "fused", "separate"]
 
 
-@pytest.mark.parametrize("fused", PATHS, ids=PATH_IDS)
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("centred", [False, True])
-def test_tiny_config(mep, orc, centred, fused):
+def test_tiny_config(mep, orc, centred, path):
     wl = ms.make_workload("tiny", centred=centred)
-    g = run(mep, wl, fused=fused)
+    g = run(mep, wl, path=path)
     r = orc.block(wl)
     check_routing(g, r)
     check_out(g["out"], r["out"])
@@ -127,12 +127,12 @@ SWEEP = [
 ]
 
 
-@pytest.mark.parametrize("fused", PATHS, ids=PATH_IDS)
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("case", SWEEP, ids=[f"s{c[0]}-t{c[1]}-h{c[2]}-I{c[3]}-E{c[4]}-k{c[5]}" for c in SWEEP])
-def test_small_sweep(mep, orc, case, fused):
+def test_small_sweep(mep, orc, case, path):
     seed, t, h, I, E, k, G, centred, gate = case
     wl = ms.small_case(seed, t, h, I, E, k, G, centred=centred, with_gate=gate)
-    g = run(mep, wl, fused=fused)
+    g = run(mep, wl, path=path)
     r = orc.block(wl)
     check_routing(g, r)
     check_out(g["out"], r["out"])
@@ -155,14 +155,14 @@ def random_cases(n, seed=7):
 RANDOM = random_cases(12)
 
 
-@pytest.mark.parametrize("fused", PATHS, ids=PATH_IDS)
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("case", RANDOM, ids=[f"r{c[0]}-t{c[1]}-h{c[2]}-I{c[3]}-E{c[4]}-k{c[5]}-G{c[6]}" for c in RANDOM])
-def test_random_shapes(mep, orc, case, fused):
+def test_random_shapes(mep, orc, case, path):
     """Seeded random shapes (row counts around the tile and CSR-tile edges,
-    any E and k, both group sizes, gated or not) on both paths."""
+    any E and k, both group sizes, gated or not) on every path."""
     seed, t, h, I, E, k, G, centred, gate = case
     wl = ms.small_case(seed, t, h, I, E, k, G, centred=centred, with_gate=gate)
-    g = run(mep, wl, fused=fused)
+    g = run(mep, wl, path=path)
     r = orc.block(wl)
     check_routing(g, r)
     check_out(g["out"], r["out"])
@@ -186,8 +186,8 @@ def test_fused_matches_separate(mep):
     """The two paths add the same terms in the same order; they differ only in
     the shared expert's output being rounded to bf16 on the fused path."""
     wl = ms.small_case(20, 150, 512, 128, 24, 4, 64, centred=True, with_gate=True)
-    a = run(mep, wl, fused=True)
-    b = run(mep, wl, fused=False)
+    a = run(mep, wl, path="fused")
+    b = run(mep, wl, path="separate")
     for key in ("topk_idx", "offsets", "csr_rows", "csr_pos"):
         assert np.array_equal(a[key], b[key]), key
     check_out(a["out"], b["out"].astype(np.float64))
@@ -227,21 +227,21 @@ def test_no_shared_expert(mep, orc):
 
 # ------------------------------------------------------------------ the five workloads
 
-@pytest.mark.parametrize("fused", PATHS, ids=PATH_IDS)
-def test_mid_config(mep, orc, fused):
+@pytest.mark.parametrize("path", PATHS)
+def test_mid_config(mep, orc, path):
     wl = ms.make_workload("mid")
-    g = run(mep, wl, fused=fused)
+    g = run(mep, wl, path=path)
     say("  oracle mid ...")
     r = orc.block(wl)
     check_routing(g, r)
     check_out(g["out"], r["out"])
 
 
-@pytest.mark.parametrize("fused", PATHS, ids=PATH_IDS)
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("name", ["decode", "decode1"])
-def test_decode_configs(mep, orc, name, fused):
+def test_decode_configs(mep, orc, name, path):
     wl = ms.make_workload(name)
-    g = run(mep, wl, fused=fused)
+    g = run(mep, wl, path=path)
     say(f"  oracle {name} ...")
     r = orc.block(wl)
     check_routing(g, r)
@@ -260,10 +260,10 @@ def full_routing_ref(orc, wl):
     return dict(topk_idx=idx, topk_w=w, offsets=offsets, csr_rows=rows, csr_w=cw, csr_pos=pos)
 
 
-@pytest.mark.parametrize("fused", PATHS, ids=PATH_IDS)
-def test_full_config(mep, orc, fused):
+@pytest.mark.parametrize("path", PATHS)
+def test_full_config(mep, orc, path):
     wl = ms.make_workload("full")
-    g = run(mep, wl, fused=fused)
+    g = run(mep, wl, path=path)
     say("  oracle routing full ...")
     r = full_routing_ref(orc, wl)
     check_routing(g, r)
@@ -284,7 +284,7 @@ def test_large_config_streamed(mep, orc):
     st = g["ring_stats"]
     n_streamed = int(((np.diff(r["offsets"].astype(np.int64)) > 0) & ~resident).sum())
     assert st["streamed"] == n_streamed and st["fetched_bytes"] == n_streamed * wl.layout.stride
-    g_res = run(mep, wl, fused=False)
+    g_res = run(mep, wl, path="separate")
     assert np.array_equal(g["out"], g_res["out"]), "ring output differs from all-resident output"
     s = sample_rows(wl.cfg.t, 10, 2)
     say(f"  oracle brute force on {s.size} rows ...")
@@ -297,7 +297,7 @@ def test_large_config_streamed(mep, orc):
 def test_ring_equals_resident_with_poison(mep, monkeypatch):
     """A small ring (4 slots, batches of 2) with released slots poisoned must not change a bit."""
     wl = ms.make_workload("mid")
-    base = run(mep, wl, fused=False)
+    base = run(mep, wl, path="separate")
     resident = np.zeros(wl.cfg.experts, dtype=bool)
     resident[::5] = True
     monkeypatch.setenv("MOE_RING_POISON", "1")
@@ -311,16 +311,16 @@ def test_ring_equals_resident_with_poison(mep, monkeypatch):
 
 def test_ring_with_everything_resident(mep):
     wl = ms.make_workload("tiny")
-    a = run(mep, wl, fused=False)
+    a = run(mep, wl, path="separate")
     b = run(mep, wl, force_ring=True, ring_slots=2, group=1)
     assert np.array_equal(a["out"], b["out"])
 
 
-@pytest.mark.parametrize("fused", PATHS, ids=PATH_IDS)
-def test_deterministic(mep, fused):
+@pytest.mark.parametrize("path", PATHS)
+def test_deterministic(mep, path):
     wl = ms.small_case(11, 200, 512, 128, 16, 4, 64, centred=True)
-    a = run(mep, wl, fused=fused)
-    b = run(mep, wl, fused=fused)
+    a = run(mep, wl, path=path)
+    b = run(mep, wl, path=path)
     for key in ("topk_idx", "topk_w", "offsets", "csr_rows", "csr_w", "csr_pos", "out"):
         assert np.array_equal(a[key], b[key]), key
 
@@ -341,6 +341,15 @@ def test_fused_accumulate(mep, orc):
     check_out(first, r["out"])
     blk.out.fill_(1.0)
     blk.fused(accumulate=1)
+    torch.cuda.synchronize()
+    check_out(blk.out.cpu().numpy(), r["out"] + 1.0)
+    # the one-call block, same semantics
+    blk.out.fill_(float("nan"))
+    blk.block(accumulate=0)
+    torch.cuda.synchronize()
+    check_out(blk.out.cpu().numpy(), r["out"])
+    blk.out.fill_(1.0)
+    blk.block(accumulate=1)
     torch.cuda.synchronize()
     check_out(blk.out.cpu().numpy(), r["out"] + 1.0)
 
@@ -420,10 +429,10 @@ def test_bad_arguments_leave_outputs_untouched(mep):
 def test_missing_record_does_not_fault(mep):
     """A used expert whose record address is 0 (and no ring) is never
     dereferenced: its entries get unspecified values, every other row is
-    unchanged, on both paths."""
+    unchanged, on every path."""
     wl = ms.small_case(24, 64, 256, 128, 8, 2, 64, centred=True)
-    for fused in (True, False):
-        ref = run(mep, wl, fused=fused)
+    for path in PATHS:
+        ref = run(mep, wl, path=path)
         blk = mep.MoeBlock.from_workload(wl)
         blk.workspace.fill_(0xFF)
         blk.route()
@@ -432,7 +441,9 @@ def test_missing_record_does_not_fault(mep):
         table = blk.table.clone()
         table[3] = 0
         blk.table = table
-        if fused:
+        if path == "block":
+            blk.block(accumulate=0)
+        elif path == "fused":
             blk.fused(accumulate=0)
         else:
             blk.shared(accumulate=0)

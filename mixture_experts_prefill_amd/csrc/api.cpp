@@ -472,14 +472,22 @@ moe_status moe_block(const uint16_t *x, const float *w_router, int32_t t, int32_
     const int h = L->hidden;
     hipError_t e = launch_router_logits(x, w_router, t, h, E, logits, s);
     if (e != hipSuccess) return hip_fail(e, "router logits");
-    e = launch_topk(logits, t, E, k, topk_idx, topk_w, s);
-    if (e != hipSuccess) return hip_fail(e, "top-k");
+    const bool merged_topk = topk_csr_schedule_fits(t);
+    if (!merged_topk) {
+        e = launch_topk(logits, t, E, k, topk_idx, topk_w, s);
+        if (e != hipSuccess) return hip_fail(e, "top-k");
+    }
     if (shared)
         if (moe_status st = shared_gate(x, t, L, shared_gate_w, ws + w.gate, s)) return st;
     GemmArgs a = fused_args(x, t, k, E, L, csr_rows, records, ws, w, shared);
     const int bm = pick_bm(t, k, E, L->inter, L->hidden);
     const SharedSeg sh{shared ? shared_record : nullptr, a.shared_p0, shared ? t : 0};
-    if (csr_schedule_fits(t)) {
+    if (merged_topk) {
+        e = launch_topk_csr_schedule(logits, t, E, k, topk_idx, topk_w, offsets, csr_rows, csr_w, csr_pos, bm,
+                                     records, const_cast<uint32_t *>(a.sched_n), const_cast<TileEntry *>(a.order),
+                                     a.xcap, sh, s);
+        if (e != hipSuccess) return hip_fail(e, "top-k, grouping and schedule");
+    } else if (csr_schedule_fits(t)) {
         e = launch_csr_schedule(topk_idx, topk_w, t, k, E, offsets, csr_rows, csr_w, csr_pos, bm, records,
                                 const_cast<uint32_t *>(a.sched_n), const_cast<TileEntry *>(a.order), a.xcap, sh, s);
         if (e != hipSuccess) return hip_fail(e, "grouping and schedule");

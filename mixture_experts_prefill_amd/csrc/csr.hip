@@ -13,6 +13,7 @@
 // A row's k experts are distinct, so "earlier entries of expert e" are the
 // entries of earlier rows: the placement is the stable order of the pages.
 #include "moe_internal.h"
+#include "topk_row.h"
 
 namespace moe {
 namespace {
@@ -377,6 +378,28 @@ __global__ void __launch_bounds__(1024) k_csr_schedule(const uint32_t *__restric
     schedule_body<kSchedSmallTiles>(soff, 0, E, bm, records, sched_n, order, xcap, sh);
 }
 
+// Decode-sized chunks (t <= 16): the top-k of each row (one wave per row),
+// then grouping and schedule, in one workgroup and one launch.
+template <int KPL>
+__global__ void __launch_bounds__(1024) k_topk_csr_schedule(const float *__restrict__ logits, int t, int E, int k,
+                                                            uint32_t *__restrict__ idx, float *__restrict__ wts,
+                                                            uint32_t *__restrict__ offsets,
+                                                            uint32_t *__restrict__ rows,
+                                                            float *__restrict__ csr_w,
+                                                            uint32_t *__restrict__ pos, int bm,
+                                                            const uint64_t *__restrict__ records,
+                                                            uint32_t *__restrict__ sched_n,
+                                                            TileEntry *__restrict__ order, int xcap,
+                                                            SharedSeg sh) {
+    __shared__ uint32_t soff[MOE_MAX_EXPERTS + 1];
+    const int wave = threadIdx.x >> 6;
+    if (wave < t) topk_row<KPL>(logits, wave, E, k, idx, wts);
+    __syncthreads();   // the rows' top-k (global memory) is visible to the whole workgroup
+    csr_small_body(idx, wts, t, k, E, offsets, rows, csr_w, pos, soff);
+    __syncthreads();
+    schedule_body<kSchedSmallTiles>(soff, 0, E, bm, records, sched_n, order, xcap, sh);
+}
+
 }  // namespace
 
 hipError_t launch_csr(const uint32_t *idx, const float *wts, int t, int k, int E,
@@ -396,6 +419,24 @@ hipError_t launch_csr(const uint32_t *idx, const float *wts, int t, int k, int E
 }
 
 bool csr_schedule_fits(int t) { return (t + TR - 1) / TR <= kCsrSmallTiles; }
+bool topk_csr_schedule_fits(int t) { return t <= 16; }
+
+hipError_t launch_topk_csr_schedule(const float *logits, int t, int E, int k, uint32_t *idx, float *wts,
+                                    uint32_t *offsets, uint32_t *rows, float *csr_w, uint32_t *pos, int bm,
+                                    const uint64_t *records, uint32_t *sched_n, TileEntry *order, int xcap,
+                                    SharedSeg sh, hipStream_t s) {
+    ProfileScope prof(MOE_PHASE_CSR, s);
+#define MOE_TCS(KPL)                                                                                            \
+    hipLaunchKernelGGL(k_topk_csr_schedule<KPL>, dim3(1), dim3(1024), 0, s, logits, t, E, k, idx, wts, offsets, \
+                       rows, csr_w, pos, bm, records, sched_n, order, xcap, sh)
+    if (E <= 64) MOE_TCS(1);
+    else if (E <= 128) MOE_TCS(2);
+    else if (E <= 256) MOE_TCS(4);
+    else if (E <= 512) MOE_TCS(8);
+    else MOE_TCS(MOE_MAX_EXPERTS / 64);
+#undef MOE_TCS
+    return hipGetLastError();
+}
 
 hipError_t launch_csr_schedule(const uint32_t *idx, const float *wts, int t, int k, int E, uint32_t *offsets,
                                uint32_t *rows, float *csr_w, uint32_t *pos, int bm, const uint64_t *records,

@@ -1,7 +1,8 @@
 """Benchmark of the routed-expert MoE prefill block on one MI355X.
 
-One step = one whole block over one chunk: moe_shared -> moe_route ->
-moe_build_csr -> moe_prefill_experts, on inputs already resident in HBM.
+One step = one whole block over one chunk, on inputs already resident in
+HBM: moe_block (routing, grouping, routed and shared experts in one call), or
+with --separate moe_shared -> moe_route -> moe_build_csr -> moe_prefill_experts.
 Default workload: the full prefill chunk (t = 4096 rows, hidden 2048, expert
 inter 768, 128 experts, top-8, shared expert inter 768, 4-bit group-64
 weights, Zipf(1.1) expert popularity).  Prints one JSON line.

@@ -492,12 +492,11 @@ moe_status moe_block(const uint16_t *x, const float *w_router, int32_t t, int32_
                                 const_cast<uint32_t *>(a.sched_n), const_cast<TileEntry *>(a.order), a.xcap, sh, s);
         if (e != hipSuccess) return hip_fail(e, "grouping and schedule");
     } else {
-        e = launch_csr(topk_idx, topk_w, t, k, E, offsets, csr_rows, csr_w, csr_pos,
-                       reinterpret_cast<uint32_t *>(ws + w.csr_hist), s);
-        if (e != hipSuccess) return hip_fail(e, "build_csr");
-        e = launch_schedule(offsets, 0, E, bm, records, const_cast<uint32_t *>(a.sched_n),
-                            const_cast<TileEntry *>(a.order), a.xcap, s, sh);
-        if (e != hipSuccess) return hip_fail(e, "schedule");
+        e = launch_csr_with_schedule(topk_idx, topk_w, t, k, E, offsets, csr_rows, csr_w, csr_pos,
+                                     reinterpret_cast<uint32_t *>(ws + w.csr_hist), bm, records,
+                                     const_cast<uint32_t *>(a.sched_n), const_cast<TileEntry *>(a.order), a.xcap,
+                                     sh, s);
+        if (e != hipSuccess) return hip_fail(e, "grouping and schedule");
     }
     return fused_gemms(a, bm, L, t, k, E, csr_pos, csr_w, out, accumulate,
                        (shared && shared_gate_w) ? reinterpret_cast<float *>(ws + w.gate) : nullptr, shared, s);

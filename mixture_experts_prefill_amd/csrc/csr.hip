@@ -71,9 +71,10 @@ __global__ void __launch_bounds__(256) k_csr_count(const uint32_t *__restrict__ 
 // every (expert, tile) entry becomes its absolute segment start.  With at most
 // 128 experts (one pass) the per-tile prefixes stay in registers; beyond
 // that they are re-read and re-scanned.
-__global__ void __launch_bounds__(1024) k_csr_scan(int tiles, int E, int total,
-                                                   uint32_t *__restrict__ hist,
-                                                   uint32_t *__restrict__ offsets) {
+// The body, also run by k_scan_schedule; `soff` (LDS, or nullptr) receives a
+// copy of the offsets for the caller's next phase.
+__device__ __forceinline__ void csr_scan_body(int tiles, int E, int total, uint32_t *__restrict__ hist,
+                                              uint32_t *__restrict__ offsets, uint32_t *soff) {
     __shared__ uint32_t tot[MOE_MAX_EXPERTS];
     __shared__ uint32_t wsum[16];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -104,8 +105,12 @@ __global__ void __launch_bounds__(1024) k_csr_scan(int tiles, int E, int total,
     if (tid < E) {
         tot[tid] = incl - mine;  // exclusive: segment start of expert tid
         offsets[tid] = incl - mine;
+        if (soff) soff[tid] = incl - mine;
     }
-    if (tid == 0) offsets[E] = (uint32_t)total;
+    if (tid == 0) {
+        offsets[E] = (uint32_t)total;
+        if (soff) soff[E] = (uint32_t)total;
+    }
     __syncthreads();
     const bool one_pass = E <= 16 * kPass;
     for (int e0 = wave * kPass; e0 < E; e0 += 16 * kPass) {
@@ -114,6 +119,12 @@ __global__ void __launch_bounds__(1024) k_csr_scan(int tiles, int E, int total,
         for (int j = 0; j < kPass; ++j)
             if (lane < tiles && e0 + j < E) hist[(size_t)(e0 + j) * tiles + lane] = tot[e0 + j] + ex[j];
     }
+}
+
+__global__ void __launch_bounds__(1024) k_csr_scan(int tiles, int E, int total,
+                                                   uint32_t *__restrict__ hist,
+                                                   uint32_t *__restrict__ offsets) {
+    csr_scan_body(tiles, E, total, hist, offsets, nullptr);
 }
 
 __global__ void __launch_bounds__(256) k_csr_place(const uint32_t *__restrict__ idx,
@@ -378,6 +389,19 @@ __global__ void __launch_bounds__(1024) k_csr_schedule(const uint32_t *__restric
     schedule_body<kSchedSmallTiles>(soff, 0, E, bm, records, sched_n, order, xcap, sh);
 }
 
+// Larger chunks: the scan of the per-tile counts and the schedule in one
+// workgroup and one launch (the placement follows in its own launch).
+__global__ void __launch_bounds__(1024) k_scan_schedule(int tiles, int E, int total, uint32_t *__restrict__ hist,
+                                                        uint32_t *__restrict__ offsets, int bm,
+                                                        const uint64_t *__restrict__ records,
+                                                        uint32_t *__restrict__ sched_n,
+                                                        TileEntry *__restrict__ order, int xcap, SharedSeg sh) {
+    __shared__ uint32_t soff[MOE_MAX_EXPERTS + 1];
+    csr_scan_body(tiles, E, total, hist, offsets, soff);
+    __syncthreads();
+    schedule_body<kSchedMaxTiles>(soff, 0, E, bm, records, sched_n, order, xcap, sh);
+}
+
 // Decode-sized chunks (t <= 16): the top-k of each row (one wave per row),
 // then grouping and schedule, in one workgroup and one launch.
 template <int KPL>
@@ -419,6 +443,19 @@ hipError_t launch_csr(const uint32_t *idx, const float *wts, int t, int k, int E
 }
 
 bool csr_schedule_fits(int t) { return (t + TR - 1) / TR <= kCsrSmallTiles; }
+
+hipError_t launch_csr_with_schedule(const uint32_t *idx, const float *wts, int t, int k, int E, uint32_t *offsets,
+                                    uint32_t *rows, float *csr_w, uint32_t *pos, uint32_t *hist, int bm,
+                                    const uint64_t *records, uint32_t *sched_n, TileEntry *order, int xcap,
+                                    SharedSeg sh, hipStream_t s) {
+    ProfileScope prof(MOE_PHASE_CSR, s);
+    const int tiles = (t + TR - 1) / TR;
+    hipLaunchKernelGGL(k_csr_count, dim3(tiles), dim3(256), 0, s, idx, t, k, E, hist);
+    hipLaunchKernelGGL(k_scan_schedule, dim3(1), dim3(1024), 0, s, tiles, E, t * k, hist, offsets, bm, records,
+                       sched_n, order, xcap, sh);
+    hipLaunchKernelGGL(k_csr_place, dim3(tiles), dim3(256), 0, s, idx, wts, t, k, E, hist, rows, csr_w, pos);
+    return hipGetLastError();
+}
 bool topk_csr_schedule_fits(int t) { return t <= 16; }
 
 hipError_t launch_topk_csr_schedule(const float *logits, int t, int E, int k, uint32_t *idx, float *wts,

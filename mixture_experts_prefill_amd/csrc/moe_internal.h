@@ -79,6 +79,11 @@ hipError_t launch_schedule(const uint32_t *offsets, int e0, int e1, int bm, cons
 // Grouping and schedule in one workgroup and one launch, for chunks whose
 // CSR fits the one-workgroup path (csr_schedule_fits).
 bool csr_schedule_fits(int t);
+// Larger chunks: count, then scan and schedule in one launch, then place.
+hipError_t launch_csr_with_schedule(const uint32_t *idx, const float *wts, int t, int k, int E, uint32_t *offsets,
+                                    uint32_t *rows, float *csr_w, uint32_t *pos, uint32_t *hist, int bm,
+                                    const uint64_t *records, uint32_t *sched_n, TileEntry *order, int xcap,
+                                    SharedSeg sh, hipStream_t s);
 // ... and, for decode-sized chunks, the top-k too (its own launch otherwise).
 bool topk_csr_schedule_fits(int t);
 hipError_t launch_topk_csr_schedule(const float *logits, int t, int E, int k, uint32_t *idx, float *wts,

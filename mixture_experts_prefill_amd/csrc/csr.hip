@@ -20,16 +20,31 @@ namespace {
 
 constexpr int TR = kCsrTileRows;
 
+// Inclusive scan over the 64 lanes of a wave with DPP moves only (no LDS
+// crossbar): row_shr 1, 2, 4, 8 scan each 16-lane row, then row_bcast 15
+// adds row 0's total to row 1 and row 2's to row 3, and row_bcast 31 adds
+// the total of rows 0-1 to rows 2-3.  Lanes whose DPP source is missing, and
+// rows outside a step's row mask, add 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_add_step(uint32_t v) {
+    return v + (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xf, false);
+}
+__device__ __forceinline__ uint32_t wave_scan_incl(uint32_t v) {
+    v = dpp_add_step<0x111, 0xf>(v);  // row_shr:1
+    v = dpp_add_step<0x112, 0xf>(v);  // row_shr:2
+    v = dpp_add_step<0x114, 0xf>(v);  // row_shr:4
+    v = dpp_add_step<0x118, 0xf>(v);  // row_shr:8
+    v = dpp_add_step<0x142, 0xa>(v);  // row_bcast:15 into rows 1, 3
+    v = dpp_add_step<0x143, 0xc>(v);  // row_bcast:31 into rows 2, 3
+    return v;
+}
+
 // Inclusive scan of one value per thread over a workgroup of 1024 threads
-// (16 waves): shuffle scan in each wave, then the wave totals.  `wsum` is
+// (16 waves): DPP scan in each wave, then the wave totals.  `wsum` is
 // 16 words of LDS.  Returns the inclusive prefix; *total gets the sum.
 __device__ __forceinline__ uint32_t block_scan_1024(uint32_t v, uint32_t *wsum, uint32_t *total) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t o = __shfl_up(v, d, 64);
-        if (lane >= d) v += o;
-    }
+    v = wave_scan_incl(v);
     if (lane == 63) wsum[wave] = v;
     __syncthreads();
     uint32_t before = 0, all = 0;
@@ -87,12 +102,7 @@ __device__ __forceinline__ void csr_scan_body(int tiles, int E, int total, uint3
             v[j] = (lane < tiles && e0 + j < E) ? hist[(size_t)(e0 + j) * tiles + lane] : 0u;
 #pragma unroll
         for (int j = 0; j < kPass; ++j) {
-            uint32_t incl = v[j];
-#pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                const uint32_t o = __shfl_up(incl, d, 64);
-                if (lane >= d) incl += o;
-            }
+            const uint32_t incl = wave_scan_incl(v[j]);
             ex[j] = incl - v[j];
             if (totals && e0 + j < E && lane == 63) tot[e0 + j] = incl;
         }

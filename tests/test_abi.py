@@ -210,3 +210,26 @@ def test_fused_validation(lib):
     rc = lib.moe_prefill_fused(P(FAKE), 4096, 31, 64, ctypes.byref(Lb), P(FAKE), P(FAKE), P(FAKE), P(FAKE),
                                P(FAKE), ctypes.byref(Lb), P(FAKE), None, P(FAKE), 0, P(FAKE), 1 << 40, None)
     assert rc == 2 and "32-bit" in lib.moe_last_error().decode()
+
+
+def test_block_validation(lib):
+    """moe_block validates like the separate calls, before anything is enqueued."""
+    L = mep.moe_layout_make(256, 128, 32)
+    Lo = mep.moe_layout_make(256, 192, 32)
+    need = mep.moe_workspace_bytes(16, 2, 8, L, L)
+
+    def call(t=16, k=2, E=8, Ls=L, ws=need, w_router=P(FAKE), rec=P(FAKE)):
+        return lib.moe_block(P(FAKE), w_router, t, k, E, ctypes.byref(L), P(FAKE),
+                             ctypes.byref(Ls) if Ls is not None else None, rec, None,
+                             P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE),
+                             P(FAKE), 0, P(FAKE), ws, None)
+
+    assert call(t=0) == 2 and "empty chunk" in lib.moe_last_error().decode()
+    assert call(k=9) == 1
+    assert call(Ls=Lo) == 1 and "must equal" in lib.moe_last_error().decode()
+    assert call(w_router=None) == 1
+    assert call(w_router=P(FAKE + 4)) == 1                 # misaligned router weights
+    assert call(rec=None) == 1                             # shared layout without a record
+    assert call(ws=need - 256) == 3
+    # without a shared expert the workspace of the routed experts alone suffices
+    assert call(Ls=None, rec=None, ws=mep.moe_workspace_bytes(16, 2, 8, L, None) - 256) == 3

@@ -152,9 +152,8 @@ static moe_status check_routing(int t, int k, int E) {
 static moe_status check_fused(const uint16_t *x, int t, int k, int E, const moe_layout *L,
                               const uint64_t *records, const moe_layout *Ls, const void *shared_record,
                               const float *out, const void *workspace, size_t workspace_bytes,
-                              const char *who) {
-    const bool block = who[0] == 'b';
-    if (!layout_ok(L) || (Ls && !layout_ok(Ls)) || (!Ls && !block))
+                              bool shared_optional, const char *who) {
+    if (!layout_ok(L) || (Ls && !layout_ok(Ls)) || (!Ls && !shared_optional))
         return fail(MOE_ERR_INVALID, "%s: layout not made by moe_layout_make", who);
     if (Ls && !fusable(L, Ls))
         return fail(MOE_ERR_INVALID, "%s: the shared layout (h %d, inter %d, group %d) must equal the routed one "
@@ -435,7 +434,8 @@ moe_status moe_prefill_fused(const uint16_t *x, int32_t t, int32_t k, int32_t E,
                              int32_t accumulate, void *workspace, size_t workspace_bytes, void *stream) {
     if (moe_status st = check_routing(t, k, E)) return st;
     if (!offsets || !csr_rows || !csr_w || !csr_pos) return fail(MOE_ERR_INVALID, "fused: null pointer");
-    if (moe_status st = check_fused(x, t, k, E, L, records, Ls, shared_record, out, workspace, workspace_bytes, "fused"))
+    if (moe_status st = check_fused(x, t, k, E, L, records, Ls, shared_record, out, workspace, workspace_bytes,
+                                    false, "fused"))
         return st;
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -463,7 +463,8 @@ moe_status moe_block(const uint16_t *x, const float *w_router, int32_t t, int32_
         return fail(MOE_ERR_INVALID, "block: null pointer");
     if (!aligned16(w_router)) return fail(MOE_ERR_INVALID, "block: w_router must be 16-byte aligned");
     const bool shared = Ls != nullptr;
-    if (moe_status st = check_fused(x, t, k, E, L, records, Ls, shared_record, out, workspace, workspace_bytes, "block"))
+    if (moe_status st = check_fused(x, t, k, E, L, records, Ls, shared_record, out, workspace, workspace_bytes,
+                                    true, "block"))
         return st;
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     hipStream_t s = static_cast<hipStream_t>(stream);

@@ -412,8 +412,11 @@ __global__ void __launch_bounds__(1024) k_scan_schedule(int tiles, int E, int to
     schedule_body<kSchedMaxTiles>(soff, 0, E, bm, records, sched_n, order, xcap, sh);
 }
 
+constexpr int kTopkCsrRows = 16;   // one wave per row in a 1024-thread workgroup
 // Decode-sized chunks (t <= 16): the top-k of each row (one wave per row),
-// then grouping and schedule, in one workgroup and one launch.
+// then grouping and schedule, in one workgroup and one launch.  The top-k
+// results pass to the grouping in LDS, and the experts' record addresses
+// are read while the top-k runs.
 template <int KPL>
 __global__ void __launch_bounds__(1024) k_topk_csr_schedule(const float *__restrict__ logits, int t, int E, int k,
                                                             uint32_t *__restrict__ idx, float *__restrict__ wts,
@@ -426,12 +429,18 @@ __global__ void __launch_bounds__(1024) k_topk_csr_schedule(const float *__restr
                                                             TileEntry *__restrict__ order, int xcap,
                                                             SharedSeg sh) {
     __shared__ uint32_t soff[MOE_MAX_EXPERTS + 1];
-    const int wave = threadIdx.x >> 6;
-    if (wave < t) topk_row<KPL>(logits, wave, E, k, idx, wts);
-    __syncthreads();   // the rows' top-k (global memory) is visible to the whole workgroup
-    csr_small_body(idx, wts, t, k, E, offsets, rows, csr_w, pos, soff);
+    __shared__ uint32_t sidx[kTopkCsrRows * MOE_MAX_K];
+    __shared__ float swts[kTopkCsrRows * MOE_MAX_K];
+    __shared__ uint64_t srec[MOE_MAX_EXPERTS];
+    const int tid = threadIdx.x, wave = tid >> 6;
+    // the record addresses load while the rows' top-k runs
+    const uint64_t rec = tid < E ? records[tid] : 0ull;
+    if (wave < t) topk_row<KPL>(logits, wave, E, k, idx, wts, sidx, swts);
+    if (tid < E) srec[tid] = rec;
     __syncthreads();
-    schedule_body<kSchedSmallTiles>(soff, 0, E, bm, records, sched_n, order, xcap, sh);
+    csr_small_body(sidx, swts, t, k, E, offsets, rows, csr_w, pos, soff);
+    __syncthreads();
+    schedule_body<kSchedSmallTiles>(soff, 0, E, bm, srec, sched_n, order, xcap, sh);
 }
 
 }  // namespace
@@ -466,7 +475,7 @@ hipError_t launch_csr_with_schedule(const uint32_t *idx, const float *wts, int t
     hipLaunchKernelGGL(k_csr_place, dim3(tiles), dim3(256), 0, s, idx, wts, t, k, E, hist, rows, csr_w, pos);
     return hipGetLastError();
 }
-bool topk_csr_schedule_fits(int t) { return t <= 16; }
+bool topk_csr_schedule_fits(int t) { return t <= kTopkCsrRows; }
 
 hipError_t launch_topk_csr_schedule(const float *logits, int t, int E, int k, uint32_t *idx, float *wts,
                                     uint32_t *offsets, uint32_t *rows, float *csr_w, uint32_t *pos, int bm,

@@ -138,6 +138,35 @@ def test_small_sweep(mep, orc, case, path):
     check_out(g["out"], r["out"])
 
 
+TIE_CASES = [(1, 64, 4), (8, 512, 10), (8, 1024, 16), (16, 130, 8), (100, 300, 12), (100, 128, 8), (600, 64, 6)]
+
+
+@pytest.mark.parametrize("path", ["block", "separate"])
+@pytest.mark.parametrize("kind", ["zero", "dup7"])
+@pytest.mark.parametrize("case", TIE_CASES, ids=[f"t{c[0]}-E{c[1]}-k{c[2]}" for c in TIE_CASES])
+def test_routing_ties(mep, orc, case, kind, path):
+    """Exactly equal logits: the selection order is logit descending, then
+    expert id ascending.  "zero": W_r = 0, every logit is +0 and the top-k is
+    experts 0..k-1 with weights 1/k.  "dup7": router row e repeats row e % 7,
+    so each row has 7 distinct logits, each held by about E/7 experts (ties
+    across lanes, and within a lane once E > 448)."""
+    import dataclasses
+
+    t, E, k = case
+    wl = ms.small_case(900 + E, t, 256, 64, E, k, 32)
+    if kind == "zero":
+        w = np.zeros_like(wl.w_router)
+    else:
+        w = np.ascontiguousarray(wl.w_router[np.arange(E) % 7])
+    wl = dataclasses.replace(wl, w_router=w)
+    g = run(mep, wl, path=path)
+    r = orc.block(wl)
+    check_routing(g, r)
+    if kind == "zero":
+        assert np.array_equal(g["topk_idx"], np.tile(np.arange(k, dtype=np.uint32), (t, 1)))
+    check_out(g["out"], r["out"])
+
+
 def random_cases(n, seed=7):
     rng = np.random.default_rng(seed)
     cases = []

@@ -29,15 +29,20 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# The dominant kernel's sources: the GEMM file and the headers it includes.
+KERNEL_SOURCES = ["mixture_experts_prefill_amd/csrc/gemm.hip", "mixture_experts_prefill_amd/csrc/moe_internal.h",
+                  "mixture_experts_prefill_amd/csrc/profile.h", "include/moe.h", "include/moe_debug.h"]
+
+
 def source_hash() -> str:
-    """Hash of the library's sources with comments and blank space removed, so
-    that counters stay attached to the code they were taken on, not its prose."""
+    """Hash of the dominant kernel's sources with comments and blank space
+    removed, so that its counters stay attached to the code they were taken
+    on, not to its prose or to the other kernels."""
     import re
 
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "mixture_experts_prefill_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
             text = fh.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
         text = re.sub(r"//[^\n]*", " ", text)

@@ -298,12 +298,13 @@ __device__ __forceinline__ void schedule_body(const uint32_t *offsets, int e0, i
         uint32_t p0, n;
         seg(le, p0, n);
         const uint32_t ne = (n + bm - 1) / bm;
-        for (uint32_t m = 0; m < n; m += bm, ++w) {
+        uint32_t m = 0;
+        for (uint32_t j = 0; j < ne; ++j, m += bm, ++w) {
             const uint32_t rows = min((uint32_t)bm, n - m);
             tp0[w] = p0 + m;
             tex[w] = (uint16_t)le;
             trows[w] = (uint8_t)(rows - 1);
-            tin[w] = (uint8_t)(m / bm);
+            tin[w] = (uint8_t)j;
             tne[w] = (uint8_t)ne;
             tbl[w] = (uint8_t)((rows + 31) / 32);
         }
@@ -339,16 +340,32 @@ __device__ __forceinline__ void schedule_body(const uint32_t *offsets, int e0, i
     // its tiles stream far more weight bytes than a routed tile.
     if (wave < 8) {
         const uint32_t s0 = xstart[wave], s1 = xstart[wave + 1];
+        auto cls_of = [&](uint32_t i) { return i < s1 ? ((int)tex[i] == n_e ? 9 : (int)tbl[i]) : 0; };
+        // the classes of the first kRegChunks * 64 tiles stay in registers
+        // across the nine passes (one LDS read each instead of nine)
+        constexpr int kRegChunks = 4;
+        int creg[kRegChunks];
+#pragma unroll
+        for (int q = 0; q < kRegChunks; ++q) creg[q] = cls_of(s0 + 64 * q + lane);
         uint32_t o = 0;
-        for (int c = 9; c >= 1; --c)
-            for (uint32_t base = s0; base < s1; base += 64) {
+        for (int c = 9; c >= 1; --c) {
+            uint32_t base = s0;
+#pragma unroll
+            for (int q = 0; q < kRegChunks; ++q, base += 64) {
+                if (base >= s1) break;
+                const bool hit = creg[q] == c;
+                const unsigned long long m = __ballot(hit);
+                if (hit) perm[s0 + o + (uint32_t)__popcll(m & ((1ull << lane) - 1ull))] = (uint16_t)(base + lane);
+                o += (uint32_t)__popcll(m);
+            }
+            for (; base < s1; base += 64) {
                 const uint32_t i = base + lane;
-                const int cls = i < s1 ? ((int)tex[i] == n_e ? 9 : (int)tbl[i]) : 0;
-                const bool hit = cls == c;
+                const bool hit = cls_of(i) == c;
                 const unsigned long long m = __ballot(hit);
                 if (hit) perm[s0 + o + (uint32_t)__popcll(m & ((1ull << lane) - 1ull))] = (uint16_t)i;
                 o += (uint32_t)__popcll(m);
             }
+        }
         if (lane == 0) sched_n[kSchedXcnt + wave] = s1 - s0;
     }
     __syncthreads();

@@ -256,7 +256,10 @@ moe_status moe_prefill_fused(const uint16_t *x, int32_t t, int32_t k, int32_t E,
  * on one stream, with the same outputs and the same arithmetic.  Being one
  * call lets it merge launches that the separate calls cannot: for chunks of
  * up to 512 rows the grouping (CSR) and the experts' tile schedule run in
- * one workgroup and one launch.
+ * one workgroup and one launch, which up to 16 rows also runs the top-k;
+ * above 512 rows the scan of the grouping's counts and the schedule share a
+ * launch.  Calls on different streams may overlap: the call keeps no state
+ * outside its arguments.
  *
  *   x, w_router, t, k, E, logits, topk_idx, topk_w   as for moe_route (h = L->hidden)
  *   offsets, csr_rows, csr_w, csr_pos                outputs, as for moe_build_csr

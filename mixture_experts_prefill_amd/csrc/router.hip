@@ -125,19 +125,23 @@ __global__ void __launch_bounds__(256) k_router(const uint16_t *__restrict__ x,
 }
 
 // Few-row router (t <= 8, h <= 4096): a workgroup of 4 waves owns every row
-// of the chunk and 4 experts, one per wave.  Each wave loads its expert's
-// whole W row into registers (h/64 floats per lane) while the workgroup
-// stages the rows' x in LDS (at most 64 KB), so the kernel waits on memory
-// about twice instead of once per 256-element step.  Lane l still owns
-// partial l of every logit and runs the same fma chains and tree.
+// of the chunk and 4 / RS experts; the RS waves of one expert take RT rows
+// each.  Each wave loads its expert's whole W row into registers (h/64
+// floats per lane) while the workgroup stages the rows' x in LDS (at most
+// 64 KB), so the kernel waits on memory about twice instead of once per
+// 256-element step.  Lane l still owns partial l of every logit and runs the
+// same fma chains and tree.  Two waves per expert for 5-8 rows halve each
+// wave's chain length and spread the experts over twice the workgroups.
 constexpr int kFewRows = 8, kFewSteps = 16;
-template <int RT>
+template <int RT, int RS>
 __global__ void __launch_bounds__(256) k_router_few(const uint16_t *__restrict__ x,
                                                     const float *__restrict__ w, int t, int h, int E,
                                                     float *__restrict__ logits) {
-    __shared__ __attribute__((aligned(16))) uint16_t xs[RT * kFewSteps * 256];
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int e = blockIdx.x * 4 + (tid >> 6);
+    constexpr int TR = RT * RS;  // rows staged
+    __shared__ __attribute__((aligned(16))) uint16_t xs[TR * kFewSteps * 256];
+    const int tid = threadIdx.x, lane = tid & 63, wv_id = tid >> 6;
+    const int e = blockIdx.x * (4 / RS) + wv_id / RS;
+    const int rbase = (wv_id % RS) * RT;
     const int steps = h >> 8;
     const float4 *wr = reinterpret_cast<const float4 *>(w + (size_t)min(e, E - 1) * h) + lane;
     // Loads are unconditional, at clamped (in-bounds) addresses, so that they
@@ -146,7 +150,7 @@ __global__ void __launch_bounds__(256) k_router_few(const uint16_t *__restrict__
 #pragma unroll
     for (int s = 0; s < kFewSteps; ++s) wv[s] = wr[min(s, steps - 1) * 64];
     // rows 0 .. t-1 are contiguous: t * h / 8 chunks of 16 bytes
-    constexpr int kCh = RT * kFewSteps * 256 / 8 / 256;
+    constexpr int kCh = TR * kFewSteps * 256 / 8 / 256;
     const int nch = t * (h >> 3);
     const uint4 *xg = reinterpret_cast<const uint4 *>(x);
     uint4 xv[kCh];
@@ -167,7 +171,7 @@ __global__ void __launch_bounds__(256) k_router_few(const uint16_t *__restrict__
         if (s < steps) {
 #pragma unroll
             for (int i = 0; i < RT; ++i) {
-                const int r = i < t ? i : t - 1;  // rows past t repeat the last row, never stored
+                const int r = rbase + i < t ? rbase + i : t - 1;  // rows past t repeat the last row, never stored
                 const uint2 v = *reinterpret_cast<const uint2 *>(xs + r * h + s * 256 + 4 * lane);
                 p[i] = __builtin_fmaf(bf16_lo(v.x), wv[s].x, p[i]);
                 p[i] = __builtin_fmaf(bf16_hi(v.x), wv[s].y, p[i]);
@@ -179,7 +183,7 @@ __global__ void __launch_bounds__(256) k_router_few(const uint16_t *__restrict__
     const float v = tree64(p, lane);
     constexpr int shift = tree_shift(RT);
     if ((lane & ((1 << shift) - 1)) == 0) {
-        const int r = lane >> shift;
+        const int r = rbase + (lane >> shift);
         if (r < t && e < E) logits[(size_t)r * E + e] = v;
     }
 }
@@ -369,11 +373,11 @@ hipError_t launch_router_logits(const uint16_t *x, const float *w, int t, int h,
         return hipGetLastError();
     }
     if (t <= kFewRows && h <= kFewSteps * 256) {
-        const dim3 grid((E + 3) / 4), block(256);
-        if (t == 1) hipLaunchKernelGGL(k_router_few<1>, grid, block, 0, s, x, w, t, h, E, logits);
-        else if (t == 2) hipLaunchKernelGGL(k_router_few<2>, grid, block, 0, s, x, w, t, h, E, logits);
-        else if (t <= 4) hipLaunchKernelGGL(k_router_few<4>, grid, block, 0, s, x, w, t, h, E, logits);
-        else hipLaunchKernelGGL(k_router_few<8>, grid, block, 0, s, x, w, t, h, E, logits);
+        const dim3 grid((E + 3) / 4), grid2((E + 1) / 2), block(256);
+        if (t == 1) hipLaunchKernelGGL((k_router_few<1, 1>), grid, block, 0, s, x, w, t, h, E, logits);
+        else if (t == 2) hipLaunchKernelGGL((k_router_few<2, 1>), grid, block, 0, s, x, w, t, h, E, logits);
+        else if (t <= 4) hipLaunchKernelGGL((k_router_few<4, 1>), grid, block, 0, s, x, w, t, h, E, logits);
+        else hipLaunchKernelGGL((k_router_few<4, 2>), grid2, block, 0, s, x, w, t, h, E, logits);
         return hipGetLastError();
     }
     if (t >= 64 && E >= 8) return launch_tile<8, 8>(x, w, t, h, E, logits, s);

@@ -167,15 +167,17 @@ def test_routing_ties(mep, orc, case, kind, path):
     check_out(g["out"], r["out"])
 
 
-EXTREME_CASES = [(8, 1024, 32), (16, 1000, 32), (100, 1024, 32), (1, 1024, 1), (16, 1, 1), (17, 777, 31)]
+EXTREME_CASES = [(8, 1024, 32), (16, 1000, 32), (100, 1024, 32), (1, 1024, 1), (16, 1, 1), (17, 777, 31),
+                 (5, 300, 7), (6, 513, 9), (7, 64, 3)]
 
 
 @pytest.mark.parametrize("path", ["block", "separate"])
 @pytest.mark.parametrize("case", EXTREME_CASES, ids=[f"t{c[0]}-E{c[1]}-k{c[2]}" for c in EXTREME_CASES])
 def test_routing_extremes(mep, orc, case, path):
     """The largest expert count and k the calls accept (E = 1024, k = 32),
-    partly filled key slots (E = 1000, 777), a single expert, and the row
-    counts around the merged decode kernel's limit (16 / 17 rows)."""
+    partly filled key slots (E = 1000, 777), a single expert, the row
+    counts around the merged decode kernel's limit (16 / 17 rows), and 5-7
+    rows (the few-row router's two waves per expert, one partly filled)."""
     t, E, k = case
     wl = ms.small_case(950 + E + k, t, 256, 64, E, k, 32)
     g = run(mep, wl, path=path)

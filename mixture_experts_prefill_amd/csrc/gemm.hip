@@ -787,7 +787,9 @@ __global__ void __launch_bounds__(CT) k_combine(const uint16_t *__restrict__ ye,
         for (int j = 0; j < 16; ++j)
             if (j0 + j < k) {
                 const uint32_t p = ps[j0 + j];
-                v[j] = *reinterpret_cast<const uint4 *>(ye + (size_t)p * h + c);
+                // ye is read once: non-temporal loads (and stores of out below)
+                const u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(ye + (size_t)p * h + c));
+                v[j] = make_uint4(q.x, q.y, q.z, q.w);
                 wj[j] = csr_w[p];
             }
 #pragma unroll
@@ -802,8 +804,9 @@ __global__ void __launch_bounds__(CT) k_combine(const uint16_t *__restrict__ ye,
             }
         }
     }
-    o[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-    o[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    typedef float f32x4_t __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store((f32x4_t){acc[0], acc[1], acc[2], acc[3]}, reinterpret_cast<f32x4_t *>(o));
+    __builtin_nontemporal_store((f32x4_t){acc[4], acc[5], acc[6], acc[7]}, reinterpret_cast<f32x4_t *>(o) + 1);
 }
 
 // Split-K reductions of the shared expert (small chunks): partial sums of

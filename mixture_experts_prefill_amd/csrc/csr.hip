@@ -378,7 +378,7 @@ __device__ __forceinline__ void schedule_body(const uint32_t *offsets, int e0, i
         te.p0 = (int)tp0[i];
         te.n = (int)trows[i] + 1;
         te.expert = e0 + (int)tex[i];
-        te.pad = 0;
+        te.tiles = (int)tne[i];
         te.rec = reinterpret_cast<const void *>(erec[tex[i]]);
         te.pad2 = 0;
         order[(size_t)x * xcap + (q - xstart[x])] = te;

@@ -196,9 +196,10 @@ __device__ __forceinline__ void dma4(uint32_t lds_addr, uint32_t voff, i32x4 rsr
 // streams once: they then do not displace the activations, router weights
 // and intermediates that the block's other kernels find in the last-level
 // cache (decode-shaped chunk: block 0.170 -> 0.155 ms, every kernel of the
-// block faster).  Tiles of many rows keep the plain loads: there the other
-// M-tiles of the expert re-read the weights (full chunk: gate/up 228 -> 229.5
-// us with the hint, the block unchanged).
+// block faster).  The matrix-core tiles use them only for 32-row tiles that
+// are their expert's only M-tile; on taller tiles the hint made gate/up
+// slower even where no other tile re-reads the weights (full chunk 234 ->
+// 237.5 us, mid 46.6 -> 48.1 us).
 __device__ __forceinline__ void dma16nt(uint32_t lds_addr, uint32_t voff, i32x4 rsrc, uint32_t soff) {
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
                  :
@@ -265,6 +266,10 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
     const int nblk = (n_out + FEAT - 1) / FEAT;
     const int xcd = blockIdx.x & 7, slot_in_xcd = blockIdx.x >> 3;
     int nb, expert = 0, p0, n, split = 0;
+    // Weights that no other tile reads (the expert's only M-tile) load with
+    // the non-temporal hint in 32-row tiles, the decode-shaped case; with
+    // taller tiles the hint measured slower.
+    bool stream_w;
     const uint8_t *rec;
     if (kDense) {
         const int per_split = ((a.t + BM - 1) / BM) * nblk;
@@ -277,6 +282,7 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
         nb = rest % nblk;
         p0 = (rest / nblk) * BM;
         n = min(BM, a.t - p0);
+        stream_w = BM == 32 && a.t <= BM;
         rec = static_cast<const uint8_t *>(a.record);
     } else {
         // The entry is loaded together with the count (the grid never
@@ -287,6 +293,7 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
         expert = te.expert;
         p0 = te.p0;
         n = te.n;
+        stream_w = BM == 32 && te.tiles == 1;
         rec = static_cast<const uint8_t *>(te.rec);
         if (!rec) return;   // a used expert left without a record: no read of address 0
     }
@@ -349,8 +356,13 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
         const int kg = kbase + ks;
         #pragma unroll
         for (int f = 0; f < 2; ++f) {
-            dma16(lds_base + wcode(slot, f), wvo[f], rrec, (uint32_t)kg * 1024u);
-            dma4(lds_base + wsb(slot, f), svo[f], rrec, (uint32_t)(kg * sb_tile_bytes));
+            if (stream_w) {
+                dma16nt(lds_base + wcode(slot, f), wvo[f], rrec, (uint32_t)kg * 1024u);
+                dma4nt(lds_base + wsb(slot, f), svo[f], rrec, (uint32_t)(kg * sb_tile_bytes));
+            } else {
+                dma16(lds_base + wcode(slot, f), wvo[f], rrec, (uint32_t)kg * 1024u);
+                dma4(lds_base + wsb(slot, f), svo[f], rrec, (uint32_t)(kg * sb_tile_bytes));
+            }
         }
     };
     auto issue = [&](int ks, int slot) {

@@ -136,118 +136,148 @@ def ingest_pmc(fetch_csv: str, write_csv: str, key: str):
     print(json.dumps({key: {k: v for k, v in entry.items() if k != "raw"}}, indent=2))
 
 
-def cpu_baseline(cfg_name: str, rows: int):
-    """The oracle, as it stands, on the first `rows` rows of the same workload."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg_name: str, rows: int, rows_1t: int):
+    """The oracle, as it stands, on the first `rows` rows of the same workload
+    with all its threads, and on the first `rows_1t` rows with one thread."""
     import dataclasses
 
     import moe_synth as ms
     import oracle
 
-    wl = ms.make_workload(cfg_name)
-    wl = dataclasses.replace(wl, x=wl.x[:rows].copy(), cfg=dataclasses.replace(wl.cfg, t=rows))
+    full = ms.make_workload(cfg_name)
+
+    def sample(n):
+        return dataclasses.replace(full, x=full.x[:n].copy(), cfg=dataclasses.replace(full.cfg, t=n))
+
+    wl = sample(rows)
+    threads = oracle.max_threads()
     # repeated until about 10 s of CPU work (at most 3 runs), for a stable rate
     times = []
     while len(times) < 3 and sum(times) < 10.0:
         t0 = time.perf_counter()
-        oracle.block(wl)
+        oracle.block(wl, with_logits=False)
         times.append(time.perf_counter() - t0)
     dt = sum(times) / len(times)
-    return {"value": rows / dt, "unit": "tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
+    one = None
+    if rows_1t > 0:
+        oracle.set_threads(1)
+        try:
+            t0 = time.perf_counter()
+            oracle.block(sample(rows_1t), with_logits=False)
+            dt1 = time.perf_counter() - t0
+        finally:
+            oracle.set_threads(threads)
+        one = {"value": round(rows_1t / dt1, 2), "unit": "tokens/s", "cores": 1,
+               "sample": f"first {rows_1t} rows, one run of {dt1:.2f} s (the touched experts' weights are "
+                         f"decoded once per call, so a small sample has a lower rate per row)"}
+    return {"value": round(rows / dt, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(), "nproc": os.cpu_count(),
             "sample": f"full block (router, top-k, CSR, routed experts, shared expert, combine) in double "
                       f"on the first {rows} of {cfg_name}'s {ms.CONFIGS[cfg_name].t} rows, {len(times)} runs "
-                      f"of {dt:.2f} s on average"}
+                      f"of {dt:.2f} s on average",
+            "single_thread": one}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    # Default warm-up: at least 20 steps and 30 ms of GPU work.  After only 5
-    # steps the timed ones still ran 5% slower (full chunk 0.513 vs
-    # 0.483-0.487 ms per step for 20, 50 or 200 warm-up steps; decode-shaped
-    # chunk 0.189 vs 0.180 ms for 5 and 50).
-    ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--config", default="full")
-    ap.add_argument("--copies", type=int, default=0,
-                    help="weight copies rotated per step (0: enough that a step's weights have left the "
-                         "256 MB MALL before the same copy comes round again)")
-    ap.add_argument("--cpu-rows", type=int, default=4096, help="rows of the oracle CPU-baseline sample (0: skip)")
-    ap.add_argument("--phases", action="store_true", help="also time every phase in an extra pass")
-    ap.add_argument("--time-every", type=int, default=5,
-                    help="time the dominant kernel's launch with HIP events in every N-th timed step")
-    ap.add_argument("--separate", action="store_true",
-                    help="run the shared expert as its own call (moe_shared) instead of inside the routed launches")
-    ap.add_argument("--copy-probe", action="store_true",
-                    help="after timing, copy 512 MiB device-to-device (calibrates HBM byte counters)")
-    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="turn two rocprofv3 --pmc counter_collection.csv files into profiles/traffic.json")
-    args = ap.parse_args()
-    if args.ingest_pmc:
-        ingest_pmc(*args.ingest_pmc, key=f"gateup_{args.config}" + ("_separate" if args.separate else ""))
-        return
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the block is built and measured "
-              f"on a single MI355X, with no sharding or collectives.", file=sys.stderr)
-        sys.exit(2)
-
+def build_block(cfg, all_resident: bool):
+    """Device buffers of one workload.  Every expert resident: routing runs
+    once on the GPU and only the records of experts some row picks are
+    generated (the others are never read); with cfg.resident and not
+    `all_resident`, the most-used experts are resident and the rest stream
+    from pinned host memory through the ring."""
     import numpy as np
     import torch
 
     import mixture_experts_prefill_amd as mep
     import moe_synth as ms
 
-    cfg = ms.CONFIGS[args.config]
-    log(f"[bench] generating workload {cfg.name} ...")
-    wl = ms.make_workload(cfg)
-    torch.cuda.set_device(0)
-    resident = None
-    blk = mep.MoeBlock.from_workload(wl)
-    log("[bench] uploaded; routing once for the residency split / counts")
+    x = ms.make_x(cfg)
+    blk = mep.MoeBlock(cfg.t, cfg.hidden, cfg.inter, cfg.inter_shared, cfg.experts, cfg.k, cfg.group)
+    blk.set_inputs(x, ms.make_router(cfg))
+    blk.set_shared(ms.make_shared(cfg))
     blk.route()
     blk.build_csr()
     torch.cuda.synchronize()
     counts = np.diff(blk.offsets.cpu().numpy().astype(np.int64))
-    if cfg.resident:
-        order = sorted([e for e in range(cfg.experts) if counts[e] > 0], key=lambda e: -counts[e])
+    touched = np.nonzero(counts > 0)[0]
+    resident = None
+    if cfg.resident and not all_resident:
+        order = sorted(touched.tolist(), key=lambda e: -counts[e])
         resident = np.zeros(cfg.experts, dtype=bool)
         resident[order[:cfg.resident]] = True
+        wl = ms.make_workload(cfg)
         blk = mep.MoeBlock.from_workload(wl, resident=resident)
-    tables = [blk.table]
-    pools = [blk.pool]
+        del wl
+    else:
+        pool = torch.empty((cfg.experts, blk.L.stride), dtype=torch.uint8, device="cuda")
+        for i in range(0, touched.size, 32):
+            ids = touched[i:i + 32]
+            recs = torch.from_numpy(ms.make_records(cfg, experts=ids.tolist()))
+            pool[torch.from_numpy(ids).to("cuda")] = recs.to("cuda")
+        blk.set_pool(pool)
+    return blk, counts, resident
+
+
+def measure(cfg, args, steps: int, warmup_steps, all_resident: bool = False, separate: bool = False):
+    """Time `steps` whole blocks of workload `cfg`; returns the measurements."""
+    import numpy as np
+    import torch
+
+    import mixture_experts_prefill_amd as mep
+
+    log(f"[bench] workload {cfg.name}: generating and uploading ...")
+    blk, counts, resident = build_block(cfg, all_resident)
+    t = cfg.t
+    # Weight copies rotated per step: the experts' records, the router weights
+    # and the shared expert's record (a model's layers each have their own).
     copies = args.copies
     if copies <= 0:
         # Between two steps on the same copy, the other copies stream
-        # (copies - 1) x the touched weight bytes; make that exceed the MALL.
-        touched_bytes = algorithmic(cfg, wl.x.shape[0], counts)["bytes_total"]
+        # (copies - 1) x the step's weight bytes; make that exceed the MALL.
+        touched_bytes = algorithmic(cfg, t, counts)["bytes_total"]
         copies = min(8, max(2, int(MALL_BYTES // touched_bytes) + 2))
+    sets = [(blk.table, blk.w_router, blk.shared_record)]
+    pools = [blk.pool]
     for c in range(1, copies if resident is None else 1):
         pool = blk.pool.clone()
         pools.append(pool)
         tab = blk.table.clone()
         nz = tab != 0
         tab[nz] = tab[nz] - blk.pool.data_ptr() + pool.data_ptr()
-        tables.append(tab)
+        sets.append((tab, blk.w_router.clone(), blk.shared_record.clone()))
 
     # the whole block in one call (moe_block) unless the shared expert must run
     # in its own call (--separate, or experts streamed through the ring)
-    path = "block" if blk.can_block and not args.separate else "separate"
+    path = "block" if blk.can_block and not separate else "separate"
     fused = path == "block" and blk.Ls is not None
 
     def step(i):
-        blk.table = tables[i % len(tables)]
+        blk.table, blk.w_router, blk.shared_record = sets[i % len(sets)]
         blk.forward(path=path)
 
+    # Untimed warm-up: by default at least 20 steps and 30 ms of GPU work.
+    # After only 5 steps the timed ones still ran 5% slower (full chunk 0.513
+    # vs 0.483-0.487 ms per step for 20, 50 or 200 warm-up steps).
     warmup = 0
     w_start = time.perf_counter()
     while True:
-        n = args.warmup if args.warmup is not None else 20
+        n = warmup_steps if warmup_steps is not None else 20
         for _ in range(n if warmup == 0 else 10):
             step(warmup)
             warmup += 1
         torch.cuda.synchronize()
-        if args.warmup is not None or time.perf_counter() - w_start >= 0.03:
+        if warmup_steps is not None or time.perf_counter() - w_start >= 0.03:
             break
-    log(f"[bench] warmup {warmup} steps")
 
     dominant = "gateup"
     # The dominant kernel's launches are timed with HIP events attached to
@@ -260,7 +290,7 @@ def main():
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     e0.record()
-    for i in range(args.steps):
+    for i in range(steps):
         mep.moe_profile_set_mask([dominant] if i % args.time_every == 0 else [])
         step(i)
     e1.record()
@@ -268,17 +298,17 @@ def main():
     wall = time.perf_counter() - w0
     prof = mep.moe_profile_end()
     gpu_ms = e0.elapsed_time(e1)
-    ms_per_step = gpu_ms / args.steps
-    t = wl.x.shape[0]
-    value = t * args.steps / (gpu_ms / 1e3)
-    log(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f} ms/step)")
+    ms_per_step = gpu_ms / steps
+    value = t * steps / (gpu_ms / 1e3)
+    log(f"[bench] {cfg.name}: {steps} steps after {warmup} warm-up: {ms_per_step:.4f} ms/step "
+        f"(wall {wall * 1e3 / steps:.3f} ms/step)")
 
     work = algorithmic(cfg, t, counts, fused)
     dom_ms, dom_n = prof[dominant]
     dom_avg_s = dom_ms / dom_n / 1e3
     # Launches per step: one, except with streamed experts, where the ring
     # runs the GEMMs once per batch; each launch then does its share.
-    timed_steps = len(range(0, args.steps, args.time_every))
+    timed_steps = len(range(0, steps, args.time_every))
     per_launch = timed_steps / dom_n
     # The kernel is MFMA-bound when its arithmetic intensity exceeds the
     # machine balance (2500 TFLOP/s / 8 TB/s = 312 FLOP/B), else HBM-bound.
@@ -303,8 +333,9 @@ def main():
     step_s = ms_per_step / 1e3
     extra = {"block_mfma_frac": round(block_flop / step_s / 1e12 / PEAK_BF16_TFLOPS, 4),
              "block_hbm_frac": round(work["bytes_total"] / step_s / 1e9 / PEAK_HBM_GBS, 4),
+             "block_algorithmic_flop": round(block_flop), "block_algorithmic_bytes": round(work["bytes_total"]),
              "touched_experts": work["touched"], "max_rows_per_expert": int(counts.max()),
-             "weight_copies": len(tables),
+             "weight_copies": len(sets),
              "calls": "moe_block (shared expert in the routed launches)" if path == "block"
                       else "moe_shared, moe_route, moe_build_csr, moe_prefill_experts"}
     if blk.ring is not None:
@@ -334,23 +365,86 @@ def main():
 
     # Per-step distribution in an extra untimed pass: an event between steps
     # (its own cost is small next to a step, but it is kept out of `value`).
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     ev[0].record()
-    for i in range(args.steps):
+    for i in range(steps):
         step(i)
         ev[i + 1].record()
     torch.cuda.synchronize()
-    per_step = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)])
+    per_step = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
     extra["step_ms_p10_p50_p90"] = [round(float(np.percentile(per_step, q)), 4) for q in (10, 50, 90)]
 
     if args.phases:
         mep.moe_profile_begin(mep.PHASES)
-        for i in range(args.steps):
+        for i in range(steps):
             step(i)
         torch.cuda.synchronize()
         ph = mep.moe_profile_end()
         extra["phase_us"] = {p: round(v[0] / v[1] * 1e3, 2) for p, v in ph.items()}
+    res = dict(value=value, ms_per_step=ms_per_step, warmup=warmup, roofline=roofline, extra=extra,
+               resident=int(resident.sum()) if resident is not None else cfg.experts)
+    del blk, sets, pools
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up steps (default: at least 20 and at least 30 ms of work)")
+    ap.add_argument("--config", default="full")
+    ap.add_argument("--all-resident", action="store_true",
+                    help="large: every expert resident in HBM instead of the top 64 plus the ring")
+    ap.add_argument("--copies", type=int, default=0,
+                    help="weight copies rotated per step (0: enough that a step's weights have left the "
+                         "256 MB MALL before the same copy comes round again)")
+    ap.add_argument("--cpu-rows", type=int, default=4096, help="rows of the oracle CPU-baseline sample (0: skip)")
+    ap.add_argument("--cpu-rows-1t", type=int, default=128,
+                    help="rows of the single-threaded oracle sample (0: skip)")
+    ap.add_argument("--decode-extra", type=int, default=1,
+                    help="with the full chunk, also time the decode-shaped chunks (t = 8 and t = 1)")
+    ap.add_argument("--phases", action="store_true", help="also time every phase in an extra pass")
+    ap.add_argument("--time-every", type=int, default=5,
+                    help="time the dominant kernel's launch with HIP events in every N-th timed step")
+    ap.add_argument("--separate", action="store_true",
+                    help="run the shared expert as its own call (moe_shared) instead of inside the routed launches")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after timing, copy 512 MiB device-to-device (calibrates HBM byte counters)")
+    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter_collection.csv files into profiles/traffic.json")
+    args = ap.parse_args()
+    if args.ingest_pmc:
+        ingest_pmc(*args.ingest_pmc, key=f"gateup_{args.config}" + ("_separate" if args.separate else ""))
+        return
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the block is built and measured "
+              f"on a single MI355X, with no sharding or collectives.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import moe_synth as ms
+
+    torch.cuda.set_device(0)
+    cfg = ms.CONFIGS[args.config]
+    res = measure(cfg, args, args.steps, args.warmup, all_resident=args.all_resident, separate=args.separate)
+    extra = res["extra"]
+    if args.config == "full" and args.decode_extra and not args.separate:
+        # The decode-shaped chunks (the HBM-bound case), timed the same way.
+        for name in ("decode", "decode1"):
+            dc = ms.CONFIGS[name]
+            d = measure(dc, args, max(args.steps, 50), args.warmup)
+            extra[f"{name}_t{dc.t}"] = {
+                "ms_per_step": round(d["ms_per_step"], 4), "tokens_per_s": round(d["value"], 1),
+                "block_hbm_frac": d["extra"]["block_hbm_frac"],
+                "block_algorithmic_bytes": d["extra"]["block_algorithmic_bytes"],
+                "touched_experts": d["extra"]["touched_experts"], "weight_copies": d["extra"]["weight_copies"],
+                "warmup": d["warmup"], "step_ms_p10_p50_p90": d["extra"]["step_ms_p10_p50_p90"],
+                "roofline": d["roofline"]}
 
     if args.copy_probe:
         src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device="cuda")
@@ -361,19 +455,21 @@ def main():
 
     cpu = None
     if args.cpu_rows > 0:
-        log(f"[bench] oracle CPU baseline on {args.cpu_rows} rows ...")
-        cpu = cpu_baseline(cfg.name, min(args.cpu_rows, t))
+        log(f"[bench] oracle CPU baseline on {args.cpu_rows} rows (+{args.cpu_rows_1t} single-threaded) ...")
+        cpu = cpu_baseline(cfg.name, min(args.cpu_rows, cfg.t), min(args.cpu_rows_1t, cfg.t))
 
+    workload = f"{cfg.name}: {cfg.description}"
+    if args.all_resident and cfg.resident:
+        workload += " (here every expert resident in HBM)"
     line = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": f"{cfg.name}: {cfg.description}", "t": t, "hidden": cfg.hidden, "inter": cfg.inter,
+        "metric": METRIC, "value": round(res["value"], 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": res["warmup"], "ms_per_step": round(res["ms_per_step"], 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": workload, "t": cfg.t, "hidden": cfg.hidden, "inter": cfg.inter,
                    "inter_shared": cfg.inter_shared, "experts": cfg.experts, "top_k": cfg.k, "group": cfg.group,
                    "weights": "int4 + fp16 scale/bias per group", "zipf_s": cfg.zipf_s,
-                   "resident_experts": int(resident.sum()) if resident is not None else cfg.experts,
-                   "parallelism": "none (1 GPU)"},
-        "roofline": roofline, "cpu_baseline": cpu, "extra": extra,
+                   "resident_experts": res["resident"], "parallelism": "none (1 GPU)"},
+        "roofline": res["roofline"], "cpu_baseline": cpu, "extra": extra,
     }
     print(json.dumps(line), flush=True)
 

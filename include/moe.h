@@ -182,7 +182,9 @@ typedef struct {
     int32_t streamed;       /* of which streamed through the ring */
     int32_t batches;        /* batches of `group` jobs */
     uint64_t fetched_bytes; /* bytes copied host -> device (streamed * stride) */
-    double wait_ms;         /* host time spent waiting to reuse ring slots */
+    double wait_ms;         /* host time blocked in the call: the stream sync of the
+                               offsets read-back (slot reuse itself is ordered on
+                               the GPU by events, so the host never waits for a slot) */
 } moe_ring_stats;
 moe_status moe_ring_get_stats(const moe_ring *ring, moe_ring_stats *out);
 

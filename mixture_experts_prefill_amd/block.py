@@ -99,6 +99,18 @@ class MoeBlock:
         self.ring_slots = torch.empty((ring_slots, stride), dtype=torch.uint8, device=self.device)
         self.ring = MoeRing(self.L, self.ring_slots, ring_slots, group)
 
+    def set_pool(self, pool: torch.Tensor):
+        """Every expert resident in `pool`, a device uint8 tensor [E, stride]
+        holding record e at row e (records of experts that no row picks are
+        never read)."""
+        same_device = pool.device.type == self.device.type and (
+            self.device.index is None or pool.device.index == self.device.index)
+        if not same_device or pool.dtype != torch.uint8 or tuple(pool.shape) != (self.E, self.L.stride):
+            raise ValueError("pool must be a uint8 [E, stride] tensor on the block's device")
+        self.pool = pool
+        self.table = pool.data_ptr() + torch.arange(self.E, dtype=torch.int64, device=self.device) * self.L.stride
+        self.host_records, self.ring = None, None
+
     def use_ring(self, ring_slots: int = 64, group: int = 8):
         """Run the all-resident records through a ring too (every batch gated by events)."""
         self.ring_slots = torch.empty((ring_slots, self.L.stride), dtype=torch.uint8, device=self.device)

@@ -263,7 +263,6 @@ __device__ __forceinline__ void schedule_body(const uint32_t *offsets, int e0, i
     __shared__ uint8_t tbl[MAXT];    // token blocks (32 rows) of each tile
     __shared__ uint8_t trows[MAXT];  // rows of each tile - 1
     __shared__ uint8_t xof[MAXT];    // XCD of each tile
-    __shared__ uint8_t tin[MAXT];    // index of the tile within its expert
     __shared__ uint8_t tne[MAXT];    // tiles of its expert
     __shared__ uint16_t perm[MAXT];  // listing position -> tile
     __shared__ uint64_t erec[MOE_MAX_EXPERTS + 1]; // record address of each expert (+ shared)
@@ -304,7 +303,6 @@ __device__ __forceinline__ void schedule_body(const uint32_t *offsets, int e0, i
             tp0[w] = p0 + m;
             tex[w] = (uint16_t)le;
             trows[w] = (uint8_t)(rows - 1);
-            tin[w] = (uint8_t)j;
             tne[w] = (uint8_t)ne;
             tbl[w] = (uint8_t)((rows + 31) / 32);
         }

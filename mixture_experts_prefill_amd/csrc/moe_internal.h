@@ -52,8 +52,6 @@ hipError_t launch_csr(const uint32_t *idx, const float *wts, int t, int k, int E
                       uint32_t *offsets, uint32_t *rows, float *csr_w, uint32_t *pos,
                       uint32_t *hist, hipStream_t s);
 
-// One M-tile of a grouped GEMM as the kernel reads it: one 32-byte load
-// gives the rows and the expert's record.
 // One M-tile of the grouped GEMMs: CSR rows [p0, p0 + n) of `expert`, the
 // expert's record, and the number of M-tiles of the expert's segment (1:
 // this tile is the only reader of the expert's weights).

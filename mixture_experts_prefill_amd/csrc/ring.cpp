@@ -74,11 +74,14 @@ moe_status ring_run(moe_ring *ring, const void *const *host_records, GemmArgs a,
     if (st.stride != L->stride) return fail(MOE_ERR_INVALID, "experts: ring slot size %llu != record stride %llu",
                                             (unsigned long long)st.stride, (unsigned long long)L->stride);
     // Read offsets and the residency table back (the pages read topk back
-    // here: experts.rs page, fn prepare_expert_jobs).
+    // here: experts.rs page, fn prepare_expert_jobs).  The host blocks until
+    // the stream has reached this point; that time is the call's host wait.
     hipError_t e = hipMemcpyAsync(st.h_offsets, offsets, sizeof(uint32_t) * (E + 1), hipMemcpyDeviceToHost, s);
     if (e == hipSuccess) e = hipMemcpyAsync(st.h_records, a.records, sizeof(uint64_t) * E, hipMemcpyDeviceToHost, s);
+    const auto sync0 = std::chrono::steady_clock::now();
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) return hip_fail(e, "experts: offsets read-back");
+    double wait_ms = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - sync0).count();
 
     RingPlan plan;
     ring_plan(st.h_offsets, st.h_records, E, st.n_slots, st.group, &plan);
@@ -107,8 +110,8 @@ moe_status ring_run(moe_ring *ring, const void *const *host_records, GemmArgs a,
     if (e == hipSuccess) e = hipStreamWaitEvent(st.copy, st.start, 0);
     if (e != hipSuccess) return hip_fail(e, "experts: ring start");
 
-    const auto t0 = std::chrono::steady_clock::now();
-    double wait_ms = 0.0;
+    // Slot reuse is ordered on the GPU (the copy stream waits on "done"), so
+    // the host does not wait in this loop; only the test delay below sleeps.
     for (int b = 0; b < nb; ++b) {
         const int j0 = plan.batch_first[b], j1 = plan.batch_first[b + 1];
         if (plan.wait_batch[b] >= 0) {
@@ -164,7 +167,6 @@ moe_status ring_run(moe_ring *ring, const void *const *host_records, GemmArgs a,
             wait_ms += std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - w0).count();
         }
     }
-    (void)t0;
     e = launch_combine(a.ye, csr_pos, csr_w, t, k, L->hidden, out, accumulate, s);
     if (e != hipSuccess) return hip_fail(e, "experts: combine");
 

@@ -47,6 +47,8 @@ def lib():
         _lib.orc_shared.argtypes = [P, I, I, I, P, I, P, P]
         _lib.orc_block.argtypes = [P, P, I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P]
         _lib.orc_tokens_bruteforce.argtypes = [P, P, I, I, I, I, I, I, I, P, P, P, P, I, I, P]
+        _lib.orc_set_threads.argtypes = [I]
+        _lib.orc_set_threads.restype = None
         for f in ("orc_layout", "orc_router_logits", "orc_topk", "orc_build_csr", "orc_expert_rows",
                   "orc_shared", "orc_block", "orc_tokens_bruteforce", "orc_max_threads"):
             getattr(_lib, f).restype = ctypes.c_int
@@ -67,6 +69,12 @@ def _check(rc: int, what: str):
 
 def max_threads() -> int:
     return lib().orc_max_threads()
+
+
+def set_threads(n: int) -> None:
+    """Threads of the oracle's parallel loops; every output belongs to one
+    thread, so results are bitwise the same at any count."""
+    lib().orc_set_threads(int(n))
 
 
 def layout(hidden: int, inter: int, group: int) -> dict:
@@ -152,8 +160,9 @@ def _record_ptrs(records: np.ndarray):
     return recs, ptrs
 
 
-def block(wl, shared_expert: bool = True):
-    """Whole block through the grouped path. Returns dict of outputs."""
+def block(wl, shared_expert: bool = True, with_logits: bool = True):
+    """Whole block through the grouped path. Returns dict of outputs (and the
+    router logits in the fixed fp32 order, unless with_logits is False)."""
     c = wl.cfg
     x = np.ascontiguousarray(wl.x, dtype=np.uint16)
     t = x.shape[0]
@@ -171,7 +180,10 @@ def block(wl, shared_expert: bool = True):
     _check(lib().orc_block(_p(x), _p(wr), t, c.hidden, c.inter, c.inter_shared, c.experts, c.k, c.group,
                            ptrs, _p(srec), _p(gate), _p(out), _p(idx), _p(w), _p(offsets), _p(rows),
                            _p(cw), _p(pos)), "block")
-    return dict(out=out, topk_idx=idx, topk_w=w, offsets=offsets, csr_rows=rows, csr_w=cw, csr_pos=pos)
+    res = dict(out=out, topk_idx=idx, topk_w=w, offsets=offsets, csr_rows=rows, csr_w=cw, csr_pos=pos)
+    if with_logits:
+        res["logits"] = router_logits(x, wr)
+    return res
 
 
 def tokens_bruteforce(wl, sample: Sequence[int], order: int = 0, shared_expert: bool = True) -> np.ndarray:

@@ -548,6 +548,17 @@ int orc_tokens_bruteforce(const uint16_t *x, const float *Wr, int t, int h, int 
     return rc;
 }
 
+/* Threads the parallel loops use from now on (the results do not depend on it). */
+void orc_set_threads(int n)
+{
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    omp_set_num_threads(n < 1 ? 1 : n);
+#else
+    (void)n;
+#endif
+}
+
 int orc_max_threads(void)
 {
 #ifdef _OPENMP

@@ -7,8 +7,12 @@ Bars (the block's acceptance criteria):
   - block output: relative Frobenius error <= 5e-3 and
     max |gpu - ref| <= 1e-2 * max |ref| (bf16 activations and weights,
     fp32 accumulation, against the oracle's double result).
-Full-size configs compare routing and CSR on every row and outputs on sampled
-rows that the oracle's brute-force path computes one by one.
+Every test also compares the router logits bitwise with the oracle's fixed
+fp32 summation order.  The five workloads run at their own shapes with both
+the plain weights and the centred ones (bias = -7.5 scale + noise, so the
+weights are near zero mean and the Frobenius check is not dominated by the
+mean component); every output row is compared with the oracle's grouped
+block.
 """
 import os
 
@@ -54,6 +58,7 @@ def run(mep, wl, resident=None, ring_slots=64, group=8, shared=True, force_ring=
     blk.forward(path=path)
     torch.cuda.synchronize()
     g = dict(
+        logits=blk.logits.cpu().numpy(),
         topk_idx=blk.topk_idx.cpu().numpy().view(np.uint32),
         topk_w=blk.topk_w.cpu().numpy(),
         offsets=blk.offsets.cpu().numpy().view(np.uint32),
@@ -69,6 +74,9 @@ def run(mep, wl, resident=None, ring_slots=64, group=8, shared=True, force_ring=
 
 
 def check_routing(g, r):
+    if "logits" in r:
+        same = g["logits"].view(np.uint32) == r["logits"].view(np.uint32)
+        assert same.all(), f"{int((~same).sum())} router logits differ from the oracle's fp32 order"
     assert np.array_equal(g["topk_idx"], r["topk_idx"]), "top-k indices differ"
     assert np.max(np.abs(g["topk_w"] - r["topk_w"])) <= W_ABS
     assert np.array_equal(g["offsets"], r["offsets"]), "offsets differ"
@@ -78,13 +86,33 @@ def check_routing(g, r):
     assert np.array_equal(g["csr_w"][g["csr_pos"]], g["topk_w"].reshape(-1)), "csr_w is not the GPU's topk_w"
 
 
-def check_out(got, ref):
+def check_out(got, ref, tag=None):
     ref = np.asarray(ref, dtype=np.float64)
     d = got.astype(np.float64) - ref
     fro = np.linalg.norm(d) / np.linalg.norm(ref)
     mx = np.max(np.abs(d)) / np.max(np.abs(ref))
-    say(f"    rel_fro={fro:.2e} max_abs_rel={mx:.2e}")
+    line = f"{'PARITY ' + tag + ' ' if tag else ''}rows={got.shape[0]} rel_fro={fro:.2e} max_abs_rel={mx:.2e}"
+    say("    " + line)
+    if tag and os.environ.get("MOE_PARITY_LOG"):
+        with open(os.environ["MOE_PARITY_LOG"], "a") as f:
+            f.write(line + "\n")
     assert fro <= REL_FRO and mx <= MAX_ABS_REL, (fro, mx)
+
+
+_REF = {}
+
+
+def workload_ref(orc, name, centred):
+    """The oracle's whole block (every row) for one of the five workloads,
+    computed once per (workload, weights) and shared by the paths."""
+    key = (name, centred)
+    if key not in _REF:
+        wl = ms.make_workload(name, centred=centred)
+        say(f"  oracle {name} centred={centred} ...")
+        _REF.clear()   # keep one at a time: the large workload's result is 64 MiB
+        _REF[key] = orc.block(wl)
+        del wl
+    return _REF[key]
 
 
 # ------------------------------------------------------------------ small shapes, full oracle
@@ -275,67 +303,79 @@ def test_no_shared_expert(mep, orc):
 
 # ------------------------------------------------------------------ the five workloads
 
+WEIGHTS = [False, True]
+WEIGHT_IDS = ["plain", "centred"]
+
+
 @pytest.mark.parametrize("path", PATHS)
-def test_mid_config(mep, orc, path):
-    wl = ms.make_workload("mid")
+@pytest.mark.parametrize("centred", WEIGHTS, ids=WEIGHT_IDS)
+def test_mid_config(mep, orc, path, centred):
+    wl = ms.make_workload("mid", centred=centred)
     g = run(mep, wl, path=path)
-    say("  oracle mid ...")
-    r = orc.block(wl)
+    r = workload_ref(orc, "mid", centred)
     check_routing(g, r)
-    check_out(g["out"], r["out"])
+    check_out(g["out"], r["out"], f"mid {WEIGHT_IDS[centred]} {path}")
 
 
 @pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("centred", WEIGHTS, ids=WEIGHT_IDS)
 @pytest.mark.parametrize("name", ["decode", "decode1"])
-def test_decode_configs(mep, orc, name, path):
-    wl = ms.make_workload(name)
+def test_decode_configs(mep, orc, name, path, centred):
+    wl = ms.make_workload(name, centred=centred)
     g = run(mep, wl, path=path)
-    say(f"  oracle {name} ...")
-    r = orc.block(wl)
+    r = workload_ref(orc, name, centred)
     check_routing(g, r)
-    check_out(g["out"], r["out"])
+    check_out(g["out"], r["out"], f"{name} {WEIGHT_IDS[centred]} {path}")
 
 
-def sample_rows(t, n, seed):
-    rng = np.random.default_rng(seed)
-    return np.unique(np.concatenate([[0, t - 1], rng.choice(t, n, replace=False)])).astype(np.int32)
-
-
-def full_routing_ref(orc, wl):
-    lg = orc.router_logits(wl.x, wl.w_router)
-    idx, w = orc.topk(lg, wl.cfg.k)
-    offsets, rows, cw, pos = orc.build_csr(idx, w, wl.cfg.experts)
-    return dict(topk_idx=idx, topk_w=w, offsets=offsets, csr_rows=rows, csr_w=cw, csr_pos=pos)
-
-
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("path", PATHS)
-def test_full_config(mep, orc, path):
-    wl = ms.make_workload("full")
+@pytest.mark.parametrize("centred", WEIGHTS, ids=WEIGHT_IDS)
+def test_full_config(mep, orc, path, centred):
+    """The full chunk (4096 rows, Zipf routing): every row against the oracle."""
+    wl = ms.make_workload("full", centred=centred)
     g = run(mep, wl, path=path)
-    say("  oracle routing full ...")
-    r = full_routing_ref(orc, wl)
+    del wl
+    r = workload_ref(orc, "full", centred)
     check_routing(g, r)
-    s = sample_rows(wl.cfg.t, 40, 1)
-    say(f"  oracle brute force on {s.size} rows ...")
-    ref = orc.tokens_bruteforce(wl, s)
-    check_out(g["out"][s], ref)
+    check_out(g["out"], r["out"], f"full {WEIGHT_IDS[centred]} {path}")
 
 
-def test_large_config_streamed(mep, orc):
-    """Top-64 experts by row count resident, the rest streamed through a 64-slot ring in batches of 8."""
-    wl = ms.make_workload("large")
-    say("  oracle routing large ...")
-    r = full_routing_ref(orc, wl)
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("centred", WEIGHTS, ids=WEIGHT_IDS)
+def test_large_config(mep, orc, centred):
+    """The large chunk: top-64 experts by row count resident and the rest
+    streamed through a 64-slot ring in batches of 8; then every expert
+    resident on the separate calls (bitwise equal to the ring) and on the
+    one-call block.  Every row of each against the oracle."""
+    wl = ms.make_workload("large", centred=centred)
+    r = workload_ref(orc, "large", centred)
     resident = orc.residency(r["offsets"], wl.cfg.resident)
+    say("  GPU ring ...")
     g = run(mep, wl, resident=resident)
     check_routing(g, r)
     st = g["ring_stats"]
     n_streamed = int(((np.diff(r["offsets"].astype(np.int64)) > 0) & ~resident).sum())
     assert st["streamed"] == n_streamed and st["fetched_bytes"] == n_streamed * wl.layout.stride
+    check_out(g["out"], r["out"], f"large {WEIGHT_IDS[centred]} ring")
+    say("  GPU all resident, separate calls ...")
     g_res = run(mep, wl, path="separate")
     assert np.array_equal(g["out"], g_res["out"]), "ring output differs from all-resident output"
-    s = sample_rows(wl.cfg.t, 10, 2)
-    say(f"  oracle brute force on {s.size} rows ...")
+    del g_res
+    say("  GPU all resident, one-call block ...")
+    g_blk = run(mep, wl, path="block")
+    del wl
+    check_routing(g_blk, r)
+    check_out(g_blk["out"], r["out"], f"large {WEIGHT_IDS[centred]} block")
+
+
+def test_bruteforce_sample_rows(mep, orc):
+    """Sampled rows of the full chunk against the oracle's per-token path,
+    which never builds the CSR (a second route to the same reference)."""
+    wl = ms.make_workload("full", centred=True)
+    g = run(mep, wl)
+    rng = np.random.default_rng(1)
+    s = np.unique(np.concatenate([[0, wl.cfg.t - 1], rng.choice(wl.cfg.t, 40, replace=False)])).astype(np.int32)
     ref = orc.tokens_bruteforce(wl, s)
     check_out(g["out"][s], ref)
 

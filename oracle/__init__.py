@@ -47,6 +47,10 @@ def lib():
         _lib.orc_shared.argtypes = [P, I, I, I, P, I, P, P]
         _lib.orc_block.argtypes = [P, P, I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P]
         _lib.orc_tokens_bruteforce.argtypes = [P, P, I, I, I, I, I, I, I, P, P, P, P, I, I, P]
+        _lib.orc_round_bf16.argtypes = [ctypes.c_double]
+        _lib.orc_round_bf16.restype = ctypes.c_uint16
+        _lib.orc_inject_norm.argtypes = [P, P, I, I, I, P, P, P, ctypes.c_double, P, P]
+        _lib.orc_inject_norm.restype = ctypes.c_int
         _lib.orc_set_threads.argtypes = [I]
         _lib.orc_set_threads.restype = None
         for f in ("orc_layout", "orc_router_logits", "orc_topk", "orc_build_csr", "orc_expert_rows",
@@ -184,6 +188,34 @@ def block(wl, shared_expert: bool = True, with_logits: bool = True):
     if with_logits:
         res["logits"] = router_logits(x, wr)
     return res
+
+
+def round_bf16(values) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) of doubles, rounded to nearest, ties to even."""
+    v = np.asarray(values, dtype=np.float64)
+    f = lib().orc_round_bf16
+    return np.array([f(float(a)) for a in v.reshape(-1)], dtype=np.uint16).reshape(v.shape)
+
+
+def inject_norm(hyper: np.ndarray, y: Optional[np.ndarray], alpha, beta, gamma, eps: float):
+    """The block output y [t, h] injected into the n residual copies hyper
+    [t, n, h] with weights beta, read back with weights alpha, RMS-normalised
+    with gain gamma [h]: returns (updated hyper fp32 [t, n, h], next block
+    input as bf16 bit patterns [t, h])."""
+    hy = np.ascontiguousarray(hyper, dtype=np.float32)
+    t, n, h = hy.shape
+    yy = None if y is None else np.ascontiguousarray(y, dtype=np.float32)
+    if yy is not None:
+        assert yy.shape == (t, h)
+    a = np.ascontiguousarray(alpha, dtype=np.float32)
+    b = np.ascontiguousarray(beta, dtype=np.float32)
+    g = np.ascontiguousarray(gamma, dtype=np.float32)
+    assert a.shape == (n,) and b.shape == (n,) and g.shape == (h,)
+    hout = np.empty_like(hy)
+    mixed = np.empty((t, h), dtype=np.uint16)
+    _check(lib().orc_inject_norm(_p(hy), _p(yy), t, n, h, _p(a), _p(b), _p(g), float(eps), _p(hout), _p(mixed)),
+           "inject_norm")
+    return hout, mixed
 
 
 def tokens_bruteforce(wl, sample: Sequence[int], order: int = 0, shared_expert: bool = True) -> np.ndarray:

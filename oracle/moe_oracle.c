@@ -40,6 +40,11 @@
  *     along the input dimension; record layout as stated in orc_layout.
  *   - Combine order: shared expert first, then experts in ascending id.
  *   - Shared gate: none (factor 1) or sigmoid(x_r . gate_w).
+ *   - Injection into the next fused norm (orc_inject_norm): the residual
+ *     stream of a row is n fp32 copies of h values; the block output y is
+ *     added to copy i with weight beta_i, the copies are read back as
+ *     z = sum_i alpha_i copy_i, and the next block's input is the RMS norm
+ *     of z times a gain gamma, rounded to bf16.
  *
  * All floating-point accumulation here is double, except the router logits,
  * which follow the fp32 order above exactly (this file must be compiled
@@ -546,6 +551,83 @@ int orc_tokens_bruteforce(const uint16_t *x, const float *Wr, int t, int h, int 
     free(lg);
     free(terms);
     return rc;
+}
+
+/* ------------------------------------------------------------------ next norm */
+
+/*
+ * Round a double to the nearest bfloat16 (ties to even), returned as its bit
+ * pattern: 8 significant bits for normal values, a fixed quantum of 2^-133
+ * below 2^-126 (the format's subnormals), infinity past the largest finite
+ * value.  Done in one step from the double, so no intermediate float
+ * rounding can move a value across a tie.
+ */
+uint16_t orc_round_bf16(double v)
+{
+    if (isnan(v))
+        return 0x7fc0;
+    int sign = signbit(v) ? 1 : 0;
+    double a = fabs(v), r;
+    if (a == 0.0)
+        return (uint16_t)(sign << 15);
+    if (a < ldexp(1.0, -126)) {
+        r = ldexp(nearbyint(ldexp(a, 133)), -133); /* default mode: ties to even */
+    } else {
+        int e;
+        double m = frexp(a, &e);                       /* a = m 2^e, m in [0.5, 1) */
+        r = ldexp(nearbyint(ldexp(m, 8)), e - 8);      /* 8 significant bits */
+    }
+    float f = (float)r;                                /* exact: r has <= 8 bits */
+    if (r >= ldexp(1.0, 128))
+        f = INFINITY;
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return (uint16_t)((u >> 16) | (uint32_t)(sign << 15));
+}
+
+/*
+ * The block output y [t x h] injected into the residual stream and read by
+ * the next fused norm (decode.rs page, step_rows: a block's MoE output is
+ * injected by the next fused norm, `pending`; prefill.rs page, pf_layer and
+ * prefill_chunk: pf_hc_read with the pending output, pf_inject).  The pages
+ * show the calls, not their arithmetic; the reading taken here:
+ *
+ *   hyper[r][i][c] += beta[i] * y[r][c]                 for the n copies i
+ *   z[r][c]         = sum_i alpha[i] * hyper[r][i][c]   (after the update)
+ *   mixed[r][c]     = bf16( z[r][c] * gamma[c] / sqrt(mean_c z[r][c]^2 + eps) )
+ *
+ * hyper is fp32 [t][n][h]; hyper_out receives the updated copies (rounded to
+ * float once from double); mixed is bf16 [t][h].  y may be NULL (nothing
+ * injected: the plain read).  All arithmetic in double.
+ */
+int orc_inject_norm(const float *hyper, const float *y, int t, int n, int h, const float *alpha,
+                    const float *beta, const float *gamma, double eps, float *hyper_out, uint16_t *mixed)
+{
+    if (t < 1 || n < 1 || h < 1 || eps < 0.0)
+        return ORC_BAD;
+#pragma omp parallel for schedule(static)
+    for (int r = 0; r < t; r++) {
+        double *z = calloc((size_t)h, sizeof(double));
+        for (int i = 0; i < n; i++) {
+            const float *hp = hyper + ((uint64_t)r * n + i) * h;
+            float *op = hyper_out + ((uint64_t)r * n + i) * h;
+            for (int c = 0; c < h; c++) {
+                double v = (double)hp[c];
+                if (y)
+                    v += (double)beta[i] * (double)y[(uint64_t)r * h + c];
+                op[c] = (float)v;
+                z[c] += (double)alpha[i] * v;
+            }
+        }
+        double ss = 0.0;
+        for (int c = 0; c < h; c++)
+            ss += z[c] * z[c];
+        double inv = 1.0 / sqrt(ss / h + eps);
+        for (int c = 0; c < h; c++)
+            mixed[(uint64_t)r * h + c] = orc_round_bf16(z[c] * inv * (double)gamma[c]);
+        free(z);
+    }
+    return ORC_OK;
 }
 
 /* Threads the parallel loops use from now on (the results do not depend on it). */

@@ -371,3 +371,115 @@ def test_generator_is_reproducible():
         want = json.load(f)["hashes"]
     for name in ("tiny", "mid"):
         assert ms.make_workload(name).content_hash() == want[name], name
+
+
+# ------------------------------------------------------------------ injection into the next norm
+
+def bf16_value(bits):
+    return ms.bf16_bits_to_f32(np.asarray(bits, dtype=np.uint16)).astype(np.float64)
+
+
+def test_round_bf16_hand_values(orc):
+    """Round to nearest, ties to even, on values placed by hand around 1.0
+    (one bf16 ulp there is 2^-7), at the subnormal quantum 2^-133, and past
+    the largest finite value."""
+    cases = [
+        (1.0, 0x3F80),
+        (1.0 + 2.0 ** -8, 0x3F80),                 # tie: to the even neighbour 1.0
+        (1.0 + 3 * 2.0 ** -8, 0x3F82),             # tie between 1+2^-7 (odd) and 1+2^-6 (even)
+        (1.0 + 2.0 ** -8 + 2.0 ** -30, 0x3F81),    # just above the tie: up
+        (1.0 + 2.0 ** -8 - 2.0 ** -30, 0x3F80),    # just below: down
+        (-(1.0 + 3 * 2.0 ** -8), 0xBF82),
+        (0.0, 0x0000), (-0.0, 0x8000),
+        (2.0 ** -126, 0x0080),                     # smallest normal
+        (2.0 ** -133, 0x0001),                     # smallest subnormal
+        (1.5 * 2.0 ** -133, 0x0002),               # subnormal tie: to even (2 quanta)
+        (2.5 * 2.0 ** -133, 0x0002),
+        ((2 - 2.0 ** -7) * 2.0 ** 127, 0x7F7F),    # largest finite
+        (2.0 ** 128, 0x7F80),                      # overflow: infinity
+        (3.0, 0x4040), (-0.15625, 0xBE20),
+    ]
+    got = orc.round_bf16([c[0] for c in cases])
+    assert [int(g) for g in got] == [c[1] for c in cases]
+
+
+def test_round_bf16_equals_generator_on_floats(orc):
+    """On values that are exactly float32 a single rounding to bf16 is the
+    whole job: equal to the input generator's own float32 -> bf16 rounding."""
+    rng = np.random.default_rng(5)
+    v = (rng.standard_normal(4000) * np.exp(rng.uniform(-30, 30, 4000))).astype(np.float32)
+    assert np.array_equal(orc.round_bf16(v.astype(np.float64)), ms.f32_to_bf16_bits(v))
+
+
+def test_inject_norm_constant_rows(orc):
+    """Rows whose copies are constant give z constant along the row, so with
+    eps = 0 the norm is exactly gamma[c] * sign(z): pins the weights alpha
+    and beta per copy, the gain's index and the sign."""
+    t, n, h = 3, 3, 64
+    alpha = np.array([0.5, -0.25, 2.0])
+    beta = np.array([1.0, 0.0, -3.0])
+    gamma = np.linspace(-2, 2, h).astype(np.float32)
+    gamma = bf16_value(bf16(gamma)).astype(np.float32)         # exactly bf16
+    cst = np.array([[1.0, 2.0, -1.0], [0.5, 4.0, 0.25], [-1.0, -1.0, -1.0]])   # hyper[r][i]
+    yv = np.array([2.0, -1.0, 0.5])
+    hyper = np.repeat(cst[:, :, None], h, axis=2).astype(np.float32)
+    y = np.repeat(yv[:, None], h, axis=1).astype(np.float32)
+    hout, mixed = orc.inject_norm(hyper, y, alpha, beta, gamma, 0.0)
+    upd = cst + beta[None, :] * yv[:, None]
+    assert np.array_equal(hout, np.repeat(upd[:, :, None], h, axis=2).astype(np.float32))
+    z = (alpha[None, :] * upd).sum(axis=1)            # [1.25 - 0 + 2*(-7)...] per row
+    assert (z != 0).all()
+    want = np.sign(z)[:, None] * gamma[None, :].astype(np.float64)
+    assert np.array_equal(bf16_value(mixed), want)
+
+
+def test_inject_norm_is_residual_plus_rms_norm(orc):
+    """One copy with alpha = beta = 1 is the plain pre-norm residual: the next
+    block input is torch's float64 rms_norm of hyper + y, correctly rounded
+    to bf16 (within half a bf16 ulp of the float64 value)."""
+    rng = np.random.default_rng(6)
+    t, h = 37, 512
+    hyper = rng.standard_normal((t, 1, h)).astype(np.float32)
+    y = (0.3 * rng.standard_normal((t, h))).astype(np.float32)
+    gamma = rng.uniform(0.5, 1.5, h).astype(np.float32)
+    eps = 1e-6
+    hout, mixed = orc.inject_norm(hyper, y, [1.0], [1.0], gamma, eps)
+    z = torch.from_numpy(hyper[:, 0].astype(np.float64)) + torch.from_numpy(y.astype(np.float64))
+    ref = torch.nn.functional.rms_norm(z, (h,), weight=torch.from_numpy(gamma.astype(np.float64)), eps=eps).numpy()
+    assert np.array_equal(hout[:, 0], (hyper[:, 0].astype(np.float64) + y).astype(np.float32))
+    got = bf16_value(mixed)
+    ulp = 2.0 ** (np.floor(np.log2(np.abs(ref))) - 7)
+    assert np.all(np.abs(got - ref) <= 0.5 * ulp * (1 + 1e-9))
+
+
+def test_inject_norm_selects_copies(orc):
+    """alpha one-hot on copy j reads copy j alone; beta = 0 leaves every copy
+    unchanged; y = None injects nothing.  References: torch float64 rms_norm."""
+    rng = np.random.default_rng(7)
+    t, n, h = 5, 4, 256
+    hyper = rng.standard_normal((t, n, h)).astype(np.float32)
+    y = rng.standard_normal((t, h)).astype(np.float32)
+    gamma = rng.uniform(-1, 1, h).astype(np.float32)
+    beta = np.array([0.5, -1.0, 2.0, 0.25], dtype=np.float32)
+    for j in range(n):
+        alpha = np.eye(n, dtype=np.float32)[j]
+        hout, mixed = orc.inject_norm(hyper, y, alpha, beta, gamma, 1e-5)
+        z = torch.from_numpy(hyper[:, j].astype(np.float64) + beta[j] * y.astype(np.float64))
+        ref = torch.nn.functional.rms_norm(z, (h,), weight=torch.from_numpy(gamma.astype(np.float64)),
+                                           eps=1e-5).numpy()
+        ulp = 2.0 ** (np.floor(np.log2(np.abs(ref))) - 7)
+        assert np.all(np.abs(bf16_value(mixed) - ref) <= 0.5 * ulp * (1 + 1e-9)), j
+    hout, _ = orc.inject_norm(hyper, y, np.ones(n), np.zeros(n), gamma, 1e-5)
+    assert np.array_equal(hout, hyper)
+    hout2, m2 = orc.inject_norm(hyper, None, np.ones(n), beta, gamma, 1e-5)
+    assert np.array_equal(hout2, hyper)
+    _, m3 = orc.inject_norm(hyper, np.zeros((t, h), np.float32), np.ones(n), beta, gamma, 1e-5)
+    assert np.array_equal(m2, m3)
+
+
+def test_inject_norm_zero_row_with_eps(orc):
+    """A row that reads as all zeros normalises to +0 (no NaN) when eps > 0."""
+    hyper = np.zeros((2, 2, 64), np.float32)
+    hyper[1] = 1.0
+    _, mixed = orc.inject_norm(hyper, None, [1.0, -1.0], [0.0, 0.0], np.ones(64, np.float32), 1e-6)
+    assert np.all(mixed == 0)

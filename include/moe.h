@@ -278,6 +278,34 @@ moe_status moe_block(const uint16_t *x, const float *w_router, int32_t t, int32_
                      float *csr_w, uint32_t *csr_pos, float *out, int32_t accumulate, void *workspace,
                      size_t workspace_bytes, void *stream);
 
+/*
+ * moe_block without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, outputs and arithmetic
+ * as moe_block, whose kernels it runs; the scratch they need (the grouping
+ * counts, the tile schedule and the hg / ye intermediates) is instead a
+ * static device array inside the library of MOE_NOALLOC_SCRATCH_BYTES
+ * (64 MiB), one per GPU, held from the library's first use on that GPU until
+ * the process ends.  The call allocates and frees nothing (with per-kernel
+ * profiling off, its default).
+ *
+ *   Returns MOE_ERR_CAPACITY, before anything is enqueued, when the chunk
+ *   needs more scratch than that: moe_workspace_bytes(t, k, E, L, Ls) must
+ *   be <= MOE_NOALLOC_SCRATCH_BYTES (decode-shaped chunks and, at hidden
+ *   2048, inter 768, k = 8 with a shared expert, up to about 1200 rows).
+ *   No part of the scratch needs to start at zero: each call writes all it
+ *   reads, so a call is not affected by what the previous one left there.
+ *   All calls on one GPU share its array: calls that overlap on one GPU
+ *   (different streams, or different host threads) race and give undefined
+ *   results; order them on one stream or with events.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (64ull << 20)
+moe_status moe_block_noalloc(const uint16_t *x, const float *w_router, int32_t t, int32_t k, int32_t E,
+                             const moe_layout *L, const uint64_t *records, const moe_layout *Ls,
+                             const void *shared_record, const uint16_t *shared_gate_w, float *logits,
+                             uint32_t *topk_idx, float *topk_w, uint32_t *offsets, uint32_t *csr_rows,
+                             float *csr_w, uint32_t *csr_pos, float *out, int32_t accumulate, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -51,7 +51,8 @@ _lib = None
 EXPORTS = ["moe_last_error", "moe_layout_make", "moe_workspace_bytes", "moe_route", "moe_build_csr",
            "moe_shared", "moe_ring_create", "moe_ring_destroy", "moe_ring_get_stats", "moe_prefill_experts",
            "moe_ring_plan_debug", "moe_profile_begin", "moe_profile_end", "moe_profile_set_mask",
-           "moe_prefill_fused", "moe_block"]
+           "moe_prefill_fused", "moe_block", "moe_block_noalloc"]
+NOALLOC_SCRATCH_BYTES = 64 << 20   # MOE_NOALLOC_SCRATCH_BYTES of include/moe.h
 PHASES = ["router", "topk", "csr", "shared_gateup", "shared_down", "schedule", "gateup", "down", "combine"]
 
 
@@ -79,6 +80,7 @@ def lib():
     L.moe_prefill_experts.argtypes = [P, I, I, I, LP, P, P, P, P, P, P, P, P, I, P, Z, P]
     L.moe_prefill_fused.argtypes = [P, I, I, I, LP, P, P, P, P, P, LP, P, P, P, I, P, Z, P]
     L.moe_block.argtypes = [P, P, I, I, I, LP, P, LP, P, P, P, P, P, P, P, P, P, P, I, P, Z, P]
+    L.moe_block_noalloc.argtypes = [P, P, I, I, I, LP, P, LP, P, P, P, P, P, P, P, P, P, P, I, P]
     L.moe_ring_plan_debug.argtypes = [P, P, I, I, I, P, P, P]
     L.moe_profile_begin.argtypes = [ctypes.c_uint32]
     L.moe_profile_begin.restype = None
@@ -87,7 +89,7 @@ def lib():
     L.moe_profile_end.argtypes = [P, P]
     L.moe_profile_end.restype = ctypes.c_int
     for f in ("moe_layout_make", "moe_route", "moe_build_csr", "moe_shared", "moe_ring_create",
-              "moe_ring_get_stats", "moe_prefill_experts", "moe_prefill_fused", "moe_block"):
+              "moe_ring_get_stats", "moe_prefill_experts", "moe_prefill_fused", "moe_block", "moe_block_noalloc"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -219,6 +221,21 @@ def moe_block(x: torch.Tensor, w_router: torch.Tensor, k: int, layout: moe_layou
                            _ptr(shared_gate_w), _ptr(logits), _ptr(topk_idx), _ptr(topk_w), _ptr(offsets),
                            _ptr(csr_rows), _ptr(csr_w), _ptr(csr_pos), _ptr(out), accumulate, _ptr(workspace),
                            workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def moe_block_noalloc(x: torch.Tensor, w_router: torch.Tensor, k: int, layout: moe_layout, records: torch.Tensor,
+                      shared_layout: Optional[moe_layout], shared_record: Optional[torch.Tensor],
+                      shared_gate_w: Optional[torch.Tensor], logits: torch.Tensor, topk_idx: torch.Tensor,
+                      topk_w: torch.Tensor, offsets: torch.Tensor, csr_rows: torch.Tensor, csr_w: torch.Tensor,
+                      csr_pos: torch.Tensor, out: torch.Tensor, accumulate: int, stream=None) -> None:
+    """moe_block on the library's static scratch instead of a workspace."""
+    t = x.shape[0]
+    E = w_router.shape[0]
+    _check(lib().moe_block_noalloc(_ptr(x), _ptr(w_router), t, k, E, ctypes.byref(layout), _ptr(records),
+                                   ctypes.byref(shared_layout) if shared_layout is not None else None,
+                                   _ptr(shared_record), _ptr(shared_gate_w), _ptr(logits), _ptr(topk_idx),
+                                   _ptr(topk_w), _ptr(offsets), _ptr(csr_rows), _ptr(csr_w), _ptr(csr_pos),
+                                   _ptr(out), accumulate, _stream(stream)))
 
 
 def moe_ring_plan_debug(offsets, resident, n_slots: int = 64, group: int = 8):

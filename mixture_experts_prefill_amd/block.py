@@ -25,7 +25,7 @@ from typing import Optional, Sequence
 import numpy as np
 import torch
 
-from . import (MoeRing, moe_block, moe_build_csr, moe_layout_make, moe_prefill_experts, moe_prefill_fused,
+from . import (MoeRing, moe_block, moe_block_noalloc, moe_build_csr, moe_layout_make, moe_prefill_experts, moe_prefill_fused,
                moe_route, moe_shared, moe_workspace_bytes)
 
 
@@ -141,6 +141,12 @@ class MoeBlock:
         moe_block(self.x, self.w_router, self.k, self.L, self.table, self.Ls, self.shared_record, self.gate_w,
                   self.logits, self.topk_idx, self.topk_w, self.offsets, self.csr_rows, self.csr_w, self.csr_pos,
                   self.out, accumulate, self.workspace, stream)
+
+    def block_noalloc(self, accumulate: int = 0, stream=None):
+        """The one-call block on the library's static scratch (no workspace)."""
+        moe_block_noalloc(self.x, self.w_router, self.k, self.L, self.table, self.Ls, self.shared_record,
+                          self.gate_w, self.logits, self.topk_idx, self.topk_w, self.offsets, self.csr_rows,
+                          self.csr_w, self.csr_pos, self.out, accumulate, stream)
 
     @property
     def can_block(self) -> bool:

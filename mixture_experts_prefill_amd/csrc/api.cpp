@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -452,22 +453,32 @@ moe_status moe_prefill_fused(const uint16_t *x, int32_t t, int32_t k, int32_t E,
                        shared_gate_w ? reinterpret_cast<float *>(ws + w.gate) : nullptr, true, s);
 }
 
-moe_status moe_block(const uint16_t *x, const float *w_router, int32_t t, int32_t k, int32_t E,
-                     const moe_layout *L, const uint64_t *records, const moe_layout *Ls,
-                     const void *shared_record, const uint16_t *shared_gate_w, float *logits,
-                     uint32_t *topk_idx, float *topk_w, uint32_t *offsets, uint32_t *csr_rows,
-                     float *csr_w, uint32_t *csr_pos, float *out, int32_t accumulate, void *workspace,
-                     size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace moe {
+
+// Argument checks of moe_block and moe_block_noalloc (everything but the
+// workspace size, which `ws_check` bytes stand in for).
+static moe_status block_check(const uint16_t *x, const float *w_router, int t, int k, int E, const moe_layout *L,
+                              const uint64_t *records, const moe_layout *Ls, const void *shared_record,
+                              const float *logits, const uint32_t *topk_idx, const float *topk_w,
+                              const uint32_t *offsets, const uint32_t *csr_rows, const float *csr_w,
+                              const uint32_t *csr_pos, const float *out, const void *workspace, size_t ws_check,
+                              const char *who) {
     if (moe_status st = check_routing(t, k, E)) return st;
     if (!w_router || !logits || !topk_idx || !topk_w || !offsets || !csr_rows || !csr_w || !csr_pos)
-        return fail(MOE_ERR_INVALID, "block: null pointer");
-    if (!aligned16(w_router)) return fail(MOE_ERR_INVALID, "block: w_router must be 16-byte aligned");
+        return fail(MOE_ERR_INVALID, "%s: null pointer", who);
+    if (!aligned16(w_router)) return fail(MOE_ERR_INVALID, "%s: w_router must be 16-byte aligned", who);
+    return check_fused(x, t, k, E, L, records, Ls, shared_record, out, workspace, ws_check, true, who);
+}
+
+// The block's launches on validated arguments.
+static moe_status block_run(const uint16_t *x, const float *w_router, int t, int k, int E, const moe_layout *L,
+                            const uint64_t *records, const moe_layout *Ls, const void *shared_record,
+                            const uint16_t *shared_gate_w, float *logits, uint32_t *topk_idx, float *topk_w,
+                            uint32_t *offsets, uint32_t *csr_rows, float *csr_w, uint32_t *csr_pos, float *out,
+                            int accumulate, uint8_t *ws, hipStream_t s) {
     const bool shared = Ls != nullptr;
-    if (moe_status st = check_fused(x, t, k, E, L, records, Ls, shared_record, out, workspace, workspace_bytes,
-                                    true, "block"))
-        return st;
-    uint8_t *ws = static_cast<uint8_t *>(workspace);
-    hipStream_t s = static_cast<hipStream_t>(stream);
     Workspace w;
     workspace_plan(t, k, E, L, Ls, &w);
     const int h = L->hidden;
@@ -501,6 +512,76 @@ moe_status moe_block(const uint16_t *x, const float *w_router, int32_t t, int32_
     }
     return fused_gemms(a, bm, L, t, k, E, csr_pos, csr_w, out, accumulate,
                        (shared && shared_gate_w) ? reinterpret_cast<float *>(ws + w.gate) : nullptr, shared, s);
+}
+
+// Scratch of moe_block_noalloc: one array per GPU, held by the loaded code
+// object until the process ends.  Host code must not use `scratch` itself
+// (on the host it is only a stand-in symbol); it uses the device address
+// that hipGetSymbolAddress returns for the current device, kept per device.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void *g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's copy of `scratch`, looked up on the
+// first call on that device.
+static moe_status scratch_ptr(uint8_t **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "block_noalloc: current device");
+    if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_INVALID, "block_noalloc: device %d >= %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "block_noalloc: scratch address");
+        if (!p) return fail(MOE_ERR_HIP, "block_noalloc: scratch address is null");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = static_cast<uint8_t *>(g_scratch_ptr[dev]);
+    return MOE_OK;
+}
+
+}  // namespace moe
+
+extern "C" {
+
+moe_status moe_block(const uint16_t *x, const float *w_router, int32_t t, int32_t k, int32_t E,
+                     const moe_layout *L, const uint64_t *records, const moe_layout *Ls,
+                     const void *shared_record, const uint16_t *shared_gate_w, float *logits,
+                     uint32_t *topk_idx, float *topk_w, uint32_t *offsets, uint32_t *csr_rows,
+                     float *csr_w, uint32_t *csr_pos, float *out, int32_t accumulate, void *workspace,
+                     size_t workspace_bytes, void *stream) {
+    if (moe_status st = block_check(x, w_router, t, k, E, L, records, Ls, shared_record, logits, topk_idx, topk_w,
+                                    offsets, csr_rows, csr_w, csr_pos, out, workspace, workspace_bytes, "block"))
+        return st;
+    return block_run(x, w_router, t, k, E, L, records, Ls, shared_record, shared_gate_w, logits, topk_idx, topk_w,
+                     offsets, csr_rows, csr_w, csr_pos, out, accumulate, static_cast<uint8_t *>(workspace),
+                     static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_block_noalloc(const uint16_t *x, const float *w_router, int32_t t, int32_t k, int32_t E,
+                             const moe_layout *L, const uint64_t *records, const moe_layout *Ls,
+                             const void *shared_record, const uint16_t *shared_gate_w, float *logits,
+                             uint32_t *topk_idx, float *topk_w, uint32_t *offsets, uint32_t *csr_rows,
+                             float *csr_w, uint32_t *csr_pos, float *out, int32_t accumulate, void *stream) {
+    // Every check that needs no device first, the scratch size among them:
+    // a non-null stand-in takes the workspace pointer's place.
+    static const uint8_t stand_in[16] = {0};
+    if (moe_status st = block_check(x, w_router, t, k, E, L, records, Ls, shared_record, logits, topk_idx, topk_w,
+                                    offsets, csr_rows, csr_w, csr_pos, out, stand_in, (size_t)-1, "block_noalloc"))
+        return st;
+    Workspace w;
+    workspace_plan(t, k, E, L, Ls, &w);
+    if (w.total > MOE_NOALLOC_SCRATCH_BYTES)
+        return fail(MOE_ERR_CAPACITY, "block_noalloc: this chunk needs %zu bytes of scratch, more than the %llu "
+                    "bytes of the library's static scratch (use moe_block with a workspace)", w.total,
+                    (unsigned long long)MOE_NOALLOC_SCRATCH_BYTES);
+    uint8_t *ws = nullptr;
+    if (moe_status st = scratch_ptr(&ws)) return st;
+    return block_run(x, w_router, t, k, E, L, records, Ls, shared_record, shared_gate_w, logits, topk_idx, topk_w,
+                     offsets, csr_rows, csr_w, csr_pos, out, accumulate, ws, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -375,6 +375,41 @@ def measure(cfg, args, steps: int, warmup_steps, all_resident: bool = False, sep
     per_step = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
     extra["step_ms_p10_p50_p90"] = [round(float(np.percentile(per_step, q)), 4) for q in (10, 50, 90)]
 
+    if args.next_norm_copies > 0 and path == "block":
+        # The block output into the next fused norm (n residual copies): the
+        # one-call block then moe_inject_norm on its output, against
+        # moe_block_next_norm, which never writes the output.
+        nc, hdim = args.next_norm_copies, cfg.hidden
+        hyper = torch.randn((t, nc, hdim), device="cuda")
+        gamma = torch.ones(hdim, device="cuda")
+        mixed = torch.empty((t, hdim), dtype=torch.int16, device="cuda")
+        nn = mep.next_norm(hyper, [1.0 / nc] * nc, [1.0] * nc, gamma, 1e-6, mixed)
+
+        def two_calls(i):
+            step(i)
+            mep.moe_inject_norm(blk.out, t, hdim, nn)
+
+        def fused_call(i):
+            blk.table, blk.w_router, blk.shared_record = sets[i % len(sets)]
+            blk.block_next_norm(nn)
+
+        nn_ms = {}
+        for name, fn in (("block_then_inject_norm", two_calls), ("block_next_norm", fused_call)):
+            for i in range(20):
+                fn(i)
+            n0 = torch.cuda.Event(enable_timing=True)
+            n1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            n0.record()
+            for i in range(steps):
+                fn(i)
+            n1.record()
+            torch.cuda.synchronize()
+            nn_ms[name] = round(n0.elapsed_time(n1) / steps, 4)
+        extra["next_norm"] = {"copies": nc, "ms_per_step": nn_ms,
+                              "saved_us": round((nn_ms["block_then_inject_norm"] - nn_ms["block_next_norm"]) * 1e3, 1)}
+        del hyper, mixed
+
     if args.phases:
         mep.moe_profile_begin(mep.PHASES)
         for i in range(steps):
@@ -407,6 +442,9 @@ def main():
                     help="rows of the single-threaded oracle sample (0: skip)")
     ap.add_argument("--decode-extra", type=int, default=1,
                     help="with the full chunk, also time the decode-shaped chunks (t = 8 and t = 1)")
+    ap.add_argument("--next-norm-copies", type=int, default=4,
+                    help="residual copies of the next-norm timing leg (the block output injected into the next "
+                         "fused norm, fused against separate calls); 0 skips it")
     ap.add_argument("--phases", action="store_true", help="also time every phase in an extra pass")
     ap.add_argument("--time-every", type=int, default=5,
                     help="time the dominant kernel's launch with HIP events in every N-th timed step")
@@ -444,7 +482,7 @@ def main():
                 "block_algorithmic_bytes": d["extra"]["block_algorithmic_bytes"],
                 "touched_experts": d["extra"]["touched_experts"], "weight_copies": d["extra"]["weight_copies"],
                 "warmup": d["warmup"], "step_ms_p10_p50_p90": d["extra"]["step_ms_p10_p50_p90"],
-                "roofline": d["roofline"]}
+                "roofline": d["roofline"], "next_norm": d["extra"].get("next_norm")}
 
     if args.copy_probe:
         src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device="cuda")

@@ -279,6 +279,66 @@ moe_status moe_block(const uint16_t *x, const float *w_router, int32_t t, int32_
                      size_t workspace_bytes, void *stream);
 
 /*
+ * The next fused norm: a block's output injected into the residual stream
+ * and read back as the next block's input (decode.rs page, fn step_rows: a
+ * block's MoE output is "pending" until the next fused norm injects it;
+ * prefill.rs page, fn pf_layer: pf_hc_read with the pending output produces
+ * the next block input `mixed`, and fn prefill_chunk: pf_inject after the
+ * last layer).  The pages show these calls, not their arithmetic; the
+ * reading here: a row's residual stream is n fp32 copies of h values, and
+ *
+ *   copy_i += beta_i * y                          (injection, i = 0..n-1)
+ *   z       = sum_i alpha_i * copy_i              (read, ascending i, fp32 fma)
+ *   mixed   = bf16(z * gamma / sqrt(mean(z^2) + eps))   (RMS norm, round to
+ *                                                        nearest even)
+ *
+ * with the row's sum of squares reduced in a fixed order (the results are
+ * bitwise reproducible).
+ *
+ *   hyper   fp32 [t][n][h], updated in place (16-byte aligned)
+ *   n       1..MOE_MAX_HC residual copies
+ *   alpha, beta  [host values] the read and injection weight of each copy
+ *   gamma   fp32 [h] norm gain
+ *   eps     >= 0
+ *   mixed   bf16 [t][h] output (16-byte aligned; must not overlap hyper)
+ */
+#define MOE_MAX_HC 16
+typedef struct {
+    float *hyper;
+    int32_t n;
+    float alpha[MOE_MAX_HC];
+    float beta[MOE_MAX_HC];
+    const float *gamma;
+    float eps;
+    uint16_t *mixed;
+} moe_next_norm;
+
+/*
+ * The next fused norm on its own: y fp32 [t][h] (or NULL: nothing injected,
+ * the copies are only read) into nn->hyper, and nn->mixed written.
+ * Requires 1 <= t <= 4096, h % 256 == 0, h <= 16384.
+ */
+moe_status moe_inject_norm(const float *y, int32_t t, int32_t h, const moe_next_norm *nn /*[host]*/,
+                           void *stream);
+
+/*
+ * moe_block whose block output goes straight into the next fused norm: the
+ * combine's last pass forms each row's output in the same order and
+ * precision as moe_block (accumulate = 0) and injects it into nn->hyper and
+ * normalises into nn->mixed in the same workgroup, so the output is never
+ * written to memory and no separate launch reads it back.  The result is
+ * bitwise that of moe_block followed by moe_inject_norm on its `out`.
+ * Arguments as for moe_block, with `nn` [host] in place of out and
+ * accumulate (h = L->hidden <= 16384).
+ */
+moe_status moe_block_next_norm(const uint16_t *x, const float *w_router, int32_t t, int32_t k, int32_t E,
+                               const moe_layout *L, const uint64_t *records, const moe_layout *Ls,
+                               const void *shared_record, const uint16_t *shared_gate_w, float *logits,
+                               uint32_t *topk_idx, float *topk_w, uint32_t *offsets, uint32_t *csr_rows,
+                               float *csr_w, uint32_t *csr_pos, const moe_next_norm *nn, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/*
  * moe_block without a workspace argument, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  Same arguments, outputs and arithmetic

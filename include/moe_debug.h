@@ -41,7 +41,8 @@ enum {
     MOE_PHASE_GATEUP = 6,      /* routed grouped gate/up + SiLU*up */
     MOE_PHASE_DOWN = 7,        /* routed grouped down */
     MOE_PHASE_COMBINE = 8,     /* weighted combine into out */
-    MOE_PHASES = 9
+    MOE_PHASE_NORM = 9,        /* injection into the residual copies and the next norm */
+    MOE_PHASES = 10
 };
 void moe_profile_begin(uint32_t mask);
 int moe_profile_end(double *ms, int64_t *launches);

@@ -42,6 +42,15 @@ class moe_layout(ctypes.Structure):
         return {f: getattr(self, f) for f, _ in self._fields_}
 
 
+MAX_HC = 16   # MOE_MAX_HC of include/moe.h
+
+
+class moe_next_norm(ctypes.Structure):
+    _fields_ = [("hyper", ctypes.c_void_p), ("n", ctypes.c_int32), ("alpha", ctypes.c_float * MAX_HC),
+                ("beta", ctypes.c_float * MAX_HC), ("gamma", ctypes.c_void_p), ("eps", ctypes.c_float),
+                ("mixed", ctypes.c_void_p)]
+
+
 class moe_ring_stats(ctypes.Structure):
     _fields_ = [("jobs", ctypes.c_int32), ("streamed", ctypes.c_int32), ("batches", ctypes.c_int32),
                 ("fetched_bytes", ctypes.c_uint64), ("wait_ms", ctypes.c_double)]
@@ -51,9 +60,9 @@ _lib = None
 EXPORTS = ["moe_last_error", "moe_layout_make", "moe_workspace_bytes", "moe_route", "moe_build_csr",
            "moe_shared", "moe_ring_create", "moe_ring_destroy", "moe_ring_get_stats", "moe_prefill_experts",
            "moe_ring_plan_debug", "moe_profile_begin", "moe_profile_end", "moe_profile_set_mask",
-           "moe_prefill_fused", "moe_block", "moe_block_noalloc"]
+           "moe_prefill_fused", "moe_block", "moe_block_noalloc", "moe_inject_norm", "moe_block_next_norm"]
 NOALLOC_SCRATCH_BYTES = 64 << 20   # MOE_NOALLOC_SCRATCH_BYTES of include/moe.h
-PHASES = ["router", "topk", "csr", "shared_gateup", "shared_down", "schedule", "gateup", "down", "combine"]
+PHASES = ["router", "topk", "csr", "shared_gateup", "shared_down", "schedule", "gateup", "down", "combine", "norm"]
 
 
 def lib():
@@ -81,6 +90,9 @@ def lib():
     L.moe_prefill_fused.argtypes = [P, I, I, I, LP, P, P, P, P, P, LP, P, P, P, I, P, Z, P]
     L.moe_block.argtypes = [P, P, I, I, I, LP, P, LP, P, P, P, P, P, P, P, P, P, P, I, P, Z, P]
     L.moe_block_noalloc.argtypes = [P, P, I, I, I, LP, P, LP, P, P, P, P, P, P, P, P, P, P, I, P]
+    NP = ctypes.POINTER(moe_next_norm)
+    L.moe_inject_norm.argtypes = [P, I, I, NP, P]
+    L.moe_block_next_norm.argtypes = [P, P, I, I, I, LP, P, LP, P, P, P, P, P, P, P, P, P, NP, P, Z, P]
     L.moe_ring_plan_debug.argtypes = [P, P, I, I, I, P, P, P]
     L.moe_profile_begin.argtypes = [ctypes.c_uint32]
     L.moe_profile_begin.restype = None
@@ -89,7 +101,7 @@ def lib():
     L.moe_profile_end.argtypes = [P, P]
     L.moe_profile_end.restype = ctypes.c_int
     for f in ("moe_layout_make", "moe_route", "moe_build_csr", "moe_shared", "moe_ring_create",
-              "moe_ring_get_stats", "moe_prefill_experts", "moe_prefill_fused", "moe_block", "moe_block_noalloc"):
+              "moe_ring_get_stats", "moe_prefill_experts", "moe_prefill_fused", "moe_block", "moe_block_noalloc", "moe_inject_norm", "moe_block_next_norm"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -236,6 +248,45 @@ def moe_block_noalloc(x: torch.Tensor, w_router: torch.Tensor, k: int, layout: m
                                    _ptr(shared_record), _ptr(shared_gate_w), _ptr(logits), _ptr(topk_idx),
                                    _ptr(topk_w), _ptr(offsets), _ptr(csr_rows), _ptr(csr_w), _ptr(csr_pos),
                                    _ptr(out), accumulate, _stream(stream)))
+
+
+def next_norm(hyper: torch.Tensor, alpha: Sequence[float], beta: Sequence[float], gamma: torch.Tensor,
+              eps: float, mixed: torch.Tensor) -> moe_next_norm:
+    """Describe the next fused norm: hyper fp32 [t, n, h] (updated in place),
+    per-copy read / injection weights, gain gamma fp32 [h], output mixed
+    bf16 [t, h]."""
+    n = hyper.shape[1]
+    if len(alpha) != n or len(beta) != n or n > MAX_HC:
+        raise ValueError("alpha and beta need one value per residual copy (at most 16)")
+    d = moe_next_norm()
+    d.hyper = _ptr(hyper)
+    d.n = n
+    for i in range(n):
+        d.alpha[i] = float(alpha[i])
+        d.beta[i] = float(beta[i])
+    d.gamma = _ptr(gamma)
+    d.eps = float(eps)
+    d.mixed = _ptr(mixed)
+    return d
+
+
+def moe_inject_norm(y: Optional[torch.Tensor], t: int, h: int, nn: moe_next_norm, stream=None) -> None:
+    _check(lib().moe_inject_norm(_ptr(y), t, h, ctypes.byref(nn), _stream(stream)))
+
+
+def moe_block_next_norm(x: torch.Tensor, w_router: torch.Tensor, k: int, layout: moe_layout, records: torch.Tensor,
+                        shared_layout: Optional[moe_layout], shared_record: Optional[torch.Tensor],
+                        shared_gate_w: Optional[torch.Tensor], logits: torch.Tensor, topk_idx: torch.Tensor,
+                        topk_w: torch.Tensor, offsets: torch.Tensor, csr_rows: torch.Tensor, csr_w: torch.Tensor,
+                        csr_pos: torch.Tensor, nn: moe_next_norm, workspace: torch.Tensor, stream=None) -> None:
+    t = x.shape[0]
+    E = w_router.shape[0]
+    _check(lib().moe_block_next_norm(_ptr(x), _ptr(w_router), t, k, E, ctypes.byref(layout), _ptr(records),
+                                     ctypes.byref(shared_layout) if shared_layout is not None else None,
+                                     _ptr(shared_record), _ptr(shared_gate_w), _ptr(logits), _ptr(topk_idx),
+                                     _ptr(topk_w), _ptr(offsets), _ptr(csr_rows), _ptr(csr_w), _ptr(csr_pos),
+                                     ctypes.byref(nn), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                     _stream(stream)))
 
 
 def moe_ring_plan_debug(offsets, resident, n_slots: int = 64, group: int = 8):

@@ -25,8 +25,8 @@ from typing import Optional, Sequence
 import numpy as np
 import torch
 
-from . import (MoeRing, moe_block, moe_block_noalloc, moe_build_csr, moe_layout_make, moe_prefill_experts, moe_prefill_fused,
-               moe_route, moe_shared, moe_workspace_bytes)
+from . import (MoeRing, moe_block, moe_block_next_norm, moe_block_noalloc, moe_build_csr, moe_layout_make,
+               moe_prefill_experts, moe_prefill_fused, moe_route, moe_shared, moe_workspace_bytes)
 
 
 def bf16_tensor(bits: np.ndarray, device) -> torch.Tensor:
@@ -141,6 +141,14 @@ class MoeBlock:
         moe_block(self.x, self.w_router, self.k, self.L, self.table, self.Ls, self.shared_record, self.gate_w,
                   self.logits, self.topk_idx, self.topk_w, self.offsets, self.csr_rows, self.csr_w, self.csr_pos,
                   self.out, accumulate, self.workspace, stream)
+
+    def block_next_norm(self, nn, stream=None):
+        """The one-call block with its output injected into the next fused
+        norm (`nn` from mixture_experts_prefill_amd.next_norm) instead of
+        written to out."""
+        moe_block_next_norm(self.x, self.w_router, self.k, self.L, self.table, self.Ls, self.shared_record,
+                            self.gate_w, self.logits, self.topk_idx, self.topk_w, self.offsets, self.csr_rows,
+                            self.csr_w, self.csr_pos, nn, self.workspace, stream)
 
     def block_noalloc(self, accumulate: int = 0, stream=None):
         """The one-call block on the library's static scratch (no workspace)."""

@@ -204,10 +204,54 @@ static moe_status shared_gate(const uint16_t *x, int t, const moe_layout *L, con
     return e == hipSuccess ? MOE_OK : hip_fail(e, "shared gate");
 }
 
-// Gate/up, down and combine of a scheduled call (the schedule already enqueued).
+// Arguments of the next-norm kernel from the caller's description.
+static NextNormArgs next_norm_args(const moe_next_norm *nn, int t, int h) {
+    NextNormArgs n;
+    std::memset(&n, 0, sizeof n);
+    n.t = t;
+    n.h = h;
+    n.n = nn->n;
+    n.hyper = nn->hyper;
+    for (int i = 0; i < nn->n; ++i) {
+        n.alpha[i] = nn->alpha[i];
+        n.beta[i] = nn->beta[i];
+    }
+    n.gamma = nn->gamma;
+    n.eps = nn->eps;
+    n.mixed = nn->mixed;
+    return n;
+}
+
+static bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+    return pa < pb + nb && pb < pa + na;
+}
+
+static moe_status check_next_norm(const moe_next_norm *nn, int t, int h, const float *y, const char *who) {
+    if (!nn) return fail(MOE_ERR_INVALID, "%s: null next-norm description", who);
+    if (nn->n < 1 || nn->n > MOE_MAX_HC)
+        return fail(MOE_ERR_INVALID, "%s: n = %d residual copies outside 1..%d", who, nn->n, MOE_MAX_HC);
+    if (!nn->hyper || !nn->gamma || !nn->mixed) return fail(MOE_ERR_INVALID, "%s: null pointer", who);
+    if (!aligned16(nn->hyper) || !aligned16(nn->gamma) || !aligned16(nn->mixed) || (y && !aligned16(y)))
+        return fail(MOE_ERR_INVALID, "%s: hyper, gamma, mixed and y must be 16-byte aligned", who);
+    if (!(nn->eps >= 0.0f) || nn->eps == __builtin_inff())
+        return fail(MOE_ERR_INVALID, "%s: eps must be finite and >= 0", who);
+    if (h % 256 || h > kNormMaxHidden)
+        return fail(MOE_ERR_INVALID, "%s: h = %d must be a multiple of 256 and at most %d", who, h, kNormMaxHidden);
+    const size_t hyper_bytes = (size_t)t * nn->n * h * 4, mixed_bytes = (size_t)t * h * 2;
+    if (overlaps(nn->hyper, hyper_bytes, nn->mixed, mixed_bytes) ||
+        (y && (overlaps(y, (size_t)t * h * 4, nn->hyper, hyper_bytes) ||
+               overlaps(y, (size_t)t * h * 4, nn->mixed, mixed_bytes))))
+        return fail(MOE_ERR_INVALID, "%s: hyper, mixed and y must not overlap", who);
+    return MOE_OK;
+}
+
+// Gate/up, down and combine of a scheduled call (the schedule already
+// enqueued); with `nn` the combine's pass goes into the next fused norm
+// instead of writing out.
 static moe_status fused_gemms(GemmArgs a, int bm, const moe_layout *L, int t, int k, int E,
                               const uint32_t *csr_pos, const float *csr_w, float *out, int accumulate,
-                              const float *g, bool shared, hipStream_t s) {
+                              const float *g, bool shared, hipStream_t s, const moe_next_norm *nn = nullptr) {
     const size_t Q = (size_t)t * (k + (shared ? 1 : 0));
     a.max_tiles = (int)(Q / bm + (size_t)E + 2);
     a.w_off = L->gate_w;
@@ -221,8 +265,20 @@ static moe_status fused_gemms(GemmArgs a, int bm, const moe_layout *L, int t, in
     a.sb_off = L->down_sb;
     e = launch_down(a, bm, s);
     if (e != hipSuccess) return hip_fail(e, "experts down");
-    e = launch_combine(a.ye, csr_pos, csr_w, t, k, L->hidden, out, accumulate, s,
-                       shared ? a.ye + (size_t)t * k * L->hidden : nullptr, g);
+    const uint16_t *ys = shared ? a.ye + (size_t)t * k * L->hidden : nullptr;
+    if (nn) {
+        NextNormArgs n = next_norm_args(nn, t, L->hidden);
+        n.ye = a.ye;
+        n.pos = csr_pos;
+        n.csr_w = csr_w;
+        n.k = k;
+        n.ys = ys;
+        n.gate = g;
+        e = launch_next_norm(n, s);
+        if (e != hipSuccess) return hip_fail(e, "combine into the next norm");
+        return MOE_OK;
+    }
+    e = launch_combine(a.ye, csr_pos, csr_w, t, k, L->hidden, out, accumulate, s, ys, g);
     if (e != hipSuccess) return hip_fail(e, "combine");
     return MOE_OK;
 }
@@ -477,7 +533,7 @@ static moe_status block_run(const uint16_t *x, const float *w_router, int t, int
                             const uint64_t *records, const moe_layout *Ls, const void *shared_record,
                             const uint16_t *shared_gate_w, float *logits, uint32_t *topk_idx, float *topk_w,
                             uint32_t *offsets, uint32_t *csr_rows, float *csr_w, uint32_t *csr_pos, float *out,
-                            int accumulate, uint8_t *ws, hipStream_t s) {
+                            int accumulate, uint8_t *ws, hipStream_t s, const moe_next_norm *nn = nullptr) {
     const bool shared = Ls != nullptr;
     Workspace w;
     workspace_plan(t, k, E, L, Ls, &w);
@@ -511,7 +567,7 @@ static moe_status block_run(const uint16_t *x, const float *w_router, int t, int
         if (e != hipSuccess) return hip_fail(e, "grouping and schedule");
     }
     return fused_gemms(a, bm, L, t, k, E, csr_pos, csr_w, out, accumulate,
-                       (shared && shared_gate_w) ? reinterpret_cast<float *>(ws + w.gate) : nullptr, shared, s);
+                       (shared && shared_gate_w) ? reinterpret_cast<float *>(ws + w.gate) : nullptr, shared, s, nn);
 }
 
 // Scratch of moe_block_noalloc: one array per GPU, held by the loaded code
@@ -582,6 +638,34 @@ moe_status moe_block_noalloc(const uint16_t *x, const float *w_router, int32_t t
     if (moe_status st = scratch_ptr(&ws)) return st;
     return block_run(x, w_router, t, k, E, L, records, Ls, shared_record, shared_gate_w, logits, topk_idx, topk_w,
                      offsets, csr_rows, csr_w, csr_pos, out, accumulate, ws, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_inject_norm(const float *y, int32_t t, int32_t h, const moe_next_norm *nn, void *stream) {
+    if (moe_status st = check_rows(t)) return st;
+    if (moe_status st = check_next_norm(nn, t, h, y, "inject_norm")) return st;
+    NextNormArgs n = next_norm_args(nn, t, h);
+    n.y = y;
+    hipError_t e = launch_next_norm(n, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "inject_norm");
+    return MOE_OK;
+}
+
+moe_status moe_block_next_norm(const uint16_t *x, const float *w_router, int32_t t, int32_t k, int32_t E,
+                               const moe_layout *L, const uint64_t *records, const moe_layout *Ls,
+                               const void *shared_record, const uint16_t *shared_gate_w, float *logits,
+                               uint32_t *topk_idx, float *topk_w, uint32_t *offsets, uint32_t *csr_rows,
+                               float *csr_w, uint32_t *csr_pos, const moe_next_norm *nn, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+    if (!nn) return fail(MOE_ERR_INVALID, "block_next_norm: null next-norm description");
+    // the copies stand in for out in the shared checks (non-null, aligned)
+    if (moe_status st = block_check(x, w_router, t, k, E, L, records, Ls, shared_record, logits, topk_idx, topk_w,
+                                    offsets, csr_rows, csr_w, csr_pos, nn->hyper, workspace, workspace_bytes,
+                                    "block_next_norm"))
+        return st;
+    if (moe_status st = check_next_norm(nn, t, L->hidden, nullptr, "block_next_norm")) return st;
+    return block_run(x, w_router, t, k, E, L, records, Ls, shared_record, shared_gate_w, logits, topk_idx, topk_w,
+                     offsets, csr_rows, csr_w, csr_pos, nullptr, 0, static_cast<uint8_t *>(workspace),
+                     static_cast<hipStream_t>(stream), nn);
 }
 
 }  // extern "C"

@@ -140,4 +140,27 @@ hipError_t launch_combine(const uint16_t *ye, const uint32_t *pos, const float *
                           int k, int h, float *out, int accumulate, hipStream_t s,
                           const uint16_t *ys = nullptr, const float *gate = nullptr);
 
+// The block output injected into the n residual copies and read by the next
+// fused norm (norm.hip).  With ye set, y is formed from the down projections
+// as the combine forms it (ye, pos, csr_w, k, ys, gate as for launch_combine)
+// and never written; otherwise y is the fp32 [t][h] buffer (or nullptr: no
+// injection).
+struct NextNormArgs {
+    const uint16_t *ye;
+    const uint32_t *pos;
+    const float *csr_w;
+    const uint16_t *ys;
+    const float *gate;
+    const float *y;
+    int t, k, h, n;
+    float *hyper;          // fp32 [t][n][h], updated in place
+    float alpha[MOE_MAX_HC], beta[MOE_MAX_HC];
+    const float *gamma;    // fp32 [h]
+    // h <= kNormMaxHidden (8 columns per thread per 2048, at most 8 chunks)
+    float eps;
+    uint16_t *mixed;       // bf16 [t][h]
+};
+constexpr int kNormMaxHidden = 16384;
+hipError_t launch_next_norm(const NextNormArgs &a, hipStream_t s);
+
 }  // namespace moe

@@ -233,3 +233,59 @@ def test_block_validation(lib):
     assert call(ws=need - 256) == 3
     # without a shared expert the workspace of the routed experts alone suffices
     assert call(Ls=None, rec=None, ws=mep.moe_workspace_bytes(16, 2, 8, L, None) - 256) == 3
+
+
+def test_block_noalloc_refuses_beyond_its_scratch(lib):
+    """moe_block_noalloc checks the chunk's scratch against its static
+    64 MiB before touching the device: the full chunk (about 204 MiB) is
+    refused, as are the argument errors moe_block refuses."""
+    L = mep.moe_layout_make(2048, 768, 64)
+    assert mep.moe_workspace_bytes(4096, 8, 128, L, L) > mep.NOALLOC_SCRATCH_BYTES
+
+    def call(t=4096, k=8, E=128, w_router=P(FAKE)):
+        return lib.moe_block_noalloc(P(FAKE), w_router, t, k, E, ctypes.byref(L), P(FAKE), ctypes.byref(L), P(FAKE),
+                                     None, P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE),
+                                     0, None)
+
+    assert call() == 2 and "scratch" in lib.moe_last_error().decode()
+    assert call(t=0) == 2 and "empty chunk" in lib.moe_last_error().decode()
+    assert call(k=200) == 1
+    assert call(w_router=None) == 1
+
+
+def test_next_norm_validation(lib):
+    """moe_inject_norm and moe_block_next_norm refuse bad descriptions of the
+    residual copies before anything is enqueued."""
+    t, h = 16, 256
+    hyper, gamma, mixed = FAKE, FAKE + (1 << 20), FAKE + (2 << 20)
+
+    def nn(n=2, eps=1e-6, hy=hyper, gm=gamma, mx=mixed):
+        d = mep.moe_next_norm()
+        d.hyper, d.n, d.gamma, d.eps, d.mixed = hy, n, gm, eps, mx
+        return d
+
+    def inj(d, y=None, tt=t, hh=h):
+        return lib.moe_inject_norm(y, tt, hh, ctypes.byref(d), None)
+
+    assert inj(nn(n=0)) == 1 and inj(nn(n=17)) == 1
+    assert inj(nn(eps=-1.0)) == 1 and inj(nn(eps=float("inf"))) == 1
+    assert inj(nn(hy=None)) == 1 and inj(nn(gm=None)) == 1 and inj(nn(mx=None)) == 1
+    assert inj(nn(mx=mixed + 8)) == 1                                  # misaligned
+    assert inj(nn(), hh=200) == 1 and inj(nn(), hh=16640) == 1         # h % 256, h > 16384
+    assert inj(nn(mx=hyper + 4096)) == 1                               # mixed inside the copies
+    assert "overlap" in lib.moe_last_error().decode()
+    assert inj(nn(), y=P(hyper + 256)) == 1                            # y inside the copies
+    assert inj(nn(), tt=0) == 2 and inj(nn(), tt=4097) == 2
+    assert lib.moe_inject_norm(None, t, h, None, None) == 1
+    L = mep.moe_layout_make(h, 128, 32)
+    need = mep.moe_workspace_bytes(t, 2, 8, L, L)
+
+    def blk(d, ws=need):
+        return lib.moe_block_next_norm(P(FAKE), P(FAKE), t, 2, 8, ctypes.byref(L), P(FAKE), ctypes.byref(L),
+                                       P(FAKE), None, P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE),
+                                       ctypes.byref(d) if d is not None else None, P(FAKE), ws, None)
+
+    assert blk(None) == 1
+    assert blk(nn(n=0)) == 1
+    assert blk(nn(), ws=need - 256) == 3
+    assert blk(nn(mx=hyper)) == 1

@@ -32,6 +32,15 @@ Record format (the stored layout, moved verbatim by the expert ring):
   is (scale fp16, bias fp16), little-endian, scale first.
 * Weight value: ``W[n, k] = scale * q + bias`` for the group ``k // G``,
   with the code ``q`` unsigned in 0..15.
+
+Low-bit (2-bit) records, the form in which streamed experts may cross the
+host link: the same sections in the same order with the same scale/bias
+layout; codes are unsigned 0..3 and a code tile (32 rows x 64 columns) is
+512 bytes, tile (ob, kb) at ``(ob * (K/64) + kb) * 512``.  Lane ``L`` (row
+``32*ob + L % 32``, columns ``64*kb + 32*(L // 32) + c``, c in [0, 32)) owns
+two little-endian 32-bit words, word ``j`` at byte ``256 * j + 4 * L`` of
+the tile; code c sits in word ``c // 16`` at bit
+``2 * ((c % 16) // 2) + 16 * (c % 2)``.
 """
 from __future__ import annotations
 
@@ -143,11 +152,12 @@ def _align(n: int, a: int) -> int:
     return (n + a - 1) // a * a
 
 
-def layout(hidden: int, inter: int, group: int) -> Layout:
+def layout(hidden: int, inter: int, group: int, bits: int = 4) -> Layout:
     """Section offsets of the record format stated in this module's docstring."""
     assert group in (32, 64), "group must be 32 or 64"
+    assert bits in (2, 4), "codes of 4 or 2 bits"
     assert hidden % 64 == 0 and inter % 64 == 0, "hidden and inter must be multiples of 64"
-    codes = hidden * inter // 2
+    codes = hidden * inter * bits // 8
     sb = hidden * inter // group * 4
     off = 0
     out = {}
@@ -179,6 +189,21 @@ def pack_codes(q: np.ndarray) -> np.ndarray:
     return np.ascontiguousarray(words).astype("<u4").view(np.uint8).reshape(-1)
 
 
+def pack_codes2(q: np.ndarray) -> np.ndarray:
+    """Encode codes q[N, K] (values 0..3) into the tiled 2-bit code section bytes."""
+    N, K = q.shape
+    assert N % TILE_ROWS == 0 and K % TILE_COLS == 0
+    q = np.asarray(q, dtype=np.uint32)
+    assert q.max(initial=0) < 4
+    # n = 32*ob + r ; k = 64*kb + 32*half + 16*j + c16, c16 = 2*u + odd
+    v = q.reshape(N // 32, 32, K // 64, 2, 2, 16)                 # [ob, r, kb, half, j, c16]
+    c16 = np.arange(16)
+    shift = (2 * (c16 // 2) + 16 * (c16 % 2)).astype(np.uint32)
+    words = (v << shift).sum(axis=-1, dtype=np.uint32)            # [ob, r, kb, half, j]
+    words = words.transpose(0, 2, 4, 3, 1)                         # [ob, kb, j, half, r] -> lane = 32*half + r
+    return np.ascontiguousarray(words).astype("<u4").view(np.uint8).reshape(-1)
+
+
 def pack_sb(scale: np.ndarray, bias: np.ndarray, group: int) -> np.ndarray:
     """Encode fp16 scale/bias [N, K/G] into the tiled sb section bytes."""
     N, ng = scale.shape
@@ -191,36 +216,39 @@ def pack_sb(scale: np.ndarray, bias: np.ndarray, group: int) -> np.ndarray:
     return np.ascontiguousarray(e).astype("<u4").view(np.uint8).reshape(-1)
 
 
-def pack_record(L: Layout, mats: Dict[str, tuple]) -> np.ndarray:
+def pack_record(L: Layout, mats: Dict[str, tuple], bits: int = 4) -> np.ndarray:
     """Build one record from logical matrices: mats[m] = (q[N,K], scale[N,K/G], bias[N,K/G])."""
     rec = np.zeros(L.stride, dtype=np.uint8)
     for m in ("gate", "up", "down"):
         q, s, b = mats[m]
         assert q.shape == matrix_shape(L, m)
-        cw = pack_codes(q)
+        cw = pack_codes(q) if bits == 4 else pack_codes2(q)
         sb = pack_sb(s, b, L.group)
         rec[L.section(m + "_w"): L.section(m + "_w") + cw.size] = cw
         rec[L.section(m + "_sb"): L.section(m + "_sb") + sb.size] = sb
     return rec
 
 
-def random_record(L: Layout, g: np.random.Generator, centred: bool = False) -> np.ndarray:
+def random_record(L: Layout, g: np.random.Generator, centred: bool = False, bits: int = 4) -> np.ndarray:
     """One record with uniform codes, scale ~ U(0.005, 0.02) and bias ~ N(0, 0.01^2), as fp16.
 
     Codes are uniform random bytes, so their order inside the section does not
     matter.  ``centred`` draws bias = -7.5*scale + N(0, 0.01^2) so that weights
-    are roughly zero-mean.
+    are roughly zero-mean.  With ``bits`` = 2 the codes span 0..3, so the
+    scale is drawn 5 times larger (the weights then span the same range) and
+    the centred bias is -1.5*scale + N(0, 0.01^2).
     """
     rec = np.zeros(L.stride, dtype=np.uint8)
+    qmax = (1 << bits) - 1
     for m in ("gate", "up", "down"):
         N, K = matrix_shape(L, m)
-        nb = N * K // 2
+        nb = N * K * bits // 8
         rec[L.section(m + "_w"): L.section(m + "_w") + nb] = np.frombuffer(g.bytes(nb), dtype=np.uint8)
         ne = N * K // L.group
-        s = g.uniform(SCALE_LO, SCALE_HI, ne)
+        s = g.uniform(SCALE_LO, SCALE_HI, ne) * (15 / qmax)
         b = g.normal(0.0, BIAS_STD, ne)
         if centred:
-            b = b - 7.5 * s.astype(np.float16).astype(np.float64)
+            b = b - qmax / 2 * s.astype(np.float16).astype(np.float64)
         s16 = s.astype(np.float16).view(np.uint16).astype(np.uint32)
         b16 = b.astype(np.float16).view(np.uint16).astype(np.uint32)
         e = (s16 | (b16 << 16)).astype("<u4").view(np.uint8)
@@ -270,14 +298,15 @@ def make_router(cfg: Config, alpha: Optional[float] = None) -> np.ndarray:
     return w.astype(np.float32)
 
 
-def make_records(cfg: Config, experts: Optional[Iterable[int]] = None, centred: bool = False) -> np.ndarray:
+def make_records(cfg: Config, experts: Optional[Iterable[int]] = None, centred: bool = False,
+                 bits: int = 4) -> np.ndarray:
     """Records [n, stride] for the given experts (default: all E), each from its own stream."""
-    L = layout(cfg.hidden, cfg.inter, cfg.group)
+    L = layout(cfg.hidden, cfg.inter, cfg.group, bits)
     ids = list(range(cfg.experts)) if experts is None else list(experts)
     out = np.empty((len(ids), L.stride), dtype=np.uint8)
-    tag = "record_c" if centred else "record"
+    tag = ("record_c" if centred else "record") + ("" if bits == 4 else f"_b{bits}")
     for i, e in enumerate(ids):
-        out[i] = random_record(L, rng(cfg.name, tag, e), centred)
+        out[i] = random_record(L, rng(cfg.name, tag, e), centred, bits)
     return out
 
 

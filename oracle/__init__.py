@@ -45,15 +45,17 @@ def lib():
         _lib.orc_residency.argtypes = [P, I, I, P]
         _lib.orc_expert_rows.argtypes = [P, I, I, I, P, P, I, P]
         _lib.orc_shared.argtypes = [P, I, I, I, P, I, P, P]
-        _lib.orc_block.argtypes = [P, P, I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P]
-        _lib.orc_tokens_bruteforce.argtypes = [P, P, I, I, I, I, I, I, I, P, P, P, P, I, I, P]
+        _lib.orc_layout_bits.argtypes = [I, I, I, I, P]
+        _lib.orc_dequant2.argtypes = [P, P, I, I, I, P]
+        _lib.orc_block.argtypes = [P, P, I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P]
+        _lib.orc_tokens_bruteforce.argtypes = [P, P, I, I, I, I, I, I, I, P, P, P, P, P, I, I, P]
         _lib.orc_round_bf16.argtypes = [ctypes.c_double]
         _lib.orc_round_bf16.restype = ctypes.c_uint16
         _lib.orc_inject_norm.argtypes = [P, P, I, I, I, P, P, P, ctypes.c_double, P, P]
         _lib.orc_inject_norm.restype = ctypes.c_int
         _lib.orc_set_threads.argtypes = [I]
         _lib.orc_set_threads.restype = None
-        for f in ("orc_layout", "orc_router_logits", "orc_topk", "orc_build_csr", "orc_expert_rows",
+        for f in ("orc_layout", "orc_layout_bits", "orc_router_logits", "orc_topk", "orc_build_csr", "orc_expert_rows",
                   "orc_shared", "orc_block", "orc_tokens_bruteforce", "orc_max_threads"):
             getattr(_lib, f).restype = ctypes.c_int
     return _lib
@@ -81,21 +83,22 @@ def set_threads(n: int) -> None:
     lib().orc_set_threads(int(n))
 
 
-def layout(hidden: int, inter: int, group: int) -> dict:
+def layout(hidden: int, inter: int, group: int, bits: int = 4) -> dict:
     out = np.zeros(7, dtype=np.uint64)
-    _check(lib().orc_layout(hidden, inter, group, _p(out)), "layout")
+    _check(lib().orc_layout_bits(hidden, inter, group, bits, _p(out)), "layout")
     keys = ["gate_w", "gate_sb", "up_w", "up_sb", "down_w", "down_sb", "stride"]
     return {k: int(v) for k, v in zip(keys, out)}
 
 
-def dequant(record: np.ndarray, matrix: str, hidden: int, inter: int, group: int) -> np.ndarray:
-    """Decode matrix 'gate' | 'up' | 'down' of one record to float64 [N, K]."""
-    L = layout(hidden, inter, group)
+def dequant(record: np.ndarray, matrix: str, hidden: int, inter: int, group: int, bits: int = 4) -> np.ndarray:
+    """Decode matrix 'gate' | 'up' | 'down' of one record (4- or 2-bit codes) to float64 [N, K]."""
+    L = layout(hidden, inter, group, bits)
     N, K = (inter, hidden) if matrix in ("gate", "up") else (hidden, inter)
     rec = np.ascontiguousarray(record, dtype=np.uint8)
     W = np.empty((N, K), dtype=np.float64)
     base = rec.ctypes.data
-    lib().orc_dequant(base + L[matrix + "_w"], base + L[matrix + "_sb"], N, K, group, _p(W))
+    f = lib().orc_dequant if bits == 4 else lib().orc_dequant2
+    f(base + L[matrix + "_w"], base + L[matrix + "_sb"], N, K, group, _p(W))
     return W
 
 
@@ -164,13 +167,20 @@ def _record_ptrs(records: np.ndarray):
     return recs, ptrs
 
 
-def block(wl, shared_expert: bool = True, with_logits: bool = True):
+def _bits_arg(record_bits):
+    return None if record_bits is None else np.ascontiguousarray(record_bits, dtype=np.uint8)
+
+
+def block(wl, shared_expert: bool = True, with_logits: bool = True, record_bits=None):
     """Whole block through the grouped path. Returns dict of outputs (and the
-    router logits in the fixed fp32 order, unless with_logits is False)."""
+    router logits in the fixed fp32 order, unless with_logits is False).
+    record_bits[e] (4 or 2) gives the code width of expert e's record in
+    wl.records (a 2-bit record occupies the start of its row); None: all 4."""
     c = wl.cfg
     x = np.ascontiguousarray(wl.x, dtype=np.uint16)
     t = x.shape[0]
     recs, ptrs = _record_ptrs(wl.records)
+    rb = _bits_arg(record_bits)
     out = np.empty((t, c.hidden), dtype=np.float32)
     idx = np.empty((t, c.k), dtype=np.uint32)
     w = np.empty((t, c.k), dtype=np.float32)
@@ -182,7 +192,7 @@ def block(wl, shared_expert: bool = True, with_logits: bool = True):
     gate = None if wl.gate_w is None else np.ascontiguousarray(wl.gate_w, dtype=np.uint16)
     wr = np.ascontiguousarray(wl.w_router, dtype=np.float32)
     _check(lib().orc_block(_p(x), _p(wr), t, c.hidden, c.inter, c.inter_shared, c.experts, c.k, c.group,
-                           ptrs, _p(srec), _p(gate), _p(out), _p(idx), _p(w), _p(offsets), _p(rows),
+                           ptrs, _p(rb), _p(srec), _p(gate), _p(out), _p(idx), _p(w), _p(offsets), _p(rows),
                            _p(cw), _p(pos)), "block")
     res = dict(out=out, topk_idx=idx, topk_w=w, offsets=offsets, csr_rows=rows, csr_w=cw, csr_pos=pos)
     if with_logits:
@@ -218,9 +228,11 @@ def inject_norm(hyper: np.ndarray, y: Optional[np.ndarray], alpha, beta, gamma, 
     return hout, mixed
 
 
-def tokens_bruteforce(wl, sample: Sequence[int], order: int = 0, shared_expert: bool = True) -> np.ndarray:
+def tokens_bruteforce(wl, sample: Sequence[int], order: int = 0, shared_expert: bool = True,
+                      record_bits=None) -> np.ndarray:
     """Per-token outputs (float64) of the sample rows, computed without grouping."""
     c = wl.cfg
+    rb = _bits_arg(record_bits)
     x = np.ascontiguousarray(wl.x, dtype=np.uint16)
     recs, ptrs = _record_ptrs(wl.records)
     s = np.ascontiguousarray(sample, dtype=np.int32)
@@ -229,6 +241,6 @@ def tokens_bruteforce(wl, sample: Sequence[int], order: int = 0, shared_expert: 
     gate = None if wl.gate_w is None else np.ascontiguousarray(wl.gate_w, dtype=np.uint16)
     wr = np.ascontiguousarray(wl.w_router, dtype=np.float32)
     _check(lib().orc_tokens_bruteforce(_p(x), _p(wr), x.shape[0], c.hidden, c.inter, c.inter_shared,
-                                       c.experts, c.k, c.group, ptrs, _p(srec), _p(gate), _p(s), s.size,
+                                       c.experts, c.k, c.group, ptrs, _p(rb), _p(srec), _p(gate), _p(s), s.size,
                                        order, _p(out)), "tokens_bruteforce")
     return out

@@ -38,6 +38,11 @@
  *     (softmax, then top-k, then renormalise), in double, rounded to float.
  *   - int4 code: unsigned q in 0..15, W = scale * q + bias, per group of G
  *     along the input dimension; record layout as stated in orc_layout.
+ *   - Low-bit records of streamed experts (experts.rs page,
+ *     prepare_expert_jobs: transient misses take the miss layout of the
+ *     low-bit store; read_expert_batch keeps 4-bit and other reads apart):
+ *     the same affine group code with 2-bit q in 0..3, layout in
+ *     orc_layout_bits and orc_dequant2.
  *   - Combine order: shared expert first, then experts in ascending id.
  *   - Shared gate: none (factor 1) or sigmoid(x_r . gate_w).
  *   - Injection into the next fused norm (orc_inject_norm): the residual
@@ -102,11 +107,13 @@ static uint64_t align_up(uint64_t n, uint64_t a) { return (n + a - 1) / a * a; }
  * (rows = outputs), the shapes the experts.rs page gives its Q views in
  * pf_experts.  out = {gate_w, gate_sb, up_w, up_sb, down_w, down_sb, stride}.
  */
-int orc_layout(int hidden, int inter, int group, uint64_t out[7])
+int orc_layout_bits(int hidden, int inter, int group, int bits, uint64_t out[7])
 {
     if (!(group == 32 || group == 64) || hidden <= 0 || inter <= 0 || hidden % 64 || inter % 64)
         return ORC_BAD;
-    uint64_t codes = (uint64_t)hidden * inter / 2;
+    if (bits != 4 && bits != 2)
+        return ORC_BAD;
+    uint64_t codes = (uint64_t)hidden * inter * bits / 8;
     uint64_t sb = (uint64_t)hidden * inter / group * 4;
     uint64_t off = 0;
     for (int m = 0; m < 3; m++) {
@@ -117,6 +124,11 @@ int orc_layout(int hidden, int inter, int group, uint64_t out[7])
     }
     out[6] = align_up(off, 4096);
     return ORC_OK;
+}
+
+int orc_layout(int hidden, int inter, int group, uint64_t out[7])
+{
+    return orc_layout_bits(hidden, inter, group, 4, out);
 }
 
 /*
@@ -150,6 +162,49 @@ void orc_dequant(const uint8_t *w, const uint8_t *sb, int N, int K, int G, doubl
             W[(uint64_t)n * K + k] = s * q + b;
         }
     }
+}
+
+/*
+ * Decode a matrix [N x K] stored with 2-bit codes (the low-bit records of
+ * streamed experts).  Code tiles are 32 rows x 64 columns of 512 bytes, tile
+ * (ob, kb) at (ob*(K/64)+kb)*512; lane L of a tile (row 32*ob + L%32,
+ * columns 64*kb + 32*(L/32) + c, c in [0,32)) owns two little-endian 32-bit
+ * words, word j at byte 256*j + 4*L; code c is in word c/16 at bit
+ * 2*((c%16)/2) + 16*(c%2).  Scale/bias entries exactly as for 4-bit codes.
+ * W[n,k] = scale*q + bias with q in 0..3.
+ */
+void orc_dequant2(const uint8_t *w, const uint8_t *sb, int N, int K, int G, double *W)
+{
+    int kt = K / 64, per_tile = 64 / G;
+#pragma omp parallel for schedule(static)
+    for (int n = 0; n < N; n++) {
+        int ob = n / 32, r = n % 32;
+        for (int k = 0; k < K; k++) {
+            int kb = k / 64, half = (k % 64) / 32, c = k % 32;
+            uint64_t tile = (uint64_t)ob * kt + kb;
+            int lane = r + 32 * half;
+            const uint8_t *wp = w + tile * 512 + 256 * (c / 16) + 4 * lane;
+            uint32_t word = (uint32_t)wp[0] | ((uint32_t)wp[1] << 8) | ((uint32_t)wp[2] << 16) |
+                            ((uint32_t)wp[3] << 24);
+            int c16 = c % 16;
+            int bit = 2 * (c16 / 2) + 16 * (c16 % 2);
+            int q = (word >> bit) & 3;
+            int gi = (k % 64) / G;
+            const uint8_t *ep = sb + (tile * per_tile * 32 + (uint64_t)gi * 32 + r) * 4;
+            double s = f16_to_double((uint16_t)(ep[0] | (ep[1] << 8)));
+            double b = f16_to_double((uint16_t)(ep[2] | (ep[3] << 8)));
+            W[(uint64_t)n * K + k] = s * q + b;
+        }
+    }
+}
+
+/* Decode with the code width of the record (4 or 2 bits). */
+static void dequant_bits(const uint8_t *w, const uint8_t *sb, int N, int K, int G, int bits, double *W)
+{
+    if (bits == 2)
+        orc_dequant2(w, sb, N, K, G, W);
+    else
+        orc_dequant(w, sb, N, K, G, W);
 }
 
 /* ------------------------------------------------------------------ router */
@@ -305,8 +360,12 @@ typedef struct {
     int h, I;
 } ffn_weights;
 
-static int ffn_decode(const uint8_t *rec, const uint64_t lay[7], int h, int I, int G, ffn_weights *f)
+/* Decode one record whose codes are `bits` wide (its layout from orc_layout_bits). */
+static int ffn_decode_bits(const uint8_t *rec, int h, int I, int G, int bits, ffn_weights *f)
 {
+    uint64_t lay[7];
+    if (orc_layout_bits(h, I, G, bits, lay))
+        return ORC_BAD;
     f->h = h;
     f->I = I;
     f->g = malloc(sizeof(double) * (size_t)h * I);
@@ -314,10 +373,16 @@ static int ffn_decode(const uint8_t *rec, const uint64_t lay[7], int h, int I, i
     f->d = malloc(sizeof(double) * (size_t)h * I);
     if (!f->g || !f->u || !f->d)
         return ORC_BAD;
-    orc_dequant(rec + lay[0], rec + lay[1], I, h, G, f->g);
-    orc_dequant(rec + lay[2], rec + lay[3], I, h, G, f->u);
-    orc_dequant(rec + lay[4], rec + lay[5], h, I, G, f->d);
+    dequant_bits(rec + lay[0], rec + lay[1], I, h, G, bits, f->g);
+    dequant_bits(rec + lay[2], rec + lay[3], I, h, G, bits, f->u);
+    dequant_bits(rec + lay[4], rec + lay[5], h, I, G, bits, f->d);
     return ORC_OK;
+}
+
+static int ffn_decode(const uint8_t *rec, const uint64_t lay[7], int h, int I, int G, ffn_weights *f)
+{
+    (void)lay;
+    return ffn_decode_bits(rec, h, I, G, 4, f);
 }
 
 static void ffn_free(ffn_weights *f)
@@ -415,9 +480,9 @@ int orc_shared(const uint8_t *rec, int h, int Is, int G, const uint16_t *x, int 
  * returned too.  shared_rec may be NULL (no shared expert).
  */
 int orc_block(const uint16_t *x, const float *Wr, int t, int h, int I, int Is, int E, int k, int G,
-              const uint8_t *const *records, const uint8_t *shared_rec, const uint16_t *gate_w,
-              float *out, uint32_t *idx, float *wts, uint32_t *offsets, uint32_t *rows,
-              float *csr_w, uint32_t *pos)
+              const uint8_t *const *records, const uint8_t *rec_bits, const uint8_t *shared_rec,
+              const uint16_t *gate_w, float *out, uint32_t *idx, float *wts, uint32_t *offsets,
+              uint32_t *rows, float *csr_w, uint32_t *pos)
 {
     uint64_t lay[7];
     if (t < 1 || orc_layout(h, I, G, lay))
@@ -436,7 +501,7 @@ int orc_block(const uint16_t *x, const float *Wr, int t, int h, int I, int Is, i
         if (n == 0)
             continue;
         ffn_weights f;
-        if (ffn_decode(records[e], lay, h, I, G, &f)) {
+        if (ffn_decode_bits(records[e], h, I, G, rec_bits ? rec_bits[e] : 4, &f)) {
             rc = ORC_BAD;
             break;
         }
@@ -469,8 +534,9 @@ int orc_block(const uint16_t *x, const float *Wr, int t, int h, int I, int Is, i
  * expert is decoded once.  out_rows is [ns x h] double.
  */
 int orc_tokens_bruteforce(const uint16_t *x, const float *Wr, int t, int h, int I, int Is, int E, int k,
-                          int G, const uint8_t *const *records, const uint8_t *shared_rec,
-                          const uint16_t *gate_w, const int *sample, int ns, int order, double *out_rows)
+                          int G, const uint8_t *const *records, const uint8_t *rec_bits,
+                          const uint8_t *shared_rec, const uint16_t *gate_w, const int *sample, int ns,
+                          int order, double *out_rows)
 {
     uint64_t lay[7];
     if (orc_layout(h, I, G, lay) || k < 1 || k > E)
@@ -496,7 +562,7 @@ int orc_tokens_bruteforce(const uint16_t *x, const float *Wr, int t, int h, int 
         if (!used)
             continue;
         ffn_weights f;
-        if (ffn_decode(records[e], lay, h, I, G, &f)) {
+        if (ffn_decode_bits(records[e], h, I, G, rec_bits ? rec_bits[e] : 4, &f)) {
             rc = ORC_BAD;
             break;
         }

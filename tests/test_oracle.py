@@ -483,3 +483,84 @@ def test_inject_norm_zero_row_with_eps(orc):
     hyper[1] = 1.0
     _, mixed = orc.inject_norm(hyper, None, [1.0, -1.0], [0.0, 0.0], np.ones(64, np.float32), 1e-6)
     assert np.all(mixed == 0)
+
+
+# ------------------------------------------------------------------ low-bit (2-bit) records
+
+def test_layout_2bit_sizes(orc):
+    """2-bit records: code sections of h*I/4 bytes, the same scale/bias sections."""
+    for h, I, G in [(256, 128, 32), (2048, 768, 64), (4096, 1536, 64)]:
+        a = orc.layout(h, I, G, 2)
+        b = ms.layout(h, I, G, 2)
+        for k, v in a.items():
+            assert v == getattr(b, k), (h, I, G, k)
+        assert a["gate_sb"] - a["gate_w"] == -(-h * I // 4 // 256) * 256
+    assert orc.layout(4096, 1536, 64, 2)["stride"] == 3 * (4096 * 1536 // 4 + 4096 * 1536 // 64 * 4)  # 5,898,240
+
+
+def test_dequant2_codes_only(orc):
+    """scale = 1, bias = 0 -> W = q exactly (pins every 2-bit code position)."""
+    h, I, G = 256, 128, 32
+    L = ms.layout(h, I, G, 2)
+    g = np.random.default_rng(11)
+    mats = {}
+    for m in ("gate", "up", "down"):
+        N, K = ms.matrix_shape(L, m)
+        mats[m] = (g.integers(0, 4, (N, K)), np.ones((N, K // G)), np.zeros((N, K // G)))
+    rec = ms.pack_record(L, mats, bits=2)
+    for m in ("gate", "up", "down"):
+        W = orc.dequant(rec, m, h, I, G, bits=2)
+        assert np.array_equal(W, mats[m][0].astype(np.float64)), m
+
+
+def test_dequant2_hand_placed_byte(orc):
+    """Byte 2 of word 1 of lane 33 in tile 0 holds the codes of columns
+    32 + 16 + {1, 3, 5, 7} of row 1 (lane 33 = row 1, column half 1; byte 2
+    = bits 16-23 = the odd codes 1, 3, 5, 7 of the word's 16).  0xE4 puts
+    0, 1, 2, 3 there; every other weight is 0."""
+    h, I, G = 256, 128, 64
+    L = ms.layout(h, I, G, 2)
+    rec = np.zeros(L.stride, dtype=np.uint8)
+    sb = ms.pack_sb(np.ones((I, h // G)), np.zeros((I, h // G)), G)     # scale 1, bias 0
+    rec[L.gate_sb: L.gate_sb + sb.size] = sb
+    rec[L.gate_w + 256 * 1 + 4 * 33 + 2] = 0xE4
+    W = orc.dequant(rec, "gate", h, I, G, bits=2)
+    want = np.zeros((I, h))
+    want[1, [49, 51, 53, 55]] = [0, 1, 2, 3]
+    assert np.array_equal(W, want)
+
+
+@pytest.mark.parametrize("centred", [False, True])
+def test_2bit_record_equals_4bit_record_with_same_codes(orc, centred):
+    """A 2-bit record and a 4-bit record holding the same codes (0..3) and
+    scale/bias decode to the same weights, so the block over experts given
+    in either form is bitwise the same."""
+    h, I, G, E = 256, 128, 32, 6
+    wl = ms.small_case(40, 24, h, I, E, 2, G, centred=centred)
+    L2 = ms.layout(h, I, G, 2)
+    rng = np.random.default_rng(12)
+    rec4 = np.zeros_like(wl.records)
+    rec2 = np.zeros_like(wl.records)
+    for e in range(E):
+        mats = {}
+        for m in ("gate", "up", "down"):
+            N, K = ms.matrix_shape(wl.layout, m)
+            s = rng.uniform(0.02, 0.08, (N, K // G)).astype(np.float16)
+            b = rng.normal(0, 0.01, (N, K // G)).astype(np.float16)
+            if centred:
+                b = (b - 1.5 * s).astype(np.float16)
+            mats[m] = (rng.integers(0, 4, (N, K)), s, b)
+        rec4[e] = ms.pack_record(wl.layout, mats)
+        rec2[e, :L2.stride] = ms.pack_record(L2, mats, bits=2)
+        for m in ("gate", "up", "down"):
+            assert np.array_equal(orc.dequant(rec4[e], m, h, I, G), orc.dequant(rec2[e, :L2.stride], m, h, I, G, 2))
+    import dataclasses
+    bits = np.array([2, 4, 2, 2, 4, 2], dtype=np.uint8)
+    a = orc.block(dataclasses.replace(wl, records=rec4))
+    mixed = rec4.copy()
+    mixed[bits == 2] = rec2[bits == 2]
+    b = orc.block(dataclasses.replace(wl, records=mixed), record_bits=bits)
+    assert np.array_equal(a["out"], b["out"])
+    s = np.arange(0, 24, 5)
+    assert np.array_equal(orc.tokens_bruteforce(dataclasses.replace(wl, records=mixed), s, record_bits=bits),
+                          orc.tokens_bruteforce(dataclasses.replace(wl, records=rec4), s))

@@ -189,7 +189,7 @@ def cpu_baseline(cfg_name: str, rows: int, rows_1t: int):
             "single_thread": one}
 
 
-def build_block(cfg, all_resident: bool):
+def build_block(cfg, all_resident: bool, miss_bits: int = 4):
     """Device buffers of one workload.  Every expert resident: routing runs
     once on the GPU and only the records of experts some row picks are
     generated (the others are never read); with cfg.resident and not
@@ -216,8 +216,14 @@ def build_block(cfg, all_resident: bool):
         resident = np.zeros(cfg.experts, dtype=bool)
         resident[order[:cfg.resident]] = True
         wl = ms.make_workload(cfg)
-        blk = mep.MoeBlock.from_workload(wl, resident=resident)
-        del wl
+        miss = None
+        if miss_bits == 2:
+            # streamed experts cross the host link as 2-bit records
+            ids = np.nonzero(~resident)[0]
+            miss = np.zeros((cfg.experts, ms.layout(cfg.hidden, cfg.inter, cfg.group, 2).stride), np.uint8)
+            miss[ids] = ms.make_records(cfg, experts=ids.tolist(), bits=2)
+        blk = mep.MoeBlock.from_workload(wl, resident=resident, miss_records=miss)
+        del wl, miss
     else:
         pool = torch.empty((cfg.experts, blk.L.stride), dtype=torch.uint8, device="cuda")
         for i in range(0, touched.size, 32):
@@ -236,7 +242,7 @@ def measure(cfg, args, steps: int, warmup_steps, all_resident: bool = False, sep
     import mixture_experts_prefill_amd as mep
 
     log(f"[bench] workload {cfg.name}: generating and uploading ...")
-    blk, counts, resident = build_block(cfg, all_resident)
+    blk, counts, resident = build_block(cfg, all_resident, args.miss_bits)
     t = cfg.t
     # Weight copies rotated per step: the experts' records, the router weights
     # and the shared expert's record (a model's layers each have their own).
@@ -342,7 +348,7 @@ def measure(cfg, args, steps: int, warmup_steps, all_resident: bool = False, sep
         # streamed experts: the host link is the bound; the ring counters are
         # those of the last call (one step)
         rs = blk.ring.stats()
-        extra["ring"] = {"streamed_experts": rs["streamed"], "batches": rs["batches"],
+        extra["ring"] = {"streamed_experts": rs["streamed"], "batches": rs["batches"], "miss_bits": args.miss_bits,
                          "fetched_bytes_per_step": rs["fetched_bytes"],
                          "h2d_GBps": round(rs["fetched_bytes"] / step_s / 1e9, 2),
                          "host_wait_ms": round(rs["wait_ms"], 3)}
@@ -434,6 +440,8 @@ def main():
     ap.add_argument("--config", default="full")
     ap.add_argument("--all-resident", action="store_true",
                     help="large: every expert resident in HBM instead of the top 64 plus the ring")
+    ap.add_argument("--miss-bits", type=int, default=4, choices=(4, 2),
+                    help="large: code width of the streamed (non-resident) experts' records over the host link")
     ap.add_argument("--copies", type=int, default=0,
                     help="weight copies rotated per step (0: enough that a step's weights have left the "
                          "256 MB MALL before the same copy comes round again)")
@@ -499,6 +507,8 @@ def main():
     workload = f"{cfg.name}: {cfg.description}"
     if args.all_resident and cfg.resident:
         workload += " (here every expert resident in HBM)"
+    elif cfg.resident and args.miss_bits == 2:
+        workload += " (streamed experts as 2-bit records, expanded on the GPU)"
     line = {
         "metric": METRIC, "value": round(res["value"], 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": res["warmup"], "ms_per_step": round(res["ms_per_step"], 4), "higher_is_better": True,

@@ -74,7 +74,7 @@ const char *moe_last_error(void);
  * scale/bias section holds, per tile in the same order, (64/group)*32
  * entries of 4 bytes (fp16 scale, fp16 bias): entry gi*32 + row%32 for the
  * tile's group gi.  Sections are 256-byte aligned, the stride 4096-byte
- * aligned.  bits is always 4.
+ * aligned.  bits is 4 (2 for the miss records of moe_layout_make_bits).
  */
 typedef struct {
     int32_t hidden, inter, group, bits;
@@ -87,6 +87,22 @@ typedef struct {
  * Returns MOE_ERR_INVALID otherwise.  Host only; needs no GPU.
  */
 moe_status moe_layout_make(int32_t hidden, int32_t inter, int32_t group, moe_layout *out);
+
+/*
+ * The layout of a record with `bits`-wide codes: 4 (as moe_layout_make) or
+ * 2, the low-bit form in which streamed experts may cross the host link
+ * (experts.rs page, fn prepare_expert_jobs: transient misses take the miss
+ * layout of the low-bit store; fn read_expert_batch reads 4-bit and low-bit
+ * records into the ring separately).  A 2-bit record has the same sections,
+ * scale/bias layout and tile order; its codes are unsigned 0..3
+ * (weight = scale * q + bias), a code tile of 32 rows x 64 columns is 512
+ * bytes, and lane L of a tile (row 32*ob + L%32, columns
+ * 64*kb + 32*(L/32) + c, c in [0, 32)) owns two little-endian 32-bit
+ * words, word j at byte 256*j + 4*L, code c in word c/16 at bit
+ * 2*((c%16)/2) + 16*(c%2).  Only the ring takes 2-bit layouts
+ * (moe_ring_set_miss_layout); the compute calls take 4-bit ones.
+ */
+moe_status moe_layout_make_bits(int32_t hidden, int32_t inter, int32_t group, int32_t bits, moe_layout *out);
 
 /*
  * Bytes of the one workspace buffer that moe_build_csr, moe_shared and
@@ -176,12 +192,29 @@ moe_status moe_ring_create(const moe_layout *L, void *slots, int32_t n_slots, in
                            moe_ring **out);
 void moe_ring_destroy(moe_ring *ring);
 
+/*
+ * Streamed records in the 2-bit miss layout Lmiss [host] (made by
+ * moe_layout_make_bits with the ring's hidden, inter and group, bits = 2):
+ * from now on moe_prefill_experts copies each streamed expert's host record
+ * (Lmiss->stride bytes) into staging slot `slot` and, once the copy is in,
+ * expands it on the GPU into the 4-bit record in ring slot `slot` that the
+ * GEMMs read.  The expansion is exact (codes 0..3 are 4-bit codes, the
+ * scale/bias sections are copied), so results equal those of 4-bit records
+ * holding the same codes; only the bytes over the host link shrink
+ * (Lmiss->stride vs the ring's stride).  Staging slots follow the ring's
+ * reuse rule.
+ *   staging  device buffer of n_slots * Lmiss->stride bytes, 16-byte
+ *            aligned, owned by the caller; Lmiss = NULL returns to 4-bit
+ *            streamed records.
+ */
+moe_status moe_ring_set_miss_layout(moe_ring *ring, const moe_layout *Lmiss, void *staging);
+
 /* Counters of the last moe_prefill_experts call that used the ring. */
 typedef struct {
     int32_t jobs;           /* non-empty experts */
     int32_t streamed;       /* of which streamed through the ring */
     int32_t batches;        /* batches of `group` jobs */
-    uint64_t fetched_bytes; /* bytes copied host -> device (streamed * stride) */
+    uint64_t fetched_bytes; /* bytes copied host -> device (streamed * record bytes) */
     double wait_ms;         /* host time blocked in the call: the stream sync of the
                                offsets read-back (slot reuse itself is ordered on
                                the GPU by events, so the host never waits for a slot) */

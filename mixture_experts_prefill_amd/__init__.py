@@ -60,7 +60,8 @@ _lib = None
 EXPORTS = ["moe_last_error", "moe_layout_make", "moe_workspace_bytes", "moe_route", "moe_build_csr",
            "moe_shared", "moe_ring_create", "moe_ring_destroy", "moe_ring_get_stats", "moe_prefill_experts",
            "moe_ring_plan_debug", "moe_profile_begin", "moe_profile_end", "moe_profile_set_mask",
-           "moe_prefill_fused", "moe_block", "moe_block_noalloc", "moe_inject_norm", "moe_block_next_norm"]
+           "moe_prefill_fused", "moe_block", "moe_block_noalloc", "moe_inject_norm", "moe_block_next_norm",
+           "moe_layout_make_bits", "moe_ring_set_miss_layout"]
 NOALLOC_SCRATCH_BYTES = 64 << 20   # MOE_NOALLOC_SCRATCH_BYTES of include/moe.h
 PHASES = ["router", "topk", "csr", "shared_gateup", "shared_down", "schedule", "gateup", "down", "combine", "norm"]
 
@@ -77,6 +78,8 @@ def lib():
     LP = ctypes.POINTER(moe_layout)
     L.moe_last_error.restype = ctypes.c_char_p
     L.moe_layout_make.argtypes = [I, I, I, LP]
+    L.moe_layout_make_bits.argtypes = [I, I, I, I, LP]
+    L.moe_ring_set_miss_layout.argtypes = [P, LP, P]
     L.moe_workspace_bytes.argtypes = [I, I, I, LP, LP]
     L.moe_workspace_bytes.restype = Z
     L.moe_route.argtypes = [P, P, I, I, I, I, P, P, P, P]
@@ -100,7 +103,7 @@ def lib():
     L.moe_profile_set_mask.restype = None
     L.moe_profile_end.argtypes = [P, P]
     L.moe_profile_end.restype = ctypes.c_int
-    for f in ("moe_layout_make", "moe_route", "moe_build_csr", "moe_shared", "moe_ring_create",
+    for f in ("moe_layout_make", "moe_layout_make_bits", "moe_ring_set_miss_layout", "moe_route", "moe_build_csr", "moe_shared", "moe_ring_create",
               "moe_ring_get_stats", "moe_prefill_experts", "moe_prefill_fused", "moe_block", "moe_block_noalloc", "moe_inject_norm", "moe_block_next_norm"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
@@ -133,6 +136,12 @@ def _stream(stream) -> Optional[int]:
 def moe_layout_make(hidden: int, inter: int, group: int) -> moe_layout:
     out = moe_layout()
     _check(lib().moe_layout_make(hidden, inter, group, ctypes.byref(out)))
+    return out
+
+
+def moe_layout_make_bits(hidden: int, inter: int, group: int, bits: int) -> moe_layout:
+    out = moe_layout()
+    _check(lib().moe_layout_make_bits(hidden, inter, group, bits, ctypes.byref(out)))
     return out
 
 
@@ -175,6 +184,13 @@ class MoeRing:
     @property
     def handle(self):
         return self._h
+
+    def set_miss_layout(self, miss_layout: Optional[moe_layout], staging: Optional[torch.Tensor]):
+        """Streamed records in the 2-bit layout `miss_layout`, staged in
+        `staging` (n_slots * miss stride bytes on the device); None: 4-bit."""
+        self.staging = staging
+        _check(lib().moe_ring_set_miss_layout(self._h, ctypes.byref(miss_layout) if miss_layout is not None else None,
+                                              _ptr(staging)))
 
     def stats(self) -> dict:
         s = moe_ring_stats()

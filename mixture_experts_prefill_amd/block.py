@@ -26,7 +26,7 @@ import numpy as np
 import torch
 
 from . import (MoeRing, moe_block, moe_block_next_norm, moe_block_noalloc, moe_build_csr, moe_layout_make,
-               moe_prefill_experts, moe_prefill_fused, moe_route, moe_shared, moe_workspace_bytes)
+               moe_layout_make_bits, moe_prefill_experts, moe_prefill_fused, moe_route, moe_shared, moe_workspace_bytes)
 
 
 def bf16_tensor(bits: np.ndarray, device) -> torch.Tensor:
@@ -64,12 +64,13 @@ class MoeBlock:
 
     @classmethod
     def from_workload(cls, wl, device="cuda", resident: Optional[np.ndarray] = None, ring_slots: int = 64,
-                      group: int = 8, shared: bool = True):
-        """Upload a moe_synth workload.  resident[e] False -> expert e streams through a ring."""
+                      group: int = 8, shared: bool = True, miss_records: Optional[np.ndarray] = None):
+        """Upload a moe_synth workload.  resident[e] False -> expert e streams
+        through a ring (as its 2-bit record miss_records[e] when given)."""
         c = wl.cfg
         b = cls(wl.x.shape[0], c.hidden, c.inter, c.inter_shared if shared else None, c.experts, c.k, c.group, device)
         b.set_inputs(wl.x, wl.w_router)
-        b.set_records(wl.records, resident, ring_slots, group)
+        b.set_records(wl.records, resident, ring_slots, group, miss_records)
         if shared:
             b.set_shared(wl.shared_record, wl.gate_w)
         return b
@@ -79,7 +80,10 @@ class MoeBlock:
         self.w_router = torch.from_numpy(np.ascontiguousarray(w_router, dtype=np.float32)).to(self.device)
 
     def set_records(self, records: np.ndarray, resident: Optional[np.ndarray] = None, ring_slots: int = 64,
-                    group: int = 8):
+                    group: int = 8, miss_records: Optional[np.ndarray] = None):
+        """records [E, stride]: 4-bit records; resident[e] False streams expert e
+        through a ring, from miss_records[e] (2-bit, [E, miss stride]) when
+        given, else from records[e]."""
         E, stride = records.shape
         assert stride == self.L.stride and E == self.E
         if resident is None:
@@ -93,11 +97,17 @@ class MoeBlock:
         if resident.all():
             self.host_records, self.ring = None, None
             return
+        src = records if miss_records is None else miss_records
         self.host_records = [None] * E
         for e in np.nonzero(~resident)[0]:
-            self.host_records[e] = torch.from_numpy(records[e]).pin_memory()
+            self.host_records[e] = torch.from_numpy(np.ascontiguousarray(src[e])).pin_memory()
         self.ring_slots = torch.empty((ring_slots, stride), dtype=torch.uint8, device=self.device)
         self.ring = MoeRing(self.L, self.ring_slots, ring_slots, group)
+        if miss_records is not None:
+            self.Lmiss = moe_layout_make_bits(self.h, self.I, self.G, 2)
+            assert miss_records.shape[1] == self.Lmiss.stride
+            staging = torch.empty((ring_slots, self.Lmiss.stride), dtype=torch.uint8, device=self.device)
+            self.ring.set_miss_layout(self.Lmiss, staging)
 
     def set_pool(self, pool: torch.Tensor):
         """Every expert resident in `pool`, a device uint8 tensor [E, stride]

@@ -292,17 +292,22 @@ extern "C" {
 const char *moe_last_error(void) { return g_err.c_str(); }
 
 moe_status moe_layout_make(int32_t hidden, int32_t inter, int32_t group, moe_layout *out) {
+    return moe_layout_make_bits(hidden, inter, group, 4, out);
+}
+
+moe_status moe_layout_make_bits(int32_t hidden, int32_t inter, int32_t group, int32_t bits, moe_layout *out) {
     if (!out) return fail(MOE_ERR_INVALID, "layout: null output");
     if (hidden <= 0 || hidden % 256) return fail(MOE_ERR_INVALID, "hidden = %d must be a positive multiple of 256", hidden);
     if (inter <= 0 || inter % 64) return fail(MOE_ERR_INVALID, "inter = %d must be a positive multiple of 64", inter);
     if (group != 32 && group != 64) return fail(MOE_ERR_INVALID, "group = %d must be 32 or 64", group);
+    if (bits != 4 && bits != 2) return fail(MOE_ERR_INVALID, "bits = %d must be 4 or 2", bits);
     moe_layout L;
     std::memset(&L, 0, sizeof L);
     L.hidden = hidden;
     L.inter = inter;
     L.group = group;
-    L.bits = 4;
-    const uint64_t codes = (uint64_t)hidden * inter / 2;
+    L.bits = bits;
+    const uint64_t codes = (uint64_t)hidden * inter * bits / 8;
     const uint64_t sb = (uint64_t)hidden * inter / group * 4;
     uint64_t off = 0;
     uint64_t *secs[6] = {&L.gate_w, &L.gate_sb, &L.up_w, &L.up_sb, &L.down_w, &L.down_sb};

@@ -160,6 +160,23 @@ struct NextNormArgs {
     float eps;
     uint16_t *mixed;       // bf16 [t][h]
 };
+// 2-bit miss records expanded into 4-bit records (lowbit.hip): up to
+// kExpandMax records per launch, src in the miss layout, dst in the routed one.
+constexpr int kExpandMax = 16;
+struct ExpandJob {
+    const uint8_t *src;
+    uint8_t *dst;
+};
+struct ExpandArgs {
+    ExpandJob job[kExpandMax];
+    int n;
+    uint64_t src_w[3], src_sb[3], dst_w[3], dst_sb[3];  // gate, up, down sections
+    uint32_t tiles[3];                                   // code tiles of each matrix
+    uint32_t sb_bytes[3];                                // scale/bias bytes of each matrix
+};
+ExpandArgs expand_args(const moe_layout *L4, const moe_layout *L2);
+hipError_t launch_expand2(const ExpandArgs &a, hipStream_t s);
+
 constexpr int kNormMaxHidden = 16384;
 hipError_t launch_next_norm(const NextNormArgs &a, hipStream_t s);
 

@@ -124,21 +124,47 @@ moe_status ring_run(moe_ring *ring, const void *const *host_records, GemmArgs a,
                 for (int j = plan.batch_first[wb]; j < plan.batch_first[wb + 1]; ++j)
                     if (plan.jobs[j].streamed) {
                         e = hipMemsetAsync(st.slots + (size_t)plan.jobs[j].slot * st.stride, 0xFF, st.stride, st.copy);
+                        if (e == hipSuccess && st.lowbit)
+                            e = hipMemsetAsync(st.staging + (size_t)plan.jobs[j].slot * st.miss.stride, 0xFF,
+                                               st.miss.stride, st.copy);
                         if (e != hipSuccess) return hip_fail(e, "experts: poison");
                     }
             }
         }
+        // Streamed records: straight into their ring slot, or, in the 2-bit
+        // miss layout, into the slot's staging area (expanded below).
+        const uint64_t rec_bytes = st.lowbit ? st.miss.stride : st.stride;
         if (!st.skip_copy)
             for (int j = j0; j < j1; ++j) {
                 const RingJob &jb = plan.jobs[j];
                 if (!jb.streamed) continue;
-                e = hipMemcpyAsync(st.slots + (size_t)jb.slot * st.stride, host_records[jb.expert], st.stride,
-                                   hipMemcpyHostToDevice, st.copy);
+                uint8_t *dst = st.lowbit ? st.staging + (size_t)jb.slot * st.miss.stride
+                                         : st.slots + (size_t)jb.slot * st.stride;
+                e = hipMemcpyAsync(dst, host_records[jb.expert], rec_bytes, hipMemcpyHostToDevice, st.copy);
                 if (e != hipSuccess) return hip_fail(e, "experts: ring copy");
             }
         e = hipEventRecord(st.fetched[b], st.copy);
         if (e == hipSuccess) e = hipStreamWaitEvent(s, st.fetched[b], 0);
         if (e != hipSuccess) return hip_fail(e, "experts: fetched event");
+        if (st.lowbit) {
+            // the batch's 2-bit records become the 4-bit records its GEMMs read
+            ExpandArgs x = expand_args(L, &st.miss);
+            for (int j = j0; j < j1; ++j) {
+                const RingJob &jb = plan.jobs[j];
+                if (!jb.streamed) continue;
+                x.job[x.n++] = ExpandJob{st.staging + (size_t)jb.slot * st.miss.stride,
+                                         st.slots + (size_t)jb.slot * st.stride};
+                if (x.n == kExpandMax) {
+                    e = launch_expand2(x, s);
+                    if (e != hipSuccess) return hip_fail(e, "experts: expand low-bit records");
+                    x.n = 0;
+                }
+            }
+            if (x.n > 0) {
+                e = launch_expand2(x, s);
+                if (e != hipSuccess) return hip_fail(e, "experts: expand low-bit records");
+            }
+        }
 
         const int e0 = plan.jobs[j0].expert, e1 = plan.jobs[j1 - 1].expert + 1;
         e = launch_schedule(offsets, e0, e1, bm, a.records, const_cast<uint32_t *>(a.sched_n),
@@ -173,7 +199,7 @@ moe_status ring_run(moe_ring *ring, const void *const *host_records, GemmArgs a,
     st.stats.jobs = (int)plan.jobs.size();
     st.stats.streamed = streamed;
     st.stats.batches = nb;
-    st.stats.fetched_bytes = st.skip_copy ? 0 : (uint64_t)streamed * st.stride;
+    st.stats.fetched_bytes = st.skip_copy ? 0 : (uint64_t)streamed * (st.lowbit ? st.miss.stride : st.stride);
     st.stats.wait_ms = wait_ms;
     return MOE_OK;
 }
@@ -229,6 +255,30 @@ void moe_ring_destroy(moe_ring *r) {
     if (st.h_records) hipHostFree(st.h_records);
     if (st.h_jobs) hipHostFree(st.h_jobs);
     delete r;
+}
+
+moe_status moe_ring_set_miss_layout(moe_ring *ring, const moe_layout *Lmiss, void *staging) {
+    if (!ring) return fail(MOE_ERR_INVALID, "ring miss layout: null ring");
+    RingState &st = ring->st;
+    if (!Lmiss) {
+        st.lowbit = false;
+        st.staging = nullptr;
+        return MOE_OK;
+    }
+    moe_layout ref;
+    if (moe_layout_make_bits(Lmiss->hidden, Lmiss->inter, Lmiss->group, Lmiss->bits, &ref) != MOE_OK ||
+        std::memcmp(&ref, Lmiss, sizeof ref) || Lmiss->bits != 2)
+        return fail(MOE_ERR_INVALID, "ring miss layout: a 2-bit layout made by moe_layout_make_bits is required");
+    moe_layout L4;
+    if (moe_layout_make(Lmiss->hidden, Lmiss->inter, Lmiss->group, &L4) != MOE_OK || L4.stride != st.stride)
+        return fail(MOE_ERR_INVALID, "ring miss layout: shape (h %d, inter %d, group %d) differs from the ring's",
+                    Lmiss->hidden, Lmiss->inter, Lmiss->group);
+    if (!staging || (reinterpret_cast<uintptr_t>(staging) & 15))
+        return fail(MOE_ERR_INVALID, "ring miss layout: staging must be a 16-byte aligned device buffer");
+    st.miss = *Lmiss;
+    st.staging = static_cast<uint8_t *>(staging);
+    st.lowbit = true;
+    return MOE_OK;
 }
 
 moe_status moe_ring_get_stats(const moe_ring *ring, moe_ring_stats *out) {

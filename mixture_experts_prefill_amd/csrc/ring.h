@@ -44,6 +44,11 @@ struct RingState {
     uint32_t *h_offsets = nullptr;
     uint64_t *h_records = nullptr;
     uint64_t *h_jobs = nullptr;
+    // Streamed records in a 2-bit miss layout (moe_ring_set_miss_layout):
+    // copied into staging slots, then expanded into the 4-bit ring slots.
+    bool lowbit = false;
+    moe_layout miss{};
+    uint8_t *staging = nullptr;
     moe_ring_stats stats{};
     bool poison = false;      // fill released slots with 0xFF before reuse (test hook)
     int delay_us = 0;         // host sleep between batch enqueues (test hook)

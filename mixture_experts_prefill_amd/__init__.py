@@ -17,7 +17,8 @@ from typing import Optional, Sequence
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmoe.so")
+# MOE_LIB_PATH names another build of the same library (for side-by-side timing)
+LIB_PATH = os.environ.get("MOE_LIB_PATH") or os.path.join(_HERE, "libmoe.so")
 MAX_ROWS = 4096
 MAX_EXPERTS = 1024
 MAX_K = 32

@@ -30,8 +30,9 @@ def log(*a):
 
 
 # The dominant kernel's sources: the GEMM file and the headers it includes.
-KERNEL_SOURCES = ["mixture_experts_prefill_amd/csrc/gemm.hip", "mixture_experts_prefill_amd/csrc/moe_internal.h",
-                  "mixture_experts_prefill_amd/csrc/profile.h", "include/moe.h", "include/moe_debug.h"]
+KERNEL_SOURCES = ["mixture_experts_prefill_amd/csrc/gemm.hip", "mixture_experts_prefill_amd/csrc/lds_dma.h",
+                  "mixture_experts_prefill_amd/csrc/moe_internal.h", "mixture_experts_prefill_amd/csrc/profile.h",
+                  "include/moe.h", "include/moe_debug.h"]
 
 
 def source_hash() -> str:
@@ -79,7 +80,7 @@ def algorithmic(cfg, t, counts, fused=False):
 
 
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
-DOMINANT_KERNEL = "k_gemm<0, 128, 4>"   # routed gate/up, 128-row tiles, 4 waves
+DOMINANT_KERNEL = "k_gemm<0,"   # the grouped gate/up kernel (any tile height; 4 waves)
 COPY_PROBE_BYTES = 512 << 20
 
 

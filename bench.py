@@ -213,9 +213,11 @@ def build_block(cfg, all_resident: bool, miss_bits: int = 4):
     touched = np.nonzero(counts > 0)[0]
     resident = None
     if cfg.resident and not all_resident:
-        order = sorted(touched.tolist(), key=lambda e: -counts[e])
-        resident = np.zeros(cfg.experts, dtype=bool)
-        resident[order[:cfg.resident]] = True
+        # the most-used experts stay resident: ranked on the GPU from the offsets
+        order = torch.empty(cfg.experts, dtype=torch.int32, device="cuda")
+        keep = torch.empty(cfg.experts, dtype=torch.uint8, device="cuda")
+        mep.moe_residency(blk.offsets, cfg.resident, order, keep)
+        resident = keep.cpu().numpy().astype(bool)
         wl = ms.make_workload(cfg)
         miss = None
         if miss_bits == 2:

@@ -312,6 +312,40 @@ moe_status moe_block(const uint16_t *x, const float *w_router, int32_t t, int32_
                      size_t workspace_bytes, void *stream);
 
 /*
+ * Residency by use, on the GPU (experts.rs page, fn prepare_expert_jobs: the
+ * non-empty experts sorted by descending row count, ties kept in expert
+ * order, and the first `budget` of them kept resident, the rest streamed).
+ *
+ *   offsets  u32 [E+1] from moe_build_csr
+ *   order    u32 [E] output: order[i] = the i-th non-empty expert by use;
+ *            0xFFFFFFFF past the last non-empty one
+ *   keep     u8 [E] output: 1 for the first min(budget, non-empty) experts
+ *            of `order`, else 0
+ * Requires 1 <= E <= 1024, budget >= 0.  Enqueues one kernel; nothing is
+ * read back.
+ */
+moe_status moe_residency(const uint32_t *offsets, int32_t E, int32_t budget, uint32_t *order, uint8_t *keep,
+                         void *stream);
+
+/*
+ * One-block lookahead (decode.rs page, fn lookahead_layer: while a block
+ * runs, the next layer's experts are predicted from the current rows, one
+ * block ahead only): the next layer's router applied to this block's input
+ * x, its top-k, the predicted rows per expert and their residency by use,
+ * all on the GPU, so the next block's kept records can be fetched while
+ * this one computes.
+ *
+ *   x, t, h, E, k       as for moe_route; w_router_next fp32 [E][h]: the next
+ *                       layer's router
+ *   logits, topk_idx, topk_w   outputs as for moe_route (the prediction)
+ *   counts   u32 [E] output: predicted rows per expert
+ *   order, keep         outputs as for moe_residency, for `budget`
+ */
+moe_status moe_lookahead(const uint16_t *x, const float *w_router_next, int32_t t, int32_t h, int32_t E,
+                         int32_t k, int32_t budget, float *logits, uint32_t *topk_idx, float *topk_w,
+                         uint32_t *counts, uint32_t *order, uint8_t *keep, void *stream);
+
+/*
  * The next fused norm: a block's output injected into the residual stream
  * and read back as the next block's input (decode.rs page, fn step_rows: a
  * block's MoE output is "pending" until the next fused norm injects it;

@@ -62,7 +62,7 @@ EXPORTS = ["moe_last_error", "moe_layout_make", "moe_workspace_bytes", "moe_rout
            "moe_shared", "moe_ring_create", "moe_ring_destroy", "moe_ring_get_stats", "moe_prefill_experts",
            "moe_ring_plan_debug", "moe_profile_begin", "moe_profile_end", "moe_profile_set_mask",
            "moe_prefill_fused", "moe_block", "moe_block_noalloc", "moe_inject_norm", "moe_block_next_norm",
-           "moe_layout_make_bits", "moe_ring_set_miss_layout"]
+           "moe_layout_make_bits", "moe_ring_set_miss_layout", "moe_residency", "moe_lookahead"]
 NOALLOC_SCRATCH_BYTES = 64 << 20   # MOE_NOALLOC_SCRATCH_BYTES of include/moe.h
 PHASES = ["router", "topk", "csr", "shared_gateup", "shared_down", "schedule", "gateup", "down", "combine", "norm"]
 
@@ -97,6 +97,8 @@ def lib():
     NP = ctypes.POINTER(moe_next_norm)
     L.moe_inject_norm.argtypes = [P, I, I, NP, P]
     L.moe_block_next_norm.argtypes = [P, P, I, I, I, LP, P, LP, P, P, P, P, P, P, P, P, P, NP, P, Z, P]
+    L.moe_residency.argtypes = [P, I, I, P, P, P]
+    L.moe_lookahead.argtypes = [P, P, I, I, I, I, I, P, P, P, P, P, P, P]
     L.moe_ring_plan_debug.argtypes = [P, P, I, I, I, P, P, P]
     L.moe_profile_begin.argtypes = [ctypes.c_uint32]
     L.moe_profile_begin.restype = None
@@ -105,7 +107,8 @@ def lib():
     L.moe_profile_end.argtypes = [P, P]
     L.moe_profile_end.restype = ctypes.c_int
     for f in ("moe_layout_make", "moe_layout_make_bits", "moe_ring_set_miss_layout", "moe_route", "moe_build_csr", "moe_shared", "moe_ring_create",
-              "moe_ring_get_stats", "moe_prefill_experts", "moe_prefill_fused", "moe_block", "moe_block_noalloc", "moe_inject_norm", "moe_block_next_norm"):
+              "moe_ring_get_stats", "moe_prefill_experts", "moe_prefill_fused", "moe_block", "moe_block_noalloc", "moe_inject_norm", "moe_block_next_norm",
+              "moe_residency", "moe_lookahead"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -304,6 +307,22 @@ def moe_block_next_norm(x: torch.Tensor, w_router: torch.Tensor, k: int, layout:
                                      _ptr(topk_w), _ptr(offsets), _ptr(csr_rows), _ptr(csr_w), _ptr(csr_pos),
                                      ctypes.byref(nn), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                      _stream(stream)))
+
+
+def moe_residency(offsets: torch.Tensor, budget: int, order: torch.Tensor, keep: torch.Tensor, stream=None) -> None:
+    """Experts ranked by row count on the GPU: order int32 [E], keep uint8 [E]."""
+    E = offsets.numel() - 1
+    _check(lib().moe_residency(_ptr(offsets), E, budget, _ptr(order), _ptr(keep), _stream(stream)))
+
+
+def moe_lookahead(x: torch.Tensor, w_router_next: torch.Tensor, k: int, budget: int, logits: torch.Tensor,
+                  topk_idx: torch.Tensor, topk_w: torch.Tensor, counts: torch.Tensor, order: torch.Tensor,
+                  keep: torch.Tensor, stream=None) -> None:
+    """The next layer's routing on this block's input and its residency by use."""
+    t, h = x.shape
+    E = w_router_next.shape[0]
+    _check(lib().moe_lookahead(_ptr(x), _ptr(w_router_next), t, h, E, k, budget, _ptr(logits), _ptr(topk_idx),
+                               _ptr(topk_w), _ptr(counts), _ptr(order), _ptr(keep), _stream(stream)))
 
 
 def moe_ring_plan_debug(offsets, resident, n_slots: int = 64, group: int = 8):

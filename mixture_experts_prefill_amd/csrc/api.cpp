@@ -673,4 +673,27 @@ moe_status moe_block_next_norm(const uint16_t *x, const float *w_router, int32_t
                      static_cast<hipStream_t>(stream), nn);
 }
 
+moe_status moe_residency(const uint32_t *offsets, int32_t E, int32_t budget, uint32_t *order, uint8_t *keep,
+                         void *stream) {
+    if (E < 1 || E > MOE_MAX_EXPERTS) return fail(MOE_ERR_INVALID, "residency: E = %d outside 1..%d", E, MOE_MAX_EXPERTS);
+    if (budget < 0) return fail(MOE_ERR_INVALID, "residency: budget = %d < 0", budget);
+    if (!offsets || !order || !keep) return fail(MOE_ERR_INVALID, "residency: null pointer");
+    hipError_t e = launch_rank_experts(offsets, nullptr, 0, E, budget, nullptr, order, keep,
+                                       static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "residency");
+    return MOE_OK;
+}
+
+moe_status moe_lookahead(const uint16_t *x, const float *w_router_next, int32_t t, int32_t h, int32_t E,
+                         int32_t k, int32_t budget, float *logits, uint32_t *topk_idx, float *topk_w,
+                         uint32_t *counts, uint32_t *order, uint8_t *keep, void *stream) {
+    if (budget < 0) return fail(MOE_ERR_INVALID, "lookahead: budget = %d < 0", budget);
+    if (!counts || !order || !keep) return fail(MOE_ERR_INVALID, "lookahead: null pointer");
+    if (moe_status st = moe_route(x, w_router_next, t, h, E, k, logits, topk_idx, topk_w, stream)) return st;
+    hipError_t e = launch_rank_experts(nullptr, topk_idx, t * k, E, budget, counts, order, keep,
+                                       static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "lookahead");
+    return MOE_OK;
+}
+
 }  // extern "C"

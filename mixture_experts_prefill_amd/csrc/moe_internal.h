@@ -177,6 +177,11 @@ struct ExpandArgs {
 ExpandArgs expand_args(const moe_layout *L4, const moe_layout *L2);
 hipError_t launch_expand2(const ExpandArgs &a, hipStream_t s);
 
+// Experts ranked by row count (residency.hip): counts from offsets, or from
+// a top-k (topk_idx non-null, tk = t*k entries); counts may be nullptr.
+hipError_t launch_rank_experts(const uint32_t *offsets, const uint32_t *topk_idx, int tk, int E, int budget,
+                               uint32_t *counts, uint32_t *order, uint8_t *keep, hipStream_t s);
+
 constexpr int kNormMaxHidden = 16384;
 hipError_t launch_next_norm(const NextNormArgs &a, hipStream_t s);
 

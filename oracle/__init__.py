@@ -43,6 +43,7 @@ def lib():
         _lib.orc_topk.argtypes = [P, I, I, I, P, P]
         _lib.orc_build_csr.argtypes = [P, P, I, I, I, P, P, P, P]
         _lib.orc_residency.argtypes = [P, I, I, P]
+        _lib.orc_residency_order.argtypes = [P, I, I, P, P]
         _lib.orc_expert_rows.argtypes = [P, I, I, I, P, P, I, P]
         _lib.orc_shared.argtypes = [P, I, I, I, P, I, P, P]
         _lib.orc_layout_bits.argtypes = [I, I, I, I, P]
@@ -133,12 +134,16 @@ def build_csr(idx: np.ndarray, wts: np.ndarray, E: int):
     return offsets, rows, cw, pos
 
 
-def residency(offsets: np.ndarray, n_keep: int) -> np.ndarray:
+def residency(offsets: np.ndarray, n_keep: int, with_order: bool = False):
+    """keep[e] (bool) for the first n_keep non-empty experts by descending
+    rows (stable in id); with_order also returns that order (u32, 0xFFFFFFFF
+    past the last non-empty expert)."""
     offsets = np.ascontiguousarray(offsets, dtype=np.uint32)
     E = offsets.size - 1
     keep = np.empty(E, dtype=np.uint8)
-    lib().orc_residency(_p(offsets), E, n_keep, _p(keep))
-    return keep.astype(bool)
+    order = np.empty(E, dtype=np.uint32)
+    lib().orc_residency_order(_p(offsets), E, n_keep, _p(keep), _p(order))
+    return (keep.astype(bool), order) if with_order else keep.astype(bool)
 
 
 def expert_rows(record: np.ndarray, hidden: int, inter: int, group: int, x: np.ndarray,

@@ -326,9 +326,11 @@ done:
 
 /*
  * Residency: non-empty experts ordered by descending row count, stable in
- * expert id; the first n_keep are marked resident (keep[e] = 1).
+ * expert id; the first n_keep are marked resident (keep[e] = 1).  order
+ * (may be NULL) receives that order, 0xFFFFFFFF past the last non-empty
+ * expert.
  */
-void orc_residency(const uint32_t *offsets, int E, int n_keep, uint8_t *keep)
+void orc_residency_order(const uint32_t *offsets, int E, int n_keep, uint8_t *keep, uint32_t *order_out)
 {
     int *order = malloc(sizeof(int) * (size_t)E);
     int n = 0;
@@ -350,7 +352,15 @@ void orc_residency(const uint32_t *offsets, int E, int n_keep, uint8_t *keep)
     }
     for (int i = 0; i < n && i < n_keep; i++)
         keep[order[i]] = 1;
+    if (order_out)
+        for (int i = 0; i < E; i++)
+            order_out[i] = i < n ? (uint32_t)order[i] : 0xffffffffu;
     free(order);
+}
+
+void orc_residency(const uint32_t *offsets, int E, int n_keep, uint8_t *keep)
+{
+    orc_residency_order(offsets, E, n_keep, keep, NULL);
 }
 
 /* ------------------------------------------------------------------ expert FFN */

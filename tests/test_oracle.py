@@ -564,3 +564,20 @@ def test_2bit_record_equals_4bit_record_with_same_codes(orc, centred):
     s = np.arange(0, 24, 5)
     assert np.array_equal(orc.tokens_bruteforce(dataclasses.replace(wl, records=mixed), s, record_bits=bits),
                           orc.tokens_bruteforce(dataclasses.replace(wl, records=rec4), s))
+
+
+def test_residency_order_is_stable_sort_by_count(orc):
+    """The by-use order equals numpy's stable sort of the non-empty experts
+    by descending count (a library routine), and keep marks its first n."""
+    rng = np.random.default_rng(21)
+    for E in (1, 5, 64, 512, 1024):
+        counts = rng.integers(0, 6, E)          # many ties and empty experts
+        counts[rng.random(E) < 0.2] = 0
+        offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.uint32)
+        nz = np.nonzero(counts)[0]
+        want = nz[np.argsort(-counts[nz], kind="stable")]
+        for n_keep in (0, 1, 7, E, E + 3):
+            keep, order = orc.residency(offsets, n_keep, with_order=True)
+            assert np.array_equal(order[: want.size], want.astype(np.uint32))
+            assert (order[want.size:] == 0xFFFFFFFF).all()
+            assert np.array_equal(np.nonzero(keep)[0], np.sort(want[:n_keep]))

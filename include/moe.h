@@ -406,6 +406,34 @@ moe_status moe_block_next_norm(const uint16_t *x, const float *w_router, int32_t
                                size_t workspace_bytes, void *stream);
 
 /*
+ * A whole MoE sub-layer from the residual stream, in one call (prefill.rs
+ * page, fn pf_layer: pf_hc_read(mlp_hc, ..., mix_out) injects the pending
+ * attention output into the residual copies and produces the block input
+ * `mixed`, which router_b and the experts then read; decode.rs page,
+ * fn step_rows: the block's own output stays pending for the next fused
+ * norm):
+ *
+ *   1. in_norm:  pending_y (fp32 [t][h], or NULL) injected into
+ *                in_norm->hyper, the copies read and RMS-normalised into
+ *                in_norm->mixed (bf16 [t][h]), as moe_inject_norm;
+ *   2. the block (moe_block) on x = in_norm->mixed;
+ *   3. out_norm: NULL -> the block output is written to out (accumulate as
+ *                for moe_block); else it goes into the next fused norm as in
+ *                moe_block_next_norm (out and accumulate unused).
+ *
+ * The result is bitwise that of the separate calls in this order.  in_norm
+ * and out_norm may describe the same residual copies (their hyper pointers
+ * equal): the block's injection then follows the first read.
+ */
+moe_status moe_block_from_residual(const float *pending_y, const moe_next_norm *in_norm, const float *w_router,
+                                   int32_t t, int32_t k, int32_t E, const moe_layout *L, const uint64_t *records,
+                                   const moe_layout *Ls, const void *shared_record, const uint16_t *shared_gate_w,
+                                   float *logits, uint32_t *topk_idx, float *topk_w, uint32_t *offsets,
+                                   uint32_t *csr_rows, float *csr_w, uint32_t *csr_pos, const moe_next_norm *out_norm,
+                                   float *out, int32_t accumulate, void *workspace, size_t workspace_bytes,
+                                   void *stream);
+
+/*
  * moe_block without a workspace argument, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  Same arguments, outputs and arithmetic

@@ -62,7 +62,8 @@ EXPORTS = ["moe_last_error", "moe_layout_make", "moe_workspace_bytes", "moe_rout
            "moe_shared", "moe_ring_create", "moe_ring_destroy", "moe_ring_get_stats", "moe_prefill_experts",
            "moe_ring_plan_debug", "moe_profile_begin", "moe_profile_end", "moe_profile_set_mask",
            "moe_prefill_fused", "moe_block", "moe_block_noalloc", "moe_inject_norm", "moe_block_next_norm",
-           "moe_layout_make_bits", "moe_ring_set_miss_layout", "moe_residency", "moe_lookahead"]
+           "moe_layout_make_bits", "moe_ring_set_miss_layout", "moe_residency", "moe_lookahead",
+           "moe_block_from_residual"]
 NOALLOC_SCRATCH_BYTES = 64 << 20   # MOE_NOALLOC_SCRATCH_BYTES of include/moe.h
 PHASES = ["router", "topk", "csr", "shared_gateup", "shared_down", "schedule", "gateup", "down", "combine", "norm"]
 
@@ -99,6 +100,8 @@ def lib():
     L.moe_block_next_norm.argtypes = [P, P, I, I, I, LP, P, LP, P, P, P, P, P, P, P, P, P, NP, P, Z, P]
     L.moe_residency.argtypes = [P, I, I, P, P, P]
     L.moe_lookahead.argtypes = [P, P, I, I, I, I, I, P, P, P, P, P, P, P]
+    L.moe_block_from_residual.argtypes = [P, NP, P, I, I, I, LP, P, LP, P, P, P, P, P, P, P, P, P, NP, P, I, P, Z,
+                                          P]
     L.moe_ring_plan_debug.argtypes = [P, P, I, I, I, P, P, P]
     L.moe_profile_begin.argtypes = [ctypes.c_uint32]
     L.moe_profile_begin.restype = None
@@ -108,7 +111,7 @@ def lib():
     L.moe_profile_end.restype = ctypes.c_int
     for f in ("moe_layout_make", "moe_layout_make_bits", "moe_ring_set_miss_layout", "moe_route", "moe_build_csr", "moe_shared", "moe_ring_create",
               "moe_ring_get_stats", "moe_prefill_experts", "moe_prefill_fused", "moe_block", "moe_block_noalloc", "moe_inject_norm", "moe_block_next_norm",
-              "moe_residency", "moe_lookahead"):
+              "moe_residency", "moe_lookahead", "moe_block_from_residual"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -323,6 +326,25 @@ def moe_lookahead(x: torch.Tensor, w_router_next: torch.Tensor, k: int, budget: 
     E = w_router_next.shape[0]
     _check(lib().moe_lookahead(_ptr(x), _ptr(w_router_next), t, h, E, k, budget, _ptr(logits), _ptr(topk_idx),
                                _ptr(topk_w), _ptr(counts), _ptr(order), _ptr(keep), _stream(stream)))
+
+
+def moe_block_from_residual(pending_y: Optional[torch.Tensor], in_norm: moe_next_norm, w_router: torch.Tensor,
+                            t: int, k: int, layout: moe_layout, records: torch.Tensor,
+                            shared_layout: Optional[moe_layout], shared_record: Optional[torch.Tensor],
+                            shared_gate_w: Optional[torch.Tensor], logits: torch.Tensor, topk_idx: torch.Tensor,
+                            topk_w: torch.Tensor, offsets: torch.Tensor, csr_rows: torch.Tensor, csr_w: torch.Tensor,
+                            csr_pos: torch.Tensor, out_norm: Optional[moe_next_norm], out: Optional[torch.Tensor],
+                            accumulate: int, workspace: torch.Tensor, stream=None) -> None:
+    """The MoE sub-layer from the residual copies: input norm, block, output (or next norm)."""
+    E = w_router.shape[0]
+    _check(lib().moe_block_from_residual(_ptr(pending_y), ctypes.byref(in_norm), _ptr(w_router), t, k, E,
+                                         ctypes.byref(layout), _ptr(records),
+                                         ctypes.byref(shared_layout) if shared_layout is not None else None,
+                                         _ptr(shared_record), _ptr(shared_gate_w), _ptr(logits), _ptr(topk_idx),
+                                         _ptr(topk_w), _ptr(offsets), _ptr(csr_rows), _ptr(csr_w), _ptr(csr_pos),
+                                         ctypes.byref(out_norm) if out_norm is not None else None, _ptr(out),
+                                         accumulate, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                         _stream(stream)))
 
 
 def moe_ring_plan_debug(offsets, resident, n_slots: int = 64, group: int = 8):

@@ -696,4 +696,34 @@ moe_status moe_lookahead(const uint16_t *x, const float *w_router_next, int32_t 
     return MOE_OK;
 }
 
+moe_status moe_block_from_residual(const float *pending_y, const moe_next_norm *in_norm, const float *w_router,
+                                   int32_t t, int32_t k, int32_t E, const moe_layout *L, const uint64_t *records,
+                                   const moe_layout *Ls, const void *shared_record, const uint16_t *shared_gate_w,
+                                   float *logits, uint32_t *topk_idx, float *topk_w, uint32_t *offsets,
+                                   uint32_t *csr_rows, float *csr_w, uint32_t *csr_pos, const moe_next_norm *out_norm,
+                                   float *out, int32_t accumulate, void *workspace, size_t workspace_bytes,
+                                   void *stream) {
+    if (moe_status st = check_rows(t)) return st;
+    if (!in_norm) return fail(MOE_ERR_INVALID, "block_from_residual: null input-norm description");
+    if (!L) return fail(MOE_ERR_INVALID, "block_from_residual: null layout");
+    if (moe_status st = check_next_norm(in_norm, t, L->hidden, pending_y, "block_from_residual (input)")) return st;
+    // the block reads x = in_norm->mixed; out_norm stands in for out when given
+    const uint16_t *x = in_norm->mixed;
+    float *out_or_copies = out_norm ? out_norm->hyper : out;
+    if (moe_status st = block_check(x, w_router, t, k, E, L, records, Ls, shared_record, logits, topk_idx, topk_w,
+                                    offsets, csr_rows, csr_w, csr_pos, out_or_copies, workspace, workspace_bytes,
+                                    "block_from_residual"))
+        return st;
+    if (out_norm)
+        if (moe_status st = check_next_norm(out_norm, t, L->hidden, nullptr, "block_from_residual (output)")) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    NextNormArgs n = next_norm_args(in_norm, t, L->hidden);
+    n.y = pending_y;
+    hipError_t e = launch_next_norm(n, s);
+    if (e != hipSuccess) return hip_fail(e, "block_from_residual: input norm");
+    return block_run(x, w_router, t, k, E, L, records, Ls, shared_record, shared_gate_w, logits, topk_idx, topk_w,
+                     offsets, csr_rows, csr_w, csr_pos, out, accumulate, static_cast<uint8_t *>(workspace), s,
+                     out_norm);
+}
+
 }  // extern "C"

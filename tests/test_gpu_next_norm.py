@@ -217,3 +217,68 @@ def test_block_next_norm_zero_experts(mep, orc, name):
     ok, exact = within_one_bf16_ulp(r["m2"], ref_m, fp32_norm_slack(hyper, alpha, gamma, 1e-6))
     print(f"    next input bitwise {exact:.6f}", flush=True)
     assert ok and exact > 0.98
+
+
+def residual_inputs(seed, t, n, h):
+    hyper, y, a_in, b_in, g_in = rand_norm_inputs(seed, t, n, h)
+    rng = np.random.default_rng(seed + 1)
+    a_out = rng.uniform(-1, 1, n).astype(np.float32)
+    b_out = rng.uniform(-2, 2, n).astype(np.float32)
+    g_out = rng.uniform(0.25, 2, h).astype(np.float32)
+    return hyper, y, (a_in, b_in, g_in), (a_out, b_out, g_out)
+
+
+ROUTES = [("mid", 2, True), ("decode", 4, True), ("full", 4, False), ("tiny", 1, True)]
+
+
+@pytest.mark.parametrize("name,n,fused_out", ROUTES, ids=[f"{c[0]}-n{c[1]}-{'next' if c[2] else 'out'}" for c in ROUTES])
+def test_block_from_residual_matches_separate_calls(mep, orc, name, n, fused_out):
+    """moe_block_from_residual equals moe_inject_norm (the pending attention
+    output into the copies, the block input produced) followed by
+    moe_block_next_norm (or moe_block), bitwise, with the same residual
+    copies described for both norms; its block input is held to the
+    oracle's norm like moe_inject_norm."""
+    wl = ms.make_workload(name, centred=True)
+    t, h = wl.x.shape
+    hyper, y, (a_in, b_in, g_in), (a_out, b_out, g_out) = residual_inputs(500 + n, t, n, h)
+    blk = mep.MoeBlock.from_workload(wl)
+    d_y = torch.from_numpy(y).cuda()
+    g_in_d, g_out_d = torch.from_numpy(g_in).cuda(), torch.from_numpy(g_out).cuda()
+
+    def run(one_call):
+        copies = torch.from_numpy(hyper).cuda()
+        nxt = torch.full((t, h), -1, dtype=torch.int16, device="cuda")
+        blk.x.fill_(float("nan"))
+        blk.workspace.fill_(0xFF)
+        blk.out.fill_(float("nan"))
+        in_nn = mep.next_norm(copies, a_in, b_in, g_in_d, 1e-6, blk.x)
+        out_nn = mep.next_norm(copies, a_out, b_out, g_out_d, 1e-6, nxt) if fused_out else None
+        if one_call:
+            mep.moe_block_from_residual(d_y, in_nn, blk.w_router, t, blk.k, blk.L, blk.table, blk.Ls,
+                                        blk.shared_record, blk.gate_w, blk.logits, blk.topk_idx, blk.topk_w,
+                                        blk.offsets, blk.csr_rows, blk.csr_w, blk.csr_pos, out_nn,
+                                        None if fused_out else blk.out, 0, blk.workspace)
+        else:
+            mep.moe_inject_norm(d_y, t, h, in_nn)
+            if fused_out:
+                blk.block_next_norm(out_nn)
+            else:
+                blk.block(accumulate=0)
+        torch.cuda.synchronize()
+        res = dict(copies=copies.cpu().numpy(), x=blk.x.view(torch.int16).cpu().numpy(), nxt=nxt.cpu().numpy(),
+                   out=blk.out.cpu().numpy(), idx=blk.topk_idx.cpu().numpy(), rows=blk.csr_rows.cpu().numpy())
+        return res
+
+    a = run(False)
+    b = run(True)
+    for key in ("copies", "x", "nxt", "idx", "rows"):
+        assert np.array_equal(a[key], b[key]), key
+    if not fused_out:
+        assert np.array_equal(a["out"].view(np.uint32), b["out"].view(np.uint32))
+        assert np.isfinite(b["out"]).all()
+    # the block input against the oracle's injection and norm
+    ref_h, ref_x = orc.inject_norm(hyper, y, a_in, b_in, g_in, 1e-6)
+    ok, exact = within_one_bf16_ulp(b["x"], ref_x, fp32_norm_slack(ref_h, a_in, g_in, 1e-6))
+    print(f"    block input bitwise {exact:.6f}", flush=True)
+    assert ok and exact > 0.98
+    del blk

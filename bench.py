@@ -29,10 +29,13 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-# The dominant kernel's sources: the GEMM file and the headers it includes.
+# The dominant kernel's sources: the GEMM file, the headers whose code it
+# compiles, and the parts of the shared internal header it reads (its
+# argument and tile-entry structs and the tiling constants); the API
+# declarations around them do not change the kernel.
 KERNEL_SOURCES = ["mixture_experts_prefill_amd/csrc/gemm.hip", "mixture_experts_prefill_amd/csrc/lds_dma.h",
-                  "mixture_experts_prefill_amd/csrc/moe_internal.h", "mixture_experts_prefill_amd/csrc/profile.h",
-                  "include/moe.h", "include/moe_debug.h"]
+                  "mixture_experts_prefill_amd/csrc/profile.h"]
+KERNEL_HEADER = "mixture_experts_prefill_amd/csrc/moe_internal.h"
 
 
 def source_hash() -> str:
@@ -41,13 +44,19 @@ def source_hash() -> str:
     on, not to its prose or to the other kernels."""
     import re
 
+    def strip(text):
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        return " ".join(text.split())
+
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
         with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
-            text = fh.read()
-        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
-        text = re.sub(r"//[^\n]*", " ", text)
-        h.update(f.encode() + " ".join(text.split()).encode())
+            h.update(f.encode() + strip(fh.read()).encode())
+    with open(os.path.join(ROOT, KERNEL_HEADER), encoding="utf-8") as fh:
+        hdr = strip(fh.read())
+    parts = re.findall(r"struct (?:GemmArgs|TileEntry) \{.*?\};", hdr) + re.findall(r"constexpr int k\w+ = [^;]*;", hdr)
+    h.update(KERNEL_HEADER.encode() + " ".join(parts).encode())
     return h.hexdigest()[:16]
 
 

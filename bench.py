@@ -91,6 +91,8 @@ def algorithmic(cfg, t, counts, fused=False):
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 DOMINANT_KERNEL = "k_gemm<0,"   # the grouped gate/up kernel (any tile height; 4 waves)
 COPY_PROBE_BYTES = 512 << 20
+READ_PROBE_BYTES = 2 << 30     # read once by the HBM read probe: 8x the MALL
+READ_PROBE_BLOCKS = 16384
 
 
 def traffic_for(kernel_key: str):
@@ -428,12 +430,23 @@ def measure(cfg, args, steps: int, warmup_steps, all_resident: bool = False, sep
                               "saved_us": round((nn_ms["block_then_inject_norm"] - nn_ms["block_next_norm"]) * 1e3, 1)}
         del hyper, mixed
 
+    # The chunk report of the prefill.rs page (struct ChunkStats) for one
+    # step: rows and expert-row statistics of the last step's grouping, the
+    # records fetched over the host link (ring only), and the GPU time of the
+    # experts' launches, from an extra pass with every phase timed by events
+    # (per-launch durations; the events' own gaps stay out of `value`).
+    cs = blk.chunk_stats()
+    n_ph = steps if args.phases else min(steps, 10)
+    mep.moe_profile_begin(mep.PHASES)
+    for i in range(n_ph):
+        step(i)
+    torch.cuda.synchronize()
+    ph = mep.moe_profile_end()
+    expert_phases = ("shared_gateup", "shared_down", "gateup", "down", "combine")
+    cs["secs"] = round(step_s, 7)
+    cs["gpu_experts_s"] = round(sum(ph[p][0] for p in expert_phases if p in ph) / n_ph / 1e3, 7)
+    extra["chunk_stats"] = cs
     if args.phases:
-        mep.moe_profile_begin(mep.PHASES)
-        for i in range(steps):
-            step(i)
-        torch.cuda.synchronize()
-        ph = mep.moe_profile_end()
         extra["phase_us"] = {p: round(v[0] / v[1] * 1e3, 2) for p, v in ph.items()}
     res = dict(value=value, ms_per_step=ms_per_step, warmup=warmup, roofline=roofline, extra=extra,
                resident=int(resident.sum()) if resident is not None else cfg.experts)
@@ -441,6 +454,37 @@ def measure(cfg, args, steps: int, warmup_steps, all_resident: bool = False, sep
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return res
+
+
+def read_probe(reps: int = 5) -> dict:
+    """The HBM read probe (moe_debug_read_probe): best of `reps` event-timed
+    launches reading READ_PROBE_BYTES once, as the practical read ceiling the
+    weight-streaming launches are compared with (the roofline keeps the
+    published 8 TB/s as its peak)."""
+    import torch
+
+    import mixture_experts_prefill_amd as mep
+
+    src = torch.ones(READ_PROBE_BYTES // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(READ_PROBE_BLOCKS, dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        mep.moe_debug_read_probe(src, READ_PROBE_BLOCKS, sink)
+    torch.cuda.synchronize()
+    best = float("inf")
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        mep.moe_debug_read_probe(src, READ_PROBE_BLOCKS, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    del src, sink
+    torch.cuda.empty_cache()
+    gbs = READ_PROBE_BYTES / (best / 1e3) / 1e9
+    return {"kernel": "k_read_probe (16-byte non-temporal loads, grid-stride, 4 in flight per thread)",
+            "bytes": READ_PROBE_BYTES, "blocks": READ_PROBE_BLOCKS, "best_ms": round(best, 4),
+            "GBps": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
 
 
 def main():
@@ -470,6 +514,8 @@ def main():
                     help="time the dominant kernel's launch with HIP events in every N-th timed step")
     ap.add_argument("--separate", action="store_true",
                     help="run the shared expert as its own call (moe_shared) instead of inside the routed launches")
+    ap.add_argument("--read-probe", type=int, default=1,
+                    help="also time the HBM read probe (the device's practical read ceiling); 0 skips it")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, copy 512 MiB device-to-device (calibrates HBM byte counters)")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -502,7 +548,19 @@ def main():
                 "block_algorithmic_bytes": d["extra"]["block_algorithmic_bytes"],
                 "touched_experts": d["extra"]["touched_experts"], "weight_copies": d["extra"]["weight_copies"],
                 "warmup": d["warmup"], "step_ms_p10_p50_p90": d["extra"]["step_ms_p10_p50_p90"],
-                "roofline": d["roofline"], "next_norm": d["extra"].get("next_norm")}
+                "roofline": d["roofline"], "next_norm": d["extra"].get("next_norm"),
+                "chunk_stats": d["extra"]["chunk_stats"]}
+
+    if args.read_probe:
+        # The practical read ceiling of this device, for the HBM-bound rows.
+        probe = read_probe()
+        extra["hbm_read_probe"] = probe
+        for key in ("decode_t8", "decode1_t1"):
+            if key in extra:
+                d = extra[key]
+                d["block_frac_of_read_probe"] = round(d["block_hbm_frac"] * PEAK_HBM_GBS / probe["GBps"], 4)
+                if d["roofline"]["bound"] == "hbm":
+                    d["roofline"]["frac_of_read_probe"] = round(d["roofline"]["achieved"] / probe["GBps"], 4)
 
     if args.copy_probe:
         src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device="cuda")

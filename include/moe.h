@@ -346,6 +346,33 @@ moe_status moe_lookahead(const uint16_t *x, const float *w_router_next, int32_t 
                          uint32_t *counts, uint32_t *order, uint8_t *keep, void *stream);
 
 /*
+ * Row statistics of a grouped chunk, for the per-chunk report of the
+ * prefill.rs page (struct ChunkStats: tokens of the chunk; the records the
+ * experts' stage fetched and their bytes, which the ring's moe_ring_stats
+ * gives for streamed experts).  Filled on the device from the grouping's
+ * offsets, so the report costs no host synchronisation until it is read.
+ *
+ *   offsets  u32 [E+1] from moe_build_csr (or moe_block)
+ *   t        rows of the chunk (copied to tokens)
+ *   stats    device memory, 4-byte aligned: the output below
+ * Requires 1 <= E <= 1024, t >= 0.  Enqueues one kernel; nothing is read
+ * back.
+ */
+typedef struct {
+    uint32_t tokens;          /* t */
+    uint32_t assignments;     /* offsets[E] - offsets[0]: rows x experts per row */
+    uint32_t experts_touched; /* experts with at least one row */
+    uint32_t rows_max;        /* most rows of one expert (0 if none is touched) */
+    uint32_t rows_min;        /* fewest rows of a touched expert (0 if none) */
+    uint32_t rows_median;     /* lower median of the touched experts' row counts:
+                                 the count at 0-based position (n - 1) / 2 of the n
+                                 counts sorted ascending (0 if none) */
+    uint32_t pad[2];
+} moe_chunk_stats;
+moe_status moe_chunk_stats_fill(const uint32_t *offsets, int32_t t, int32_t E, moe_chunk_stats *stats,
+                                void *stream);
+
+/*
  * The next fused norm: a block's output injected into the residual stream
  * and read back as the next block's input (decode.rs page, fn step_rows: a
  * block's MoE output is "pending" until the next fused norm injects it;

@@ -1,5 +1,6 @@
 /*
- * moe_debug.h -- host-only inspection hooks of libmoe, for tests.
+ * moe_debug.h -- inspection and measurement hooks of libmoe, for tests and
+ * benchmarks.
  *
  * moe_ring_plan_debug: the expert ring's host schedule for one call, without
  * touching a GPU.  offsets [E+1] as produced by moe_build_csr; resident [E]
@@ -15,6 +16,7 @@
  */
 #ifndef MOE_DEBUG_H
 #define MOE_DEBUG_H
+#include <stddef.h>
 #include <stdint.h>
 #ifdef __cplusplus
 extern "C" {
@@ -52,6 +54,19 @@ int moe_profile_end(double *ms, int64_t *launches);
  * benchmark can time a sample of its steps' launches.
  */
 void moe_profile_set_mask(uint32_t mask);
+
+/*
+ * HBM read probe, the reference point of the HBM-bound kernels: one launch
+ * that reads `bytes` of device memory at `src` once (16-byte non-temporal
+ * loads, four in flight per thread, `blocks` workgroups of 256 threads in a
+ * grid-stride loop) and keeps nothing but a word per workgroup in `sink`
+ * (u32 [blocks], written only for one unlikely checksum, so the loads cannot
+ * be dropped).  Time it with events on `stream`: bytes / time is the read
+ * bandwidth a plain streaming kernel reaches on this device.  src 16-byte
+ * aligned, bytes a multiple of 16, 1 <= blocks <= 65536.  Returns 0, 1 for
+ * bad arguments, 5 for a launch error.
+ */
+int moe_debug_read_probe(const void *src, size_t bytes, int32_t blocks, uint32_t *sink, void *stream);
 #ifdef __cplusplus
 }
 #endif

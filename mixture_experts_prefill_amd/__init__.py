@@ -63,7 +63,7 @@ EXPORTS = ["moe_last_error", "moe_layout_make", "moe_workspace_bytes", "moe_rout
            "moe_ring_plan_debug", "moe_profile_begin", "moe_profile_end", "moe_profile_set_mask",
            "moe_prefill_fused", "moe_block", "moe_block_noalloc", "moe_inject_norm", "moe_block_next_norm",
            "moe_layout_make_bits", "moe_ring_set_miss_layout", "moe_residency", "moe_lookahead",
-           "moe_block_from_residual"]
+           "moe_block_from_residual", "moe_chunk_stats_fill", "moe_debug_read_probe"]
 NOALLOC_SCRATCH_BYTES = 64 << 20   # MOE_NOALLOC_SCRATCH_BYTES of include/moe.h
 PHASES = ["router", "topk", "csr", "shared_gateup", "shared_down", "schedule", "gateup", "down", "combine", "norm"]
 
@@ -99,6 +99,9 @@ def lib():
     L.moe_inject_norm.argtypes = [P, I, I, NP, P]
     L.moe_block_next_norm.argtypes = [P, P, I, I, I, LP, P, LP, P, P, P, P, P, P, P, P, P, NP, P, Z, P]
     L.moe_residency.argtypes = [P, I, I, P, P, P]
+    L.moe_chunk_stats_fill.argtypes = [P, I, I, P, P]
+    L.moe_debug_read_probe.argtypes = [P, Z, I, P, P]
+    L.moe_debug_read_probe.restype = ctypes.c_int
     L.moe_lookahead.argtypes = [P, P, I, I, I, I, I, P, P, P, P, P, P, P]
     L.moe_block_from_residual.argtypes = [P, NP, P, I, I, I, LP, P, LP, P, P, P, P, P, P, P, P, P, NP, P, I, P, Z,
                                           P]
@@ -111,7 +114,7 @@ def lib():
     L.moe_profile_end.restype = ctypes.c_int
     for f in ("moe_layout_make", "moe_layout_make_bits", "moe_ring_set_miss_layout", "moe_route", "moe_build_csr", "moe_shared", "moe_ring_create",
               "moe_ring_get_stats", "moe_prefill_experts", "moe_prefill_fused", "moe_block", "moe_block_noalloc", "moe_inject_norm", "moe_block_next_norm",
-              "moe_residency", "moe_lookahead", "moe_block_from_residual"):
+              "moe_residency", "moe_lookahead", "moe_block_from_residual", "moe_chunk_stats_fill"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -316,6 +319,36 @@ def moe_residency(offsets: torch.Tensor, budget: int, order: torch.Tensor, keep:
     """Experts ranked by row count on the GPU: order int32 [E], keep uint8 [E]."""
     E = offsets.numel() - 1
     _check(lib().moe_residency(_ptr(offsets), E, budget, _ptr(order), _ptr(keep), _stream(stream)))
+
+
+CHUNK_STATS_FIELDS = ["tokens", "assignments", "experts_touched", "rows_max", "rows_min", "rows_median"]
+
+
+def moe_chunk_stats_fill(offsets: torch.Tensor, t: int, stats: torch.Tensor, stream=None) -> None:
+    """Row statistics of a grouped chunk into `stats` (int32 [8] on the
+    device, the fields of CHUNK_STATS_FIELDS then two pad words)."""
+    if stats.numel() * stats.element_size() < 32:
+        raise ValueError("stats needs 32 bytes")
+    E = offsets.numel() - 1
+    _check(lib().moe_chunk_stats_fill(_ptr(offsets), t, E, _ptr(stats), _stream(stream)))
+
+
+def chunk_stats(offsets: torch.Tensor, t: int, stream=None) -> dict:
+    """moe_chunk_stats_fill, then the fields read back (synchronises)."""
+    stats = torch.empty(8, dtype=torch.int32, device=offsets.device)
+    moe_chunk_stats_fill(offsets, t, stats, stream)
+    v = stats.cpu().numpy().view("uint32")
+    return {f: int(v[i]) for i, f in enumerate(CHUNK_STATS_FIELDS)}
+
+
+def moe_debug_read_probe(src: torch.Tensor, blocks: int, sink: torch.Tensor, stream=None) -> None:
+    """One launch reading all of `src` (the HBM read probe); sink int32 [blocks]."""
+    nbytes = src.numel() * src.element_size()
+    if sink.numel() < blocks:
+        raise ValueError("sink needs one word per workgroup")
+    st = lib().moe_debug_read_probe(_ptr(src), nbytes, blocks, _ptr(sink), _stream(stream))
+    if st != 0:
+        raise MoeError(st, "read probe: bad arguments" if st == 1 else "read probe: launch failed")
 
 
 def moe_lookahead(x: torch.Tensor, w_router_next: torch.Tensor, k: int, budget: int, logits: torch.Tensor,

@@ -25,8 +25,9 @@ from typing import Optional, Sequence
 import numpy as np
 import torch
 
-from . import (MoeRing, moe_block, moe_block_next_norm, moe_block_noalloc, moe_build_csr, moe_layout_make,
-               moe_layout_make_bits, moe_prefill_experts, moe_prefill_fused, moe_route, moe_shared, moe_workspace_bytes)
+from . import (MoeRing, chunk_stats, moe_block, moe_block_next_norm, moe_block_noalloc, moe_build_csr,
+               moe_layout_make, moe_layout_make_bits, moe_prefill_experts, moe_prefill_fused, moe_route, moe_shared,
+               moe_workspace_bytes)
 
 
 def bf16_tensor(bits: np.ndarray, device) -> torch.Tensor:
@@ -138,6 +139,19 @@ class MoeBlock:
     def build_csr(self, stream=None):
         moe_build_csr(self.topk_idx, self.topk_w, self.E, self.offsets, self.csr_rows, self.csr_w, self.csr_pos,
                       self.workspace, stream)
+
+    def chunk_stats(self, stream=None) -> dict:
+        """Report of the last call (prefill.rs page, struct ChunkStats): its
+        rows and the grouping's expert-row statistics (moe_chunk_stats_fill),
+        and the records fetched over the host link, their bytes and the
+        host's wait for ring slots, all 0 when every expert is resident.
+        Synchronises."""
+        st = chunk_stats(self.offsets, self.t, stream)
+        rs = self.ring.stats() if self.ring is not None else None
+        st["fetched"] = rs["streamed"] if rs else 0
+        st["fetched_bytes"] = rs["fetched_bytes"] if rs else 0
+        st["wait_s"] = rs["wait_ms"] / 1e3 if rs else 0.0
+        return st
 
     def shared(self, accumulate: int = 0, stream=None):
         moe_shared(self.x, self.Ls, self.shared_record, self.gate_w, self.out, accumulate, self.workspace, stream)

@@ -684,6 +684,18 @@ moe_status moe_residency(const uint32_t *offsets, int32_t E, int32_t budget, uin
     return MOE_OK;
 }
 
+moe_status moe_chunk_stats_fill(const uint32_t *offsets, int32_t t, int32_t E, moe_chunk_stats *stats,
+                                void *stream) {
+    if (E < 1 || E > MOE_MAX_EXPERTS)
+        return fail(MOE_ERR_INVALID, "chunk stats: E = %d outside 1..%d", E, MOE_MAX_EXPERTS);
+    if (t < 0) return fail(MOE_ERR_INVALID, "chunk stats: t = %d < 0", t);
+    if (!offsets || !stats) return fail(MOE_ERR_INVALID, "chunk stats: null pointer");
+    if (reinterpret_cast<uintptr_t>(stats) & 3) return fail(MOE_ERR_INVALID, "chunk stats: stats not 4-byte aligned");
+    hipError_t e = launch_chunk_stats(offsets, t, E, stats, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "chunk stats");
+    return MOE_OK;
+}
+
 moe_status moe_lookahead(const uint16_t *x, const float *w_router_next, int32_t t, int32_t h, int32_t E,
                          int32_t k, int32_t budget, float *logits, uint32_t *topk_idx, float *topk_w,
                          uint32_t *counts, uint32_t *order, uint8_t *keep, void *stream) {

@@ -181,6 +181,8 @@ hipError_t launch_expand2(const ExpandArgs &a, hipStream_t s);
 // a top-k (topk_idx non-null, tk = t*k entries); counts may be nullptr.
 hipError_t launch_rank_experts(const uint32_t *offsets, const uint32_t *topk_idx, int tk, int E, int budget,
                                uint32_t *counts, uint32_t *order, uint8_t *keep, hipStream_t s);
+// Row statistics of a grouped chunk (residency.hip), into device memory.
+hipError_t launch_chunk_stats(const uint32_t *offsets, int t, int E, moe_chunk_stats *stats, hipStream_t s);
 
 constexpr int kNormMaxHidden = 16384;
 hipError_t launch_next_norm(const NextNormArgs &a, hipStream_t s);

@@ -1,0 +1,42 @@
+// HBM read probe: the bandwidth a plain streaming read reaches on this
+// device, against which the weight-streaming (decode-shaped) GEMM launches
+// are read.  Each thread issues four 16-byte non-temporal loads per
+// iteration of a grid-stride loop and folds them into one word; the word is
+// stored only for one checksum value, so the loads stay but nothing is
+// written in practice.
+#include <hip/hip_runtime.h>
+
+#include "../../include/moe_debug.h"
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ void __launch_bounds__(256) k_read_probe(const u32x4 *__restrict__ p, size_t n, uint32_t *__restrict__ sink) {
+    constexpr int U = 4;
+    const size_t stride = (size_t)gridDim.x * 256;
+    size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    uint32_t acc = 0;
+    for (; i + (U - 1) * stride < n; i += U * stride) {
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(p + i + u * stride);
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    for (; i < n; i += stride) {
+        const u32x4 v = __builtin_nontemporal_load(p + i);
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    if (acc == 0x9E3779B9u) sink[blockIdx.x] = acc;
+}
+
+}  // namespace
+
+extern "C" int moe_debug_read_probe(const void *src, size_t bytes, int32_t blocks, uint32_t *sink, void *stream) {
+    if (!src || !sink || (reinterpret_cast<uintptr_t>(src) & 15) || (bytes & 15) || blocks < 1 || blocks > 65536)
+        return 1;
+    hipLaunchKernelGGL(k_read_probe, dim3((unsigned)blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const u32x4 *>(src), bytes / 16, sink);
+    return hipGetLastError() == hipSuccess ? 0 : 5;
+}

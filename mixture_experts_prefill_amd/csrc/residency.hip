@@ -57,7 +57,64 @@ __global__ void __launch_bounds__(1024) k_rank_experts(const uint32_t *__restric
     }
 }
 
+// Row statistics of the chunk in one workgroup of 1024 threads: expert e's
+// row count from the offsets into LDS; touched / max / min by LDS atomics
+// (integer, so the result does not depend on their order); the median is
+// the count of the touched expert whose ascending rank (count, then expert
+// id) is (n - 1) / 2, found by the same broadcast loop as the ranking above.
+__global__ void __launch_bounds__(1024) k_chunk_stats(const uint32_t *__restrict__ offsets, int t, int E,
+                                                      moe_chunk_stats *__restrict__ out) {
+    __shared__ uint32_t cnt[MOE_MAX_EXPERTS];
+    __shared__ uint32_t touched, cmax, cmin, med;
+    const int tid = threadIdx.x;
+    if (tid == 0) {
+        touched = 0;
+        cmax = 0;
+        cmin = 0xffffffffu;
+        med = 0;
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += 1024) {
+        const uint32_t c = offsets[e + 1] - offsets[e];
+        cnt[e] = c;
+        if (c > 0) {
+            atomicAdd(&touched, 1u);
+            atomicMax(&cmax, c);
+            atomicMin(&cmin, c);
+        }
+    }
+    __syncthreads();
+    const uint32_t n = touched;
+    for (int e = tid; e < E; e += 1024) {
+        const uint32_t c = cnt[e];
+        if (c == 0) continue;
+        uint32_t rank = 0;
+        for (int j = 0; j < E; ++j) {
+            const uint32_t cj = cnt[j];
+            rank += (cj > 0) && (cj < c || (cj == c && j < e));
+        }
+        if (rank == (n - 1) / 2) med = c;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        moe_chunk_stats r;
+        r.tokens = (uint32_t)t;
+        r.assignments = offsets[E] - offsets[0];
+        r.experts_touched = n;
+        r.rows_max = cmax;
+        r.rows_min = n ? cmin : 0u;
+        r.rows_median = med;
+        r.pad[0] = r.pad[1] = 0;
+        *out = r;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_chunk_stats(const uint32_t *offsets, int t, int E, moe_chunk_stats *stats, hipStream_t s) {
+    hipLaunchKernelGGL(k_chunk_stats, dim3(1), dim3(1024), 0, s, offsets, t, E, stats);
+    return hipGetLastError();
+}
 
 hipError_t launch_rank_experts(const uint32_t *offsets, const uint32_t *topk_idx, int tk, int E, int budget,
                                uint32_t *counts, uint32_t *order, uint8_t *keep, hipStream_t s) {

@@ -289,3 +289,26 @@ def test_next_norm_validation(lib):
     assert blk(nn(n=0)) == 1
     assert blk(nn(), ws=need - 256) == 3
     assert blk(nn(mx=hyper)) == 1
+
+
+def test_chunk_stats_validation(lib):
+    """moe_chunk_stats_fill refuses bad arguments before anything is enqueued."""
+    f = lib.moe_chunk_stats_fill
+    assert f(P(FAKE), 16, 0, P(FAKE), None) == 1
+    assert f(P(FAKE), 16, 1025, P(FAKE), None) == 1
+    assert f(P(FAKE), -1, 8, P(FAKE), None) == 1
+    assert f(None, 16, 8, P(FAKE), None) == 1
+    assert f(P(FAKE), 16, 8, None, None) == 1
+    assert f(P(FAKE), 16, 8, P(FAKE + 2), None) == 1                   # stats misaligned
+    assert "aligned" in lib.moe_last_error().decode()
+
+
+def test_read_probe_validation(lib):
+    """moe_debug_read_probe refuses bad arguments without launching."""
+    f = lib.moe_debug_read_probe
+    assert f(None, 1 << 20, 64, P(FAKE), None) == 1
+    assert f(P(FAKE), 1 << 20, 64, None, None) == 1
+    assert f(P(FAKE + 8), 1 << 20, 64, P(FAKE), None) == 1              # src misaligned
+    assert f(P(FAKE), (1 << 20) + 4, 64, P(FAKE), None) == 1            # not whole 16-byte loads
+    assert f(P(FAKE), 1 << 20, 0, P(FAKE), None) == 1
+    assert f(P(FAKE), 1 << 20, 65537, P(FAKE), None) == 1

@@ -684,6 +684,18 @@ moe_status moe_residency(const uint32_t *offsets, int32_t E, int32_t budget, uin
     return MOE_OK;
 }
 
+int moe_debug_schedule(const uint32_t *offsets, int32_t E, int32_t bm, const uint64_t *records,
+                       const void *shared_rec, int32_t shared_p0, int32_t shared_n, uint32_t *sched_n,
+                       void *order, int32_t xcap, void *stream) {
+    if (!offsets || !records || !sched_n || !order || E < 1 || E > MOE_MAX_EXPERTS ||
+        (bm != 32 && bm != 64 && bm != 128) || xcap < 1 || shared_p0 < 0 || shared_n < 0 ||
+        (shared_rec && shared_n < 1))
+        return 1;
+    hipError_t e = launch_schedule(offsets, 0, E, bm, records, sched_n, static_cast<TileEntry *>(order), xcap,
+                                   static_cast<hipStream_t>(stream), SharedSeg{shared_rec, shared_p0, shared_n});
+    return e == hipSuccess ? 0 : 5;
+}
+
 moe_status moe_chunk_stats_fill(const uint32_t *offsets, int32_t t, int32_t E, moe_chunk_stats *stats,
                                 void *stream) {
     if (E < 1 || E > MOE_MAX_EXPERTS)

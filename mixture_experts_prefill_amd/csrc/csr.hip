@@ -263,7 +263,7 @@ __device__ __forceinline__ void schedule_body(const uint32_t *offsets, int e0, i
     __shared__ uint8_t tbl[MAXT];    // token blocks (32 rows) of each tile
     __shared__ uint8_t trows[MAXT];  // rows of each tile - 1
     __shared__ uint8_t xof[MAXT];    // XCD of each tile
-    __shared__ uint8_t tne[MAXT];    // tiles of its expert
+    __shared__ uint16_t tne[MAXT];   // tiles of its expert
     __shared__ uint16_t perm[MAXT];  // listing position -> tile
     __shared__ uint64_t erec[MOE_MAX_EXPERTS + 1]; // record address of each expert (+ shared)
     __shared__ uint32_t xstart[9];
@@ -293,6 +293,14 @@ __device__ __forceinline__ void schedule_body(const uint32_t *offsets, int e0, i
     }
     uint32_t T;
     uint32_t w = block_scan_1024(cnt, wsum, &T) - cnt;
+    // The tile arrays hold MAXT tiles and each XCD's list xcap: offsets that
+    // would need more (never those of a chunk whose size the host checked)
+    // schedule nothing rather than write past them.  T is the same in every
+    // thread, so the whole workgroup leaves together.
+    if (T > (uint32_t)MAXT || T > (uint32_t)xcap) {
+        if (tid < 16) sched_n[tid] = 0u;
+        return;
+    }
     for (int le = a; le < b; ++le) {
         uint32_t p0, n;
         seg(le, p0, n);
@@ -303,7 +311,7 @@ __device__ __forceinline__ void schedule_body(const uint32_t *offsets, int e0, i
             tp0[w] = p0 + m;
             tex[w] = (uint16_t)le;
             trows[w] = (uint8_t)(rows - 1);
-            tne[w] = (uint8_t)ne;
+            tne[w] = (uint16_t)ne;
             tbl[w] = (uint8_t)((rows + 31) / 32);
         }
     }

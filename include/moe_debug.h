@@ -72,7 +72,9 @@ int moe_debug_read_probe(const void *src, size_t bytes, int32_t blocks, uint32_t
  * The grouped GEMMs' tile schedule alone, for tests: the schedule kernel
  * that moe_prefill_experts and moe_prefill_fused enqueue before their GEMMs,
  * run on a CSR `offsets` [E+1] (device memory, non-decreasing) for experts
- * 0 .. E-1 with M-tiles of `bm` rows (32, 64 or 128), each entry's record
+ * 0 .. E-1 with M-tiles of `bm` rows (32, 64 or 128; `rows_bound` >= 0, the
+ * most rows a segment can hold, only picks how the kernel fills its tiles:
+ * the schedule is the same for any value), each entry's record
  * address taken from `records` [E] (device memory; only copied), plus an
  * optional segment of shared_n dense rows at positions shared_p0 .. with
  * record address shared_rec (NULL: none).  Writes sched_n (u32 [16], device:
@@ -83,7 +85,7 @@ int moe_debug_read_probe(const void *src, size_t bytes, int32_t blocks, uint32_t
  * zero and writes no entry.  Returns 0, 1 for bad arguments, 5 for a launch
  * error.
  */
-int moe_debug_schedule(const uint32_t *offsets, int32_t E, int32_t bm, const uint64_t *records,
+int moe_debug_schedule(const uint32_t *offsets, int32_t E, int32_t bm, int32_t rows_bound, const uint64_t *records,
                        const void *shared_rec, int32_t shared_p0, int32_t shared_n, uint32_t *sched_n,
                        void *order, int32_t xcap, void *stream);
 #ifdef __cplusplus

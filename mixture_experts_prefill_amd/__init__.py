@@ -103,7 +103,7 @@ def lib():
     L.moe_chunk_stats_fill.argtypes = [P, I, I, P, P]
     L.moe_debug_read_probe.argtypes = [P, Z, I, P, P]
     L.moe_debug_read_probe.restype = ctypes.c_int
-    L.moe_debug_schedule.argtypes = [P, I, I, P, P, I, I, P, P, I, P]
+    L.moe_debug_schedule.argtypes = [P, I, I, I, P, P, I, I, P, P, I, P]
     L.moe_debug_schedule.restype = ctypes.c_int
     L.moe_lookahead.argtypes = [P, P, I, I, I, I, I, P, P, P, P, P, P, P]
     L.moe_block_from_residual.argtypes = [P, NP, P, I, I, I, LP, P, LP, P, P, P, P, P, P, P, P, P, NP, P, I, P, Z,
@@ -354,15 +354,15 @@ def moe_debug_read_probe(src: torch.Tensor, blocks: int, sink: torch.Tensor, str
         raise MoeError(st, "read probe: bad arguments" if st == 1 else "read probe: launch failed")
 
 
-def moe_debug_schedule(offsets: torch.Tensor, bm: int, records: torch.Tensor, shared_rec: Optional[int],
-                       shared_p0: int, shared_n: int, sched_n: torch.Tensor, order: torch.Tensor, xcap: int,
-                       stream=None) -> None:
+def moe_debug_schedule(offsets: torch.Tensor, bm: int, rows_bound: int, records: torch.Tensor,
+                       shared_rec: Optional[int], shared_p0: int, shared_n: int, sched_n: torch.Tensor,
+                       order: torch.Tensor, xcap: int, stream=None) -> None:
     """The tile schedule alone (see include/moe_debug.h): sched_n int32 [16],
     order int32 [8 * xcap * 8] (32-byte entries)."""
     E = offsets.numel() - 1
     if sched_n.numel() * sched_n.element_size() < 64 or order.numel() * order.element_size() < 8 * xcap * 32:
         raise ValueError("sched_n needs 64 bytes and order 8 * xcap * 32 bytes")
-    st = lib().moe_debug_schedule(_ptr(offsets), E, bm, _ptr(records), shared_rec, shared_p0, shared_n,
+    st = lib().moe_debug_schedule(_ptr(offsets), E, bm, rows_bound, _ptr(records), shared_rec, shared_p0, shared_n,
                                   _ptr(sched_n), _ptr(order), xcap, _stream(stream))
     if st != 0:
         raise MoeError(st, "schedule: bad arguments" if st == 1 else "schedule: launch failed")

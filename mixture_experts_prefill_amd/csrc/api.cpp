@@ -470,7 +470,7 @@ moe_status moe_prefill_experts(const uint16_t *x, int32_t t, int32_t k, int32_t 
                         accumulate, reinterpret_cast<uint64_t *>(ws + w.jobs), s);
     }
 
-    hipError_t e = launch_schedule(offsets, 0, E, bm, records, const_cast<uint32_t *>(a.sched_n),
+    hipError_t e = launch_schedule(offsets, 0, E, bm, t, records, const_cast<uint32_t *>(a.sched_n),
                                    const_cast<TileEntry *>(a.order), a.xcap, s);
     if (e != hipSuccess) return hip_fail(e, "schedule");
     a.w_off = L->gate_w;
@@ -506,7 +506,7 @@ moe_status moe_prefill_fused(const uint16_t *x, int32_t t, int32_t k, int32_t E,
     GemmArgs a = fused_args(x, t, k, E, L, csr_rows, records, ws, w, true);
     const int bm = pick_bm(t, k, E, L->inter, L->hidden);
     if (moe_status st = shared_gate(x, t, L, shared_gate_w, ws + w.gate, s)) return st;
-    hipError_t e = launch_schedule(offsets, 0, E, bm, records, const_cast<uint32_t *>(a.sched_n),
+    hipError_t e = launch_schedule(offsets, 0, E, bm, t, records, const_cast<uint32_t *>(a.sched_n),
                                    const_cast<TileEntry *>(a.order), a.xcap, s,
                                    SharedSeg{shared_record, a.shared_p0, t});
     if (e != hipSuccess) return hip_fail(e, "schedule");
@@ -684,14 +684,14 @@ moe_status moe_residency(const uint32_t *offsets, int32_t E, int32_t budget, uin
     return MOE_OK;
 }
 
-int moe_debug_schedule(const uint32_t *offsets, int32_t E, int32_t bm, const uint64_t *records,
+int moe_debug_schedule(const uint32_t *offsets, int32_t E, int32_t bm, int32_t rows_bound, const uint64_t *records,
                        const void *shared_rec, int32_t shared_p0, int32_t shared_n, uint32_t *sched_n,
                        void *order, int32_t xcap, void *stream) {
     if (!offsets || !records || !sched_n || !order || E < 1 || E > MOE_MAX_EXPERTS ||
-        (bm != 32 && bm != 64 && bm != 128) || xcap < 1 || shared_p0 < 0 || shared_n < 0 ||
+        (bm != 32 && bm != 64 && bm != 128) || rows_bound < 0 || xcap < 1 || shared_p0 < 0 || shared_n < 0 ||
         (shared_rec && shared_n < 1))
         return 1;
-    hipError_t e = launch_schedule(offsets, 0, E, bm, records, sched_n, static_cast<TileEntry *>(order), xcap,
+    hipError_t e = launch_schedule(offsets, 0, E, bm, rows_bound, records, sched_n, static_cast<TileEntry *>(order), xcap,
                                    static_cast<hipStream_t>(stream), SharedSeg{shared_rec, shared_p0, shared_n});
     return e == hipSuccess ? 0 : 5;
 }

@@ -73,8 +73,10 @@ struct SharedSeg {
     const void *rec;
     int p0, n;
 };
-hipError_t launch_schedule(const uint32_t *offsets, int e0, int e1, int bm, const uint64_t *records,
-                           uint32_t *sched_n, TileEntry *order, int xcap, hipStream_t s,
+// rows_bound: the most rows a segment can hold (the chunk's t); only picks
+// how the tiles are filled, any value gives the same schedule.
+hipError_t launch_schedule(const uint32_t *offsets, int e0, int e1, int bm, int rows_bound,
+                           const uint64_t *records, uint32_t *sched_n, TileEntry *order, int xcap, hipStream_t s,
                            SharedSeg sh = SharedSeg{nullptr, 0, 0});
 
 // Grouping and schedule in one workgroup and one launch, for chunks whose

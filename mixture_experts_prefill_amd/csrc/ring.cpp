@@ -167,7 +167,7 @@ moe_status ring_run(moe_ring *ring, const void *const *host_records, GemmArgs a,
         }
 
         const int e0 = plan.jobs[j0].expert, e1 = plan.jobs[j1 - 1].expert + 1;
-        e = launch_schedule(offsets, e0, e1, bm, a.records, const_cast<uint32_t *>(a.sched_n),
+        e = launch_schedule(offsets, e0, e1, bm, t, a.records, const_cast<uint32_t *>(a.sched_n),
                             const_cast<TileEntry *>(a.order), a.xcap, s);
         if (e != hipSuccess) return hip_fail(e, "experts: schedule");
         int rows = 0;

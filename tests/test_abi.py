@@ -317,16 +317,17 @@ def test_read_probe_validation(lib):
 def test_schedule_debug_validation(lib):
     """moe_debug_schedule refuses bad arguments without launching."""
     f = lib.moe_debug_schedule
-    ok = dict(off=P(FAKE), E=8, bm=128, rec=P(FAKE), srec=None, sp0=0, sn=0, sched=P(FAKE), order=P(FAKE), xcap=64)
+    ok = dict(off=P(FAKE), E=8, bm=128, rb=4096, rec=P(FAKE), srec=None, sp0=0, sn=0, sched=P(FAKE),
+              order=P(FAKE), xcap=64)
 
     def call(**kw):
         a = dict(ok, **kw)
-        return f(a["off"], a["E"], a["bm"], a["rec"], a["srec"], a["sp0"], a["sn"], a["sched"], a["order"],
-                 a["xcap"], None)
+        return f(a["off"], a["E"], a["bm"], a["rb"], a["rec"], a["srec"], a["sp0"], a["sn"], a["sched"],
+                 a["order"], a["xcap"], None)
 
     assert call(off=None) == 1 and call(rec=None) == 1 and call(sched=None) == 1 and call(order=None) == 1
     assert call(E=0) == 1 and call(E=1025) == 1
     assert call(bm=48) == 1 and call(bm=256) == 1
-    assert call(xcap=0) == 1
+    assert call(xcap=0) == 1 and call(rb=-1) == 1
     assert call(sp0=-1) == 1 and call(sn=-1) == 1
     assert call(srec=P(FAKE), sn=0) == 1                               # a shared record needs rows

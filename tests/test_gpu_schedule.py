@@ -54,7 +54,7 @@ def model(offsets, bm, records, shared):
     return sched_n, lists
 
 
-def run(offsets, bm, records, shared, xcap=None):
+def run(offsets, bm, records, shared, xcap=None, rows_bound=0):
     import mixture_experts_prefill_amd as mep
 
     E = len(offsets) - 1
@@ -66,7 +66,7 @@ def run(offsets, bm, records, shared, xcap=None):
     sched_n = torch.full((16,), -7, dtype=torch.int32, device="cuda")
     # room for 8 full lists of `cap` entries whatever xcap is passed
     order = torch.full((8 * max(cap, xcap) * 8,), -5, dtype=torch.int32, device="cuda")
-    mep.moe_debug_schedule(d_off, bm, d_rec, shared[0] if shared else None, shared[1] if shared else 0,
+    mep.moe_debug_schedule(d_off, bm, rows_bound, d_rec, shared[0] if shared else None, shared[1] if shared else 0,
                            shared[2] if shared else 0, sched_n, order, xcap)
     torch.cuda.synchronize()
     sn = sched_n.cpu().numpy().astype(np.int64)
@@ -75,17 +75,20 @@ def run(offsets, bm, records, shared, xcap=None):
 
 
 def check(offsets, bm, records, shared):
+    """Both ways the kernel fills its tiles (one thread per segment, or all
+    threads with a search: picked by the rows bound) give the model's lists."""
     want_n, want = model(offsets, bm, records, shared)
-    sn, ent, xcap = run(offsets, bm, records, shared)
-    assert sn[0] == want_n[0] and list(sn[8:16]) == want_n[8:16], (list(sn), want_n)
-    for x in range(8):
-        got = []
-        for q in range(want_n[8 + x]):
-            e = ent[x * xcap + q]
-            rec = int(np.array(e[4:6], np.int32).view(np.uint64)[0])
-            got.append((int(e[0]), int(e[1]), int(e[2]), int(e[3]), rec))
-            assert e[6] == 0 and e[7] == 0
-        assert got == want[x], x
+    for rows_bound in (0, 1 << 20):
+        sn, ent, xcap = run(offsets, bm, records, shared, rows_bound=rows_bound)
+        assert sn[0] == want_n[0] and list(sn[8:16]) == want_n[8:16], (rows_bound, list(sn), want_n)
+        for x in range(8):
+            got = []
+            for q in range(want_n[8 + x]):
+                e = ent[x * xcap + q]
+                rec = int(np.array(e[4:6], np.int32).view(np.uint64)[0])
+                got.append((int(e[0]), int(e[1]), int(e[2]), int(e[3]), rec))
+                assert e[6] == 0 and e[7] == 0
+            assert got == want[x], (rows_bound, x)
 
 
 def random_offsets(rng, E, total, zipf=None, empty=0.3):
@@ -139,6 +142,7 @@ def test_schedule_refuses_lists_too_small():
     offsets = random_offsets(rng, 64, 4096, empty=0.0)
     records = np.arange(64, dtype=np.uint64) + 1
     want_n, _ = model(offsets, 32, records, None)
-    sn, ent, xcap = run(offsets, 32, records, None, xcap=want_n[0] - 1)
-    assert (sn == 0).all()
-    assert (ent == -5).all()
+    for rows_bound in (0, 1 << 20):
+        sn, ent, xcap = run(offsets, 32, records, None, xcap=want_n[0] - 1, rows_bound=rows_bound)
+        assert (sn == 0).all()
+        assert (ent == -5).all()

@@ -30,11 +30,13 @@ def log(*a):
 
 
 # The dominant kernel's sources: the GEMM file, the headers whose code it
-# compiles, and the parts of the shared internal header it reads (its
-# argument and tile-entry structs and the tiling constants); the API
-# declarations around them do not change the kernel.
+# compiles, the schedule that orders its tiles (the order decides which
+# weights and rows are still in L2, so its traffic), and the parts of the
+# shared internal header it reads (its argument and tile-entry structs and
+# the tiling constants); the API declarations around them do not change the
+# kernel.
 KERNEL_SOURCES = ["mixture_experts_prefill_amd/csrc/gemm.hip", "mixture_experts_prefill_amd/csrc/lds_dma.h",
-                  "mixture_experts_prefill_amd/csrc/profile.h"]
+                  "mixture_experts_prefill_amd/csrc/profile.h", "mixture_experts_prefill_amd/csrc/csr.hip"]
 KERNEL_HEADER = "mixture_experts_prefill_amd/csrc/moe_internal.h"
 
 

@@ -245,10 +245,11 @@ __global__ void __launch_bounds__(1024) k_csr_small(const uint32_t *__restrict__
 //   2. each XCD gets a contiguous share of those tiles of about one eighth of
 //      the total cost (kTileCostBase + token blocks per tile), so an expert's
 //      tiles share one L2;
-//   3. within its share, an XCD lists its tiles by token blocks, descending,
-//      in expert order within a count, so an expert's full tiles run back to
-//      back (they reuse its weights from L2) and the cheapest tiles fill the
-//      end of the launch;
+//   3. within its share, an XCD lists the shared expert's tiles, then every
+//      tile of the experts with several tiles (in expert order, so an
+//      expert's tiles run back to back and reuse its weights from L2), then
+//      the one-tile experts by token blocks, descending, so the cheapest
+//      tiles fill the end of the launch;
 //   4. every listed tile is written as a TileEntry (rows, expert, record
 //      address) to order[x * xcap + j].
 // sched_n[kSchedXcnt + x] is the number of tiles of XCD x, sched_n[0] the total.
@@ -381,13 +382,17 @@ __device__ __forceinline__ void schedule_body(const uint32_t *offsets, int e0, i
         for (int x = lo; x <= (int)xof[i]; ++x) xstart[x] = i;
     }
     __syncthreads();
-    // 3. wave x lists XCD x's tiles by token blocks, descending, and in
-    // expert order within a count (a stable partition): an expert's full
-    // tiles still run back to back, and the last workgroups an XCD starts
-    // are its cheapest, so the launch ends with short tiles instead of long
-    // ones (the tail was up to one full tile long).  The shared expert's
-    // tiles come first (class 9): its rows are dense and, in small chunks,
-    // its tiles stream far more weight bytes than a routed tile.
+    // 3. wave x lists XCD x's tiles by class, descending, and in tile order
+    // within a class (a stable partition).  The shared expert's tiles come
+    // first (class 9): its rows are dense and, in small chunks, its tiles
+    // stream far more weight bytes than a routed tile.  Every tile of an
+    // expert with several tiles takes class 4, so the expert's tiles, its
+    // last partial one included, run back to back while its weights are in
+    // the XCD's L2 (full chunk, against listing partial tiles by their own
+    // token blocks: gate/up fetches 440 instead of 535 MB, down 182 instead
+    // of 230 MB, block 0.455 -> 0.448 ms).  The experts with one tile follow
+    // by token blocks, descending, so the last workgroups an XCD starts are
+    // its cheapest and the launch ends with short tiles.
     // A counting sort without branches: one pass over the XCD's tiles counts
     // each class (a ballot per class), the counts give each class's first
     // position, and a second pass places every tile at its class's position
@@ -395,7 +400,9 @@ __device__ __forceinline__ void schedule_body(const uint32_t *offsets, int e0, i
     static_assert(kMaxBM <= 128, "token-block classes 1-4");
     if (wave < 8) {
         const uint32_t s0 = xstart[wave], s1 = xstart[wave + 1];
-        auto cls_of = [&](uint32_t i) { return i < s1 ? ((int)tex[i] == n_e ? 9 : (int)tbl[i]) : 0; };
+        auto cls_of = [&](uint32_t i) {
+            return i < s1 ? ((int)tex[i] == n_e ? 9 : tne[i] > 1 ? 4 : (int)tbl[i]) : 0;
+        };
         constexpr int kClasses = 5;
         constexpr int kCls[kClasses] = {9, 4, 3, 2, 1};  // listing order
         uint32_t next[kClasses];                         // next free position of each class

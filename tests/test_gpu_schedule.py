@@ -6,8 +6,10 @@ for entry against a plain Python statement of the rule the kernel follows:
   2. tile i (cost 4 + its 32-row token blocks, prefix S_i before it, total C)
      goes to XCD min(7, floor(8 (2 S_i + c_i) / (2 C))): contiguous shares
      of about an eighth of the cost each;
-  3. each XCD lists its tiles by class, descending (the shared segment's
-     tiles first, then 4, 3, 2, 1 token blocks), in tile order within a class;
+  3. each XCD lists its tiles by class, descending, in tile order within a
+     class: the shared segment's tiles (class 9), then every tile of an
+     expert with several tiles (class 4, so an expert's tiles stay
+     together), then the one-tile experts by token blocks (4, 3, 2, 1);
   4. every entry carries (first row, rows, expert, tiles of its expert,
      record address); sched_n[0] = tiles, sched_n[8 + x] = tiles of XCD x.
 
@@ -36,8 +38,9 @@ def model(offsets, bm, records, shared):
         ne = (n + bm - 1) // bm
         for j in range(ne):
             rows = min(bm, n - j * bm)
-            tiles.append(dict(p0=p0 + j * bm, n=rows, expert=e, tiles=ne, rec=rec, tb=(rows + 31) // 32,
-                              cls=9 if (shared is not None and e == E) else (rows + 31) // 32))
+            tb = (rows + 31) // 32
+            cls = 9 if (shared is not None and e == E) else 4 if ne > 1 else tb
+            tiles.append(dict(p0=p0 + j * bm, n=rows, expert=e, tiles=ne, rec=rec, tb=tb, cls=cls))
     T = len(tiles)
     C = sum(COST_BASE + t["tb"] for t in tiles)
     S = 0

@@ -253,7 +253,12 @@ static moe_status fused_gemms(GemmArgs a, int bm, const moe_layout *L, int t, in
                               const uint32_t *csr_pos, const float *csr_w, float *out, int accumulate,
                               const float *g, bool shared, hipStream_t s, const moe_next_norm *nn = nullptr) {
     const size_t Q = (size_t)t * (k + (shared ? 1 : 0));
-    a.max_tiles = (int)(Q / bm + (size_t)E + 2);
+    // With t <= bm every non-empty expert, and the shared segment, is a single
+    // tile: the tighter bound shrinks the grid to the workgroups that can
+    // have work (decode-shaped chunk: 6336 -> 1152 gate/up workgroups
+    // launched; block 0.1588 -> 0.1575 and 0.1562 -> 0.1559 ms on two boxes,
+    // t = 1: 0.0549 -> 0.0541 ms).
+    a.max_tiles = t <= bm ? std::min(E, t * k) + (shared ? 1 : 0) : (int)(Q / bm + (size_t)E + 2);
     a.w_off = L->gate_w;
     a.sb_off = L->gate_sb;
     a.w2_off = L->up_w;
@@ -463,7 +468,7 @@ moe_status moe_prefill_experts(const uint16_t *x, int32_t t, int32_t k, int32_t 
     a.hg = reinterpret_cast<uint16_t *>(ws + w.hg);
     a.ye = reinterpret_cast<uint16_t *>(ws + w.ye);
     const int bm = pick_bm(t, k, E, L->inter, L->hidden);
-    a.max_tiles = (int)((size_t)t * k / bm + (size_t)E + 1);
+    a.max_tiles = t <= bm ? std::min(E, t * k) : (int)((size_t)t * k / bm + (size_t)E + 1);
 
     if (ring || host_records) {
         return ring_run(ring, host_records, a, bm, offsets, csr_pos, csr_w, t, k, E, L, out,

@@ -30,13 +30,14 @@ def log(*a):
 
 
 # The dominant kernel's sources: the GEMM file, the headers whose code it
-# compiles, the schedule that orders its tiles (the order decides which
-# weights and rows are still in L2, so its traffic), and the parts of the
-# shared internal header it reads (its argument and tile-entry structs and
-# the tiling constants); the API declarations around them do not change the
-# kernel.
+# compiles, the function that orders its tiles (schedule_body in csr.hip: the
+# order decides which weights and rows are still in L2, so the traffic), and
+# the parts of the shared internal header it reads (its argument and
+# tile-entry structs and the tiling constants); the API declarations and the
+# other kernels around them do not change the GEMM.
 KERNEL_SOURCES = ["mixture_experts_prefill_amd/csrc/gemm.hip", "mixture_experts_prefill_amd/csrc/lds_dma.h",
-                  "mixture_experts_prefill_amd/csrc/profile.h", "mixture_experts_prefill_amd/csrc/csr.hip"]
+                  "mixture_experts_prefill_amd/csrc/profile.h"]
+SCHEDULE_SOURCE = "mixture_experts_prefill_amd/csrc/csr.hip"
 KERNEL_HEADER = "mixture_experts_prefill_amd/csrc/moe_internal.h"
 
 
@@ -55,6 +56,10 @@ def source_hash() -> str:
     for f in KERNEL_SOURCES:
         with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
             h.update(f.encode() + strip(fh.read()).encode())
+    with open(os.path.join(ROOT, SCHEDULE_SOURCE), encoding="utf-8") as fh:
+        sch = strip(fh.read())
+    m = re.search(r"template <int MAXT> __device__ __forceinline__ void schedule_body\(.*?sched_n\[0\] = T; \}", sch)
+    h.update(SCHEDULE_SOURCE.encode() + (m.group(0) if m else sch).encode())
     with open(os.path.join(ROOT, KERNEL_HEADER), encoding="utf-8") as fh:
         hdr = strip(fh.read())
     parts = re.findall(r"struct (?:GemmArgs|TileEntry) \{.*?\};", hdr) + re.findall(r"constexpr int k\w+ = [^;]*;", hdr)

@@ -186,7 +186,8 @@ __device__ __forceinline__ void csr_small_body(const uint32_t *__restrict__ idx,
     __shared__ uint32_t wsum[16];
     const int tid = threadIdx.x;
     const int tiles = (t + TR - 1) / TR;
-    for (int i = tid; i < kCsrSmallTiles * MOE_MAX_EXPERTS; i += 1024) (&mask[0][0])[i] = 0ull;
+    // only the chunk's own row tiles are read below
+    for (int i = tid; i < tiles * MOE_MAX_EXPERTS; i += 1024) (&mask[0][0])[i] = 0ull;
     __syncthreads();
     for (int i = tid; i < t * k; i += 1024) {
         const int r = i / k;

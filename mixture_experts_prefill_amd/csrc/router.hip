@@ -14,6 +14,7 @@
 // adds its partner's copy of them, so after 6 levels lane l holds output l
 // (addition is commutative, so p[a] + p[b] computed on either lane is the
 // same value the tree defines).
+#include "lds_dma.h"
 #include "moe_internal.h"
 #include "topk_row.h"
 
@@ -197,48 +198,57 @@ __global__ void __launch_bounds__(256) k_router_few(const uint16_t *__restrict__
 // per CU, else 16 x 16 with 4 waves of 8 x 8 (64 KB, two per CU), whose 4x
 // more workgroups fill the GPU for mid-sized chunks (t = 512, E = 64:
 // 20.5 -> 12.0 us; at t = 4096, E = 128 the 32 x 32 shape is faster, 47 vs 57 us).
+// W (fp32, used as stored) goes from memory straight into its LDS buffer by
+// DMA one step ahead; only x, which is widened, passes through registers
+// (two steps ahead), so the registers the staging held are free for the
+// compute loop's LDS reads.
 template <int LR, int LE, int WR, int WE>
 __global__ void __launch_bounds__(64 * (LR / WR) * (LE / WE), (LR * LE >= 1024) ? 1 : 2)
 k_router_lds(const uint16_t *__restrict__ x, const float *__restrict__ w, int t, int h, int E,
              float *__restrict__ logits) {
-    constexpr int kThreads = 64 * (LR / WR) * (LE / WE);
-    constexpr int kXSrc = LR * 512;                         // x bytes (bf16) per step
-    constexpr int kXBytes = LR * 1024, kWBytes = LE * 1024; // staged bytes (x as fp32)
+    using namespace lds;
+    constexpr int kWaves = (LR / WR) * (LE / WE);
+    constexpr int kThreads = 64 * kWaves;
+    constexpr int kXBytes = LR * 1024, kWBytes = LE * 1024; // staged bytes per step (x as fp32)
     constexpr int kWavesE = LE / WE;                        // waves along the experts
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2][kXBytes + kWBytes];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // x: LR rows x 32 source chunks of 8 bf16 (16 bytes), kPer per thread;
+    // W: LE rows of 1 KB, one DMA of 64 x 16 bytes each, kWPer per wave.
+    constexpr int kPer = LR * 32 / kThreads, kWPer = LE / kWaves;
+    static_assert(kPer * kThreads == LR * 32 && kWPer * kWaves == LE, "whole chunks per thread / wave");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_x[2][kXBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_w[2][kWBytes];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int e_blocks = (E + LE - 1) / LE;
     const int r0 = (blockIdx.x / e_blocks) * LR, e0 = (blockIdx.x % e_blocks) * LE;
     const int wr = (wave / kWavesE) * WR, we = (wave % kWavesE) * WE;   // this wave's rows / experts
 
-    // Staging: 16-byte source chunks, x first (LR rows x 32 chunks of 8 bf16,
-    // each stored as 32 bytes of fp32) then W (LE x 64).
-    constexpr int kChunks = (kXSrc + kWBytes) / 16, kPer = kChunks / kThreads;
-    static_assert(kChunks % kThreads == 0, "whole chunks per thread");
+    // Rows past t read row t - 1 (computed, never stored), so every load is
+    // unconditional and the compiler's wait counts stay exact.
     const uint8_t *src[kPer];
-    bool ok[kPer];
 #pragma unroll
     for (int c = 0; c < kPer; ++c) {
         const int ch = tid + kThreads * c;
-        if (ch < kXSrc / 16) {
-            const int r = ch >> 5, q = ch & 31;
-            ok[c] = r0 + r < t;
-            src[c] = reinterpret_cast<const uint8_t *>(x + (size_t)min(r0 + r, t - 1) * h) + q * 16;
-        } else {
-            const int cw = ch - kXSrc / 16;
-            const int e = cw >> 6, q = cw & 63;
-            ok[c] = e0 + e < E;
-            src[c] = reinterpret_cast<const uint8_t *>(w + (size_t)min(e0 + e, E - 1) * h) + q * 16;
-        }
+        const int r = ch >> 5, q = ch & 31;
+        src[c] = reinterpret_cast<const uint8_t *>(x + (size_t)min(r0 + r, t - 1) * h) + q * 16;
     }
-    // step s covers elements [256 s, 256 s + 256): x bytes 512 s, W bytes 1024 s
-    auto load = [&](int s, uint4 *v) {
+    // Experts past E read row E - 1: computed, never stored.
+    const i32x4 rw = buffer_rsrc(w);
+    uint32_t wvo[kWPer];
 #pragma unroll
-        for (int c = 0; c < kPer; ++c) {
-            const int ch = tid + kThreads * c;
-            const size_t off = (ch < kXSrc / 16) ? (size_t)s * 512 : (size_t)s * 1024;
-            v[c] = ok[c] ? *reinterpret_cast<const uint4 *>(src[c] + off) : make_uint4(0, 0, 0, 0);
-        }
+    for (int j = 0; j < kWPer; ++j)
+        wvo[j] = (uint32_t)min(e0 + wave * kWPer + j, E - 1) * (uint32_t)h * 4u + (uint32_t)lane * 16u;
+    const uint32_t wl = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(&lds_w[0][0]));
+    // step s covers elements [256 s, 256 s + 256): x bytes 512 s, W bytes 1024 s
+    auto load_x = [&](int s, uint4 *v) {
+#pragma unroll
+        for (int c = 0; c < kPer; ++c)
+            v[c] = *reinterpret_cast<const uint4 *>(src[c] + (size_t)s * 512);
+    };
+    auto load_w = [&](int s) {
+#pragma unroll
+        for (int j = 0; j < kWPer; ++j)
+            dma16(wl + (s & 1) * kWBytes + (wave * kWPer + j) * 1024, wvo[j], rw, (uint32_t)s * 1024u);
     };
 
     constexpr int N = WR * WE;  // outputs of the wave
@@ -247,55 +257,83 @@ k_router_lds(const uint16_t *__restrict__ x, const float *__restrict__ w, int t,
 #pragma unroll
     for (int o = 0; o < N; ++o) p[o] = 0.0f;
 
-    // Staged chunks are loaded two steps ahead into two register sets (the
-    // step's compute is shorter than a load's latency from L2 or HBM), so the
-    // loop is unrolled by two to keep each set in fixed registers.
+    // Issue order: W of step s + 1, then x of step s + 2; so when step s + 1
+    // starts, the compiler's wait for its x registers (everything but the
+    // x loads of s + 2 complete) also covers its W, and wait_vm<kPer>
+    // states it.  The loop is unrolled by two to keep each x register set in
+    // fixed registers.  Past the last step the loads repeat the last step
+    // into the free buffer, so every step waits for the same count.
     uint4 va[kPer], vb[kPer];
     const int steps = h >> 8;
-    load(0, va);
-    if (steps > 1) load(1, vb);
+    load_w(0);
+    load_x(0, va);
+    load_x(min(1, steps - 1), vb);
     auto step = [&](int s, uint4 (&v)[kPer]) {
-        uint8_t *buf = lds[s & 1];
+        uint8_t *xb = lds_x[s & 1];
+        const uint8_t *wb = lds_w[s & 1];
 #pragma unroll
-        for (int c = 0; c < kPer; ++c) {
+        for (int c = 0; c < kPer; ++c) {  // 8 bf16 -> 8 fp32 (exact)
             const int ch = tid + kThreads * c;
-            if (ch < kXSrc / 16) {  // 8 bf16 -> 8 fp32 (exact)
-                const uint4 q = v[c];
-                *reinterpret_cast<float4 *>(buf + ch * 32) = make_float4(bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.y), bf16_hi(q.y));
-                *reinterpret_cast<float4 *>(buf + ch * 32 + 16) = make_float4(bf16_lo(q.z), bf16_hi(q.z), bf16_lo(q.w), bf16_hi(q.w));
-            } else {
-                *reinterpret_cast<uint4 *>(buf + kXBytes + (ch - kXSrc / 16) * 16) = v[c];
-            }
+            const uint4 q = v[c];
+            *reinterpret_cast<float4 *>(xb + ch * 32) = make_float4(bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.y), bf16_hi(q.y));
+            *reinterpret_cast<float4 *>(xb + ch * 32 + 16) = make_float4(bf16_lo(q.z), bf16_hi(q.z), bf16_lo(q.w), bf16_hi(q.w));
         }
-        __syncthreads();
-        if (s + 2 < steps) load(s + 2, v);
+        wait_vm<kPer>();      // this step's W (only the x loads of s + 1 may be in flight)
+        barrier_no_fence();   // x and W of step s are in LDS; buffers of s - 1 are free
+        load_w(min(s + 1, steps - 1));
+        load_x(min(s + 2, steps - 1), v);
         float wv[WE][4];
 #pragma unroll
         for (int j = 0; j < WE; ++j) {
-            const float4 q = *reinterpret_cast<const float4 *>(buf + kXBytes + (we + j) * 1024 + lane * 16);
+            const float4 q = *reinterpret_cast<const float4 *>(wb + (we + j) * 1024 + lane * 16);
             wv[j][0] = q.x;
             wv[j][1] = q.y;
             wv[j][2] = q.z;
             wv[j][3] = q.w;
         }
+        // Rows in groups of four: the LDS reads of group g + 1 are issued
+        // ahead of group g's FMAs, so a read's latency hides behind 4 WE x 4
+        // FMAs instead of being waited for right after its issue.
+        constexpr int G = WR / 4;
+        float4 xq[2][4];
 #pragma unroll
-        for (int i = 0; i < WR; ++i) {
-            const float4 q = *reinterpret_cast<const float4 *>(buf + (wr + i) * 1024 + lane * 16);
-            const float x0 = q.x, x1 = q.y, x2 = q.z, x3 = q.w;
+        for (int i = 0; i < 4; ++i) xq[0][i] = *reinterpret_cast<const float4 *>(xb + (wr + i) * 1024 + lane * 16);
 #pragma unroll
-            for (int j = 0; j < WE; ++j) {
-                float &acc = p[i * WE + j];
-                acc = __builtin_fmaf(x0, wv[j][0], acc);
-                acc = __builtin_fmaf(x1, wv[j][1], acc);
-                acc = __builtin_fmaf(x2, wv[j][2], acc);
-                acc = __builtin_fmaf(x3, wv[j][3], acc);
+        for (int g = 0; g < G; ++g) {
+            if (g + 1 < G) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    xq[(g + 1) & 1][i] = *reinterpret_cast<const float4 *>(xb + (wr + 4 * (g + 1) + i) * 1024 + lane * 16);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float4 q = xq[g & 1][i];
+#pragma unroll
+                for (int j = 0; j < WE; ++j) {
+                    float &acc = p[(4 * g + i) * WE + j];
+                    acc = __builtin_fmaf(q.x, wv[j][0], acc);
+                    acc = __builtin_fmaf(q.y, wv[j][1], acc);
+                    acc = __builtin_fmaf(q.z, wv[j][2], acc);
+                    acc = __builtin_fmaf(q.w, wv[j][3], acc);
+                }
+            }
+            if (g + 1 < G) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);        // next group's reads first
+                __builtin_amdgcn_sched_group_barrier(0x002, 16 * WE, 0);  // then this group's FMAs
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     };
-    for (int s = 0; s < steps; s += 2) {
+    // Pairs without a condition inside, so that every entry to the loop head
+    // has the same loads in flight (x of the step in va, then x of the next
+    // in vb) and the compiler waits for va alone.
+    int s = 0;
+    for (; s + 1 < steps; s += 2) {
         step(s, va);
-        if (s + 1 < steps) step(s + 1, vb);
+        step(s + 1, vb);
     }
+    if (s < steps) step(s, va);
+    wait_vm<0>();  // retire the trailing (repeated) loads
 
     // Transposed butterfly over the 64 partials: 6 splitting levels leave
     // N / 64 outputs per lane: output `lane` (N = 64), or outputs 2 lane and

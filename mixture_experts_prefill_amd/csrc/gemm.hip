@@ -146,8 +146,12 @@ struct Stage {
 // and 32, i.e. no bank conflicts for 32-, 64- or 128-bank LDS.
 __device__ __forceinline__ int xswz(int r) { return (r ^ (r >> 3)) & 7; }
 
-template <int MODE, int BM, int WAVES>
-__global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const GemmArgs a) {
+// FEW: a routed launch whose every tile has one or two rows (few_row_launch):
+// only the few-row path, with the waves splitting K, a 3-stage weight ring
+// (46 KB of LDS, three workgroups per CU) and the (tile, feature block)
+// units spread evenly over the XCDs.
+template <int MODE, int BM, int WAVES, bool FEW = false>
+__global__ void __launch_bounds__(64 * WAVES, FEW ? 3 : (WAVES >= 8 ? 1 : 2)) k_gemm(const GemmArgs a) {
     constexpr bool kGateUp = (MODE == GU_GATHER || MODE == GU_DENSE || MODE == GU_PART);
     constexpr bool kPart = (MODE == GU_PART || MODE == DOWN_PART);
     constexpr bool kDense = (MODE == GU_DENSE || MODE == DOWN_OUT || kPart);
@@ -174,7 +178,9 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
     constexpr int EB = (MODE == DOWN_OUT || kPart) ? 4 : 2;
     constexpr int EROW = 32 * EB + 16;
     constexpr int RING = NS * STAGE, EPI = WAVES * 32 * EROW;
-    constexpr int LDS_BYTES = RING > EPI ? RING : EPI;
+    static_assert(!FEW || (BM == 32 && WAVES == 4 && (MODE == GU_GATHER || MODE == DOWN_YE)),
+                  "few-row launches: routed, 32-row tiles, 4 waves");
+    constexpr int LDS_BYTES = FEW ? NS * XSTAGE + 3 * WSTAGE : RING > EPI ? RING : EPI;
     __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[LDS_BYTES];
     // LDS byte address of the ring (wave-uniform, for the DMA's M0).
     const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds_raw));
@@ -189,7 +195,13 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
     // Dense: each XCD runs a contiguous eighth of the (M-tile, feature block)
     // pairs.  Either way an XCD's CUs share the weights and rows in its L2.
     const int n_out = kGateUp ? a.inter : a.hidden;
-    const int nblk = (n_out + FEAT - 1) / FEAT;
+    // Few-row launches: the workgroup's waves split the K steps of one
+    // fragment pair, so a workgroup covers 32 gate/up features (64 down) and
+    // a launch has four times the workgroups streaming weights (each wave's
+    // loop over all of K is bound by its own per-step waits).
+    constexpr bool ksplit = FEW;
+    const int feat_wg = ksplit ? (kGateUp ? 32 : 64) : FEAT;
+    const int nblk = (n_out + feat_wg - 1) / feat_wg;
     const int xcd = blockIdx.x & 7, slot_in_xcd = blockIdx.x >> 3;
     int nb, expert = 0, p0, n, split = 0;
     // Weights that no other tile reads (the expert's only M-tile) load with
@@ -210,6 +222,29 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
         n = min(BM, a.t - p0);
         stream_w = BM == 32 && a.t <= BM;
         rec = static_cast<const uint8_t *>(a.record);
+    } else if (FEW) {
+        // Every (tile, feature block) unit of the XCD lists taken in order,
+        // list after list, a contiguous eighth of them per XCD: whole tiles
+        // per XCD leave some XCDs two tiles and others one when a chunk
+        // touches about as many experts as there are XCDs.
+        const int units = (int)a.sched_n[0] * nblk;
+        const int chunk = (units + 7) >> 3;
+        const int u = xcd * chunk + slot_in_xcd;
+        if (slot_in_xcd >= chunk || u >= units) return;
+        int i = u / nblk, y = 0;
+        nb = u % nblk;
+        for (; y < 7; ++y) {                              // the list that holds tile i
+            const int c = (int)a.sched_n[kSchedXcnt + y];
+            if (i < c) break;
+            i -= c;
+        }
+        const TileEntry te = a.order[y * a.xcap + i];
+        expert = te.expert;
+        p0 = te.p0;
+        n = te.n;
+        stream_w = true;
+        rec = static_cast<const uint8_t *>(te.rec);
+        if (!rec) return;
     } else {
         // The entry is loaded together with the count (the grid never
         // exceeds xcap slots per XCD, so the read stays inside the list).
@@ -233,10 +268,11 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
     const int kbase = split * nk;
     const int obs = n_out >> 5;
     int ob[2];
+    const int fblk = ksplit ? nb : nb * WAVES + wave;   // this wave's fragment pair
     if (kGateUp) {
-        ob[0] = ob[1] = nb * WAVES + wave;               // gate and up of the same 32 features
+        ob[0] = ob[1] = fblk;                            // gate and up of the same 32 features
     } else {
-        ob[0] = (nb * WAVES + wave) * 2;                 // two adjacent 32-feature blocks
+        ob[0] = fblk * 2;                                // two adjacent 32-feature blocks
         ob[1] = ob[0] + 1;
     }
     const bool live0 = ob[0] < obs, live1 = ob[1] < obs;
@@ -554,6 +590,14 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
         asm volatile("v_mov_b32 %0, 0x3f803f80" : "=v"(one2));     // bf16 1.0 pair
         const int half = lane >> 5;
         const int rowb = K * 2;                           // bytes of one staged row
+        // K steps [k0, k0 + kw) of this wave (all of them unless the waves
+        // split K; the host then picks step counts that divide by 4).  The
+        // first NSG steps go out before the rows: their addresses need only
+        // the tile entry, the rows' need the row ids loaded first.
+        const int kw = ksplit ? nk / WAVES : nk;
+        const int k0 = ksplit ? wave * kw : 0;
+        #pragma unroll
+        for (int j = 0; j < NSG; ++j) issue_g(k0 + min(j, kw - 1), j);
         {
             // rows r < NR at LDS byte r * rowb; 1 KB DMA chunks, lane i of
             // chunk j carries bytes 1024 j + 16 i (rows are 128-byte multiples,
@@ -589,25 +633,23 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
         for (int f = 0; f < 2; ++f)
             #pragma unroll
             for (int r = 0; r < NR; ++r) acc[f][r] = 0.0f;
-        #pragma unroll
-        for (int j = 0; j < NSG; ++j) issue_g(min(j, nk - 1), j);
-        // the rows (issued first) and step 0 of this wave have landed; the
-        // barrier makes every wave's rows visible
-        wait_vm<(NSG - 1) * VMW>();
+        // every wave's rows and this wave's first NSG steps have landed; the
+        // barrier makes the rows visible to all waves
+        wait_vm<0>();
         barrier_no_fence();
         Stage cur;
         uint4 xc[NR][4];
         read_g(0, cur);
-        read_x(0, xc);
-        for (int kb = 0; kb < nk; ++kb) {
-            // step kb+1 of this wave has landed; its reads of slot kb are done
+        read_x(k0, xc);
+        for (int j = 0; j < kw; ++j) {
+            // local step j+1 of this wave has landed; its reads of slot j are done
             wait_vm<(NSG - 2) * VMW>();
             __builtin_amdgcn_s_waitcnt((15 << 0) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
-            issue_g(min(kb + NSG, nk - 1), kb + NSG);
+            issue_g(k0 + min(j + NSG, kw - 1), j + NSG);
             Stage nxt;
             uint4 xn[NR][4];
-            read_g(kb + 1, nxt);                          // past the end: a reloaded step, unused
-            read_x(min(kb + 1, nk - 1), xn);
+            read_g(j + 1, nxt);                           // past the end: a reloaded step, unused
+            read_x(k0 + min(j + 1, kw - 1), xn);
             #pragma unroll
             for (int r = 0; r < NR; ++r) {
                 float X = 0.0f;
@@ -646,6 +688,30 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
                                                                  false, false);
                 acc[f][r] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
             }
+        if (ksplit) {
+            // the waves' K ranges, added in wave order by wave 0: every wave
+            // is done with its ring (loads retired above) and the staged
+            // rows, so the row area holds the partial sums
+            float *red = reinterpret_cast<float *>(lds_raw);   // [WAVES][2][NR][32]
+            barrier_no_fence();
+            if (lane < 32) {
+                #pragma unroll
+                for (int f = 0; f < 2; ++f)
+                    #pragma unroll
+                    for (int r = 0; r < NR; ++r) red[((wave * 2 + f) * NR + r) * 32 + lane] = acc[f][r];
+            }
+            barrier_no_fence();
+            if (wave != 0) return;
+            #pragma unroll
+            for (int f = 0; f < 2; ++f)
+                #pragma unroll
+                for (int r = 0; r < NR; ++r) {
+                    float v = red[(f * NR + r) * 32 + (lane & 31)];
+                    #pragma unroll
+                    for (int w = 1; w < WAVES; ++w) v += red[((w * 2 + f) * NR + r) * 32 + (lane & 31)];
+                    acc[f][r] = v;
+                }
+        }
         if (!live0) return;
         const int feat = lane & 31;
         #pragma unroll
@@ -668,25 +734,29 @@ __global__ void __launch_bounds__(64 * WAVES, WAVES >= 8 ? 1 : 2) k_gemm(const G
         }
     };
     if constexpr (!kDense) {
+        static_assert(BM != 32 || NS * XSTAGE == kFewRowBytes, "few-row staging size known to the host");
         // few rows whose whole K fits in the row ring: the no-MFMA path
-        if (n <= 2 && ((n * K * 2 + 1023) >> 10) * 1024 <= NS * XSTAGE) {
+        // (a few-row launch has only such tiles: n <= t <= 2, rows checked
+        // to fit by the host)
+        if (FEW || (n <= 2 && ((n * K * 2 + 1023) >> 10) * 1024 <= NS * XSTAGE)) {
             if (n == 1) gemv(std::integral_constant<int, 1>{});
             else gemv(std::integral_constant<int, 2>{});
             return;
         }
     }
-
-    const int tbr = (n + 31) >> 5;
-    if constexpr (TB == 4) {
-        if (tbr >= 4) body(std::integral_constant<int, 4>{});
-        else if (tbr == 3) body(std::integral_constant<int, 3>{});
-        else if (tbr == 2) body(std::integral_constant<int, 2>{});
-        else body(std::integral_constant<int, 1>{});
-    } else if constexpr (TB == 2) {
-        if (tbr >= 2) body(std::integral_constant<int, 2>{});
-        else body(std::integral_constant<int, 1>{});
-    } else {
-        body(std::integral_constant<int, 1>{});
+    if constexpr (!FEW) {   // (a discarded branch: no matrix-core path in a few-row launch)
+        const int tbr = (n + 31) >> 5;
+        if constexpr (TB == 4) {
+            if (tbr >= 4) body(std::integral_constant<int, 4>{});
+            else if (tbr == 3) body(std::integral_constant<int, 3>{});
+            else if (tbr == 2) body(std::integral_constant<int, 2>{});
+            else body(std::integral_constant<int, 1>{});
+        } else if constexpr (TB == 2) {
+            if (tbr >= 2) body(std::integral_constant<int, 2>{});
+            else body(std::integral_constant<int, 1>{});
+        } else {
+            body(std::integral_constant<int, 1>{});
+        }
     }
 }
 
@@ -849,10 +919,13 @@ hipError_t launch_waves(const GemmArgs &a, int bm, hipStream_t s, hipEvent_t e0,
     const bool part = (MODE == GU_PART || MODE == DOWN_PART);
     const bool dense = (MODE == GU_DENSE || MODE == DOWN_OUT || part);
     const int n_out = gu ? a.inter : a.hidden;
-    const int feat = gu ? 32 * WAVES : 64 * WAVES;
+    const bool few = (MODE == GU_GATHER || MODE == DOWN_YE) && bm == 32 && few_row_launch(a.t, gu ? a.hidden : a.inter);
+    const int feat = few ? (gu ? 32 : 64) : (gu ? 32 * WAVES : 64 * WAVES);
     const int nblk = (n_out + feat - 1) / feat;
     int grid;
-    if (dense) {
+    if (few) {
+        grid = (int)(8 * (((long)a.max_tiles * nblk + 7) / 8));
+    } else if (dense) {
         // 1-D grid, rounded so every XCD slot of the remap exists
         grid = (((a.t + bm - 1) / bm * nblk * (part ? a.ksplit : 1) + 7) / 8) * 8 + 8;
     } else {
@@ -871,6 +944,12 @@ hipError_t launch_waves(const GemmArgs &a, int bm, hipStream_t s, hipEvent_t e0,
         else
             hipLaunchKernelGGL(kernel, dim3(grid), dim3(threads), 0, s, a);
     };
+    if constexpr ((MODE == GU_GATHER || MODE == DOWN_YE) && WAVES == 4) {
+        if (few) {
+            go(k_gemm<MODE, 32, 4, true>, 256);
+            return hipGetLastError();
+        }
+    }
     switch (bm) {
     case 32:
         if constexpr (WAVES == 4)

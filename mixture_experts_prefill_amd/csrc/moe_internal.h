@@ -125,6 +125,19 @@ struct GemmArgs {
     // (only when shared_rows != 0).
     int shared_rows, shared_p0;
 };
+// Staged-row bytes of the few-row path in 32-row tiles (the row ring of
+// k_gemm<MODE, 32, 4>); the kernel checks that the two agree.
+constexpr int kFewRowBytes = 16384;
+// Whether a routed launch over K inputs (h for gate/up, I for down) of a
+// call of t rows runs as a few-row launch (k_gemm<MODE, 32, 4, true>): every
+// tile then has t <= 2 rows whose whole K fits the row ring, and the waves
+// split the K steps, each keeping at least 16 (with 6 per wave, the down
+// projection of the decode-shaped t = 1 chunk, each workgroup's start-up
+// outweighed the split: 11.5 -> 22 us).
+inline bool few_row_launch(int t, int K) {
+    return t >= 1 && t <= 2 && ((t * K * 2 + 1023) / 1024) * 1024 <= kFewRowBytes && (K / 64) % 4 == 0 &&
+           K / 64 / 4 >= 16;
+}
 
 hipError_t launch_gateup(const GemmArgs &a, int bm, hipStream_t s);
 hipError_t launch_down(const GemmArgs &a, int bm, hipStream_t s);

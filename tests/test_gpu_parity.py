@@ -152,6 +152,8 @@ SWEEP = [
     (18, 4096, 256, 64, 64, 32, 64, False, True), # the row cap with k = 32: 131072 CSR entries
     (22, 4000, 256, 64, 1024, 8, 64, True, False),# 63 CSR tiles (ragged last) with E = 1024 counts each
     (23, 1000, 256, 64, 300, 4, 32, False, False),# 32 x 32 LDS router tiles with ragged rows and experts
+    (24, 2, 4096, 256, 12, 3, 64, True, False),   # few-row gate/up launch (waves split K), two-row tiles
+    (25, 1, 8192, 320, 40, 5, 32, False, True),   # few-row gate/up launch, 32 K steps per wave, gated
 ]
 
 

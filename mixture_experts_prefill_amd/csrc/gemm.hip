@@ -147,9 +147,9 @@ struct Stage {
 __device__ __forceinline__ int xswz(int r) { return (r ^ (r >> 3)) & 7; }
 
 // FEW: a routed launch whose every tile has one or two rows (few_row_launch):
-// only the few-row path, with the waves splitting K, a 3-stage weight ring
-// (46 KB of LDS, three workgroups per CU) and the (tile, feature block)
-// units spread evenly over the XCDs.
+// only the few-row path, with the waves splitting K and a 3-stage weight
+// ring (46 KB of LDS, three workgroups per CU, so an XCD's list of two
+// decode-shaped tiles, 2 x 48 workgroups, runs in one round).
 template <int MODE, int BM, int WAVES, bool FEW = false>
 __global__ void __launch_bounds__(64 * WAVES, FEW ? 3 : (WAVES >= 8 ? 1 : 2)) k_gemm(const GemmArgs a) {
     constexpr bool kGateUp = (MODE == GU_GATHER || MODE == GU_DENSE || MODE == GU_PART);
@@ -222,29 +222,6 @@ __global__ void __launch_bounds__(64 * WAVES, FEW ? 3 : (WAVES >= 8 ? 1 : 2)) k_
         n = min(BM, a.t - p0);
         stream_w = BM == 32 && a.t <= BM;
         rec = static_cast<const uint8_t *>(a.record);
-    } else if (FEW) {
-        // Every (tile, feature block) unit of the XCD lists taken in order,
-        // list after list, a contiguous eighth of them per XCD: whole tiles
-        // per XCD leave some XCDs two tiles and others one when a chunk
-        // touches about as many experts as there are XCDs.
-        const int units = (int)a.sched_n[0] * nblk;
-        const int chunk = (units + 7) >> 3;
-        const int u = xcd * chunk + slot_in_xcd;
-        if (slot_in_xcd >= chunk || u >= units) return;
-        int i = u / nblk, y = 0;
-        nb = u % nblk;
-        for (; y < 7; ++y) {                              // the list that holds tile i
-            const int c = (int)a.sched_n[kSchedXcnt + y];
-            if (i < c) break;
-            i -= c;
-        }
-        const TileEntry te = a.order[y * a.xcap + i];
-        expert = te.expert;
-        p0 = te.p0;
-        n = te.n;
-        stream_w = true;
-        rec = static_cast<const uint8_t *>(te.rec);
-        if (!rec) return;
     } else {
         // The entry is loaded together with the count (the grid never
         // exceeds xcap slots per XCD, so the read stays inside the list).
@@ -923,9 +900,7 @@ hipError_t launch_waves(const GemmArgs &a, int bm, hipStream_t s, hipEvent_t e0,
     const int feat = few ? (gu ? 32 : 64) : (gu ? 32 * WAVES : 64 * WAVES);
     const int nblk = (n_out + feat - 1) / feat;
     int grid;
-    if (few) {
-        grid = (int)(8 * (((long)a.max_tiles * nblk + 7) / 8));
-    } else if (dense) {
+    if (dense) {
         // 1-D grid, rounded so every XCD slot of the remap exists
         grid = (((a.t + bm - 1) / bm * nblk * (part ? a.ksplit : 1) + 7) / 8) * 8 + 8;
     } else {

@@ -175,6 +175,10 @@ __global__ void __launch_bounds__(256) k_csr_place(const uint32_t *__restrict__ 
 constexpr int kCsrSmallTiles = 8;
 // The body, also run by k_csr_schedule; `soff` (LDS, or nullptr) receives a
 // copy of the offsets for the caller's next phase.
+// PRELOAD: the entries come from global memory and are loaded once, all at
+// once; otherwise (the merged decode kernel: from LDS, at most 16 rows) each
+// pass reads them where they are.
+template <bool PRELOAD>
 __device__ __forceinline__ void csr_small_body(const uint32_t *__restrict__ idx,
                                                const float *__restrict__ wts, int t, int k, int E,
                                                uint32_t *__restrict__ offsets,
@@ -186,13 +190,37 @@ __device__ __forceinline__ void csr_small_body(const uint32_t *__restrict__ idx,
     __shared__ uint32_t wsum[16];
     const int tid = threadIdx.x;
     const int tiles = (t + TR - 1) / TR;
+    // The thread's entries i = tid + 1024 j (at most 16: t <= 512, k <= 32);
+    // with PRELOAD loaded once and all at once, so the grouping waits for
+    // memory once rather than once per entry in each of its two passes
+    // (mid chunk, t = 512: block 0.1129 -> 0.1098 ms).
+    constexpr int kPer = kCsrSmallTiles * TR * MOE_MAX_K / 1024;
+    const int n = t * k;
+    uint32_t ev[PRELOAD ? kPer : 1];
+    float wv[PRELOAD ? kPer : 1];
+    if constexpr (PRELOAD) {
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int i = tid + 1024 * j;
+            ev[j] = i < n ? idx[i] : 0xffffffffu;
+            wv[j] = i < n ? wts[i] : 0.0f;
+        }
+    }
     // only the chunk's own row tiles are read below
     for (int i = tid; i < tiles * MOE_MAX_EXPERTS; i += 1024) (&mask[0][0])[i] = 0ull;
     __syncthreads();
-    for (int i = tid; i < t * k; i += 1024) {
-        const int r = i / k;
-        const uint32_t e = idx[i];
-        if (e < (uint32_t)E) atomicOr(&mask[r / TR][e], 1ull << (r % TR));
+    if constexpr (PRELOAD) {
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int i = tid + 1024 * j, r = i / k;
+            if (ev[j] < (uint32_t)E) atomicOr(&mask[r / TR][ev[j]], 1ull << (r % TR));
+        }
+    } else {
+        for (int i = tid; i < n; i += 1024) {
+            const int r = i / k;
+            const uint32_t e = idx[i];
+            if (e < (uint32_t)E) atomicOr(&mask[r / TR][e], 1ull << (r % TR));
+        }
     }
     __syncthreads();
     // expert tid: counts per tile, total, then its segment start
@@ -219,15 +247,20 @@ __device__ __forceinline__ void csr_small_body(const uint32_t *__restrict__ idx,
         if (soff) soff[E] = (uint32_t)(t * k);
     }
     __syncthreads();
-    for (int i = tid; i < t * k; i += 1024) {
+    auto place = [&](int i, uint32_t e, float w) {
         const int r = i / k, tile = r / TR, rr = r % TR;
-        const uint32_t e = idx[i];
-        if (e >= (uint32_t)E) continue;
+        if (e >= (uint32_t)E) return;   // also every preloaded i >= t k
         const unsigned long long below = (rr == 0) ? 0ull : (mask[tile][e] & ((1ull << rr) - 1ull));
         const uint32_t p = base[tile][e] + (uint32_t)__popcll(below);
         rows[p] = (uint32_t)r;
-        csr_w[p] = wts[i];
+        csr_w[p] = w;
         pos[i] = p;
+    };
+    if constexpr (PRELOAD) {
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) place(tid + 1024 * j, ev[j], wv[j]);
+    } else {
+        for (int i = tid; i < n; i += 1024) place(i, idx[i], wts[i]);
     }
 }
 
@@ -237,7 +270,7 @@ __global__ void __launch_bounds__(1024) k_csr_small(const uint32_t *__restrict__
                                                     uint32_t *__restrict__ rows,
                                                     float *__restrict__ csr_w,
                                                     uint32_t *__restrict__ pos) {
-    csr_small_body(idx, wts, t, k, E, offsets, rows, csr_w, pos, nullptr);
+    csr_small_body<true>(idx, wts, t, k, E, offsets, rows, csr_w, pos, nullptr);
 }
 
 // One workgroup builds the M-tile schedule of experts [e0, e1):
@@ -478,7 +511,7 @@ __global__ void __launch_bounds__(1024) k_csr_schedule(const uint32_t *__restric
                                                        TileEntry *__restrict__ order, int xcap,
                                                        SharedSeg sh) {
     __shared__ uint32_t soff[MOE_MAX_EXPERTS + 1];
-    csr_small_body(idx, wts, t, k, E, offsets, rows, csr_w, pos, soff);
+    csr_small_body<true>(idx, wts, t, k, E, offsets, rows, csr_w, pos, soff);
     __syncthreads();
     schedule_body<kSchedSmallTiles>(soff, 0, E, bm, records, sched_n, order, xcap, sh, sched_parallel(t, bm));
 }
@@ -536,7 +569,7 @@ __global__ void __launch_bounds__(1024) k_topk_csr_schedule(const float *__restr
     if (wave < t) topk_row<KPL>(logits, wave, E, k, idx, wts, sidx, swts);
     if (tid < E) srec[tid] = rec;
     __syncthreads();
-    csr_small_body(sidx, swts, t, k, E, offsets, rows, csr_w, pos, soff);
+    csr_small_body<false>(sidx, swts, t, k, E, offsets, rows, csr_w, pos, soff);
     __syncthreads();
     schedule_body<kSchedSmallTiles>(soff, 0, E, bm, srec, sched_n, order, xcap, sh, sched_parallel(t, bm));
 }

@@ -59,19 +59,29 @@ __device__ __forceinline__ uint32_t block_scan_1024(uint32_t v, uint32_t *wsum, 
     return v + before;
 }
 
-// Block of 256 threads per tile of 64 rows.
-__global__ void __launch_bounds__(256) k_csr_count(const uint32_t *__restrict__ idx, int t, int k,
-                                                   int E, uint32_t *__restrict__ hist) {
+// Block of 256 threads per tile of 64 rows.  A thread's entries (at most 8:
+// 64 rows x k <= 32) are loaded before any is used, so the kernel waits for
+// memory once.
+constexpr int kCountThreads = 256, kTileEntriesPer = TR * MOE_MAX_K / kCountThreads;
+__global__ void __launch_bounds__(kCountThreads) k_csr_count(const uint32_t *__restrict__ idx, int t, int k,
+                                                             int E, uint32_t *__restrict__ hist) {
     __shared__ unsigned long long mask[MOE_MAX_EXPERTS];
     const int tile = blockIdx.x;
-    for (int e = threadIdx.x; e < E; e += blockDim.x) mask[e] = 0ull;
-    __syncthreads();
     const int r0 = tile * TR;
     const int nr = min(TR, t - r0);
-    for (int i = threadIdx.x; i < nr * k; i += blockDim.x) {
-        const int r = i / k;
-        const uint32_t e = idx[(size_t)(r0 + r) * k + (i % k)];
-        if (e < (uint32_t)E) atomicOr(&mask[e], 1ull << r);
+    const uint32_t *tidx = idx + (size_t)r0 * k;   // the tile's nr k entries, row-major
+    uint32_t ev[kTileEntriesPer];
+#pragma unroll
+    for (int j = 0; j < kTileEntriesPer; ++j) {
+        const int i = threadIdx.x + kCountThreads * j;
+        ev[j] = i < nr * k ? tidx[i] : 0xffffffffu;
+    }
+    for (int e = threadIdx.x; e < E; e += blockDim.x) mask[e] = 0ull;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kTileEntriesPer; ++j) {
+        const int i = threadIdx.x + kCountThreads * j;
+        if (ev[j] < (uint32_t)E) atomicOr(&mask[ev[j]], 1ull << (i / k));
     }
     __syncthreads();
     const int tiles = gridDim.x;
@@ -135,26 +145,39 @@ __device__ __forceinline__ void csr_place_body(int tile, int tiles, const uint32
                                                const uint32_t *__restrict__ base, uint32_t *__restrict__ rows,
                                                float *__restrict__ csr_w, uint32_t *__restrict__ pos) {
     __shared__ unsigned long long mask[MOE_MAX_EXPERTS];
-    for (int e = threadIdx.x; e < E; e += blockDim.x) mask[e] = 0ull;
-    __syncthreads();
     const int r0 = tile * TR;
     const int nr = min(TR, t - r0);
-    for (int i = threadIdx.x; i < nr * k; i += blockDim.x) {
-        const int r = i / k;
-        const uint32_t e = idx[(size_t)(r0 + r) * k + (i % k)];
-        if (e < (uint32_t)E) atomicOr(&mask[e], 1ull << r);
+    const size_t e0 = (size_t)r0 * k;              // the tile's first entry (row-major)
+    // a thread's entries (at most 8 with 256 threads), loaded together once
+    constexpr int kMaxPer = TR * MOE_MAX_K / 256;
+    uint32_t ev[kMaxPer];
+    float wv[kMaxPer];
+    const int nt = blockDim.x;
+#pragma unroll
+    for (int j = 0; j < kMaxPer; ++j) {
+        const int i = threadIdx.x + nt * j;
+        const bool in = i < nr * k;
+        ev[j] = in ? idx[e0 + i] : 0xffffffffu;
+        wv[j] = in ? wts[e0 + i] : 0.0f;
+    }
+    for (int e = threadIdx.x; e < E; e += blockDim.x) mask[e] = 0ull;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kMaxPer; ++j) {
+        const int i = threadIdx.x + nt * j;
+        if (ev[j] < (uint32_t)E) atomicOr(&mask[ev[j]], 1ull << (i / k));
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < nr * k; i += blockDim.x) {
-        const int r = i / k;
-        const size_t src = (size_t)(r0 + r) * k + (i % k);
-        const uint32_t e = idx[src];
-        if (e >= (uint32_t)E) continue;
+#pragma unroll
+    for (int j = 0; j < kMaxPer; ++j) {
+        const int i = threadIdx.x + nt * j, r = i / k;
+        const uint32_t e = ev[j];
+        if (e >= (uint32_t)E) continue;               // also every i >= nr k
         const unsigned long long below = (r == 0) ? 0ull : (mask[e] & ((1ull << r) - 1ull));
         const uint32_t p = base[(size_t)e * tiles + tile] + (uint32_t)__popcll(below);
         rows[p] = (uint32_t)(r0 + r);
-        csr_w[p] = wts[src];
-        pos[src] = p;
+        csr_w[p] = wv[j];
+        pos[e0 + i] = p;
     }
 }
 

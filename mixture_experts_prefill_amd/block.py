@@ -99,9 +99,14 @@ class MoeBlock:
             self.host_records, self.ring = None, None
             return
         src = records if miss_records is None else miss_records
+        # the streamed records in one pinned buffer, in expert order, so the
+        # ring can copy runs of consecutive experts at once
+        ids = np.nonzero(~resident)[0]
+        self.host_pool = torch.empty((ids.size, src.shape[1]), dtype=torch.uint8).pin_memory()
+        self.host_pool.numpy()[:] = src[ids]
         self.host_records = [None] * E
-        for e in np.nonzero(~resident)[0]:
-            self.host_records[e] = torch.from_numpy(np.ascontiguousarray(src[e])).pin_memory()
+        for i, e in enumerate(ids):
+            self.host_records[e] = self.host_pool[i]
         self.ring_slots = torch.empty((ring_slots, stride), dtype=torch.uint8, device=self.device)
         self.ring = MoeRing(self.L, self.ring_slots, ring_slots, group)
         if miss_records is not None:

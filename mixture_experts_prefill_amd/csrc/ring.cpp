@@ -132,16 +132,33 @@ moe_status ring_run(moe_ring *ring, const void *const *host_records, GemmArgs a,
             }
         }
         // Streamed records: straight into their ring slot, or, in the 2-bit
-        // miss layout, into the slot's staging area (expanded below).
+        // miss layout, into the slot's staging area (expanded below).  A run
+        // of streamed jobs whose host records follow one another (the next
+        // job's record starts where this one ends) goes out as one copy: their
+        // slots follow one another too (a batch's streamed jobs take
+        // consecutive slots and never wrap), and each copy has a fixed cost
+        // on the link that per-record copies pay once per record.
         const uint64_t rec_bytes = st.lowbit ? st.miss.stride : st.stride;
         if (!st.skip_copy)
-            for (int j = j0; j < j1; ++j) {
+            for (int j = j0; j < j1;) {
                 const RingJob &jb = plan.jobs[j];
-                if (!jb.streamed) continue;
+                if (!jb.streamed) {
+                    ++j;
+                    continue;
+                }
                 uint8_t *dst = st.lowbit ? st.staging + (size_t)jb.slot * st.miss.stride
                                          : st.slots + (size_t)jb.slot * st.stride;
-                e = hipMemcpyAsync(dst, host_records[jb.expert], rec_bytes, hipMemcpyHostToDevice, st.copy);
+                const uint8_t *src = static_cast<const uint8_t *>(host_records[jb.expert]);
+                uint64_t bytes = rec_bytes;
+                int jn = j + 1;
+                while (jn < j1 && plan.jobs[jn].streamed && plan.jobs[jn].slot == plan.jobs[jn - 1].slot + 1 &&
+                       static_cast<const uint8_t *>(host_records[plan.jobs[jn].expert]) == src + bytes) {
+                    bytes += rec_bytes;
+                    ++jn;
+                }
+                e = hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, st.copy);
                 if (e != hipSuccess) return hip_fail(e, "experts: ring copy");
+                j = jn;
             }
         e = hipEventRecord(st.fetched[b], st.copy);
         if (e == hipSuccess) e = hipStreamWaitEvent(s, st.fetched[b], 0);

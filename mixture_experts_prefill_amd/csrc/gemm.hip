@@ -375,10 +375,10 @@ __global__ void __launch_bounds__(64 * WAVES, FEW ? 3 : (WAVES >= 8 ? 1 : 2)) k_
         read_w(0, cur);
         bf16x8 af[2], bcur[TBR];
         read_b(0, 0, bcur);
-        {
-            const Deq d0 = deq_consts(cur.sb[0]), d1 = deq_consts(cur.sb[1]);
-            frag(cur, 0, d0, d1, af);
-        }
+        // dequantisation constants of the current K step's two fragments,
+        // formed once (region 3 of the step before forms the next ones)
+        Deq dq0 = deq_consts(cur.sb[0]), dq1 = deq_consts(cur.sb[1]);
+        frag(cur, 0, dq0, dq1, af);
 
         // K step kb: four MFMA steps of K = 16, each a scheduling region of its
         // own.  Region st issues the LDS reads of region st+1's operands (the next
@@ -394,7 +394,7 @@ __global__ void __launch_bounds__(64 * WAVES, FEW ? 3 : (WAVES >= 8 ? 1 : 2)) k_
         // plus an immediate: no per-step address arithmetic on the VALU.
         auto kstep = [&](int kb, auto slot_c) {
             constexpr int SL = decltype(slot_c)::value;   // == kb % NS
-            const Deq d0 = deq_consts(cur.sb[0]), d1 = deq_consts(cur.sb[1]);
+            const Deq d0 = dq0, d1 = dq1;
             Stage nxt;
             #pragma unroll
             for (int st = 0; st < 4; ++st) {
@@ -406,8 +406,9 @@ __global__ void __launch_bounds__(64 * WAVES, FEW ? 3 : (WAVES >= 8 ? 1 : 2)) k_
                 } else {
                     read_w(SL + 1, nxt);                       // past the end: a reloaded step, unused
                     read_b(SL + 1, 0, bnxt);
-                    const Deq e0 = deq_consts(nxt.sb[0]), e1 = deq_consts(nxt.sb[1]);
-                    frag(nxt, 0, e0, e1, af);
+                    dq0 = deq_consts(nxt.sb[0]);
+                    dq1 = deq_consts(nxt.sb[1]);
+                    frag(nxt, 0, dq0, dq1, af);
                 }
                 #pragma unroll
                 for (int b = 0; b < TBR; ++b) {

@@ -81,6 +81,8 @@ def algorithmic(cfg, t, counts, fused=False):
     touched = int((np.asarray(counts) > 0).sum())
     gu_weights = 2 * (h * I // 2 + h * I // cfg.group * 4)   # gate + up codes and scale/bias of one record
     gu_weights_s = 2 * (h * Is // 2 + h * Is // cfg.group * 4)
+    dn_weights = h * I // 2 + h * I // cfg.group * 4         # down codes and scale/bias of one record
+    dn_weights_s = h * Is // 2 + h * Is // cfg.group * 4
     sh = 1.0 if fused else 0.0
     return dict(
         flop_gateup=4.0 * t * k * h * I + sh * 4.0 * t * h * Is,
@@ -88,6 +90,10 @@ def algorithmic(cfg, t, counts, fused=False):
         # expert's when fused), x rows once, SiLU*up written once
         bytes_gateup=touched * gu_weights + sh * gu_weights_s + 2.0 * t * h + 2.0 * t * k * I + sh * 2.0 * t * Is,
         flop_down=2.0 * t * k * h * I + sh * 2.0 * t * h * Is,
+        # down kernel: down weights of the touched experts (and the shared
+        # expert's when fused), SiLU*up read once, ye written once
+        bytes_down=touched * dn_weights + sh * dn_weights_s + 2.0 * t * k * I + sh * 2.0 * t * Is
+                   + 2.0 * t * k * h + sh * 2.0 * t * h,
         flop_shared=(1.0 - sh) * 6.0 * t * h * Is,
         flop_router=2.0 * t * h * E,
         bytes_total=touched * R + Rs + 4.0 * E * h + 2.0 * t * h + 4.0 * t * h,
@@ -96,7 +102,11 @@ def algorithmic(cfg, t, counts, fused=False):
 
 
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
-DOMINANT_KERNEL = "k_gemm<0,"   # the grouped gate/up kernel (any tile height; 4 waves)
+# The dominant kernel: the merged grouped gate/up + down launch where the
+# block uses it (moe_block and moe_prefill_fused, chunks of more than two
+# rows), else the grouped gate/up kernel (any tile height; 4 waves).
+MERGED_KERNEL = "k_gemm_gu_down"
+GATEUP_KERNEL = "k_gemm<0,"
 COPY_PROBE_BYTES = 512 << 20
 READ_PROBE_BYTES = 2 << 30     # read once by the HBM read probe: 8x the MALL
 READ_PROBE_BLOCKS = 16384
@@ -114,12 +124,14 @@ def traffic_for(kernel_key: str):
     return ent.get("bytes_per_launch")
 
 
-def ingest_pmc(fetch_csv: str, write_csv: str, key: str):
+def ingest_pmc(fetch_csv: str, write_csv: str, config: str, separate: bool):
     """Per-launch HBM bytes of the dominant kernel from two rocprofv3 --pmc runs.
 
     Each counter (KiB per dispatch) is scaled by the ratio of known bytes to
     what the same counter reads for the copy probe (a device-to-device copy of
-    COPY_PROBE_BYTES, which reads and writes that many bytes once).
+    COPY_PROBE_BYTES, which reads and writes that many bytes once).  The
+    dominant kernel is the merged gate/up + down launch when the run has it,
+    else the gate/up launch.
     """
     import csv
 
@@ -131,10 +143,13 @@ def ingest_pmc(fetch_csv: str, write_csv: str, key: str):
             vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
         return vals
 
+    merged = any(MERGED_KERNEL in k for k in per_kernel(fetch_csv, "FETCH_SIZE"))
+    kernel = MERGED_KERNEL if merged else GATEUP_KERNEL
+    key = ("experts_" if merged else "gateup_") + config + ("_separate" if separate else "")
     out = {}
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         vals = per_kernel(path, counter)
-        dom = [v for k, vs in vals.items() if DOMINANT_KERNEL in k for v in vs]
+        dom = [v for k, vs in vals.items() if kernel in k for v in vs]
         cp = [v for k, vs in vals.items() if "copyBuffer" in k or "copy" in k.lower() for v in vs
               if v * 1024 > COPY_PROBE_BYTES / 2]
         if not dom or not cp:
@@ -142,7 +157,7 @@ def ingest_pmc(fetch_csv: str, write_csv: str, key: str):
         factor = COPY_PROBE_BYTES / (max(cp) * 1024)
         out[counter] = dict(kib_per_launch=sum(dom) / len(dom), copy_kib=max(cp), factor=factor,
                             bytes_per_launch=sum(dom) / len(dom) * 1024 * factor)
-    entry = dict(kernel=DOMINANT_KERNEL, source_hash=source_hash(),
+    entry = dict(kernel=kernel, source_hash=source_hash(),
                  fetch_bytes=round(out["FETCH_SIZE"]["bytes_per_launch"]),
                  write_bytes=round(out["WRITE_SIZE"]["bytes_per_launch"]),
                  bytes_per_launch=round(out["FETCH_SIZE"]["bytes_per_launch"] + out["WRITE_SIZE"]["bytes_per_launch"]),
@@ -306,7 +321,6 @@ def measure(cfg, args, steps: int, warmup_steps, all_resident: bool = False, sep
         if warmup_steps is not None or time.perf_counter() - w_start >= 0.03:
             break
 
-    dominant = "gateup"
     # The dominant kernel's launches are timed with HIP events attached to
     # them (hipExtLaunchKernel) in every `--time-every`-th timed step: the
     # attached events leave ~5 us of idle time on each side of the kernel, so
@@ -318,7 +332,7 @@ def measure(cfg, args, steps: int, warmup_steps, all_resident: bool = False, sep
     w0 = time.perf_counter()
     e0.record()
     for i in range(steps):
-        mep.moe_profile_set_mask([dominant] if i % args.time_every == 0 else [])
+        mep.moe_profile_set_mask(["gateup", "experts"] if i % args.time_every == 0 else [])
         step(i)
     e1.record()
     torch.cuda.synchronize()
@@ -331,6 +345,14 @@ def measure(cfg, args, steps: int, warmup_steps, all_resident: bool = False, sep
         f"(wall {wall * 1e3 / steps:.3f} ms/step)")
 
     work = algorithmic(cfg, t, counts, fused)
+    # The merged gate/up + down launch ("experts") when the block ran it,
+    # else the gate/up launch.
+    dominant = "experts" if "experts" in prof else "gateup"
+    if dominant == "experts":
+        dom_flop = work["flop_gateup"] + work["flop_down"]
+        dom_bytes = work["bytes_gateup"] + work["bytes_down"]
+    else:
+        dom_flop, dom_bytes = work["flop_gateup"], work["bytes_gateup"]
     dom_ms, dom_n = prof[dominant]
     dom_avg_s = dom_ms / dom_n / 1e3
     # Launches per step: one, except with streamed experts, where the ring
@@ -339,21 +361,27 @@ def measure(cfg, args, steps: int, warmup_steps, all_resident: bool = False, sep
     per_launch = timed_steps / dom_n
     # The kernel is MFMA-bound when its arithmetic intensity exceeds the
     # machine balance (2500 TFLOP/s / 8 TB/s = 312 FLOP/B), else HBM-bound.
-    intensity = work["flop_gateup"] / work["bytes_gateup"]
-    kname = ("k_gemm gate/up (routed experts and the shared expert in one grouped launch, int4 -> bf16 MFMA, "
-             "SiLU*up epilogue)" if fused else "k_gemm gate/up (routed, grouped int4 -> bf16 MFMA, SiLU*up epilogue)")
-    tkey = f"gateup_{cfg.name}" + ("" if fused else "_separate")
+    intensity = dom_flop / dom_bytes
+    if dominant == "experts":
+        kname = ("k_gemm_gu_down: grouped gate/up (SiLU*up epilogue) and down of the routed experts and the "
+                 "shared expert in one launch, int4 -> bf16 MFMA")
+        tkey = f"experts_{cfg.name}"
+    else:
+        kname = ("k_gemm gate/up (routed experts and the shared expert in one grouped launch, int4 -> bf16 MFMA, "
+                 "SiLU*up epilogue)" if fused else
+                 "k_gemm gate/up (routed, grouped int4 -> bf16 MFMA, SiLU*up epilogue)")
+        tkey = f"gateup_{cfg.name}" + ("" if fused else "_separate")
     if intensity >= PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
-        achieved = work["flop_gateup"] * per_launch / dom_avg_s / 1e12
+        achieved = dom_flop * per_launch / dom_avg_s / 1e12
         roofline = {"kernel": kname, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                    "traffic": traffic_for(tkey), "algorithmic": round(work["flop_gateup"] * per_launch),
+                    "traffic": traffic_for(tkey), "algorithmic": round(dom_flop * per_launch),
                     "avg_launch_us": round(dom_avg_s * 1e6, 2), "launches_per_step": round(1 / per_launch, 2)}
     else:
-        achieved = work["bytes_gateup"] * per_launch / dom_avg_s / 1e9
+        achieved = dom_bytes * per_launch / dom_avg_s / 1e9
         roofline = {"kernel": kname, "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                    "traffic": traffic_for(tkey), "algorithmic": round(work["bytes_gateup"] * per_launch),
+                    "traffic": traffic_for(tkey), "algorithmic": round(dom_bytes * per_launch),
                     "avg_launch_us": round(dom_avg_s * 1e6, 2), "launches_per_step": round(1 / per_launch, 2)}
 
     block_flop = work["flop_gateup"] + work["flop_down"] + work["flop_shared"]
@@ -449,7 +477,7 @@ def measure(cfg, args, steps: int, warmup_steps, all_resident: bool = False, sep
         step(i)
     torch.cuda.synchronize()
     ph = mep.moe_profile_end()
-    expert_phases = ("shared_gateup", "shared_down", "gateup", "down", "combine")
+    expert_phases = ("shared_gateup", "shared_down", "gateup", "down", "experts", "combine")
     cs["secs"] = round(step_s, 7)
     cs["gpu_experts_s"] = round(sum(ph[p][0] for p in expert_phases if p in ph) / n_ph / 1e3, 7)
     extra["chunk_stats"] = cs
@@ -529,7 +557,7 @@ def main():
                     help="turn two rocprofv3 --pmc counter_collection.csv files into profiles/traffic.json")
     args = ap.parse_args()
     if args.ingest_pmc:
-        ingest_pmc(*args.ingest_pmc, key=f"gateup_{args.config}" + ("_separate" if args.separate else ""))
+        ingest_pmc(*args.ingest_pmc, config=args.config, separate=args.separate)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the block is built and measured "

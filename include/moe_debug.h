@@ -44,7 +44,8 @@ enum {
     MOE_PHASE_DOWN = 7,        /* routed grouped down */
     MOE_PHASE_COMBINE = 8,     /* weighted combine into out */
     MOE_PHASE_NORM = 9,        /* injection into the residual copies and the next norm */
-    MOE_PHASES = 10
+    MOE_PHASE_EXPERTS = 10,    /* routed grouped gate/up + SiLU*up and down in one launch */
+    MOE_PHASES = 11
 };
 void moe_profile_begin(uint32_t mask);
 int moe_profile_end(double *ms, int64_t *launches);
@@ -69,6 +70,17 @@ void moe_profile_set_mask(uint32_t mask);
 int moe_debug_read_probe(const void *src, size_t bytes, int32_t blocks, uint32_t *sink, void *stream);
 
 /*
+ * Which XCD (accelerator complex die) each workgroup of a launch runs on,
+ * for the test of what the merged gate/up + down launch relies on: a
+ * launch of `blocks` workgroups of 64 threads writes xcc[i] = the hardware
+ * XCC id of workgroup i (u32 [blocks], device).  The merged launch needs
+ * workgroups whose ids agree modulo 8 to share an XCD (and so an L2).
+ * 1 <= blocks <= 1 << 20.  Returns 0, 1 for bad arguments, 5 for a launch
+ * error.
+ */
+int moe_debug_xcc_map(uint32_t *xcc, int32_t blocks, void *stream);
+
+/*
  * The grouped GEMMs' tile schedule alone, for tests: the schedule kernel
  * that moe_prefill_experts and moe_prefill_fused enqueue before their GEMMs,
  * run on a CSR `offsets` [E+1] (device memory, non-decreasing) for experts
@@ -79,7 +91,7 @@ int moe_debug_read_probe(const void *src, size_t bytes, int32_t blocks, uint32_t
  * optional segment of shared_n dense rows at positions shared_p0 .. with
  * record address shared_rec (NULL: none).  Writes sched_n (u32 [16], device:
  * [0] = tiles, [8 + x] = tiles listed for XCD x) and `order` (device,
- * [8][xcap] entries of 32 bytes {int32 p0, n, expert, tiles; u64 rec; u64 0}:
+ * [8][xcap] entries of 32 bytes {int32 p0, n, expert, tiles; u64 rec; u32 done = 0, 0}:
  * XCD x's list from entry x * xcap).  The schedule refuses, on the device, a
  * call whose tiles exceed xcap or its own capacity: it then sets sched_n to
  * zero and writes no entry.  Returns 0, 1 for bad arguments, 5 for a launch

@@ -64,9 +64,10 @@ EXPORTS = ["moe_last_error", "moe_layout_make", "moe_workspace_bytes", "moe_rout
            "moe_prefill_fused", "moe_block", "moe_block_noalloc", "moe_inject_norm", "moe_block_next_norm",
            "moe_layout_make_bits", "moe_ring_set_miss_layout", "moe_residency", "moe_lookahead",
            "moe_block_from_residual", "moe_chunk_stats_fill", "moe_debug_read_probe",
-           "moe_debug_schedule"]
+           "moe_debug_schedule", "moe_debug_xcc_map"]
 NOALLOC_SCRATCH_BYTES = 64 << 20   # MOE_NOALLOC_SCRATCH_BYTES of include/moe.h
-PHASES = ["router", "topk", "csr", "shared_gateup", "shared_down", "schedule", "gateup", "down", "combine", "norm"]
+PHASES = ["router", "topk", "csr", "shared_gateup", "shared_down", "schedule", "gateup", "down", "combine", "norm",
+          "experts"]
 
 
 def lib():
@@ -105,6 +106,8 @@ def lib():
     L.moe_debug_read_probe.restype = ctypes.c_int
     L.moe_debug_schedule.argtypes = [P, I, I, I, P, P, I, I, P, P, I, P]
     L.moe_debug_schedule.restype = ctypes.c_int
+    L.moe_debug_xcc_map.argtypes = [P, I, P]
+    L.moe_debug_xcc_map.restype = ctypes.c_int
     L.moe_lookahead.argtypes = [P, P, I, I, I, I, I, P, P, P, P, P, P, P]
     L.moe_block_from_residual.argtypes = [P, NP, P, I, I, I, LP, P, LP, P, P, P, P, P, P, P, P, P, NP, P, I, P, Z,
                                           P]
@@ -352,6 +355,15 @@ def moe_debug_read_probe(src: torch.Tensor, blocks: int, sink: torch.Tensor, str
     st = lib().moe_debug_read_probe(_ptr(src), nbytes, blocks, _ptr(sink), _stream(stream))
     if st != 0:
         raise MoeError(st, "read probe: bad arguments" if st == 1 else "read probe: launch failed")
+
+
+def moe_debug_xcc_map(blocks: int, device=None, stream=None):
+    """The XCC id of each of `blocks` workgroups of one launch (synchronises)."""
+    xcc = torch.full((blocks,), -1, dtype=torch.int32, device=device or "cuda")
+    st = lib().moe_debug_xcc_map(_ptr(xcc), blocks, _stream(stream))
+    if st != 0:
+        raise MoeError(st, "xcc map: bad arguments" if st == 1 else "xcc map: launch failed")
+    return xcc.cpu().numpy().view("uint32")
 
 
 def moe_debug_schedule(offsets: torch.Tensor, bm: int, rows_bound: int, records: torch.Tensor,

@@ -259,17 +259,24 @@ static moe_status fused_gemms(GemmArgs a, int bm, const moe_layout *L, int t, in
     // launched; block 0.1588 -> 0.1575 and 0.1562 -> 0.1559 ms on two boxes,
     // t = 1: 0.0549 -> 0.0541 ms).
     a.max_tiles = t <= bm ? std::min(E, t * k) + (shared ? 1 : 0) : (int)(Q / bm + (size_t)E + 2);
-    a.w_off = L->gate_w;
-    a.sb_off = L->gate_sb;
-    a.w2_off = L->up_w;
-    a.sb2_off = L->up_sb;
-    hipError_t e = launch_gateup(a, bm, s);
-    if (e != hipSuccess) return hip_fail(e, "experts gate/up");
+    GemmArgs gu = a;
+    gu.w_off = L->gate_w;
+    gu.sb_off = L->gate_sb;
+    gu.w2_off = L->up_w;
+    gu.sb2_off = L->up_sb;
     a.act = a.hg;
     a.w_off = L->down_w;
     a.sb_off = L->down_sb;
-    e = launch_down(a, bm, s);
-    if (e != hipSuccess) return hip_fail(e, "experts down");
+    hipError_t e;
+    if (gateup_down_merged(gu, bm)) {
+        e = launch_gateup_down(gu, a, bm, s);
+        if (e != hipSuccess) return hip_fail(e, "experts gate/up and down");
+    } else {
+        e = launch_gateup(gu, bm, s);
+        if (e != hipSuccess) return hip_fail(e, "experts gate/up");
+        e = launch_down(a, bm, s);
+        if (e != hipSuccess) return hip_fail(e, "experts down");
+    }
     const uint16_t *ys = shared ? a.ye + (size_t)t * k * L->hidden : nullptr;
     if (nn) {
         NextNormArgs n = next_norm_args(nn, t, L->hidden);

@@ -503,6 +503,7 @@ __device__ __forceinline__ void schedule_body(const uint32_t *offsets, int e0, i
         te.expert = e0 + (int)tex[i];
         te.tiles = (int)tne[i];
         te.rec = reinterpret_cast<const void *>(erec[tex[i]]);
+        te.done = 0;
         te.pad2 = 0;
         order[(size_t)x * xcap + (q - xstart[x])] = te;
     }

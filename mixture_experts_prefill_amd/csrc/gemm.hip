@@ -150,8 +150,30 @@ __device__ __forceinline__ int xswz(int r) { return (r ^ (r >> 3)) & 7; }
 // only the few-row path, with the waves splitting K and a 3-stage weight
 // ring (46 KB of LDS, three workgroups per CU, so an XCD's list of two
 // decode-shaped tiles, 2 x 48 workgroups, runs in one round).
+// LDS bytes of one workgroup of k_gemm<MODE, BM, WAVES, FEW> (see gemm_wg).
+template <int MODE, int BM, int WAVES, bool FEW>
+constexpr int gemm_lds_bytes() {
+    constexpr bool part = (MODE == GU_PART || MODE == DOWN_PART);
+    constexpr int XSTAGE = BM * 128, WSTAGE = WAVES * 2 * (1024 + 256), STAGE = XSTAGE + WSTAGE;
+    constexpr int NS = (WAVES == 4 && BM == 128) ? 3 : (4 * STAGE <= 160 * 1024) ? 4 : 3;
+    constexpr int EB = (MODE == DOWN_OUT || part) ? 4 : 2;
+    constexpr int RING = NS * STAGE, EPI = WAVES * 32 * (32 * EB + 16);
+    return FEW ? NS * XSTAGE + 3 * WSTAGE : RING > EPI ? RING : EPI;
+}
+
+// Spin limit of a down workgroup that waits for its tile's gate/up
+// workgroups in the merged launch (k_gemm_gu_down): each poll is an atomic
+// round trip plus a sleep of about 0.3 us, so the limit (tens of ms) is
+// far beyond any one gate/up workgroup's run (well under a millisecond);
+// past it the workgroup goes on without them rather than hold the GPU.
+constexpr int kTileWaitSpins = 1 << 15;
+
+// One workgroup `bid` of a grouped launch.  Returns the index of the tile
+// entry it ran (routed launches), else -1.  With `wait_tile`, before any
+// load of its activation rows it waits until the tile entry's completion
+// count (TileEntry::done, an L2 atomic) reaches a.wait_need.
 template <int MODE, int BM, int WAVES, bool FEW = false>
-__global__ void __launch_bounds__(64 * WAVES, FEW ? 3 : (WAVES >= 8 ? 1 : 2)) k_gemm(const GemmArgs a) {
+__device__ __forceinline__ int gemm_wg(const GemmArgs &a, int bid, uint8_t *lds_raw, bool wait_tile) {
     constexpr bool kGateUp = (MODE == GU_GATHER || MODE == GU_DENSE || MODE == GU_PART);
     constexpr bool kPart = (MODE == GU_PART || MODE == DOWN_PART);
     constexpr bool kDense = (MODE == GU_DENSE || MODE == DOWN_OUT || kPart);
@@ -181,7 +203,7 @@ __global__ void __launch_bounds__(64 * WAVES, FEW ? 3 : (WAVES >= 8 ? 1 : 2)) k_
     static_assert(!FEW || (BM == 32 && WAVES == 4 && (MODE == GU_GATHER || MODE == DOWN_YE)),
                   "few-row launches: routed, 32-row tiles, 4 waves");
     constexpr int LDS_BYTES = FEW ? NS * XSTAGE + 3 * WSTAGE : RING > EPI ? RING : EPI;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[LDS_BYTES];
+    static_assert(LDS_BYTES == gemm_lds_bytes<MODE, BM, WAVES, FEW>(), "one LDS size rule");
     // LDS byte address of the ring (wave-uniform, for the DMA's M0).
     const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds_raw));
 
@@ -202,8 +224,8 @@ __global__ void __launch_bounds__(64 * WAVES, FEW ? 3 : (WAVES >= 8 ? 1 : 2)) k_
     constexpr bool ksplit = FEW;
     const int feat_wg = ksplit ? (kGateUp ? 32 : 64) : FEAT;
     const int nblk = (n_out + feat_wg - 1) / feat_wg;
-    const int xcd = blockIdx.x & 7, slot_in_xcd = blockIdx.x >> 3;
-    int nb, expert = 0, p0, n, split = 0;
+    const int xcd = bid & 7, slot_in_xcd = bid >> 3;
+    int nb, expert = 0, p0, n, split = 0, tix = -1;
     // Weights that no other tile reads (the expert's only M-tile) load with
     // the non-temporal hint in 32-row tiles, the decode-shaped case; with
     // taller tiles the hint measured slower.
@@ -214,7 +236,7 @@ __global__ void __launch_bounds__(64 * WAVES, FEW ? 3 : (WAVES >= 8 ? 1 : 2)) k_
         const int total = per_split * (kPart ? a.ksplit : 1);
         const int chunk = (total + 7) >> 3;
         const int logical = xcd * chunk + slot_in_xcd;
-        if (slot_in_xcd >= chunk || logical >= total) return;
+        if (slot_in_xcd >= chunk || logical >= total) return -1;
         split = logical / per_split;
         const int rest = logical % per_split;
         nb = rest % nblk;
@@ -225,15 +247,16 @@ __global__ void __launch_bounds__(64 * WAVES, FEW ? 3 : (WAVES >= 8 ? 1 : 2)) k_
     } else {
         // The entry is loaded together with the count (the grid never
         // exceeds xcap slots per XCD, so the read stays inside the list).
-        const TileEntry te = a.order[xcd * a.xcap + slot_in_xcd / nblk];
-        if (slot_in_xcd >= (int)a.sched_n[kSchedXcnt + xcd] * nblk) return;
+        tix = xcd * a.xcap + slot_in_xcd / nblk;
+        const TileEntry te = a.order[tix];
+        if (slot_in_xcd >= (int)a.sched_n[kSchedXcnt + xcd] * nblk) return -1;
         nb = slot_in_xcd % nblk;
         expert = te.expert;
         p0 = te.p0;
         n = te.n;
         stream_w = BM == 32 && te.tiles == 1;
         rec = static_cast<const uint8_t *>(te.rec);
-        if (!rec) return;   // a used expert left without a record: no read of address 0
+        if (!rec) return -1;   // a used expert left without a record: no read of address 0
     }
     (void)expert;
 
@@ -711,6 +734,27 @@ __global__ void __launch_bounds__(64 * WAVES, FEW ? 3 : (WAVES >= 8 ? 1 : 2)) k_
             }
         }
     };
+    if (!kDense && wait_tile) {
+        // The tile's rows come from the gate/up workgroups of the same XCD
+        // list entry, which ran on this XCD (workgroup i goes to XCD i mod 8
+        // and the merged launch keeps each tile's producers and consumers on
+        // one residue), so their stores sit in this XCD's L2; once the count
+        // is complete only this CU's vector L1 may hold stale lines.
+        // The count is read with an atomic add of a.wait_zero (0, unknown to
+        // the compiler), so the read is a read-modify-write performed where
+        // the gate/up workgroups' additions are, never a plain load.
+        if (tid == 0) {
+            uint32_t *done = const_cast<uint32_t *>(&a.order[tix].done);
+            for (int i = 0; i < kTileWaitSpins; ++i) {
+                if (__hip_atomic_fetch_add(done, (uint32_t)a.wait_zero, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >=
+                    (uint32_t)a.wait_need)
+                    break;
+                __builtin_amdgcn_s_sleep(10);
+            }
+        }
+        __syncthreads();
+        asm volatile("buffer_inv sc0" ::: "memory");
+    }
     if constexpr (!kDense) {
         static_assert(BM != 32 || NS * XSTAGE == kFewRowBytes, "few-row staging size known to the host");
         // few rows whose whole K fits in the row ring: the no-MFMA path
@@ -719,7 +763,7 @@ __global__ void __launch_bounds__(64 * WAVES, FEW ? 3 : (WAVES >= 8 ? 1 : 2)) k_
         if (FEW || (n <= 2 && ((n * K * 2 + 1023) >> 10) * 1024 <= NS * XSTAGE)) {
             if (n == 1) gemv(std::integral_constant<int, 1>{});
             else gemv(std::integral_constant<int, 2>{});
-            return;
+            return tix;
         }
     }
     if constexpr (!FEW) {   // (a discarded branch: no matrix-core path in a few-row launch)
@@ -735,6 +779,44 @@ __global__ void __launch_bounds__(64 * WAVES, FEW ? 3 : (WAVES >= 8 ? 1 : 2)) k_
         } else {
             body(std::integral_constant<int, 1>{});
         }
+    }
+    return tix;
+}
+
+template <int MODE, int BM, int WAVES, bool FEW = false>
+__global__ void __launch_bounds__(64 * WAVES, FEW ? 3 : (WAVES >= 8 ? 1 : 2)) k_gemm(const GemmArgs a) {
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[gemm_lds_bytes<MODE, BM, WAVES, FEW>()];
+    gemm_wg<MODE, BM, WAVES, FEW>(a, blockIdx.x, lds_raw, false);
+}
+
+// The routed gate/up and down projections in one launch: workgroups
+// [0, g1) run the gate/up grid, the rest the down grid over the same tile
+// lists.  A gate/up workgroup, once its SiLU*up rows are stored, adds one
+// to its tile entry's count; a down workgroup waits for the count of its
+// tile to reach the tile's number of gate/up workgroups.  Workgroups reach
+// each XCD in ascending order, so every gate/up workgroup of an XCD is
+// dispatched before its first down workgroup, which therefore only fills
+// slots the gate/up launch would have left idle at its end; g1 is a
+// multiple of 8, so a tile's down workgroups run on the XCD of its gate/up
+// workgroups and read their rows from that XCD's L2.
+template <int BM>
+__global__ void __launch_bounds__(256, 2) k_gemm_gu_down(const GemmArgs gu, const GemmArgs dn, int g1) {
+    constexpr int kLds = gemm_lds_bytes<GU_GATHER, BM, 4, false>() > gemm_lds_bytes<DOWN_YE, BM, 4, false>()
+                             ? gemm_lds_bytes<GU_GATHER, BM, 4, false>()
+                             : gemm_lds_bytes<DOWN_YE, BM, 4, false>();
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[kLds];
+    const int bid = blockIdx.x;
+    if (bid < g1) {
+        const int tix = gemm_wg<GU_GATHER, BM, 4, false>(gu, bid, lds_raw, false);
+        if (tix >= 0) {
+            wait_vm<0>();   // this wave's stores of hg have reached the L2
+            __syncthreads();
+            if (threadIdx.x == 0)
+                __hip_atomic_fetch_add(const_cast<uint32_t *>(&gu.order[tix].done), 1u, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+        }
+    } else {
+        gemm_wg<DOWN_YE, BM, 4, false>(dn, bid - g1, lds_raw, true);
     }
 }
 
@@ -891,6 +973,8 @@ __global__ void __launch_bounds__(256) k_shared_gate(const uint16_t *__restrict_
     if (lane == 0) g[r] = 1.0f / (1.0f + expf(-s));
 }
 
+inline int routed_per_xcd(const GemmArgs &a, int bm);
+
 template <int MODE, int WAVES>
 hipError_t launch_waves(const GemmArgs &a, int bm, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     const bool gu = (MODE == GU_GATHER || MODE == GU_DENSE || MODE == GU_PART);
@@ -905,11 +989,7 @@ hipError_t launch_waves(const GemmArgs &a, int bm, hipStream_t s, hipEvent_t e0,
         // 1-D grid, rounded so every XCD slot of the remap exists
         grid = (((a.t + bm - 1) / bm * nblk * (part ? a.ksplit : 1) + 7) / 8) * 8 + 8;
     } else {
-        // An XCD's tiles cost at most an eighth of the total plus one tile,
-        // and each costs at least kTileCostBase + 1, which bounds their count.
-        const long T = a.max_tiles, cmax = kTileCostBase + bm / 32, cmin = kTileCostBase + 1;
-        const long per_xcd = std::min<long>(T, (T * cmax / 8 + cmax) / cmin + 1);
-        grid = (int)(8 * per_xcd * nblk);
+        grid = 8 * routed_per_xcd(a, bm) * nblk;
     }
     // hipExtLaunchKernel only when timing events are attached: it leaves an
     // idle gap of a few microseconds before the kernel even without events
@@ -940,6 +1020,14 @@ hipError_t launch_waves(const GemmArgs &a, int bm, hipStream_t s, hipEvent_t e0,
     return hipGetLastError();
 }
 
+// Workgroups per XCD of a routed launch: an XCD's tiles cost at most an
+// eighth of the total plus one tile, and each costs at least
+// kTileCostBase + 1, which bounds their count.
+inline int routed_per_xcd(const GemmArgs &a, int bm) {
+    const long T = a.max_tiles, cmax = kTileCostBase + bm / 32, cmin = kTileCostBase + 1;
+    return (int)std::min<long>(T, (T * cmax / 8 + cmax) / cmin + 1);
+}
+
 template <int MODE>
 hipError_t launch_mode(const GemmArgs &a, int bm, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     // 4 waves (one per SIMD), so two workgroups share a CU and one's
@@ -957,6 +1045,35 @@ hipError_t launch_gateup(const GemmArgs &a, int bm, hipStream_t s) {
     const hipEvent_t e0 = prof.start(), e1 = prof.stop();
     if (a.order) return launch_mode<GU_GATHER>(a, bm, s, e0, e1);
     return a.ksplit > 1 ? launch_mode<GU_PART>(a, bm, s, e0, e1) : launch_mode<GU_DENSE>(a, bm, s, e0, e1);
+}
+
+bool gateup_down_merged(const GemmArgs &a, int bm) {
+    return a.order && (bm == 32 || bm == 64 || bm == 128) && !few_row_launch(a.t, a.hidden) &&
+           !few_row_launch(a.t, a.inter);
+}
+
+hipError_t launch_gateup_down(const GemmArgs &gu, const GemmArgs &dn, int bm, hipStream_t s) {
+    ProfileScope prof(MOE_PHASE_EXPERTS, s, true);
+    const hipEvent_t e0 = prof.start(), e1 = prof.stop();
+    if (!gateup_down_merged(gu, bm)) return hipErrorInvalidValue;
+    const int per_xcd = routed_per_xcd(gu, bm);
+    const int nblk_gu = (gu.inter + 127) / 128, nblk_dn = (dn.hidden + 255) / 256;
+    const int g1 = 8 * per_xcd * nblk_gu, grid = g1 + 8 * per_xcd * nblk_dn;
+    GemmArgs d = dn;
+    d.wait_need = nblk_gu;
+    d.wait_zero = 0;
+    auto go = [&](auto kernel) {
+        if (e0 || e1)
+            hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, s, e0, e1, 0, gu, d, g1);
+        else
+            hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, s, gu, d, g1);
+    };
+    switch (bm) {
+    case 32: go(k_gemm_gu_down<32>); break;
+    case 64: go(k_gemm_gu_down<64>); break;
+    default: go(k_gemm_gu_down<128>); break;
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_down(const GemmArgs &a, int bm, hipStream_t s) {

@@ -54,11 +54,13 @@ hipError_t launch_csr(const uint32_t *idx, const float *wts, int t, int k, int E
 
 // One M-tile of the grouped GEMMs: CSR rows [p0, p0 + n) of `expert`, the
 // expert's record, and the number of M-tiles of the expert's segment (1:
-// this tile is the only reader of the expert's weights).
+// this tile is the only reader of the expert's weights).  `done` counts the
+// tile's finished gate/up workgroups in the merged gate/up + down launch
+// (written 0 by the schedule, then only by L2 atomics).
 struct TileEntry {
     int p0, n, expert, tiles;
     const void *rec;
-    uint64_t pad2;
+    uint32_t done, pad2;
 };
 static_assert(sizeof(TileEntry) == 32, "one 32-byte load per tile");
 
@@ -124,6 +126,10 @@ struct GemmArgs {
     // p >= shared_p0 are the shared expert's rows, x row p - shared_p0
     // (only when shared_rows != 0).
     int shared_rows, shared_p0;
+    // Merged gate/up + down launch: the gate/up workgroups per tile, whose
+    // completion a down workgroup waits for, and a zero the kernel adds
+    // atomically to read the count.
+    int wait_need, wait_zero;
 };
 // Staged-row bytes of the few-row path in 32-row tiles (the row ring of
 // k_gemm<MODE, 32, 4>); the kernel checks that the two agree.
@@ -140,6 +146,10 @@ inline bool few_row_launch(int t, int K) {
 }
 
 hipError_t launch_gateup(const GemmArgs &a, int bm, hipStream_t s);
+// The routed gate/up and down projections in one launch (k_gemm_gu_down),
+// for routed launches that are not few-row launches (gateup_down_merged).
+bool gateup_down_merged(const GemmArgs &a, int bm);
+hipError_t launch_gateup_down(const GemmArgs &gu, const GemmArgs &dn, int bm, hipStream_t s);
 hipError_t launch_down(const GemmArgs &a, int bm, hipStream_t s);
 hipError_t launch_reduce_gu(const float *part, int S, int t, int I, uint16_t *hs, hipStream_t s);
 hipError_t launch_reduce_down(const float *part, int S, int t, int h, const float *gate, float *out,

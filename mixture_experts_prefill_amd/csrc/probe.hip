@@ -1,5 +1,5 @@
-// HBM read probe: the bandwidth a plain streaming read reaches on this
-// device, against which the weight-streaming (decode-shaped) GEMM launches
+// Device probes.  HBM read probe: the bandwidth a plain streaming read
+// reaches on this device, against which the weight-streaming (decode-shaped) GEMM launches
 // are read.  Each thread issues four 16-byte non-temporal loads per
 // iteration of a grid-stride loop and folds them into one word; the word is
 // stored only for one checksum value, so the loads stay but nothing is
@@ -31,7 +31,21 @@ __global__ void __launch_bounds__(256) k_read_probe(const u32x4 *__restrict__ p,
     if (acc == 0x9E3779B9u) sink[blockIdx.x] = acc;
 }
 
+// Each workgroup's hardware XCC id (s_getreg of HW_REG_XCC_ID; its low
+// bits are the die within the partition).
+__global__ void __launch_bounds__(64) k_xcc_map(uint32_t *__restrict__ xcc) {
+    uint32_t id;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(id));
+    if (threadIdx.x == 0) xcc[blockIdx.x] = id & 0xf;
+}
+
 }  // namespace
+
+extern "C" int moe_debug_xcc_map(uint32_t *xcc, int32_t blocks, void *stream) {
+    if (!xcc || blocks < 1 || blocks > (1 << 20)) return 1;
+    hipLaunchKernelGGL(k_xcc_map, dim3((unsigned)blocks), dim3(64), 0, static_cast<hipStream_t>(stream), xcc);
+    return hipGetLastError() == hipSuccess ? 0 : 5;
+}
 
 extern "C" int moe_debug_read_probe(const void *src, size_t bytes, int32_t blocks, uint32_t *sink, void *stream) {
     if (!src || !sink || (reinterpret_cast<uintptr_t>(src) & 15) || (bytes & 15) || blocks < 1 || blocks > 65536)

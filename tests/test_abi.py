@@ -314,6 +314,14 @@ def test_read_probe_validation(lib):
     assert f(P(FAKE), 1 << 20, 65537, P(FAKE), None) == 1
 
 
+def test_xcc_map_validation(lib):
+    """moe_debug_xcc_map refuses bad arguments without launching."""
+    f = lib.moe_debug_xcc_map
+    assert f(None, 8, None) == 1
+    assert f(P(FAKE), 0, None) == 1
+    assert f(P(FAKE), (1 << 20) + 1, None) == 1
+
+
 def test_schedule_debug_validation(lib):
     """moe_debug_schedule refuses bad arguments without launching."""
     f = lib.moe_debug_schedule

@@ -363,9 +363,9 @@ def measure(cfg, args, steps: int, warmup_steps, all_resident: bool = False, sep
     # machine balance (2500 TFLOP/s / 8 TB/s = 312 FLOP/B), else HBM-bound.
     intensity = dom_flop / dom_bytes
     if dominant == "experts":
-        kname = ("k_gemm_gu_down: grouped gate/up (SiLU*up epilogue) and down of the routed experts and the "
-                 "shared expert in one launch, int4 -> bf16 MFMA")
-        tkey = f"experts_{cfg.name}"
+        kname = ("k_gemm_gu_down: grouped gate/up (SiLU*up epilogue) and down of the routed experts"
+                 + (" and the shared expert" if fused else "") + " in one launch, int4 -> bf16 MFMA")
+        tkey = f"experts_{cfg.name}" + ("" if fused else "_separate")
     else:
         kname = ("k_gemm gate/up (routed experts and the shared expert in one grouped launch, int4 -> bf16 MFMA, "
                  "SiLU*up epilogue)" if fused else

@@ -254,7 +254,7 @@ moe_status moe_prefill_experts(const uint16_t *x, int32_t t, int32_t k, int32_t 
                                void *stream);
 
 /*
- * The shared expert and the routed experts in the same two grouped launches
+ * The shared expert and the routed experts in the same grouped launches
  * (experts.rs page, fn pf_experts: the shared expert's qmm/silu_mul over all
  * rows, shared_add_rows, then the routed experts).  The result is that of
  * moe_shared(accumulate) followed by moe_prefill_experts(accumulate = 1) with

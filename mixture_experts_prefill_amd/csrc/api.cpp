@@ -485,17 +485,23 @@ moe_status moe_prefill_experts(const uint16_t *x, int32_t t, int32_t k, int32_t 
     hipError_t e = launch_schedule(offsets, 0, E, bm, t, records, const_cast<uint32_t *>(a.sched_n),
                                    const_cast<TileEntry *>(a.order), a.xcap, s);
     if (e != hipSuccess) return hip_fail(e, "schedule");
-    a.w_off = L->gate_w;
-    a.sb_off = L->gate_sb;
-    a.w2_off = L->up_w;
-    a.sb2_off = L->up_sb;
-    e = launch_gateup(a, bm, s);
-    if (e != hipSuccess) return hip_fail(e, "experts gate/up");
+    GemmArgs gu = a;
+    gu.w_off = L->gate_w;
+    gu.sb_off = L->gate_sb;
+    gu.w2_off = L->up_w;
+    gu.sb2_off = L->up_sb;
     a.act = a.hg;
     a.w_off = L->down_w;
     a.sb_off = L->down_sb;
-    e = launch_down(a, bm, s);
-    if (e != hipSuccess) return hip_fail(e, "experts down");
+    if (gateup_down_merged(gu, bm)) {
+        e = launch_gateup_down(gu, a, bm, s);
+        if (e != hipSuccess) return hip_fail(e, "experts gate/up and down");
+    } else {
+        e = launch_gateup(gu, bm, s);
+        if (e != hipSuccess) return hip_fail(e, "experts gate/up");
+        e = launch_down(a, bm, s);
+        if (e != hipSuccess) return hip_fail(e, "experts down");
+    }
     e = launch_combine(a.ye, csr_pos, csr_w, t, k, L->hidden, out, accumulate, s);
     if (e != hipSuccess) return hip_fail(e, "combine");
     return MOE_OK;

@@ -406,6 +406,30 @@ def test_ring_with_everything_resident(mep):
     assert np.array_equal(a["out"], b["out"])
 
 
+WAIT_CASES = [
+    (31, 256, 8192, 128, 8, 1, 64),   # one gate/up workgroup per tile over 128 K steps; a tile's 32 down workgroups wait
+    (32, 96, 4096, 256, 4, 2, 32),    # three tiles, each of two gate/up and sixteen down workgroups
+]
+
+
+@pytest.mark.parametrize("case", WAIT_CASES, ids=[f"t{c[1]}-h{c[2]}-I{c[3]}-E{c[4]}-k{c[5]}" for c in WAIT_CASES])
+def test_merged_launch_waits(mep, orc, case):
+    """Chunks whose down workgroups reach their tile long before its gate/up
+    workgroups finish (few tiles per XCD, long K): the merged gate/up + down
+    launch (moe_prefill_experts on resident experts) against the oracle and
+    bitwise against the ring's separate gate/up and down launches."""
+    seed, t, h, I, E, k, G = case
+    wl = ms.small_case(seed, t, h, I, E, k, G, centred=True)
+    g = run(mep, wl, path="separate")
+    b = run(mep, wl, force_ring=True, ring_slots=8, group=2)
+    assert np.array_equal(g["out"], b["out"]), "merged launch differs from the two launches"
+    r = orc.block(wl)
+    check_routing(g, r)
+    check_out(g["out"], r["out"])
+    blk = run(mep, wl, path="block")
+    check_out(blk["out"], r["out"])
+
+
 @pytest.mark.parametrize("path", PATHS)
 def test_deterministic(mep, path):
     wl = ms.small_case(11, 200, 512, 128, 16, 4, 64, centred=True)

@@ -146,10 +146,6 @@ struct Stage {
 // and 32, i.e. no bank conflicts for 32-, 64- or 128-bank LDS.
 __device__ __forceinline__ int xswz(int r) { return (r ^ (r >> 3)) & 7; }
 
-// FEW: a routed launch whose every tile has one or two rows (few_row_launch):
-// only the few-row path, with the waves splitting K and a 3-stage weight
-// ring (46 KB of LDS, three workgroups per CU, so an XCD's list of two
-// decode-shaped tiles, 2 x 48 workgroups, runs in one round).
 // LDS bytes of one workgroup of k_gemm<MODE, BM, WAVES, FEW> (see gemm_wg).
 template <int MODE, int BM, int WAVES, bool FEW>
 constexpr int gemm_lds_bytes() {
@@ -172,6 +168,10 @@ constexpr int kTileWaitSpins = 1 << 15;
 // entry it ran (routed launches), else -1.  With `wait_tile`, before any
 // load of its activation rows it waits until the tile entry's completion
 // count (TileEntry::done, an L2 atomic) reaches a.wait_need.
+// FEW: a routed launch whose every tile has one or two rows (few_row_launch):
+// only the few-row path, with the waves splitting K and a 3-stage weight
+// ring (46 KB of LDS, three workgroups per CU, so an XCD's list of two
+// decode-shaped tiles, 2 x 48 workgroups, runs in one round).
 template <int MODE, int BM, int WAVES, bool FEW = false>
 __device__ __forceinline__ int gemm_wg(const GemmArgs &a, int bid, uint8_t *lds_raw, bool wait_tile) {
     constexpr bool kGateUp = (MODE == GU_GATHER || MODE == GU_DENSE || MODE == GU_PART);

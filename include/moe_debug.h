@@ -81,6 +81,21 @@ int moe_debug_read_probe(const void *src, size_t bytes, int32_t blocks, uint32_t
 int moe_debug_xcc_map(uint32_t *xcc, int32_t blocks, void *stream);
 
 /*
+ * The wait of the merged gate/up + down launch, for tests of its give-up
+ * path.  A down workgroup polls its tile's completion count (an atomic round
+ * trip and a short sleep per poll) at most `spins` times (0: the default of
+ * 32768, tens of milliseconds); if the count is still short it writes bf16
+ * NaN over its rows and features of the down output instead of computing
+ * them, so the block's output shows the failure.  extra = 1 makes every
+ * down workgroup wait for one completion more than its tile can reach,
+ * which forces that path (with a small `spins`, a launch still ends in
+ * well under a second); 0 is normal operation.  Applies to launches enqueued
+ * after the call, process-wide.  0 <= spins <= 32768, extra 0 or 1.  Returns
+ * 0, or 1 for bad arguments.
+ */
+int moe_debug_tile_wait(int32_t spins, int32_t extra);
+
+/*
  * The grouped GEMMs' tile schedule alone, for tests: the schedule kernel
  * that moe_prefill_experts and moe_prefill_fused enqueue before their GEMMs,
  * run on a CSR `offsets` [E+1] (device memory, non-decreasing) for experts

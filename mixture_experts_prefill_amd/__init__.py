@@ -64,7 +64,7 @@ EXPORTS = ["moe_last_error", "moe_layout_make", "moe_workspace_bytes", "moe_rout
            "moe_prefill_fused", "moe_block", "moe_block_noalloc", "moe_inject_norm", "moe_block_next_norm",
            "moe_layout_make_bits", "moe_ring_set_miss_layout", "moe_residency", "moe_lookahead",
            "moe_block_from_residual", "moe_chunk_stats_fill", "moe_debug_read_probe",
-           "moe_debug_schedule", "moe_debug_xcc_map"]
+           "moe_debug_schedule", "moe_debug_xcc_map", "moe_debug_tile_wait"]
 NOALLOC_SCRATCH_BYTES = 64 << 20   # MOE_NOALLOC_SCRATCH_BYTES of include/moe.h
 PHASES = ["router", "topk", "csr", "shared_gateup", "shared_down", "schedule", "gateup", "down", "combine", "norm",
           "experts"]
@@ -108,6 +108,8 @@ def lib():
     L.moe_debug_schedule.restype = ctypes.c_int
     L.moe_debug_xcc_map.argtypes = [P, I, P]
     L.moe_debug_xcc_map.restype = ctypes.c_int
+    L.moe_debug_tile_wait.argtypes = [I, I]
+    L.moe_debug_tile_wait.restype = ctypes.c_int
     L.moe_lookahead.argtypes = [P, P, I, I, I, I, I, P, P, P, P, P, P, P]
     L.moe_block_from_residual.argtypes = [P, NP, P, I, I, I, LP, P, LP, P, P, P, P, P, P, P, P, P, NP, P, I, P, Z,
                                           P]
@@ -364,6 +366,14 @@ def moe_debug_xcc_map(blocks: int, device=None, stream=None):
     if st != 0:
         raise MoeError(st, "xcc map: bad arguments" if st == 1 else "xcc map: launch failed")
     return xcc.cpu().numpy().view("uint32")
+
+
+def moe_debug_tile_wait(spins: int = 0, extra: int = 0):
+    """Poll limit and forced shortfall of the merged launch's tile wait
+    (0, 0: normal operation); see moe_debug_tile_wait in moe_debug.h."""
+    st = lib().moe_debug_tile_wait(spins, extra)
+    if st != 0:
+        raise MoeError(st, "tile wait: bad arguments")
 
 
 def moe_debug_schedule(offsets: torch.Tensor, bm: int, rows_bound: int, records: torch.Tensor,

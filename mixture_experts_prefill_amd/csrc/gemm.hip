@@ -32,6 +32,7 @@
 // dense rows (moe_prefill_fused), and tiles of one or two rows take a
 // matrix-core-free path (see gemv below).
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include <hip/hip_ext.h>
@@ -160,8 +161,11 @@ constexpr int gemm_lds_bytes() {
 // Spin limit of a down workgroup that waits for its tile's gate/up
 // workgroups in the merged launch (k_gemm_gu_down): each poll is an atomic
 // round trip plus a sleep of about 0.3 us, so the limit (tens of ms) is
-// far beyond any one gate/up workgroup's run (well under a millisecond);
-// past it the workgroup goes on without them rather than hold the GPU.
+// far beyond any one gate/up workgroup's run (well under a millisecond).
+// Past it the workgroup does not hold the GPU any longer: it writes NaN in
+// place of its outputs, so that a wait that never completes shows in the
+// block's output instead of leaving plausible values computed from rows
+// that were not ready.
 constexpr int kTileWaitSpins = 1 << 15;
 
 // One workgroup `bid` of a grouped launch.  Returns the index of the tile
@@ -734,7 +738,7 @@ __device__ __forceinline__ int gemm_wg(const GemmArgs &a, int bid, uint8_t *lds_
             }
         }
     };
-    if (!kDense && wait_tile) {
+    if (MODE == DOWN_YE && wait_tile) {
         // The tile's rows come from the gate/up workgroups of the same XCD
         // list entry, which ran on this XCD (workgroup i goes to XCD i mod 8
         // and the merged launch keeps each tile's producers and consumers on
@@ -743,16 +747,29 @@ __device__ __forceinline__ int gemm_wg(const GemmArgs &a, int bid, uint8_t *lds_
         // The count is read with an atomic add of a.wait_zero (0, unknown to
         // the compiler), so the read is a read-modify-write performed where
         // the gate/up workgroups' additions are, never a plain load.
+        __shared__ int gave_up;
         if (tid == 0) {
             uint32_t *done = const_cast<uint32_t *>(&a.order[tix].done);
-            for (int i = 0; i < kTileWaitSpins; ++i) {
+            int ready = 0;
+            for (int i = 0; i < a.wait_spins; ++i) {
                 if (__hip_atomic_fetch_add(done, (uint32_t)a.wait_zero, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >=
-                    (uint32_t)a.wait_need)
+                    (uint32_t)a.wait_need) {
+                    ready = 1;
                     break;
+                }
                 __builtin_amdgcn_s_sleep(10);
             }
+            gave_up = !ready;
         }
         __syncthreads();
+        if (gave_up) {
+            // bf16 quiet NaN over this workgroup's rows and features of ye
+            const int c0 = nb * feat_wg, nc = min(feat_wg, n_out - c0);
+            if constexpr (MODE == DOWN_YE)
+                for (int i = tid; i < n * nc; i += 64 * WAVES)
+                    a.ye[(size_t)(p0 + i / nc) * n_out + c0 + i % nc] = 0x7fc0;
+            return tix;
+        }
         asm volatile("buffer_inv sc0" ::: "memory");
     }
     if constexpr (!kDense) {
@@ -975,6 +992,9 @@ __global__ void __launch_bounds__(256) k_shared_gate(const uint16_t *__restrict_
 
 inline int routed_per_xcd(const GemmArgs &a, int bm);
 
+// moe_debug_tile_wait's settings (host side, process-wide).
+std::atomic<int> g_wait_spins{0}, g_wait_extra{0};
+
 template <int MODE, int WAVES>
 hipError_t launch_waves(const GemmArgs &a, int bm, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     const bool gu = (MODE == GU_GATHER || MODE == GU_DENSE || MODE == GU_PART);
@@ -1040,6 +1060,11 @@ hipError_t launch_mode(const GemmArgs &a, int bm, hipStream_t s, hipEvent_t e0, 
 
 }  // namespace
 
+void tile_wait_debug(int *spins, int *extra) {
+    *spins = g_wait_spins.load(std::memory_order_relaxed);
+    *extra = g_wait_extra.load(std::memory_order_relaxed);
+}
+
 hipError_t launch_gateup(const GemmArgs &a, int bm, hipStream_t s) {
     ProfileScope prof(a.order ? MOE_PHASE_GATEUP : MOE_PHASE_SHARED_GU, s, true);
     const hipEvent_t e0 = prof.start(), e1 = prof.stop();
@@ -1060,8 +1085,11 @@ hipError_t launch_gateup_down(const GemmArgs &gu, const GemmArgs &dn, int bm, hi
     const int nblk_gu = (gu.inter + 127) / 128, nblk_dn = (dn.hidden + 255) / 256;
     const int g1 = 8 * per_xcd * nblk_gu, grid = g1 + 8 * per_xcd * nblk_dn;
     GemmArgs d = dn;
-    d.wait_need = nblk_gu;
+    int spins = 0, extra = 0;
+    tile_wait_debug(&spins, &extra);
+    d.wait_need = nblk_gu + extra;
     d.wait_zero = 0;
+    d.wait_spins = spins > 0 ? spins : kTileWaitSpins;
     auto go = [&](auto kernel) {
         if (e0 || e1)
             hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, s, e0, e1, 0, gu, d, g1);
@@ -1121,3 +1149,10 @@ hipError_t launch_combine(const uint16_t *ye, const uint32_t *pos, const float *
 }
 
 }  // namespace moe
+
+extern "C" int moe_debug_tile_wait(int32_t spins, int32_t extra) {
+    if (spins < 0 || spins > moe::kTileWaitSpins || extra < 0 || extra > 1) return 1;
+    moe::g_wait_spins.store(spins, std::memory_order_relaxed);
+    moe::g_wait_extra.store(extra, std::memory_order_relaxed);
+    return 0;
+}

@@ -127,10 +127,16 @@ struct GemmArgs {
     // (only when shared_rows != 0).
     int shared_rows, shared_p0;
     // Merged gate/up + down launch: the gate/up workgroups per tile, whose
-    // completion a down workgroup waits for, and a zero the kernel adds
-    // atomically to read the count.
-    int wait_need, wait_zero;
+    // completion a down workgroup waits for, a zero the kernel adds
+    // atomically to read the count, and the most polls of the count before
+    // the workgroup gives up (and writes NaN in place of its outputs).
+    int wait_need, wait_zero, wait_spins;
 };
+// Merged launch wait settings for tests (moe_debug_tile_wait): the poll
+// limit (0: the default) and a number added to the count a down workgroup
+// waits for (0; above 0 the wait cannot complete and every down workgroup
+// takes its give-up path).
+void tile_wait_debug(int *spins, int *extra);
 // Staged-row bytes of the few-row path in 32-row tiles (the row ring of
 // k_gemm<MODE, 32, 4>); the kernel checks that the two agree.
 constexpr int kFewRowBytes = 16384;

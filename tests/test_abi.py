@@ -322,6 +322,19 @@ def test_xcc_map_validation(lib):
     assert f(P(FAKE), (1 << 20) + 1, None) == 1
 
 
+def test_tile_wait_validation(lib):
+    """moe_debug_tile_wait accepts its documented range only, and 0, 0
+    restores normal operation."""
+    f = lib.moe_debug_tile_wait
+    assert f(-1, 0) == 1
+    assert f(32769, 0) == 1
+    assert f(0, -1) == 1
+    assert f(0, 2) == 1
+    assert f(16, 1) == 0
+    assert f(32768, 0) == 0
+    assert f(0, 0) == 0
+
+
 def test_schedule_debug_validation(lib):
     """moe_debug_schedule refuses bad arguments without launching."""
     f = lib.moe_debug_schedule

@@ -430,6 +430,30 @@ def test_merged_launch_waits(mep, orc, case):
     check_out(blk["out"], r["out"])
 
 
+def test_merged_launch_gives_up_visibly(mep, orc):
+    """A tile wait that cannot complete, forced from the host (one completion
+    more than a tile's gate/up workgroups can give, at most 16 polls): every
+    down workgroup of the merged launch takes its give-up path and writes NaN
+    in place of its outputs, so every output row is NaN and every launch
+    ends.  The normal settings then give the oracle's result again."""
+    wl = ms.small_case(32, 96, 4096, 256, 4, 2, 32, centred=True)
+    r = orc.block(wl)
+    blk = mep.MoeBlock.from_workload(wl)
+    # zero intermediates: without the give-up writes every output would be finite
+    blk.workspace.zero_()
+    try:
+        mep.moe_debug_tile_wait(16, 1)
+        blk.forward(path="block")
+        torch.cuda.synchronize()
+    finally:
+        mep.moe_debug_tile_wait(0, 0)
+    bad = blk.out.cpu().numpy()
+    del blk
+    assert np.isnan(bad).all(), f"{int(np.isfinite(bad).sum())} outputs finite after a failed wait"
+    good = run(mep, wl, path="block")
+    check_out(good["out"], r["out"])
+
+
 @pytest.mark.parametrize("path", PATHS)
 def test_deterministic(mep, path):
     wl = ms.small_case(11, 200, 512, 128, 16, 4, 64, centred=True)
